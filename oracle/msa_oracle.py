@@ -1,0 +1,189 @@
+"""Plain fp64 CPU oracle for MSA block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product: only
+the tests, the smoke check and the CPU-baseline leg of the benchmark import
+it.  The HIP library never calls it and shares no code with it.
+
+What it computes follows the "MiniMax Sparse Attention" page (paper by Lai
+et al., 2026), section Summary, second paragraph, and section Key points,
+bullet "Benchmark configuration":
+
+  * Index Branch: each key/value block is scored by max-pooling token-level
+    dot products of an index query with the block's index keys;
+  * each GQA group picks its own Top-k blocks, and the block that holds the
+    query's own position is always kept (k counts that block: B_k = 128 and
+    k = 16 give 2,048 attended tokens per query);
+  * Main Branch: exact softmax attention restricted to the kept blocks, for
+    every query head of the group.
+
+Readings where the page is silent (each also listed in the design notes):
+  * queries are the LAST len_q tokens of their sequence, so query i sits at
+    position p = len_kv - len_q + i and sees keys 0..p (causal);
+  * the score is the raw dot product (no scale), pooled over causal keys
+    only; a block with no causal key scores -inf;
+  * selection is per (query token, group); ties go to the lower block
+    index; the output lists the kept blocks in ascending order, padded with
+    -1 when fewer than k blocks are causal;
+  * one softmax over the union of the kept keys (not one per block), scaled
+    by `scale`; LSE is the natural log-sum-exp of the scaled logits;
+  * query head h belongs to group h // (H / G).
+
+Everything runs in float64 on exact upcasts of the inputs.  Loops are over
+rows; the inner steps are numpy matrix products and reductions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of an fp32/bf16/fp64 array (numpy or torch) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: upcast exactly before leaving torch
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _gather_f64(x, keys: np.ndarray, g: int) -> np.ndarray:
+    """Rows `keys` of group g of a [L, G, d] array (numpy or CPU torch), as float64."""
+    if hasattr(x, "detach"):
+        import torch
+        return _f64(x[torch.from_numpy(keys), g, :])
+    return _f64(x[keys, g, :])
+
+
+def query_positions(len_q: int, len_kv: int) -> np.ndarray:
+    """Absolute positions of a sequence's queries: the last len_q tokens."""
+    if len_q > len_kv:
+        raise ValueError("a sequence cannot have more queries than keys")
+    return np.arange(len_kv - len_q, len_kv, dtype=np.int64)
+
+
+def num_blocks(len_kv: int, block_size: int) -> int:
+    return -(-len_kv // block_size)
+
+
+def block_scores(q_idx, k_idx, pos, block_size: int, num_block_cols: int | None = None,
+                 row_chunk: int = 256) -> np.ndarray:
+    """Index Branch block scores of one sequence (Summary, paragraph 2).
+
+    q_idx: [n, G, d_idx] index queries of the rows to score;
+    k_idx: [len_kv, G, d_idx] index keys of the whole sequence;
+    pos:   [n] absolute positions of those rows.
+    Returns S [G, n, NB] with S[g,t,j] = max over keys s of block j with
+    s <= pos[t] of <q_idx[t,g], k_idx[s,g]>, and -inf where block j holds no
+    such key.  NB defaults to ceil(len_kv / B); a larger num_block_cols pads
+    with -inf columns.
+    """
+    q = _f64(q_idx)
+    pos = np.asarray(pos, dtype=np.int64)
+    n, G, _ = q.shape
+    L = k_idx.shape[0]
+    nb = num_blocks(L, block_size)
+    ncol = nb if num_block_cols is None else num_block_cols
+    S = np.full((G, n, ncol), NEG_INF)
+    key_pos = np.arange(nb * block_size)
+    row_chunk = max(1, min(row_chunk, (1 << 24) // max(L, 1)))
+    for g in range(G):
+        kg = _f64(k_idx[:, g, :])
+        for r0 in range(0, n, row_chunk):
+            r1 = min(n, r0 + row_chunk)
+            dots = np.full((r1 - r0, nb * block_size), NEG_INF)
+            dots[:, :L] = q[r0:r1, g, :] @ kg.T           # token-level dot products
+            dots[key_pos[None, :] > pos[r0:r1, None]] = NEG_INF   # causal keys only
+            S[g, r0:r1, :nb] = dots.reshape(r1 - r0, nb, block_size).max(axis=2)
+    return S
+
+
+def select_blocks(S, pos, block_size: int, top_k: int) -> np.ndarray:
+    """Per-group Top-k with the current block always kept (Summary, paragraph 2).
+
+    S: [G, n, NB] block scores; pos: [n].
+    For row t the current block is J = pos[t] // B.  The candidates are the
+    blocks 0..J-1.  If there are at most k-1 of them all are kept; otherwise
+    the k-1 best are kept, ordered by score (higher first) and then by block
+    index (lower first).  J is added.  Returns int32 [G, n, k], ascending,
+    padded with -1.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    G, n, _ = S.shape
+    out = np.full((G, n, top_k), -1, dtype=np.int32)
+    for g in range(G):
+        for t in range(n):
+            J = int(pos[t] // block_size)
+            if J <= top_k - 1:
+                kept = list(range(J + 1))
+            else:
+                cand = np.arange(J)
+                # lexsort: last key is primary -> score descending, then index ascending
+                order = np.lexsort((cand, -S[g, t, :J]))
+                kept = sorted(int(j) for j in cand[order[:top_k - 1]]) + [J]
+            out[g, t, :len(kept)] = kept
+    return out
+
+
+def kept_keys(block_row, p: int, block_size: int) -> np.ndarray:
+    """Key positions attended by a query at position p given its kept blocks."""
+    keys = []
+    for j in np.asarray(block_row):
+        if j < 0:
+            continue
+        s0 = int(j) * block_size
+        s1 = min(s0 + block_size, p + 1)
+        keys.extend(range(s0, s1))
+    return np.array(sorted(keys), dtype=np.int64)
+
+
+def sparse_attention(q, k, v, block_idx, pos, block_size: int, scale: float):
+    """Main Branch: exact softmax attention over the kept blocks (Summary, paragraph 2).
+
+    q: [n, H, d]; k, v: [len_kv, G, d]; block_idx: [G, n, k]; pos: [n].
+    For row t and head h of group g, the key set is every causal key
+    (s <= pos[t]) of the kept blocks of (g, t).  One softmax over that set:
+      z_s = scale * <q[t,h], k[s,g]>,  w = exp(z - max z),
+      out[t,h] = sum_s w_s v[s,g] / sum_s w_s,  lse[t,h] = max z + log sum w.
+    Returns (out [n, H, d], lse [n, H]) in float64.
+    """
+    qf = _f64(q)
+    n, H, d = qf.shape
+    G = block_idx.shape[0]
+    hpg = H // G
+    dv = v.shape[-1]                      # value width (the library requires dv == d)
+    out = np.zeros((n, H, dv))
+    lse = np.full((n, H), NEG_INF)
+    pos = np.asarray(pos, dtype=np.int64)
+    for t in range(n):
+        for g in range(G):
+            keys = kept_keys(block_idx[g, t], int(pos[t]), block_size)
+            if keys.size == 0:
+                continue
+            kg = _gather_f64(k, keys, g)
+            vg = _gather_f64(v, keys, g)
+            for h in range(g * hpg, (g + 1) * hpg):
+                z = scale * (kg @ qf[t, h])
+                m = z.max()
+                w = np.exp(z - m)
+                l = w.sum()
+                out[t, h] = (w @ vg) / l
+                lse[t, h] = m + np.log(l)
+    return out, lse
+
+
+def msa_forward(q, k, v, q_idx, k_idx, len_q: int, len_kv: int, block_size: int,
+                top_k: int, scale: float, rows=None):
+    """Whole path for one sequence: scores -> kept blocks -> attention.
+
+    `rows` optionally restricts the computation to a subset of the
+    sequence's query rows (indices into 0..len_q-1); the inputs are always
+    the whole sequence.  Returns dict(scores, block_idx, out, lse, pos).
+    """
+    pos_all = query_positions(len_q, len_kv)
+    rows = np.arange(len_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    pos = pos_all[rows]
+    S = block_scores(q_idx[rows], k_idx, pos, block_size)
+    idx = select_blocks(S, pos, block_size, top_k)
+    out, lse = sparse_attention(q[rows], k, v, idx, pos, block_size, scale)
+    return {"scores": S, "block_idx": idx, "out": out, "lse": lse, "pos": pos}

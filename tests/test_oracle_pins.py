@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test ties one oracle function to something independent: a hand-worked
+example, an exhaustive search, a closed form, or a different library's
+implementation of a special case (torch's scaled_dot_product_attention in
+float64 on the CPU, scipy's softmax).  A plausible slip in the oracle (a
+dropped causal mask, an off-by-one block edge, a wrong tie order, a
+transposed operand, a per-block instead of joint softmax) fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import msa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_small.json")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------- golden ---
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_golden_scores_and_selection():
+    gd = _golden()
+    k_idx = np.array(gd["k_idx"], float)[:, None, :]
+    q_idx = np.array(gd["q_idx"], float)[:, None, :]
+    pos = O.query_positions(6, 6)
+    S = O.block_scores(q_idx, k_idx, pos, gd["block_size"])
+    exp = np.array([[np.nan if v is None else v for v in row] for row in gd["scores"]])
+    got = S[0]
+    assert np.array_equal(np.isinf(got), np.isnan(exp))
+    assert np.array_equal(got[~np.isinf(got)], exp[~np.isnan(exp)])
+    idx = O.select_blocks(S, pos, gd["block_size"], gd["top_k"])
+    assert idx[0].tolist() == gd["block_idx"]
+
+
+def test_golden_attention_zero_q():
+    gd = _golden()
+    a = gd["attention_zero_q"]
+    pos = O.query_positions(6, 6)
+    idx = np.array(gd["block_idx"], np.int32)[None]
+    q = np.zeros((6, 1, 1))
+    k = np.array(gd["k_idx"], float)[:, None, :1]   # any keys: Q = 0
+    v = np.array(a["v"], float)[:, None, None]
+    out, lse = O.sparse_attention(q, k, v, idx, pos, gd["block_size"], 1.0)
+    assert np.allclose(out[:, 0, 0], a["out"], rtol=0, atol=1e-15)
+    assert np.allclose(lse[:, 0], np.log(a["lse_terms"]), rtol=0, atol=1e-15)
+    for t in range(6):
+        assert O.kept_keys(idx[0, t], t, gd["block_size"]).tolist() == a["kept_keys"][t]
+
+
+def test_golden_attention_pow2():
+    gd = _golden()
+    a = gd["attention_pow2"]
+    pos = O.query_positions(6, 6)
+    idx = np.array(gd["block_idx"], np.int32)[None]
+    q = np.full((6, 1, 1), math.log(2.0))
+    k = np.array(a["k"], float)[:, None, None]
+    v = np.array(a["v"], float)[:, None, None]
+    out, lse = O.sparse_attention(q, k, v, idx, pos, gd["block_size"], 1.0)
+    rows = a["rows"]
+    assert np.allclose(out[rows, 0, 0], a["out"], rtol=0, atol=1e-14)
+    assert np.allclose(lse[rows, 0], np.log(a["lse_terms"]), rtol=0, atol=1e-14)
+
+
+def test_golden_selection_ties():
+    gd = _golden()["selection_ties"]
+    S = np.array(gd["scores"], float)[None, None, :]
+    pos = np.array([gd["position"]])
+    for k, expected in gd["cases"]:
+        assert O.select_blocks(S, pos, gd["block_size"], k)[0, 0].tolist() == expected
+
+
+# ------------------------------------------------------------ block scores ---
+
+def _scores_by_loops(q_idx, k_idx, pos, B):
+    """Brute force with Python loops and math.fsum (no matrix products)."""
+    n, G, _ = q_idx.shape
+    L = k_idx.shape[0]
+    nb = -(-L // B)
+    S = np.full((G, n, nb), -np.inf)
+    for g in range(G):
+        for t in range(n):
+            for s in range(L):
+                if s > pos[t]:
+                    continue
+                dot = math.fsum(float(a) * float(b) for a, b in zip(q_idx[t, g], k_idx[s, g]))
+                j = s // B
+                S[g, t, j] = max(S[g, t, j], dot)
+    return S
+
+
+@pytest.mark.parametrize("L,lq,B,G,di", [(37, 37, 8, 2, 3), (50, 7, 16, 1, 5), (9, 9, 4, 3, 2),
+                                          (64, 64, 64, 1, 4), (65, 1, 8, 2, 3)])
+def test_scores_match_loop_bruteforce(L, lq, B, G, di):
+    rng = np.random.default_rng(L * 100 + B)
+    q = _rand(rng, lq, G, di)
+    k = _rand(rng, L, G, di)
+    pos = O.query_positions(lq, L)
+    S = O.block_scores(q, k, pos, B)
+    ref = _scores_by_loops(q, k, pos, B)
+    assert np.array_equal(np.isinf(S), np.isinf(ref))
+    fin = ~np.isinf(ref)
+    assert np.allclose(S[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_scores_block_one_is_masked_dot_matrix():
+    """B = 1: every block is one key, so S is the causally masked q_idx k_idx^T."""
+    rng = np.random.default_rng(3)
+    q = _rand(rng, 20, 2, 6)
+    k = _rand(rng, 20, 2, 6)
+    pos = O.query_positions(20, 20)
+    S = O.block_scores(q, k, pos, 1)
+    for g in range(2):
+        full = torch.from_numpy(q[:, g]) @ torch.from_numpy(k[:, g]).T   # torch, not numpy
+        full = full.masked_fill(torch.ones(20, 20, dtype=torch.bool).triu(1), -math.inf)
+        fin = ~np.isinf(S[g])
+        assert np.array_equal(fin, ~np.isinf(full.numpy()))
+        assert np.allclose(S[g][fin], full.numpy()[fin], rtol=1e-13, atol=1e-13)
+
+
+def test_scores_invariant_to_key_order_inside_block():
+    rng = np.random.default_rng(4)
+    L, B = 96, 16
+    q = _rand(rng, 8, 2, 4)
+    k = _rand(rng, L, 2, 4)
+    pos = O.query_positions(8, L)          # positions 88..95: blocks 0..4 fully causal
+    S = O.block_scores(q, k, pos, B)
+    k2 = k.copy()
+    for j in range(5):
+        perm = rng.permutation(B)
+        k2[j * B:(j + 1) * B] = k[j * B + perm]
+    S2 = O.block_scores(q, k2, pos, B)
+    assert np.allclose(S, S2, rtol=1e-13, atol=1e-13)
+
+
+def test_scores_pick_max_not_other_pooling():
+    """A single huge key in a block must set the block score (max-pooling)."""
+    L, B = 32, 8
+    q = np.ones((1, 1, 2))
+    k = np.zeros((L, 1, 2))
+    k[13, 0] = [5.0, 5.0]       # block 1
+    k[2, 0] = [-50.0, 0.0]      # block 0: a large negative key must not matter
+    S = O.block_scores(q, k, np.array([31]), B)
+    assert S[0, 0].tolist() == [0.0, 10.0, 0.0, 0.0]
+
+
+# --------------------------------------------------------------- selection ---
+
+def _dominates(S_row, sel, cand):
+    """Every kept candidate beats every dropped one under (score desc, index asc)."""
+    for a in sel:
+        for b in cand:
+            if b in sel:
+                continue
+            if not (S_row[a] > S_row[b] or (S_row[a] == S_row[b] and a < b)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_is_the_unique_dominating_subset(seed):
+    """Exhaustive search over all subsets of size k-1 on tiny rows with many ties."""
+    rng = np.random.default_rng(seed)
+    B, L = 2, 16
+    nb = L // B
+    n = L
+    S = rng.integers(-2, 3, size=(1, n, nb)).astype(float)   # small integers -> ties
+    pos = O.query_positions(n, L)
+    for k in (1, 2, 3, 5, 9):
+        idx = O.select_blocks(S, pos, B, k)
+        for t in range(n):
+            J = pos[t] // B
+            cand = list(range(J))
+            row = idx[0, t]
+            valid = [int(j) for j in row if j >= 0]
+            assert valid == sorted(valid), "output must be ascending"
+            assert valid[-1] == J, "current block must be kept"
+            assert all(j == -1 for j in row[len(valid):])
+            if len(cand) <= k - 1:
+                assert valid == list(range(J + 1))
+                continue
+            winners = [set(c) for c in itertools.combinations(cand, k - 1)
+                       if _dominates(S[0, t], set(c), cand)]
+            assert len(winners) == 1
+            assert set(valid[:-1]) == winners[0]
+
+
+def test_selection_forced_block_even_if_worst():
+    S = np.array([[[9.0, 8.0, 7.0, -100.0]]])
+    idx = O.select_blocks(S, np.array([7]), 2, 2)    # current block 3 scores worst
+    assert idx[0, 0].tolist() == [0, 3]
+
+
+# --------------------------------------------------------------- attention ---
+
+def _case(seed, L, lq, H, G, d, B):
+    rng = np.random.default_rng(seed)
+    return (_rand(rng, lq, H, d), _rand(rng, L, G, d), _rand(rng, L, G, d),
+            O.query_positions(lq, L))
+
+
+def _sdpa(q, k, v, mask, scale):
+    """torch SDPA in float64 on CPU; mask [n, L] bool (True = attend)."""
+    n, H, d = q.shape
+    G = k.shape[1]
+    hpg = H // G
+    qt = torch.from_numpy(q).permute(1, 0, 2)                       # [H, n, d]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(hpg, 0).contiguous()
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(hpg, 0).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("L,lq,B", [(40, 40, 8), (64, 64, 16), (70, 13, 16), (33, 1, 8)])
+def test_dense_when_k_covers_every_block(L, lq, B):
+    """k >= number of blocks: MSA is plain causal attention (torch SDPA, fp64)."""
+    H, G, d = 4, 2, 8
+    q, k, v, pos = _case(L + lq, L, lq, H, G, d, B)
+    q_idx = np.random.default_rng(1).standard_normal((lq, G, 3))
+    k_idx = np.random.default_rng(2).standard_normal((L, G, 3))
+    scale = 1 / math.sqrt(d)
+    nb = -(-L // B)
+    res = O.msa_forward(q, k, v, q_idx, k_idx, lq, L, B, nb, scale)
+    mask = np.arange(L)[None, :] <= pos[:, None]
+    ref = _sdpa(q, k, v, mask, scale)
+    assert np.abs(res["out"] - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("L,lq,B", [(48, 48, 8), (70, 20, 16)])
+def test_k1_attends_only_current_block(L, lq, B):
+    """k = 1: only keys in [B*floor(p/B), p] are attended (local causal window)."""
+    H, G, d = 2, 1, 8
+    q, k, v, pos = _case(7, L, lq, H, G, d, B)
+    rng = np.random.default_rng(8)
+    q_idx, k_idx = rng.standard_normal((lq, G, 4)), rng.standard_normal((L, G, 4))
+    scale = 0.3
+    res = O.msa_forward(q, k, v, q_idx, k_idx, lq, L, B, 1, scale)
+    s = np.arange(L)[None, :]
+    mask = (s <= pos[:, None]) & (s >= (pos[:, None] // B) * B)
+    ref = _sdpa(q, k, v, mask, scale)
+    assert np.abs(res["out"] - ref).max() < 1e-12
+
+
+def _random_selection(rng, G, pos, B, k):
+    """Arbitrary valid kept-block lists (not the oracle's Top-k), to test attention alone."""
+    n = len(pos)
+    idx = np.full((G, n, k), -1, np.int32)
+    for g in range(G):
+        for t in range(n):
+            J = int(pos[t] // B)
+            others = rng.permutation(J)[:k - 1] if J > 0 else np.array([], int)
+            kept = sorted(int(x) for x in others) + [J]
+            idx[g, t, :len(kept)] = kept
+    return idx
+
+
+def _mask_from_selection(idx_row, p, L, B):
+    """Independent key mask: key s attended iff its block is listed and s <= p."""
+    blocks = set(int(j) for j in idx_row if j >= 0)
+    return np.array([(s <= p) and (s // B in blocks) for s in range(L)])
+
+
+def test_attention_matches_sdpa_on_arbitrary_selection():
+    L, lq, B, H, G, d, k = 90, 30, 8, 6, 3, 16, 4
+    q, kk, v, pos = _case(11, L, lq, H, G, d, B)
+    idx = _random_selection(np.random.default_rng(12), G, pos, B, k)
+    scale = 0.2
+    out, lse = O.sparse_attention(q, kk, v, idx, pos, B, scale)
+    hpg = H // G
+    for g in range(G):
+        mask = np.stack([_mask_from_selection(idx[g, t], pos[t], L, B) for t in range(lq)])
+        ref = _sdpa(q[:, g * hpg:(g + 1) * hpg], kk[:, g:g + 1], v[:, g:g + 1], mask, scale)
+        assert np.abs(out[:, g * hpg:(g + 1) * hpg] - ref).max() < 1e-12
+
+
+def test_attention_constant_v():
+    L, lq, B, H, G, d, k = 50, 50, 8, 4, 2, 8, 3
+    q, kk, v, pos = _case(13, L, lq, H, G, d, B)
+    c = np.linspace(-2, 3, d)
+    v[:] = c
+    idx = _random_selection(np.random.default_rng(14), G, pos, B, k)
+    out, _ = O.sparse_attention(q, kk, v, idx, pos, B, 0.7)
+    assert np.abs(out - c).max() < 1e-12
+
+
+def test_attention_zero_q_is_mean_over_kept_keys():
+    L, lq, B, H, G, d, k = 60, 60, 8, 2, 2, 4, 3
+    _, kk, v, pos = _case(15, L, lq, H, G, d, B)
+    q = np.zeros((lq, H, d))
+    idx = _random_selection(np.random.default_rng(16), G, pos, B, k)
+    out, lse = O.sparse_attention(q, kk, v, idx, pos, B, 1.0)
+    for g in range(G):
+        for t in range(lq):
+            m = _mask_from_selection(idx[g, t], pos[t], L, B)
+            assert np.allclose(out[t, g], v[m, g].mean(axis=0), atol=1e-13)
+            assert abs(lse[t, g] - math.log(m.sum())) < 1e-13
+
+
+def test_attention_weights_via_one_hot_v():
+    """V = identity rows exposes the weights: they sum to 1, vanish off the kept keys,
+    and equal scipy's softmax of the kept logits (one joint softmax, not per block)."""
+    L, lq, B, H, G, d, k = 24, 24, 4, 1, 1, 5, 3
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((lq, H, d))
+    kk = rng.standard_normal((L, G, d))
+    v = np.eye(L)[:, None, :]                  # value of key s is e_s
+    pos = O.query_positions(lq, L)
+    idx = _random_selection(rng, G, pos, B, k)
+    scale = 0.9
+    out, lse = O.sparse_attention(q, kk, v, idx, pos, B, scale)
+    for t in range(lq):
+        m = _mask_from_selection(idx[0, t], pos[t], L, B)
+        w = out[t, 0]
+        assert abs(w.sum() - 1) < 1e-13
+        assert np.all(w[~m] == 0) and np.all(w[m] > 0)
+        z = scale * (kk[m, 0] @ q[t, 0])
+        assert np.allclose(w[m], scipy.special.softmax(z), atol=1e-14)
+        assert abs(lse[t, 0] - scipy.special.logsumexp(z)) < 1e-12
+
+
+def test_lse_bruteforce_fsum():
+    L, lq, B, H, G, d, k = 30, 10, 4, 2, 1, 3, 3
+    q, kk, v, pos = _case(19, L, lq, H, G, d, B)
+    idx = _random_selection(np.random.default_rng(20), G, pos, B, k)
+    _, lse = O.sparse_attention(q, kk, v, idx, pos, B, 1.3)
+    for t in range(lq):
+        keys = [s for s in range(L) if _mask_from_selection(idx[0, t], pos[t], L, B)[s]]
+        for h in range(H):
+            z = [1.3 * math.fsum(q[t, h, c] * kk[s, 0, c] for c in range(d)) for s in keys]
+            ref = math.log(math.fsum(math.exp(x) for x in z))
+            assert abs(lse[t, h] - ref) < 1e-12
+
+
+def test_attention_invariant_to_block_list_order():
+    L, lq, B, H, G, d, k = 64, 16, 8, 2, 1, 8, 4
+    q, kk, v, pos = _case(21, L, lq, H, G, d, B)
+    idx = _random_selection(np.random.default_rng(22), G, pos, B, k)
+    out1, _ = O.sparse_attention(q, kk, v, idx, pos, B, 0.5)
+    out2, _ = O.sparse_attention(q, kk, v, idx[:, :, ::-1].copy(), pos, B, 0.5)
+    assert np.abs(out1 - out2).max() < 1e-13
+
+
+def test_head_to_group_map_is_contiguous():
+    """Heads g*hpg .. g*hpg+hpg-1 use group g: giving group 1 constant values shows it."""
+    L, lq, B, H, G, d = 32, 32, 8, 4, 2, 4
+    q, kk, v, pos = _case(23, L, lq, H, G, d, B)
+    v[:, 1, :] = 7.0
+    idx = _random_selection(np.random.default_rng(24), G, pos, B, 2)
+    out, _ = O.sparse_attention(q, kk, v, idx, pos, B, 1.0)
+    assert np.abs(out[:, 2:4] - 7.0).max() < 1e-12
+    assert np.abs(out[:, 0:2] - 7.0).min() > 1e-6
+
+
+# -------------------------------------------------------------- workloads ---
+
+def test_planted_queries_keep_planted_blocks():
+    """On a planted workload, a planted query keeps every causal planted block
+    whenever there are at most k-1 of them (their scores sit far above the rest)."""
+    import workloads as W
+    w = W.Workload("pin-planted", 4, 2, 8, 64, 128, 16, "f32", True,
+                   len_q=(4096,), len_kv=(4096,))
+    inp = W.make_inputs(w, with_attention=False)
+    pos = O.query_positions(4096, 4096)
+    rows = np.array(inp["planted_q"][0][0][-40:] + inp["planted_q"][0][1][-40:])
+    S = O.block_scores(inp["q_idx"][rows], inp["k_idx"], pos[rows], 128)
+    idx = O.select_blocks(S, pos[rows], 128, 16)
+    checked = 0
+    for g in range(2):
+        pb = set(inp["planted_blocks"][0][g])
+        for i, t in enumerate(rows):
+            if t not in inp["planted_q"][0][g]:
+                continue
+            J = pos[t] // 128
+            causal_planted = {j for j in pb if j < J}
+            if 0 < len(causal_planted) <= 15:
+                assert causal_planted <= set(idx[g, i].tolist())
+                checked += 1
+    assert checked > 20
