@@ -1,0 +1,231 @@
+"""Python binding of the MSA block-sparse attention library (libmsa.so, gfx950).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the HIP kernels behind the C
+ABI of include/msa.h.  There is no CPU fallback: without the built library
+(or without a GPU) these functions raise.
+
+    prob = Problem.from_lengths(len_q, len_kv, H, G, d, d_idx, B, k, "bf16", device)
+    scores = index_score(prob, q_idx, k_idx)          # msa_index_score
+    block_idx = topk_select(prob, scores)             # msa_topk_select
+    out, lse = sparse_attn_fwd(prob, q, k, v, block_idx, return_lse=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_SUCCESS = 0
+STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHAPE",
+                3: "MSA_ERR_UNSUPPORTED_DTYPE", 4: "MSA_ERR_MISALIGNED",
+                5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_DEVICE"}
+DTYPES = {"bf16": 0, "f32": 1}
+SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
+EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
+            "msa_sparse_attn_fwd", "msa_status_string", "msa_last_error_message",
+            "msa_abi_version")
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class CProblem(ctypes.Structure):
+    """Mirror of msa_problem_t (include/msa.h)."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_groups", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int64),
+        ("total_q", ctypes.c_int64),
+        ("total_kv", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+        ("cu_q", ctypes.c_void_p),
+        ("cu_kv", ctypes.c_void_p),
+    ]
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmsa.so (once).  Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_long_msa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(CProblem)
+    vp, st = ctypes.c_void_p, ctypes.c_int
+    lib.msa_index_score.argtypes = [P, vp, vp, vp, vp]
+    lib.msa_index_score.restype = st
+    lib.msa_topk_select.argtypes = [P, vp, vp, vp]
+    lib.msa_topk_select.restype = st
+    lib.msa_sparse_attn_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_sparse_attn_workspace_size.restype = st
+    lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msa_sparse_attn_fwd.restype = st
+    lib.msa_status_string.argtypes = [st]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_last_error_message.argtypes = []
+    lib.msa_last_error_message.restype = ctypes.c_char_p
+    lib.msa_abi_version.argtypes = []
+    lib.msa_abi_version.restype = ctypes.c_int
+    _lib_handle = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != MSA_SUCCESS:
+        msg = load_library().msa_last_error_message().decode()
+        raise MsaError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Problem:
+    """Shapes of one call sequence; owns the device offset arrays it points to."""
+
+    def __init__(self, cu_q: torch.Tensor, cu_kv: torch.Tensor, len_q: Sequence[int],
+                 len_kv: Sequence[int], num_q_heads: int, num_kv_groups: int, head_dim: int,
+                 idx_dim: int, block_size: int, top_k: int, dtype: str = "bf16",
+                 softmax_scale: Optional[float] = None, schedule: str = "auto"):
+        self.cu_q, self.cu_kv = cu_q, cu_kv            # keep alive
+        self.len_q, self.len_kv = list(len_q), list(len_kv)
+        self.H, self.G, self.d, self.d_idx = num_q_heads, num_kv_groups, head_dim, idx_dim
+        self.B, self.top_k, self.dtype = block_size, top_k, dtype
+        self.scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+        self.max_q_len = max(self.len_q) if self.len_q else 0
+        self.max_kv_len = max(self.len_kv) if self.len_kv else 0
+        self.total_q, self.total_kv = sum(self.len_q), sum(self.len_kv)
+        self.nb_max = -(-self.max_kv_len // block_size)
+        self.c = CProblem(len(self.len_q), num_q_heads, num_kv_groups, head_dim, idx_dim,
+                          block_size, top_k, DTYPES[dtype], SCHEDULES[schedule], self.max_q_len,
+                          self.max_kv_len, self.total_q, self.total_kv, self.scale,
+                          cu_q.data_ptr(), cu_kv.data_ptr())
+
+    @classmethod
+    def from_lengths(cls, len_q, len_kv, num_q_heads, num_kv_groups, head_dim, idx_dim,
+                     block_size, top_k, dtype="bf16", device="cuda", **kw) -> "Problem":
+        cu_q = [0]
+        cu_kv = [0]
+        for a, b in zip(len_q, len_kv):
+            cu_q.append(cu_q[-1] + a)
+            cu_kv.append(cu_kv[-1] + b)
+        dev = torch.device(device)
+        return cls(torch.tensor(cu_q, dtype=torch.int64, device=dev),
+                   torch.tensor(cu_kv, dtype=torch.int64, device=dev), len_q, len_kv,
+                   num_q_heads, num_kv_groups, head_dim, idx_dim, block_size, top_k, dtype, **kw)
+
+    def with_schedule(self, schedule: str) -> "Problem":
+        return Problem(self.cu_q, self.cu_kv, self.len_q, self.len_kv, self.H, self.G, self.d,
+                       self.d_idx, self.B, self.top_k, self.dtype, self.scale, schedule)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def index_score(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                scores: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """msa_index_score: block scores [G, total_q, NBmax] fp32."""
+    _need(q_idx, "q_idx", (prob.total_q, prob.G, prob.d_idx), prob.torch_dtype)
+    _need(k_idx, "k_idx", (prob.total_kv, prob.G, prob.d_idx), prob.torch_dtype)
+    if scores is None:
+        scores = torch.empty((prob.G, prob.total_q, prob.nb_max), dtype=torch.float32,
+                             device=q_idx.device)
+    _need(scores, "scores", (prob.G, prob.total_q, prob.nb_max), torch.float32)
+    s = _stream(q_idx.device) if stream is None else stream
+    _check(load_library().msa_index_score(prob.ref(), _ptr(q_idx), _ptr(k_idx), _ptr(scores), s))
+    return scores
+
+
+def topk_select(prob: Problem, scores: torch.Tensor, block_idx: Optional[torch.Tensor] = None,
+                stream: Optional[int] = None) -> torch.Tensor:
+    """msa_topk_select: kept blocks [G, total_q, k] int32, ascending, -1 padded."""
+    _need(scores, "scores", (prob.G, prob.total_q, prob.nb_max), torch.float32)
+    if block_idx is None:
+        block_idx = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.int32,
+                                device=scores.device)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    s = _stream(scores.device) if stream is None else stream
+    _check(load_library().msa_topk_select(prob.ref(), _ptr(scores), _ptr(block_idx), s))
+    return block_idx
+
+
+def workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_sparse_attn_workspace_size(prob.ref(), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    block_idx: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """msa_sparse_attn_fwd: (out [total_q, H, d], lse [total_q, H] or None)."""
+    dt = prob.torch_dtype
+    _need(q, "q", (prob.total_q, prob.H, prob.d), dt)
+    _need(k, "k", (prob.total_kv, prob.G, prob.d), dt)
+    _need(v, "v", (prob.total_kv, prob.G, prob.d), dt)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    if out is None:
+        out = torch.empty((prob.total_q, prob.H, prob.d), dtype=dt, device=q.device)
+    _need(out, "out", (prob.total_q, prob.H, prob.d), dt)
+    lse = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    need = workspace_size(prob)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q.device) if stream is None else stream
+    _check(load_library().msa_sparse_attn_fwd(prob.ref(), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(block_idx), _ptr(out), _ptr(lse),
+                                              _ptr(workspace), wbytes, s))
+    return out, lse
+
+
+def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):
+    """The whole path: index_score -> topk_select -> sparse_attn_fwd."""
+    scores = index_score(prob, q_idx, k_idx)
+    block_idx = topk_select(prob, scores)
+    out, lse = sparse_attn_fwd(prob, q, k, v, block_idx, return_lse=return_lse)
+    return out, lse, block_idx, scores
+
+
+# Names matching the C entry points.
+msa_index_score = index_score
+msa_topk_select = topk_select
+msa_sparse_attn_fwd = sparse_attn_fwd

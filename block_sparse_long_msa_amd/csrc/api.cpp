@@ -1,0 +1,255 @@
+// Host side of the C ABI declared in include/msa.h: argument validation
+// (pure host code, before any HIP call), launch-geometry selection and
+// dispatch to the kernels.  The library keeps no state between calls apart
+// from the per-thread error text.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "launch.hpp"
+#include "msa.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status_t fail(msa_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error.clear();
+  return MSA_SUCCESS;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int kMaxBlocksPerRow = 8192;  // top-k keeps a row's candidates in registers
+constexpr int kMaxHpg = 16;             // heads of a group are MFMA columns (16 wide)
+constexpr int kDecodeBlocksPerSplit = 4;
+
+msa_status_t check_problem(const msa_problem_t *p, msa::Dims *d) {
+  if (p == nullptr) return fail(MSA_ERR_NULL_POINTER, "problem descriptor is NULL");
+  if (p->num_seqs < 1) return fail(MSA_ERR_BAD_SHAPE, "num_seqs must be >= 1 (got %d)", p->num_seqs);
+  if (p->num_q_heads < 1 || p->num_kv_groups < 1)
+    return fail(MSA_ERR_BAD_SHAPE, "num_q_heads and num_kv_groups must be >= 1");
+  if (p->num_q_heads % p->num_kv_groups != 0)
+    return fail(MSA_ERR_BAD_SHAPE, "num_q_heads (%d) must be a multiple of num_kv_groups (%d)",
+                p->num_q_heads, p->num_kv_groups);
+  if (p->num_q_heads / p->num_kv_groups > kMaxHpg)
+    return fail(MSA_ERR_BAD_SHAPE, "at most %d query heads per KV group are supported", kMaxHpg);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(MSA_ERR_BAD_SHAPE, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->idx_dim != 32 && p->idx_dim != 64 && p->idx_dim != 128)
+    return fail(MSA_ERR_BAD_SHAPE, "idx_dim must be 32, 64 or 128 (got %d)", p->idx_dim);
+  if (p->block_size != 64 && p->block_size != 128)
+    return fail(MSA_ERR_BAD_SHAPE, "block_size must be 64 or 128 (got %d)", p->block_size);
+  if (p->top_k < 1 || p->top_k > 64)
+    return fail(MSA_ERR_BAD_SHAPE, "top_k must be in [1, 64] (got %d)", p->top_k);
+  if (p->dtype != MSA_BF16 && p->dtype != MSA_F32)
+    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "dtype must be MSA_BF16 or MSA_F32 (got %d)", p->dtype);
+  if (p->schedule < MSA_SCHED_AUTO || p->schedule > MSA_SCHED_KV_MAJOR)
+    return fail(MSA_ERR_BAD_SHAPE, "unknown schedule %d", p->schedule);
+  if (p->max_q_len < 0 || p->max_kv_len < 0 || p->total_q < 0 || p->total_kv < 0)
+    return fail(MSA_ERR_BAD_SHAPE, "lengths must be non-negative");
+  if (p->total_q < p->max_q_len || p->total_kv < p->max_kv_len)
+    return fail(MSA_ERR_BAD_SHAPE, "total_q/total_kv must be >= max_q_len/max_kv_len");
+  if (p->max_q_len > p->max_kv_len)
+    return fail(MSA_ERR_BAD_SHAPE, "max_q_len (%d) exceeds max_kv_len (%lld)", p->max_q_len,
+                (long long)p->max_kv_len);
+  const int64_t nb = (p->max_kv_len + p->block_size - 1) / p->block_size;
+  if (nb > kMaxBlocksPerRow)
+    return fail(MSA_ERR_BAD_SHAPE, "ceil(max_kv_len / block_size) = %lld exceeds %d",
+                (long long)nb, kMaxBlocksPerRow);
+  if ((int64_t)p->num_seqs * p->num_kv_groups > 65535)
+    return fail(MSA_ERR_BAD_SHAPE, "num_seqs * num_kv_groups must be <= 65535");
+  if (p->total_q > (int64_t)INT32_MAX)
+    return fail(MSA_ERR_BAD_SHAPE, "total_q must fit in int32 (got %lld)", (long long)p->total_q);
+  if (!(p->softmax_scale > 0.f) || p->softmax_scale > 1e30f)
+    return fail(MSA_ERR_BAD_SHAPE, "softmax_scale must be positive and finite");
+  if (p->cu_q == nullptr || p->cu_kv == nullptr)
+    return fail(MSA_ERR_NULL_POINTER, "cu_q and cu_kv must be device pointers");
+  if (!aligned(p->cu_q, 8) || !aligned(p->cu_kv, 8))
+    return fail(MSA_ERR_MISALIGNED, "cu_q and cu_kv must be 8-byte aligned");
+  d->num_seqs = p->num_seqs;
+  d->H = p->num_q_heads;
+  d->G = p->num_kv_groups;
+  d->d = p->head_dim;
+  d->d_idx = p->idx_dim;
+  d->B = p->block_size;
+  d->top_k = p->top_k;
+  d->max_q_len = p->max_q_len;
+  d->max_kv_len = p->max_kv_len;
+  d->total_q = p->total_q;
+  d->total_kv = p->total_kv;
+  d->nb_max = (int)nb;
+  d->scale = p->softmax_scale;
+  d->cu_q = p->cu_q;
+  d->cu_kv = p->cu_kv;
+  return MSA_SUCCESS;
+}
+
+msa_status_t check_tensor(const void *ptr, const char *name, bool needed) {
+  if (!needed) return MSA_SUCCESS;
+  if (ptr == nullptr) return fail(MSA_ERR_NULL_POINTER, "%s is NULL", name);
+  if (!aligned(ptr, 16)) return fail(MSA_ERR_MISALIGNED, "%s must be 16-byte aligned", name);
+  return MSA_SUCCESS;
+}
+
+msa_status_t launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+enum class AttnPath { kDecodeSplit, kQueryMajor, kKvMajor };
+
+AttnPath attn_path(const msa_problem_t *p, const msa::Dims &d, int *n_split) {
+  *n_split = 1;
+  if (d.max_q_len == 1) {
+    *n_split = (d.top_k + kDecodeBlocksPerSplit - 1) / kDecodeBlocksPerSplit;
+    return AttnPath::kDecodeSplit;
+  }
+  if (p->dtype == MSA_BF16 && p->schedule == MSA_SCHED_KV_MAJOR) return AttnPath::kKvMajor;
+  return AttnPath::kQueryMajor;
+}
+
+size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
+  int n_split = 1;
+  switch (attn_path(p, d, &n_split)) {
+    case AttnPath::kDecodeSplit:
+      if (n_split <= 1) return 0;
+      return (size_t)n_split * (size_t)d.total_q * (size_t)d.H * (size_t)(d.d + 1) * sizeof(float);
+    case AttnPath::kKvMajor:
+      return msa::kvmajor_workspace_bytes(d);
+    case AttnPath::kQueryMajor:
+      return 0;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_index_score(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                             float *scores, void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q_idx, "q_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k_idx, "k_idx", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(scores, "scores", any_q && d.nb_max > 0)) != MSA_SUCCESS) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!any_q || d.nb_max == 0) return ok();
+  if (prob->dtype == MSA_F32)
+    return launched(msa::launch_index_score_f32(d, static_cast<const float *>(q_idx),
+                                                static_cast<const float *>(k_idx), scores, s),
+                    "index_score_f32");
+  const uint16_t *qi = static_cast<const uint16_t *>(q_idx);
+  const uint16_t *ki = static_cast<const uint16_t *>(k_idx);
+  if (msa::decode_index_supported(d))
+    return launched(msa::launch_index_score_decode_bf16(d, qi, ki, scores, s), "index_score_decode");
+  return launched(msa::launch_index_score_bf16(d, qi, ki, scores, s), "index_score_mfma");
+}
+
+msa_status_t msa_topk_select(const msa_problem_t *prob, const float *scores, int32_t *block_idx,
+                             void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any_q = d.total_q > 0;
+  if ((st = check_tensor(scores, "scores", any_q && d.nb_max > 0)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if (!any_q) return ok();
+  return launched(msa::launch_topk(d, scores, block_idx, reinterpret_cast<hipStream_t>(stream)),
+                  "topk_select");
+}
+
+msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = workspace_bytes(prob, d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const void *k,
+                                 const void *v, const int32_t *block_idx, void *out, float *lse,
+                                 void *workspace, size_t workspace_bytes_given, void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q, "q", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k, "k", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(v, "v", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(MSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const size_t need = workspace_bytes(prob, d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int n_split = 1;
+  const AttnPath path = attn_path(prob, d, &n_split);
+  if (path == AttnPath::kKvMajor)
+    return launched(msa::launch_attn_kvmajor_bf16(d, static_cast<const uint16_t *>(q),
+                                                  static_cast<const uint16_t *>(k),
+                                                  static_cast<const uint16_t *>(v), block_idx,
+                                                  static_cast<uint16_t *>(out), lse, workspace, s),
+                    "attn_kvmajor");
+  float *part_o = nullptr, *part_lse = nullptr;
+  if (n_split > 1) {
+    part_o = static_cast<float *>(workspace);
+    part_lse = part_o + (size_t)n_split * d.total_q * d.H * d.d;
+  }
+  hipError_t e;
+  if (prob->dtype == MSA_F32)
+    e = msa::launch_attn_qmajor_f32(d, static_cast<const float *>(q), static_cast<const float *>(k),
+                                    static_cast<const float *>(v), block_idx,
+                                    static_cast<float *>(out), lse, n_split, part_o, part_lse, s);
+  else
+    e = msa::launch_attn_qmajor_bf16(d, static_cast<const uint16_t *>(q),
+                                     static_cast<const uint16_t *>(k),
+                                     static_cast<const uint16_t *>(v), block_idx,
+                                     static_cast<uint16_t *>(out), lse, n_split, part_o, part_lse, s);
+  if (e != hipSuccess || n_split == 1) return launched(e, "attn_query_major");
+  return launched(msa::launch_combine_splits(d, n_split, part_o, part_lse, out,
+                                             prob->dtype == MSA_BF16, lse, s),
+                  "attn_combine_splits");
+}
+
+const char *msa_status_string(msa_status_t status) {
+  switch (status) {
+    case MSA_SUCCESS: return "success";
+    case MSA_ERR_NULL_POINTER: return "null pointer";
+    case MSA_ERR_BAD_SHAPE: return "unsupported or inconsistent shape";
+    case MSA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case MSA_ERR_MISALIGNED: return "misaligned pointer";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MSA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char *msa_last_error_message(void) { return g_last_error.c_str(); }
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal host-side launch entry points of the kernels (not part of the C ABI).
+// Every function launches asynchronously on `stream` and returns the status of
+// the launch itself (hipGetLastError after the launch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct Dims {
+  int num_seqs, H, G, d, d_idx, B, top_k;
+  int max_q_len;
+  int64_t max_kv_len, total_q, total_kv;
+  int nb_max;          // ceil(max_kv_len / B): score row stride
+  float scale;
+  const int64_t *cu_q, *cu_kv;
+};
+
+// Index Branch block scores.
+hipError_t launch_index_score_bf16(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx,
+                                   float *scores, hipStream_t s);
+hipError_t launch_index_score_decode_bf16(const Dims &p, const uint16_t *q_idx,
+                                          const uint16_t *k_idx, float *scores, hipStream_t s);
+bool decode_index_supported(const Dims &p);
+hipError_t launch_index_score_f32(const Dims &p, const float *q_idx, const float *k_idx,
+                                  float *scores, hipStream_t s);
+
+// Top-k with the current block forced.
+hipError_t launch_topk(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s);
+
+// Attention, query-major (one work item per query row, group and split).
+// With n_split > 1 the splits write normalised partials to `part_o`
+// [n_split, total_q, H, d] fp32 and `part_lse` [n_split, total_q, H] and
+// launch_combine_splits merges them.
+hipError_t launch_attn_qmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                   const uint16_t *v, const int32_t *block_idx, uint16_t *out,
+                                   float *lse, int n_split, float *part_o, float *part_lse,
+                                   hipStream_t s);
+hipError_t launch_attn_qmajor_f32(const Dims &p, const float *q, const float *k, const float *v,
+                                  const int32_t *block_idx, float *out, float *lse, int n_split,
+                                  float *part_o, float *part_lse, hipStream_t s);
+hipError_t launch_combine_splits(const Dims &p, int n_split, const float *part_o,
+                                 const float *part_lse, void *out, bool out_bf16, float *lse,
+                                 hipStream_t s);
+
+// Attention, KV-major prefill (bf16): see attn_kvmajor.hip.
+size_t kvmajor_workspace_bytes(const Dims &p);
+hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                    const uint16_t *v, const int32_t *block_idx, uint16_t *out,
+                                    float *lse, void *workspace, hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,106 @@
+// Device-side helpers shared by the MSA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// bf16 <-> fp32.  bf16 is the top half of an fp32, so widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round-to-nearest-even narrowing of fp32 to bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return as_bf16x8(z);
+}
+
+// 16-byte loads (pointer must be 16-byte aligned).
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, const u32x4 &v) {
+  *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// MFMA wrappers.  Operand layouts (wave64):
+//  32x32x16: A[i][k] in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8);
+//            C[i][j] in lane j + 32*((i/4)%2), register 4*(i/8) + i%4.
+//  16x16x32: A[i][k] in lane i + 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8);
+//            C[i][j] in lane j + 16*(i/4), register i%4.
+// Only the row/column placement matters for correctness: the contraction
+// index is summed, so any bijection of k used identically by A and B works.
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Cross-lane helpers (wave64).
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int mbcnt64(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Per-sequence geometry.  Queries are the last len_q tokens of the sequence,
+// so local query i sits at position base + i with base = len_kv - len_q.
+struct SeqGeom {
+  int64_t q0, lq, kv0, lkv, base;
+};
+__device__ __forceinline__ SeqGeom seq_geom(const int64_t *cu_q, const int64_t *cu_kv, int b) {
+  SeqGeom s;
+  s.q0 = cu_q[b];
+  s.lq = cu_q[b + 1] - s.q0;
+  s.kv0 = cu_kv[b];
+  s.lkv = cu_kv[b + 1] - s.kv0;
+  s.base = s.lkv - s.lq;
+  return s;
+}
+// Sequence holding packed query row `row` (binary search over cu_q).
+__device__ __forceinline__ int find_seq(const int64_t *cu_q, int num_seqs, int64_t row) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace msa

@@ -1,0 +1,154 @@
+/*
+ * msa.h - C ABI of the MSA block-sparse attention library (gfx950 / MI355X).
+ *
+ * The library computes the three steps of MiniMax Sparse Attention as the
+ * "MiniMax Sparse Attention" page (paper by Lai et al., 2026) describes them
+ * in its Summary, second paragraph:
+ *
+ *   1. msa_index_score  - the Index Branch scores every key/value block by
+ *                         max-pooling token-level dot products of an index
+ *                         query with the block's index keys;
+ *   2. msa_topk_select  - each GQA group keeps its own Top-k blocks; the
+ *                         block holding the query's own position is always
+ *                         kept (and counts as one of the k, as in the page's
+ *                         Key points, "Benchmark configuration": B_k = 128
+ *                         and k = 16 give 2,048 attended tokens);
+ *   3. msa_sparse_attn_fwd - the Main Branch runs exact softmax attention
+ *                         restricted to the kept blocks, for every query
+ *                         head of the group (prefill and decode).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Sequences are packed back to back.  cu_q / cu_kv hold num_seqs + 1 row
+ *    offsets (int64, DEVICE memory).  Sequence b owns query rows
+ *    [cu_q[b], cu_q[b+1]) and key/value rows [cu_kv[b], cu_kv[b+1]).
+ *  - Queries are the LAST len_q tokens of their sequence: local query i of
+ *    sequence b sits at absolute position p = len_kv(b) - len_q(b) + i and
+ *    sees keys 0..p (causal).  len_q(b) <= len_kv(b) is required; rows that
+ *    break it are treated as having no causal key (scores -inf, no block
+ *    kept, output 0, lse -inf) and never read out of bounds.
+ *  - Blocks have block_size keys; block j of a sequence spans its keys
+ *    [j*B, min((j+1)*B, len_kv)).  The current block of a query at p is
+ *    J = floor(p / B).
+ *  - Query head h belongs to KV group h / (H / G) (contiguous GQA groups).
+ *  - Layouts (row-major, innermost last, no padding between rows):
+ *        q, out  [total_q,  H, d]        k, v   [total_kv, G, d]
+ *        q_idx   [total_q,  G, d_idx]    k_idx  [total_kv, G, d_idx]
+ *        scores  [G, total_q, NBmax] fp32, NBmax = ceil(max_kv_len / B)
+ *        block_idx [G, total_q, top_k] int32
+ *        lse     [total_q, H] fp32
+ *    Element type of q, k, v, q_idx, k_idx and out is `dtype` (bf16 or
+ *    fp32).  Every device pointer must be 16-byte aligned.
+ *  - Every pointer is DEVICE memory unless marked "host".  The caller owns
+ *    and frees all memory; the library never allocates, frees, copies to the
+ *    host or synchronises.  Calls are asynchronous on `stream` (a
+ *    hipStream_t; NULL = the default stream).
+ *  - Errors: all arguments are validated on the host before anything is
+ *    launched; on any error nothing is launched, outputs are untouched and
+ *    a status != MSA_SUCCESS is returned (details in
+ *    msa_last_error_message(), per thread).  A failed launch returns
+ *    MSA_ERR_DEVICE.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Inputs holding NaN or Inf give unspecified values
+ *    (but no out-of-bounds access).
+ *  - Supported shapes: head_dim d in {64, 128}; idx_dim d_idx in {32, 64,
+ *    128}; block_size in {64, 128}; H % G == 0 with 1 <= H/G <= 16;
+ *    1 <= top_k <= 64; NBmax <= 8192.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum {
+  MSA_SUCCESS = 0,
+  MSA_ERR_NULL_POINTER = 1,
+  MSA_ERR_BAD_SHAPE = 2,
+  MSA_ERR_UNSUPPORTED_DTYPE = 3,
+  MSA_ERR_MISALIGNED = 4,
+  MSA_ERR_WORKSPACE_TOO_SMALL = 5,
+  MSA_ERR_DEVICE = 6
+} msa_status_t;
+
+typedef enum { MSA_BF16 = 0, MSA_F32 = 1 } msa_dtype_t;
+
+/* How msa_sparse_attn_fwd orders its work for multi-query (prefill) rows.
+ * Both give the same result up to fp32 rounding order. */
+typedef enum {
+  MSA_SCHED_AUTO = 0,        /* library choice (KV-major for bf16 prefill) */
+  MSA_SCHED_QUERY_MAJOR = 1, /* one work item per (query, group): gathers its k blocks */
+  MSA_SCHED_KV_MAJOR = 2     /* one work item per (group, kept block, query chunk),
+                                then a per-query merge (bf16 only) */
+} msa_schedule_t;
+
+typedef struct {
+  int32_t num_seqs;        /* >= 1 */
+  int32_t num_q_heads;     /* H */
+  int32_t num_kv_groups;   /* G */
+  int32_t head_dim;        /* d */
+  int32_t idx_dim;         /* d_idx */
+  int32_t block_size;      /* B */
+  int32_t top_k;           /* k, counts the always-kept current block */
+  int32_t dtype;           /* msa_dtype_t */
+  int32_t schedule;        /* msa_schedule_t (attention only) */
+  int32_t max_q_len;       /* host: max over sequences of len_q */
+  int64_t max_kv_len;      /* host: max over sequences of len_kv */
+  int64_t total_q;         /* host: cu_q[num_seqs] */
+  int64_t total_kv;        /* host: cu_kv[num_seqs] */
+  float softmax_scale;     /* multiplies q.k before the softmax (e.g. 1/sqrt(d)) */
+  const int64_t *cu_q;     /* device [num_seqs + 1] */
+  const int64_t *cu_kv;    /* device [num_seqs + 1] */
+} msa_problem_t;
+
+/* Step 1 - Index Branch block scores.
+ * scores[g, r, j] = max over keys s of block j with s <= p(r) of
+ *                   sum_c q_idx[r, g, c] * k_idx[s, g, c]   (fp32 accumulate)
+ * and -inf for every j > J(r) up to NBmax - 1.  No scale is applied.
+ * bf16 inputs use bf16 MFMA products (exact in fp32) with fp32 sums. */
+msa_status_t msa_index_score(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                             float *scores, void *stream);
+
+/* Step 2 - per-group Top-k with the current block forced.
+ * For row r with current block J: if J <= k-1 the kept set is {0..J};
+ * otherwise the k-1 best of blocks 0..J-1 by (score descending, block index
+ * ascending) plus J.  block_idx[g, r, :] lists the kept blocks ascending
+ * (so J is the last valid entry) and pads with -1.  Exact on the fp32
+ * scores it is given: pure comparisons, no exponentials. */
+msa_status_t msa_topk_select(const msa_problem_t *prob, const float *scores, int32_t *block_idx,
+                             void *stream);
+
+/* Bytes of device workspace msa_sparse_attn_fwd needs for this problem and
+ * schedule (0 is possible).  Writes the size to *bytes (host). */
+msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes);
+
+/* Step 3 - exact softmax attention over the kept blocks.
+ * For query row r, head h of group g: keys = every s <= p(r) inside a block
+ * listed in block_idx[g, r, :] (entries < 0 are ignored; entries must be
+ * distinct and <= J(r)); z_s = softmax_scale * q[r,h].k[s,g];
+ * out[r,h] = sum_s exp(z_s - m) v[s,g] / sum_s exp(z_s - m), m = max z.
+ * If lse is not NULL, lse[r,h] = m + ln(sum_s exp(z_s - m)).
+ * Rows with max_q_len == 1 use the split-KV decode kernels.  out has the
+ * input dtype (bf16 rounding to nearest even).  `workspace` must hold at
+ * least msa_sparse_attn_workspace_size() bytes (it may be NULL if that is
+ * 0); its contents need no initialisation and are clobbered. */
+msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const void *k,
+                                 const void *v, const int32_t *block_idx, void *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *msa_status_string(msa_status_t status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *msa_last_error_message(void);
+/* MSA_ABI_VERSION of the loaded library. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

@@ -1,0 +1,162 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, the ctypes mirror of msa_problem_t matches the C layout, and
+host-side validation rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_long_msa_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH),
+                                reason="libmsa.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("msa_index_score", "msa_topk_select", "msa_sparse_attn_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.load_library()
+    names = _declared_functions()
+    assert set(names) == set(msa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.msa_abi_version() == 1
+
+
+def test_problem_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "msa.h"\n'
+        "int main(void){printf(\"%zu\", sizeof(msa_problem_t));"
+        + "".join(f'printf(" %zu", offsetof(msa_problem_t, {f}));'
+                  for f, _ in msa.CProblem._fields_)
+        + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(msa.CProblem)
+    assert vals[1:] == [getattr(msa.CProblem, f).offset for f, _ in msa.CProblem._fields_]
+
+
+def test_header_compiles_as_plain_c_and_cpp(tmp_path):
+    for lang, compiler in (("c", "gcc"), ("c++", "g++")):
+        src = tmp_path / f"h.{ 'c' if lang == 'c' else 'cpp'}"
+        src.write_text('#include "msa.h"\nint main(void){return MSA_ABI_VERSION - 1;}\n')
+        subprocess.run([compiler, "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(tmp_path / f"h_{lang}")], check=True)
+
+
+# ---------------------------------------------------------------- validation
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; validation never dereferences it
+
+
+def _prob(**over):
+    vals = dict(num_seqs=1, num_q_heads=8, num_kv_groups=2, head_dim=128, idx_dim=64,
+                block_size=128, top_k=4, dtype=0, schedule=0, max_q_len=256, max_kv_len=256,
+                total_q=256, total_kv=256, softmax_scale=0.088, cu_q=FAKE, cu_kv=FAKE)
+    vals.update(over)
+    return msa.CProblem(**vals)
+
+
+def _score(p, qi=FAKE, ki=FAKE, sc=FAKE):
+    lib = msa.load_library()
+    return lib.msa_index_score(ctypes.byref(p), qi, ki, sc, None)
+
+
+def _attn(p, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0):
+    lib = msa.load_library()
+    return lib.msa_sparse_attn_fwd(ctypes.byref(p), q, k, v, idx, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", 0, 2), ("num_q_heads", 0, 2), ("num_kv_groups", 3, 2),
+    ("num_q_heads", 64, 2),            # 32 heads per group > 16
+    ("head_dim", 96, 2), ("idx_dim", 48, 2), ("block_size", 32, 2),
+    ("top_k", 0, 2), ("top_k", 65, 2), ("dtype", 7, 3), ("schedule", 9, 2),
+    ("max_q_len", -1, 2), ("max_q_len", 512, 2),  # more queries than keys
+    ("total_q", 10, 2), ("max_kv_len", 128 * 8193, 2), ("softmax_scale", 0.0, 2),
+    ("softmax_scale", float("nan"), 2), ("cu_q", None, 1), ("cu_kv", FAKE + 4, 4),
+])
+def test_bad_problem_is_rejected(field, value, status):
+    p = _prob(**{field: value})
+    if field == "max_kv_len":
+        p.total_kv = value
+    assert _score(p) == status
+    assert _attn(p) == status
+    assert msa.load_library().msa_last_error_message().decode() != ""
+
+
+def test_null_problem():
+    lib = msa.load_library()
+    assert lib.msa_index_score(None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.msa_topk_select(None, FAKE, FAKE, None) == 1
+    assert lib.msa_sparse_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("which", ["qi", "ki", "sc"])
+def test_index_score_pointer_checks(which):
+    p = _prob()
+    args = dict(qi=FAKE, ki=FAKE, sc=FAKE)
+    args[which] = None
+    assert _score(p, **args) == 1
+    args[which] = FAKE + 8
+    assert _score(p, **args) == 4
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "idx", "out"])
+def test_attention_pointer_checks(which):
+    p = _prob()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, out=FAKE)
+    args[which] = None
+    assert _attn(p, **args) == 1
+    args[which] = FAKE + 2
+    assert _attn(p, **args) == 4
+
+
+def test_workspace_size_and_too_small():
+    lib = msa.load_library()
+    n = ctypes.c_size_t(123)
+    # prefill, query-major: no workspace
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(_prob(schedule=1)), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # decode: split-KV partials, 8 splits of 4 blocks for k = 32
+    pd = _prob(num_seqs=4, max_q_len=1, total_q=4, top_k=32, max_kv_len=4096, total_kv=16384)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(pd), ctypes.byref(n)) == 0
+    assert n.value == 8 * 4 * 8 * (128 + 1) * 4
+    assert _attn(pd, ws=FAKE, wsb=n.value - 1) == 5
+    assert _attn(pd, ws=None, wsb=n.value) == 1
+    assert _attn(pd, ws=FAKE + 16, wsb=n.value) == 4
+
+
+def test_empty_batch_is_a_no_op():
+    """total_q = 0 returns success without touching the device."""
+    p = _prob(max_q_len=0, total_q=0)
+    assert _score(p, qi=None, sc=None) == 0
+    lib = msa.load_library()
+    assert lib.msa_topk_select(ctypes.byref(p), None, None, None) == 0
+    assert _attn(p, q=None, idx=None, out=None) == 0
+
+
+def test_status_strings():
+    lib = msa.load_library()
+    for code in range(7):
+        assert lib.msa_status_string(code).decode()
+    assert lib.msa_status_string(99).decode() == "unknown status"

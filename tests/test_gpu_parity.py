@@ -1,0 +1,179 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small cases are checked on every row; the long-context workloads on sampled
+rows (first rows, block edges, planted rows, random rows, last rows), with the
+launch configuration the benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_msa_amd as msa
+import workloads as W
+from oracle import msa_oracle as O
+from tests import msa_check as C
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # name, len_q, len_kv, H, G, d, d_idx, B, k
+    ("ragged-1000", [1000], [1000], 8, 2, 128, 64, 128, 4),
+    ("varlen-chunked", [300, 1, 700, 0], [300, 513, 1500, 64], 4, 4, 64, 32, 64, 3),
+    ("hpg16-dsi128", [777], [777], 16, 1, 128, 128, 64, 8),
+    ("k1", [520], [600], 4, 2, 64, 64, 128, 1),
+    ("k-covers-all", [640], [640], 4, 1, 128, 64, 64, 16),
+    ("two-tiles-of-queries", [600], [2000], 8, 8, 128, 64, 128, 5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_all_rows(case, dtype):
+    name, lq, lkv, H, G, d, di, B, k = case
+    _log(f"case {name} {dtype}")
+    inp = W.random_case(SMALL.index(case), lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+    st = C.run_and_check(inp, H, G, d, di, B, k, dtype)
+    _log(f"  {st}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_kv_major_schedule(dtype):
+    """Both prefill schedules give the oracle's result."""
+    name, lq, lkv, H, G, d, di, B, k = SMALL[0]
+    inp = W.random_case(5, lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+    for sched in ("query_major", "kv_major"):
+        if sched == "kv_major" and dtype == "f32":
+            continue
+        _log(f"schedule {sched} {dtype}")
+        C.run_and_check(inp, H, G, d, di, B, k, dtype, schedule=sched)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_decode_batch(dtype):
+    """max_q_len == 1: streaming index kernel and split-KV attention."""
+    lkv = [1, 127, 128, 129, 5000, 64, 3000]
+    inp = W.random_case(11, [1] * len(lkv), lkv, 8, 2, 128, 64, 128, 4, dtype, device=DEV)
+    C.run_and_check(inp, 8, 2, 128, 64, 128, 4, dtype)
+    inp = W.random_case(12, [1] * 3, [4096, 70, 9000], 16, 8, 64, 64, 64, 9, dtype, device=DEV)
+    C.run_and_check(inp, 16, 8, 64, 64, 64, 9, dtype)
+
+
+def test_tiny_fp32_workload_every_row():
+    w = W.WORKLOADS["tiny-fp32"]
+    inp = W.make_inputs(w, device=DEV, seed=0)
+    st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
+                         w.block_size, w.top_k, w.dtype)
+    _log(f"tiny-fp32 {st}")
+    assert st["rows"] == 1024
+
+
+def test_topk_exact_on_synthetic_scores():
+    """Selection alone, on generated score rows with many exact ties: bit-exact."""
+    for nb, lq, levels in ((16, 1024, 3), (300, 300 * 64, 2), (1100, 70000, 0), (8192, 2048, 5)):
+        B = 64 if nb != 8192 else 128
+        k = 13 if nb < 8192 else 64
+        lkv = nb * B
+        lq = min(lq, lkv)
+        G = 2
+        prob = msa.Problem.from_lengths([lq], [lkv], 4, G, 64, 64, B, k, "bf16", DEV)
+        scores = W.random_scores(nb, G, lq, nb, levels=levels)
+        idx = msa.topk_select(prob, scores.to(DEV)).cpu().numpy()
+        pos = O.query_positions(lq, lkv)
+        rows = np.unique(np.concatenate([np.arange(0, lq, max(1, lq // 300)), [lq - 1]]))
+        ref = O.select_blocks(scores[:, rows, :].numpy(), pos[rows], B, k)
+        assert np.array_equal(idx[:, rows, :], ref), f"nb={nb}"
+        _log(f"topk nb={nb} rows={len(rows)} ok")
+
+
+def test_closed_forms_constant_v_and_zero_q():
+    """Constant V gives that constant; Q = 0 gives the mean of V over the kept keys."""
+    lq, lkv, H, G, d, di, B, k = [900], [1300], 8, 2, 128, 64, 128, 4
+    inp = W.random_case(21, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    prob = C.problem_for(inp, H, G, d, di, B, k, "bf16")
+    scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
+    idx = msa.topk_select(prob, scores)
+    c = torch.linspace(-3, 3, d, device=DEV).to(torch.bfloat16)
+    v_const = c.expand(lkv[0], G, d).contiguous()
+    for sched in ("query_major", "kv_major"):
+        p2 = prob.with_schedule(sched)
+        out, _ = msa.sparse_attn_fwd(p2, inp["q"], inp["k"], v_const, idx)
+        assert (out.float() - c.float()).abs().max().item() <= 1e-2
+        q0 = torch.zeros_like(inp["q"])
+        out0, lse0 = msa.sparse_attn_fwd(p2, q0, inp["k"], inp["v"], idx, return_lse=True)
+        idx_h = idx.cpu().numpy()
+        pos = O.query_positions(lq[0], lkv[0])
+        v_h = inp["v"].float().cpu().numpy()
+        out0_h = out0.float().cpu().numpy()
+        lse0_h = lse0.cpu().numpy()
+        for t in range(0, lq[0], 37):
+            for g in range(G):
+                keys = [s for s in range(lkv[0]) if s <= pos[t] and (s // B) in set(idx_h[g, t])]
+                mean = v_h[keys, g].mean(axis=0)
+                for h in range(g * (H // G), (g + 1) * (H // G)):
+                    assert np.abs(out0_h[t, h] - mean).max() <= 1e-2
+                    assert abs(lse0_h[t, h] - math.log(len(keys))) <= 1e-4
+
+
+def test_deterministic():
+    lq, lkv, H, G, d, di, B, k = [1000], [1000], 8, 2, 128, 64, 128, 6
+    inp = W.random_case(31, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    for sched in ("query_major", "kv_major"):
+        prob = C.problem_for(inp, H, G, d, di, B, k, "bf16", sched)
+        a = msa.msa_forward(prob, inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], True)
+        b = msa.msa_forward(prob, inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], True)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_empty_batch():
+    prob = msa.Problem.from_lengths([0], [0], 4, 2, 64, 64, 64, 4, "bf16", DEV)
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=DEV)
+    s = msa.index_score(prob, e, e)
+    idx = msa.topk_select(prob, s)
+    out, _ = msa.sparse_attn_fwd(prob, q, e, e, idx)
+    assert out.shape == (0, 4, 64)
+
+
+# ---------------------------------------------------------- full workloads --
+
+def _sample_rows(lq, planted, seed, n_random=24):
+    rng = np.random.default_rng(seed)
+    rows = set([0, 1, 2, 127, 128, 129, lq - 2, lq - 1])
+    rows.update(rng.integers(0, lq, n_random).tolist())
+    for g_rows in planted:
+        if g_rows:
+            rows.update(rng.choice(g_rows, size=min(3, len(g_rows)), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < lq))
+
+
+@pytest.mark.parametrize("name", ["prefill-32k", "prefill-128k", "chunked-prefill-1m"])
+def test_long_prefill_sampled(name):
+    w = W.WORKLOADS[name]
+    _log(f"workload {name}: generating")
+    inp = W.make_inputs(w, device=DEV, seed=0)
+    rows = [_sample_rows(inp["len_q"][0], inp["planted_q"][0] if inp["planted_q"] else [], 1)]
+    _log(f"workload {name}: running + oracle on {len(rows[0])} rows")
+    st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
+                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows)
+    _log(f"  {st}")
+
+
+def test_decode_workload_sampled():
+    w = W.WORKLOADS["decode-64x256k"]
+    _log("decode workload: generating")
+    inp = W.make_inputs(w, device=DEV, seed=0)
+    rows = [[0] if i % 8 == 0 else [] for i in range(w.num_seqs)]
+    st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
+                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows)
+    _log(f"  {st}")

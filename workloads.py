@@ -180,3 +180,18 @@ def random_case(seed: int, len_q: Sequence[int], len_kv: Sequence[int], H: int, 
     w = Workload(f"case-{seed}", H, G, d, d_idx, block_size, top_k, dtype, False,
                  len_q=tuple(len_q), len_kv=tuple(len_kv))
     return make_inputs(w, device=device, seed=seed)
+
+
+def random_scores(seed: int, G: int, total_q: int, nb: int, levels: int = 0,
+                  device="cpu") -> torch.Tensor:
+    """Synthetic fp32 block-score rows [G, total_q, nb] for checking selection alone.
+
+    levels > 0 draws integers in [-levels, levels] (many exact ties);
+    levels == 0 draws N(0, 1).  A few rows are made constant (all tied)."""
+    g = torch.Generator(device="cpu").manual_seed(_seed(seed, "scores", nb))
+    if levels > 0:
+        s = torch.randint(-levels, levels + 1, (G, total_q, nb), generator=g).to(torch.float32)
+    else:
+        s = torch.randn((G, total_q, nb), generator=g, dtype=torch.float32)
+    s[:, ::17, :] = 1.0
+    return s.to(device)
