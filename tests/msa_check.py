@@ -77,6 +77,8 @@ def check_selection(gpu_idx: np.ndarray, ref_idx: np.ndarray, S: np.ndarray, pos
             if J <= k - 1:
                 assert valid == list(range(J + 1))
                 continue
+            if k == 1:          # only the current block is kept
+                continue
             cand = S[g, t, :J]
             order = np.sort(cand)[::-1]
             delta = 1e-3 * max(abs(order[k - 2]), abs(order[k - 1]))
