@@ -1,14 +1,494 @@
-// KV-major prefill attention (work in progress): not yet available.
+// Main Branch attention for prefill, KV-major ("MiniMax Sparse Attention"
+// page: exact softmax attention restricted to the kept blocks, Summary,
+// paragraph 2; the page's kernels order the loop KV-outer and balance skewed
+// block popularity with pre-scheduled chunks and a two-phase combine without
+// atomics, Summary paragraph 3 and Key points "Kernel design").
+//
+// Query-major gathering loads a 64 KiB K/V block for only H/G rows.  Here the
+// loop is inverted: every kept (group, block) pair is one bucket holding the
+// (query, slot) entries that kept it, and a work item stages ONE block in LDS
+// and runs it against up to 256 gathered (query, head) rows with MFMA.  Each
+// item writes a normalised partial result (O / l in bf16 and its log2-sum-exp)
+// into the slot of the query's kept-block list; a merge kernel then combines
+// the slots of every (query, head) in slot order (deterministic, no atomics).
+//
+// Kernels, in launch order:
+//   kv_clear        counts and cursors <- 0
+//   kv_count        entries per bucket (integer atomics: only counting)
+//   kv_scan         exclusive scans -> entry offsets and work-item offsets
+//   kv_scatter      entry lists (t << 6 | slot) per bucket
+//   kv_partial      one work item = one bucket chunk of <= 256/hpg queries
+//   kv_diag         the current (diagonal) block of every query, causal mask
+//   kv_merge        per query: LSE-weighted merge of its slots -> out, lse
+// Buckets never hold a query's current block: that block is shared by the
+// whole 128-query block of positions, so kv_diag runs it densely.
 #include "launch.hpp"
+#include "msa_common.hpp"
 
 namespace msa {
+namespace {
 
-size_t kvmajor_workspace_bytes(const Dims &) { return 0; }
+constexpr int kRowsPerItem = 256;  // gathered (query, head) rows per work item
+constexpr int kWaves = 4;
 
-hipError_t launch_attn_kvmajor_bf16(const Dims &, const uint16_t *, const uint16_t *,
-                                    const uint16_t *, const int32_t *, uint16_t *, float *, void *,
-                                    hipStream_t) {
-  return hipErrorNotSupported;
+struct KvWs {
+  int32_t *counts, *cursor, *entry_off, *item_off, *entries;
+  float *part_lse;     // [total_q][K][H]      log2-sum-exp of each slot
+  uint16_t *part_o;    // [total_q][K][H][d]   O / l of each slot, bf16
+  int64_t nbk, max_entries, max_items;
+  size_t total_bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+KvWs carve(const Dims &p, void *base) {
+  KvWs w;
+  w.nbk = (int64_t)p.G * p.num_seqs * p.nb_max;
+  w.max_entries = (int64_t)p.G * p.total_q * p.top_k;
+  const int qch = kRowsPerItem / (p.H / p.G);
+  w.max_items = w.max_entries / qch + w.nbk + 1;
+  size_t off = 0;
+  char *c = static_cast<char *>(base);
+  auto take = [&](size_t bytes) {
+    char *r = c == nullptr ? nullptr : c + off;
+    off += align256(bytes);
+    return r;
+  };
+  w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
+  w.cursor = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
+  w.entry_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
+  w.item_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
+  w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_entries));
+  w.part_lse = reinterpret_cast<float *>(take(sizeof(float) * p.total_q * p.top_k * p.H));
+  w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * p.total_q * p.top_k * p.H * p.d));
+  w.total_bytes = off;
+  return w;
+}
+
+// Row position helpers shared by the schedule kernels.
+struct RowInfo {
+  int b;
+  int64_t p;  // absolute position of the query (negative: no causal key)
+};
+__device__ __forceinline__ RowInfo row_info(const int64_t *cu_q, const int64_t *cu_kv,
+                                            int num_seqs, int64_t row) {
+  RowInfo r;
+  r.b = find_seq(cu_q, num_seqs, row);
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, r.b);
+  r.p = sq.base + (row - sq.q0);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void kv_clear_kernel(int32_t *a, int32_t *b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    a[i] = 0;
+    b[i] = 0;
+  }
+}
+
+// Thread per (g, row, slot).  An entry is a kept block strictly below the
+// query's current block (its keys are all causal).
+__global__ __launch_bounds__(256) void kv_count_kernel(
+    const int32_t *__restrict__ block_idx, int32_t *__restrict__ counts,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
+    int64_t total_q, int K, int BS, int nb_max) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)G * total_q * K) return;
+  const int64_t gr = e / K;
+  const int g = (int)(gr / total_q);
+  const int64_t row = gr - (int64_t)g * total_q;
+  const int j = block_idx[e];
+  if (j < 0) return;
+  const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
+  if (ri.p < 0 || (int64_t)j >= ri.p / BS) return;
+  atomicAdd(&counts[((int64_t)g * num_seqs + ri.b) * nb_max + j], 1);
+}
+
+__global__ __launch_bounds__(256) void kv_scatter_kernel(
+    const int32_t *__restrict__ block_idx, int32_t *__restrict__ cursor,
+    const int32_t *__restrict__ entry_off, int32_t *__restrict__ entries,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
+    int64_t total_q, int K, int BS, int nb_max) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)G * total_q * K) return;
+  const int64_t gr = e / K;
+  const int slot = (int)(e - gr * K);
+  const int g = (int)(gr / total_q);
+  const int64_t row = gr - (int64_t)g * total_q;
+  const int j = block_idx[e];
+  if (j < 0) return;
+  const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
+  if (ri.p < 0 || (int64_t)j >= ri.p / BS) return;
+  const int64_t bkt = ((int64_t)g * num_seqs + ri.b) * nb_max + j;
+  const int pos = atomicAdd(&cursor[bkt], 1);
+  entries[entry_off[bkt] + pos] = (int32_t)((row << 6) | slot);
+}
+
+// Single work-group exclusive scans of the bucket counts (entries) and of the
+// per-bucket work-item counts ceil(count / qch).
+__global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t *__restrict__ counts,
+                                                       int32_t *__restrict__ entry_off,
+                                                       int32_t *__restrict__ item_off,
+                                                       int64_t nbk, int qch) {
+  __shared__ int32_t sa[1024], sb[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (nbk + 1023) / 1024;
+  const int64_t lo = min<int64_t>(nbk, tid * per), hi = min<int64_t>(nbk, lo + per);
+  int32_t a = 0, b = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t c = counts[i];
+    a += c;
+    b += (c + qch - 1) / qch;
+  }
+  sa[tid] = a;
+  sb[tid] = b;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t va = tid >= off ? sa[tid - off] : 0;
+    const int32_t vb = tid >= off ? sb[tid - off] : 0;
+    __syncthreads();
+    sa[tid] += va;
+    sb[tid] += vb;
+    __syncthreads();
+  }
+  int32_t ra = sa[tid] - a, rb = sb[tid] - b;  // exclusive prefix of this segment
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t c = counts[i];
+    entry_off[i] = ra;
+    item_off[i] = rb;
+    ra += c;
+    rb += (c + qch - 1) / qch;
+  }
+  if (tid == 1023) {
+    entry_off[nbk] = sa[1023];
+    item_off[nbk] = sb[1023];
+  }
+}
+
+// LDS tile of one K/V block: K row-major [key][d] (stride D+8) and V
+// transposed [d][key] (stride BS+4); both strides keep the MFMA operand reads
+// free of LDS bank conflicts.
+template <int D, int BS>
+struct KvTile {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = BS + 4;
+  uint16_t k[BS * KSTR];
+  uint16_t vt[D * VSTR];
+};
+
+// Stage block rows [s0, s0 + BS) of group g (rows >= lkv become zeros).
+template <int D, int BS>
+__device__ __forceinline__ void stage_kv(KvTile<D, BS> &t, const uint16_t *__restrict__ k,
+                                         const uint16_t *__restrict__ v, int64_t kv0, int64_t s0,
+                                         int64_t lkv, int G, int g) {
+  constexpr int OCT = D / 8;
+  const int tid = threadIdx.x;
+  const int64_t rs = (int64_t)G * D;
+  const uint16_t *kb = k + ((kv0 + s0) * G + g) * (int64_t)D;
+  const uint16_t *vb = v + ((kv0 + s0) * G + g) * (int64_t)D;
+  for (int c = tid; c < BS * OCT; c += kWaves * 64) {
+    const int key = c / OCT, o = c - (c / OCT) * OCT;
+    const u32x4 w = s0 + key < lkv ? ld16(kb + key * rs + 8 * o) : u32x4{0u, 0u, 0u, 0u};
+    st16(t.k + key * KvTile<D, BS>::KSTR + 8 * o, w);
+  }
+  constexpr int KQ = BS / 4;
+  for (int task = tid; task < KQ * OCT; task += kWaves * 64) {
+    const int kq = task % KQ, o = task / KQ;
+    u32x4 w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 4 * kq + r;
+      w[r] = s0 + key < lkv ? ld16(vb + key * rs + 8 * o) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu, a1 = (w[1][e >> 1] >> sh) & 0xffffu;
+      const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu, a3 = (w[3][e >> 1] >> sh) & 0xffffu;
+      u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
+      *reinterpret_cast<u32x2 *>(t.vt + (8 * o + e) * KvTile<D, BS>::VSTR + 4 * kq) = pk;
+    }
+  }
+}
+
+// One wave, 32 rows (MFMA columns) against the staged block:
+//   S^T (keys x rows) = K . Q^T, softmax per row (log2 domain), O^T = V^T . P^T.
+// Row r of the tile is valid if `valid`; its query head is `qh` and position
+// `pos` (keys s0 + key > pos are masked when MASK).  Writes O / l (bf16) and
+// log2-sum-exp to `o_dst` / `lse_dst` (per-lane row pointers; null = skip).
+template <int D, int BS, bool MASK>
+__device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16_t *qrow,
+                                            bool valid, int64_t s0, int64_t pos,
+                                            float scale_log2, uint16_t *o_dst, float *lse_dst) {
+  constexpr int NC = D / 16;     // MFMA steps over d
+  constexpr int KT = BS / 32;    // 32-key tiles
+  constexpr int DT = D / 32;     // 32-wide dv tiles
+  const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+  bf16x8 qb[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qb[c] = valid ? as_bf16x8(ld16(qrow + 16 * c + 8 * half)) : zero_bf16x8();
+  f32x16 s[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    s[kt] = f32x16{};
+    const uint16_t *ar = t.k + (kt * 32 + col) * KvTile<D, BS>::KSTR + 8 * half;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      s[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + 16 * c)), qb[c], s[kt]);
+  }
+  float m = neg_inf();
+  // causal limit inside the block: keys with local index > lim are masked
+  const int lim = MASK ? (int)min<int64_t>(max<int64_t>(pos - s0, -1), BS) : BS;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float z = s[kt][r] * scale_log2;
+      if (MASK && kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) > lim) z = neg_inf();
+      s[kt][r] = z;
+      m = fmaxf(m, z);
+    }
+  }
+  m = fmaxf(m, shfl_xor_f(m, 32));
+  const float msafe = m == neg_inf() ? 0.f : m;
+  // P in bf16, one 16-key MFMA step at a time: step ks takes registers
+  // 8*(ks&1) .. +7 of S^T tile ks/2, i.e. keys 16ks + 4*half + {0..3} and
+  // 16ks + 8 + 4*half + {0..3}; V^T is read below with the same key order.
+  u32x4 pk[BS / 16];
+  float l = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < BS / 16; ++ks) {
+    const int r0 = 8 * (ks & 1);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(s[ks >> 1][r0 + i] - msafe);
+      l += e[i];
+    }
+    pk[ks] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                   pack_bf16x2(e[6], e[7])};
+  }
+  l += shfl_xor_f(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const bool store = valid && o_dst != nullptr;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x16 o = {};
+    const uint16_t *vr = t.vt + (32 * dt + col) * KvTile<D, BS>::VSTR + 4 * half;
+#pragma unroll
+    for (int ks = 0; ks < BS / 16; ++ks) {
+      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 16 * ks);
+      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 * ks + 8);
+      u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
+      o = mfma32x32x16(as_bf16x8(aw), as_bf16x8(pk[ks]), o);
+    }
+    if (store) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w2 = {pack_bf16x2(o[4 * i] * inv, o[4 * i + 1] * inv),
+                    pack_bf16x2(o[4 * i + 2] * inv, o[4 * i + 3] * inv)};
+        *reinterpret_cast<u32x2 *>(o_dst + 32 * dt + 8 * i + 4 * half) = w2;
+      }
+    }
+  }
+  if (!store) return;
+  if (half == 0) *lse_dst = l > 0.f ? m + log2f(l) : neg_inf();
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256, 2) void kv_partial_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ entry_off, const int32_t *__restrict__ item_off,
+    const int32_t *__restrict__ entries, uint16_t *__restrict__ part_o,
+    float *__restrict__ part_lse, const int64_t *__restrict__ cu_q,
+    const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
+    int64_t nbk, int qch, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
+  const int item = blockIdx.x;
+  if (item >= item_off[nbk]) return;
+  int64_t lo = 0, hi = nbk - 1;  // last bucket with item_off <= item
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (item_off[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  const int64_t bkt = lo;
+  const int g = (int)(bkt / ((int64_t)num_seqs * nb_max));
+  const int64_t rem = bkt - (int64_t)g * num_seqs * nb_max;
+  const int b = (int)(rem / nb_max);
+  const int j = (int)(rem - (int64_t)b * nb_max);
+  const int first = (item - item_off[bkt]) * qch;
+  const int n = min(qch, counts[bkt] - first);
+  const int32_t *ent = entries + entry_off[bkt] + first;
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  const int64_t s0 = (int64_t)j * BS;
+  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
+  __syncthreads();
+  const int hpg = H / G;
+  const int nrows = n * hpg;
+  const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
+  for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
+    const int r = rt * 32 + col;
+    const bool valid = r < nrows;
+    const int qi = valid ? r / hpg : 0;
+    const int hh = valid ? r - qi * hpg : 0;
+    const int32_t e = valid ? ent[qi] : 0;
+    const int64_t row = e >> 6;
+    const int slot = e & 63;
+    const int h = g * hpg + hh;
+    const uint16_t *qrow = q + (row * H + h) * (int64_t)D;
+    const int64_t ps = (row * K + slot) * H + h;
+    attend_rows<D, BS, false>(tile, qrow, valid, s0, 0, scale_log2, part_o + ps * D,
+                              part_lse + ps);
+  }
+}
+
+// The current block of each 128-query block of positions, with the causal
+// mask; its partial goes to the slot holding that block (if listed).
+template <int D, int BS>
+__global__ __launch_bounds__(256, 2) void kv_diag_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const int32_t *__restrict__ block_idx,
+    uint16_t *__restrict__ part_o, float *__restrict__ part_lse,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
+    int G, int K, int nb_max, int64_t total_q, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
+  const int J = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  // local queries whose position lies in block J
+  const int64_t i0 = max<int64_t>(0, (int64_t)J * BS - sq.base);
+  const int64_t i1 = min<int64_t>(sq.lq, (int64_t)(J + 1) * BS - sq.base);
+  if (i1 <= i0) return;
+  const int64_t s0 = (int64_t)J * BS;
+  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
+  __syncthreads();
+  const int hpg = H / G;
+  const int nrows = (int)(i1 - i0) * hpg;
+  const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
+  for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
+    const int r = rt * 32 + col;
+    bool valid = r < nrows;
+    const int qi = valid ? r / hpg : 0;
+    const int hh = valid ? r - qi * hpg : 0;
+    const int64_t row = sq.q0 + i0 + qi;
+    const int64_t pos = sq.base + i0 + qi;
+    const int h = g * hpg + hh;
+    int slot = -1;
+    if (valid) {
+      const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
+      for (int s = 0; s < K; ++s)
+        if (br[s] == J) slot = s;
+    }
+    const bool write = valid && slot >= 0;
+    const int64_t ps = (row * K + (slot < 0 ? 0 : slot)) * H + h;
+    const uint16_t *qrow = q + (row * H + h) * (int64_t)D;
+    attend_rows<D, BS, true>(tile, qrow, valid, s0, pos, scale_log2,
+                             write ? part_o + ps * D : nullptr, part_lse + ps);
+  }
+}
+
+// Per query row: merge the slots whose block is causal (0 <= j <= J).
+// 256 threads; each thread owns 8 consecutive output values of one head.
+template <int D>
+__global__ __launch_bounds__(256) void kv_merge_kernel(
+    const int32_t *__restrict__ block_idx, const uint16_t *__restrict__ part_o,
+    const float *__restrict__ part_lse, uint16_t *__restrict__ out, float *__restrict__ lse,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
+    int G, int K, int BS, int64_t total_q) {
+  const int64_t row = blockIdx.x;
+  const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
+  const int64_t J = ri.p < 0 ? -1 : ri.p / BS;
+  const int hpg = H / G;
+  constexpr int OPH = D / 8;  // octets per head
+  for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
+    const int h = oc / OPH, o = oc - (oc / OPH) * OPH;
+    const int g = h / hpg;
+    const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
+    // slots in use: every causal block below J, and the last slot listing J
+    // (the one kv_diag wrote)
+    int diag_slot = -1;
+    for (int s = 0; s < K; ++s)
+      if (br[s] == J) diag_slot = s;
+    float M = neg_inf();
+    for (int s = 0; s < K; ++s) {
+      const int j = br[s];
+      if ((j >= 0 && j < J) || s == diag_slot) M = fmaxf(M, part_lse[(row * K + s) * H + h]);
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    if (M != neg_inf()) {
+      for (int s = 0; s < K; ++s) {
+        const int j = br[s];
+        if (!((j >= 0 && j < J) || s == diag_slot)) continue;
+        const int64_t ps = (row * K + s) * H + h;
+        const float ls = part_lse[ps];
+        if (ls == neg_inf()) continue;
+        const float w = exp2f(ls - M);
+        W += w;
+        const u32x4 x = ld16(part_o + ps * D + 8 * o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(w, bf16_lo(x[i]), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(w, bf16_hi(x[i]), acc[2 * i + 1]);
+        }
+      }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    u32x4 r = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+               pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    st16(out + (row * H + h) * (int64_t)D + 8 * o, r);
+    if (lse != nullptr && o == 0) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
+  }
+}
+
+template <int D, int BS>
+hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const int32_t *block_idx, uint16_t *out, float *lse, void *workspace,
+                      hipStream_t s) {
+  KvWs w = carve(p, workspace);
+  const int hpg = p.H / p.G;
+  const int qch = kRowsPerItem / hpg;
+  const float sl2 = p.scale * kLog2e;
+  const int64_t n_ent = (int64_t)p.G * p.total_q * p.top_k;
+  hipLaunchKernelGGL(kv_clear_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
+                     w.counts, w.cursor, w.nbk);
+  hipLaunchKernelGGL(kv_count_kernel, dim3((unsigned)((n_ent + 255) / 256)), dim3(256), 0, s,
+                     block_idx, w.counts, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q, p.top_k,
+                     p.B, p.nb_max);
+  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, w.entry_off,
+                     w.item_off, w.nbk, qch);
+  hipLaunchKernelGGL(kv_scatter_kernel, dim3((unsigned)((n_ent + 255) / 256)), dim3(256), 0, s,
+                     block_idx, w.cursor, w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs,
+                     p.G, p.total_q, p.top_k, p.B, p.nb_max);
+  hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s, q,
+                     k, v, w.counts, w.entry_off, w.item_off, w.entries, w.part_o, w.part_lse,
+                     p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
+  hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(256), 0, s,
+                     q, k, v, block_idx, w.part_o, w.part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H,
+                     p.G, p.top_k, p.nb_max, p.total_q, sl2);
+  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), 0, s, block_idx,
+                     w.part_o, w.part_lse, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
+                     p.top_k, p.B, p.total_q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t kvmajor_workspace_bytes(const Dims &p) { return carve(p, nullptr).total_bytes; }
+
+hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                    const uint16_t *v, const int32_t *block_idx, uint16_t *out,
+                                    float *lse, void *workspace, hipStream_t s) {
+  if (p.total_q <= 0) return hipSuccess;
+#define MSA_KV_CASE(D_, BS_) \
+  if (p.d == D_ && p.B == BS_) return launch_all<D_, BS_>(p, q, k, v, block_idx, out, lse, workspace, s);
+  MSA_KV_CASE(64, 64) MSA_KV_CASE(64, 128) MSA_KV_CASE(128, 64) MSA_KV_CASE(128, 128)
+#undef MSA_KV_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace msa
