@@ -237,6 +237,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       s[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + 16 * c)), qb[c], s[kt]);
+    __builtin_amdgcn_sched_barrier(0);  // keep one key tile's operands live at a time
   }
   float m = neg_inf();
   // causal limit inside the block: keys with local index > lim are masked
@@ -284,6 +285,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16
       u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
       o = mfma32x32x16(as_bf16x8(aw), as_bf16x8(pk[ks]), o);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (store) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
