@@ -124,6 +124,7 @@ AttnPath attn_path(const msa_problem_t *p, const msa::Dims &d, int *n_split) {
 }
 
 size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
+  if (d.total_q == 0) return 0;  // nothing is launched
   int n_split = 1;
   switch (attn_path(p, d, &n_split)) {
     case AttnPath::kDecodeSplit:
