@@ -87,22 +87,69 @@ __global__ __launch_bounds__(256) void kv_clear_kernel(int32_t *a, int32_t *b, i
   }
 }
 
-// Thread per (g, row, slot).  An entry is a kept block strictly below the
-// query's current block (its keys are all causal).
+// Count and scatter work on tiles of kEntTile consecutive (row, slot) entries
+// of one group.  Entries are kept blocks strictly below the query's current
+// block (all their keys are causal).  Buckets of the tile's first sequence are
+// counted in an LDS histogram first, so a tile issues one global atomic per
+// touched bucket instead of one per entry; rows of other sequences (tiles that
+// straddle a sequence boundary) go straight to global atomics.  The order of
+// entries inside a bucket is not fixed, but every entry's result is computed
+// independently of its neighbours, so outputs do not depend on it.
+constexpr int kEntPerThread = 32;
+constexpr int kEntTile = 256 * kEntPerThread;
+
+struct EntryRef {
+  int64_t bkt;   // bucket, or -1 if the entry is not a partial-attention entry
+  int bin;       // LDS bin (block index) if the entry belongs to the tile's first sequence, else -1
+};
+
+__device__ __forceinline__ EntryRef entry_ref(const int32_t *__restrict__ block_idx,
+                                              int64_t e, int g, int64_t total_q, int K, int BS,
+                                              int nb_max, int num_seqs, int b0,
+                                              const SeqGeom &s0, const int64_t *cu_q,
+                                              const int64_t *cu_kv) {
+  EntryRef r{-1, -1};
+  const int64_t gr = e / K;
+  const int64_t row = gr - (int64_t)g * total_q;
+  const int j = block_idx[e];
+  if (j < 0) return r;
+  int b = b0;
+  int64_t p;
+  if (row >= s0.q0 && row < s0.q0 + s0.lq) {
+    p = s0.base + (row - s0.q0);
+  } else {
+    const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
+    b = ri.b;
+    p = ri.p;
+  }
+  if (p < 0 || (int64_t)j >= p / BS) return r;
+  r.bkt = ((int64_t)g * num_seqs + b) * nb_max + j;
+  r.bin = b == b0 ? j : -1;
+  return r;
+}
+
 __global__ __launch_bounds__(256) void kv_count_kernel(
     const int32_t *__restrict__ block_idx, int32_t *__restrict__ counts,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
     int64_t total_q, int K, int BS, int nb_max) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)G * total_q * K) return;
-  const int64_t gr = e / K;
-  const int g = (int)(gr / total_q);
-  const int64_t row = gr - (int64_t)g * total_q;
-  const int j = block_idx[e];
-  if (j < 0) return;
-  const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
-  if (ri.p < 0 || (int64_t)j >= ri.p / BS) return;
-  atomicAdd(&counts[((int64_t)g * num_seqs + ri.b) * nb_max + j], 1);
+  extern __shared__ int32_t hist[];  // nb_max bins
+  const int g = blockIdx.y;
+  const int64_t e0 = (int64_t)g * total_q * K + (int64_t)blockIdx.x * kEntTile;
+  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * total_q * K);
+  if (e0 >= e_end) return;
+  const int b0 = find_seq(cu_q, num_seqs, (e0 / K) - (int64_t)g * total_q);
+  const SeqGeom s0 = seq_geom(cu_q, cu_kv, b0);
+  for (int i = threadIdx.x; i < nb_max; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int64_t e = e0 + threadIdx.x; e < e_end; e += 256) {
+    const EntryRef r = entry_ref(block_idx, e, g, total_q, K, BS, nb_max, num_seqs, b0, s0, cu_q, cu_kv);
+    if (r.bin >= 0) atomicAdd(&hist[r.bin], 1);
+    else if (r.bkt >= 0) atomicAdd(&counts[r.bkt], 1);
+  }
+  __syncthreads();
+  const int64_t bbase = ((int64_t)g * num_seqs + b0) * nb_max;
+  for (int i = threadIdx.x; i < nb_max; i += 256)
+    if (hist[i] != 0) atomicAdd(&counts[bbase + i], hist[i]);
 }
 
 __global__ __launch_bounds__(256) void kv_scatter_kernel(
@@ -110,19 +157,46 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
     const int32_t *__restrict__ entry_off, int32_t *__restrict__ entries,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
     int64_t total_q, int K, int BS, int nb_max) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)G * total_q * K) return;
-  const int64_t gr = e / K;
-  const int slot = (int)(e - gr * K);
-  const int g = (int)(gr / total_q);
-  const int64_t row = gr - (int64_t)g * total_q;
-  const int j = block_idx[e];
-  if (j < 0) return;
-  const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
-  if (ri.p < 0 || (int64_t)j >= ri.p / BS) return;
-  const int64_t bkt = ((int64_t)g * num_seqs + ri.b) * nb_max + j;
-  const int pos = atomicAdd(&cursor[bkt], 1);
-  entries[entry_off[bkt] + pos] = (int32_t)((row << 6) | slot);
+  extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
+  const int g = blockIdx.y;
+  const int64_t e0 = (int64_t)g * total_q * K + (int64_t)blockIdx.x * kEntTile;
+  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * total_q * K);
+  if (e0 >= e_end) return;
+  const int b0 = find_seq(cu_q, num_seqs, (e0 / K) - (int64_t)g * total_q);
+  const SeqGeom s0 = seq_geom(cu_q, cu_kv, b0);
+  for (int i = threadIdx.x; i < nb_max; i += 256) hist[i] = 0;
+  __syncthreads();
+  int rank[kEntPerThread];
+#pragma unroll
+  for (int i = 0; i < kEntPerThread; ++i) {
+    const int64_t e = e0 + threadIdx.x + 256 * i;
+    rank[i] = -1;
+    if (e < e_end) {
+      const EntryRef r = entry_ref(block_idx, e, g, total_q, K, BS, nb_max, num_seqs, b0, s0, cu_q, cu_kv);
+      if (r.bin >= 0) {
+        rank[i] = atomicAdd(&hist[r.bin], 1);
+      } else if (r.bkt >= 0) {
+        const int pos = atomicAdd(&cursor[r.bkt], 1);
+        const int64_t row = e / K - (int64_t)g * total_q;
+        entries[entry_off[r.bkt] + pos] = (int32_t)((row << 6) | (int)(e % K));
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t bbase = ((int64_t)g * num_seqs + b0) * nb_max;
+  for (int i = threadIdx.x; i < nb_max; i += 256) {
+    const int c = hist[i];
+    hist[i] = c != 0 ? entry_off[bbase + i] + atomicAdd(&cursor[bbase + i], c) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kEntPerThread; ++i) {
+    if (rank[i] < 0) continue;
+    const int64_t e = e0 + threadIdx.x + 256 * i;
+    const int j = block_idx[e];
+    const int64_t row = e / K - (int64_t)g * total_q;
+    entries[hist[j] + rank[i]] = (int32_t)((row << 6) | (int)(e % K));
+  }
 }
 
 // Single work-group exclusive scans of the bucket counts (entries) and of the
@@ -394,56 +468,85 @@ __global__ __launch_bounds__(256, 2) void kv_diag_kernel(
 }
 
 // Per query row: merge the slots whose block is causal (0 <= j <= J).
-// 256 threads; each thread owns 8 consecutive output values of one head.
+// Phase 1 turns the slots' log2-sum-exps into merge weights in LDS (w = 0 for
+// unused slots); phase 2 streams the bf16 partials, each thread owning 8
+// consecutive output values of one head, with the slot loop unrolled so
+// several 16-byte loads are in flight.  Unused slots are never multiplied
+// (their memory may hold anything): the select below drops them.
 template <int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(
     const int32_t *__restrict__ block_idx, const uint16_t *__restrict__ part_o,
     const float *__restrict__ part_lse, uint16_t *__restrict__ out, float *__restrict__ lse,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
     int G, int K, int BS, int64_t total_q) {
+  extern __shared__ float wsh[];  // [K][H] weights, then [H] 1/sum
   const int64_t row = blockIdx.x;
   const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
   const int64_t J = ri.p < 0 ? -1 : ri.p / BS;
   const int hpg = H / G;
-  constexpr int OPH = D / 8;  // octets per head
-  for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
-    const int h = oc / OPH, o = oc - (oc / OPH) * OPH;
+  float *winv = wsh + K * H;
+  for (int h = threadIdx.x; h < H; h += 256) {
     const int g = h / hpg;
     const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
-    // slots in use: every causal block below J, and the last slot listing J
-    // (the one kv_diag wrote)
-    int diag_slot = -1;
+    int diag_slot = -1;  // the last slot listing J is the one the diagonal kernel wrote
     for (int s = 0; s < K; ++s)
       if (br[s] == J) diag_slot = s;
     float M = neg_inf();
     for (int s = 0; s < K; ++s) {
       const int j = br[s];
-      if ((j >= 0 && j < J) || s == diag_slot) M = fmaxf(M, part_lse[(row * K + s) * H + h]);
+      const bool use = (j >= 0 && j < J) || s == diag_slot;
+      const float ls = use ? part_lse[(row * K + s) * H + h] : neg_inf();
+      wsh[s * H + h] = ls;
+      M = fmaxf(M, ls);
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
-    if (M != neg_inf()) {
-      for (int s = 0; s < K; ++s) {
-        const int j = br[s];
-        if (!((j >= 0 && j < J) || s == diag_slot)) continue;
-        const int64_t ps = (row * K + s) * H + h;
-        const float ls = part_lse[ps];
-        if (ls == neg_inf()) continue;
-        const float w = exp2f(ls - M);
-        W += w;
-        const u32x4 x = ld16(part_o + ps * D + 8 * o);
+    for (int s = 0; s < K; ++s) {
+      const float ls = wsh[s * H + h];
+      const float w = (M == neg_inf() || ls == neg_inf()) ? 0.f : exp2f(ls - M);
+      wsh[s * H + h] = w;
+      W += w;
+    }
+    winv[h] = W > 0.f ? 1.f / W : 0.f;
+    if (lse != nullptr) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
+  }
+  __syncthreads();
+  constexpr int OPH = D / 8;  // octets per head
+  const uint16_t *base = part_o + row * (int64_t)K * H * D;
+  for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
+    const int h = oc / OPH;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t *src = base + (int64_t)oc * 8;
+    int s = 0;
+    for (; s + 4 <= K; s += 4) {
+      u32x4 x[4];
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w[u] = wsh[(s + u) * H + h];
+        x[u] = ld16(src + (int64_t)(s + u) * H * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(w, bf16_lo(x[i]), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(w, bf16_hi(x[i]), acc[2 * i + 1]);
+          acc[2 * i] += w[u] > 0.f ? w[u] * bf16_lo(x[u][i]) : 0.f;
+          acc[2 * i + 1] += w[u] > 0.f ? w[u] * bf16_hi(x[u][i]) : 0.f;
         }
       }
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
+    for (; s < K; ++s) {
+      const float w = wsh[s * H + h];
+      const u32x4 x = ld16(src + (int64_t)s * H * D);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w > 0.f ? w * bf16_lo(x[i]) : 0.f;
+        acc[2 * i + 1] += w > 0.f ? w * bf16_hi(x[i]) : 0.f;
+      }
+    }
+    const float inv = winv[h];
     u32x4 r = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-    st16(out + (row * H + h) * (int64_t)D + 8 * o, r);
-    if (lse != nullptr && o == 0) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
+    st16(out + row * (int64_t)H * D + (int64_t)oc * 8, r);
   }
 }
 
@@ -455,24 +558,26 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   const int hpg = p.H / p.G;
   const int qch = kRowsPerItem / hpg;
   const float sl2 = p.scale * kLog2e;
-  const int64_t n_ent = (int64_t)p.G * p.total_q * p.top_k;
   hipLaunchKernelGGL(kv_clear_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
                      w.counts, w.cursor, w.nbk);
-  hipLaunchKernelGGL(kv_count_kernel, dim3((unsigned)((n_ent + 255) / 256)), dim3(256), 0, s,
-                     block_idx, w.counts, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q, p.top_k,
-                     p.B, p.nb_max);
+  const int64_t per_g = p.total_q * p.top_k;
+  const dim3 tiles((unsigned)((per_g + kEntTile - 1) / kEntTile), p.G);
+  const size_t hist_bytes = sizeof(int32_t) * p.nb_max;
+  hipLaunchKernelGGL(kv_count_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.counts,
+                     p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q, p.top_k, p.B, p.nb_max);
   hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, w.entry_off,
                      w.item_off, w.nbk, qch);
-  hipLaunchKernelGGL(kv_scatter_kernel, dim3((unsigned)((n_ent + 255) / 256)), dim3(256), 0, s,
-                     block_idx, w.cursor, w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs,
-                     p.G, p.total_q, p.top_k, p.B, p.nb_max);
+  hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
+                     w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
+                     p.top_k, p.B, p.nb_max);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s, q,
                      k, v, w.counts, w.entry_off, w.item_off, w.entries, w.part_o, w.part_lse,
                      p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(256), 0, s,
                      q, k, v, block_idx, w.part_o, w.part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H,
                      p.G, p.top_k, p.nb_max, p.total_q, sl2);
-  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), 0, s, block_idx,
+  const size_t merge_lds = sizeof(float) * ((size_t)p.top_k * p.H + p.H);
+  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), merge_lds, s, block_idx,
                      w.part_o, w.part_lse, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
                      p.top_k, p.B, p.total_q);
   return hipGetLastError();

@@ -7,11 +7,13 @@
 // Three kernels:
 //  * index_score_mfma_kernel  - bf16 prefill.  A work-group owns 256 queries
 //    x 32 key blocks of one (sequence, group).  The 256 index queries stay in
-//    registers as MFMA B operands for the whole work-group; key blocks are
-//    staged through LDS (register prefetch of the next block); each wave
-//    computes S^T = K * Q^T tiles (keys x queries) with 32x32x16 bf16 MFMA so
-//    a lane holds 16 keys of ONE query column and the block max is an in-lane
-//    max chain plus one cross-half step.  Causal masking is applied only to
+//    registers as MFMA B operands for the whole work-group; key blocks stream
+//    through a 2-3 stage LDS ring filled by direct global->LDS loads (no
+//    register staging; an XOR swizzle applied through the source addresses
+//    keeps the operand reads free of bank conflicts); each wave computes
+//    S^T = K * Q^T tiles (keys x queries) with 32x32x16 bf16 MFMA so a lane
+//    holds 16 keys of ONE query column and the block max is an in-lane max
+//    chain plus one cross-half step.  Causal masking is applied only to
 //    blocks that can hold keys past a query's position.
 //  * index_score_decode_kernel - bf16, one query per sequence: a streaming
 //    scan of the index-key cache (HBM-bound).  Lanes read consecutive 16-byte
@@ -25,27 +27,43 @@ namespace msa {
 namespace {
 
 constexpr int kQT = 256;  // queries per work-group (4 waves x 2 x 32 columns)
-constexpr int kKC = 32;   // key blocks per work-group
+constexpr int kKC = 16;   // key blocks per work-group
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 template <int DI, int BS>
-__global__ __launch_bounds__(256) void index_score_mfma_kernel(
+struct IdxTile {
+  static constexpr int CPR = DI / 8;                 // 16-byte chunks per key row
+  static constexpr int CHUNKS = BS * CPR;            // chunks per key block
+  static constexpr int CPT = CHUNKS / 256;           // chunks per thread per block
+  static constexpr int STAGE = CHUNKS * 16;          // bytes per staged block
+  static constexpr int RPB = 16 / CPR;               // rows sharing one 64-bank line
+  static_assert(CHUNKS % 256 == 0, "a block must split evenly over 256 threads");
+  // LDS position of 16-byte chunk q of key row r: chunks are XOR-swizzled so
+  // the 32 rows read by one MFMA operand load hit distinct banks.
+  __device__ static __forceinline__ int swz(int r, int q) { return r * CPR + (q ^ ((r / RPB) % CPR)); }
+};
+
+template <int DI, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_score_mfma_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     float *__restrict__ scores, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int G, int nb_max, int64_t total_q) {
-  constexpr int QT = kQT, KC = kKC;
-  constexpr int KT = BS / 32;        // 32-key tiles per block
-  constexpr int NK = DI / 16;        // MFMA steps over d_idx
-  constexpr int KROW = DI + 8;       // LDS row stride in bf16 (+16 B vs bank conflicts)
-  constexpr int CPR = DI / 8;        // 16-byte chunks per key row
-  constexpr int CPT = BS * CPR / 256;
-  static_assert((BS * CPR) % 256 == 0, "a block must split evenly over 256 threads");
-  constexpr int RSTR = QT + 1;       // LDS result row stride (floats)
-
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BS * KROW];
+  using T = IdxTile<DI, BS>;
+  constexpr int QT = kQT, KC = kKC, CPR = T::CPR, CPT = T::CPT;
+  constexpr int KT = BS / 32;  // 32-key tiles per block
+  constexpr int NK = DI / 16;  // MFMA steps over d_idx
+  constexpr int RSTR = QT + 1; // result tile row stride (floats)
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][T::STAGE];
   __shared__ float res[KC * RSTR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int kc = blockIdx.x, qt = blockIdx.y, bg = blockIdx.z;
   const int b = bg / G, g = bg - b * G;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
@@ -58,95 +76,144 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(
   const int ncol = j1 - j0;
   const int64_t p_first = sq.base + t0, p_last = sq.base + t0 + nq - 1;
   const int64_t jmax = p_last < 0 ? -1 : p_last / BS;
+  // blocks >= jmask may hold keys past some query's position
   const int jmask = p_first < 0 ? 0 : (int)(p_first / BS);
   const int jc_end = (int)min<int64_t>(j1, jmax + 1);
+  const int nblk = max(0, jc_end - j0);
   float *out_rows = scores + ((int64_t)g * total_q + sq.q0 + t0) * nb_max + j0;
 
-  if (jc_end <= j0) {  // no query of the tile reaches this chunk
-    for (int i = tid; i < nq * ncol; i += 256) {
-      const int r = i / ncol;
-      out_rows[(int64_t)r * nb_max + (i - r * ncol)] = neg_inf();
+  if (nblk > 0) {
+    // The tile's index queries as B operands (Q^T: d_idx x queries).
+    bf16x8 qb[2][NK];
+    int lim0[2];  // key limits relative to block j0: key s is causal iff s <= pos
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int qn = wave * 64 + s * 32 + col;
+      const int64_t pos = sq.base + t0 + qn;
+      lim0[s] = (int)min<int64_t>(max<int64_t>(pos - (int64_t)j0 * BS, -1), (int64_t)KC * BS);
+      if (qn < nq) {
+        const uint16_t *src = q_idx + ((sq.q0 + t0 + qn) * G + g) * (int64_t)DI + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NK; ++c) qb[s][c] = as_bf16x8(ld16(src + 16 * c));
+      } else {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) qb[s][c] = zero_bf16x8();
+      }
     }
-    return;
-  }
 
-  // The tile's index queries as B operands (Q^T: d_idx x queries).
-  bf16x8 qb[2][NK];
-  int64_t pos[2];
+    // Staging: thread tid moves chunks tid + 256*i of each block; chunk P is
+    // key row P / CPR, 16-byte column P % CPR, stored at its swizzled place.
+    const int64_t kstride = (int64_t)G * DI;
+    const uint16_t *kbase = k_idx + ((sq.kv0 + (int64_t)j0 * BS) * G + g) * (int64_t)DI;
+    const int64_t rows_left = sq.lkv - (int64_t)j0 * BS;  // key rows of the chunk that exist
+    auto fetch = [&](int it, u32x4 (&regs)[CPT]) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int qn = wave * 64 + s * 32 + (lane & 31);
-    pos[s] = sq.base + t0 + qn;
-    if (qn < nq) {
-      const uint16_t *src = q_idx + ((sq.q0 + t0 + qn) * G + g) * (int64_t)DI + 8 * half;
+      for (int i = 0; i < CPT; ++i) {
+        const int P = tid + 256 * i;
+        const int r = P / CPR, c = P % CPR;
+        // rows past the sequence end are read from its last row (masked later)
+        const int64_t row = min<int64_t>((int64_t)it * BS + r, rows_left - 1);
+        regs[i] = ld16(kbase + row * kstride + 8 * c);
+      }
+    };
+    auto store = [&](const u32x4 (&regs)[CPT], uint8_t *dst) {
 #pragma unroll
-      for (int c = 0; c < NK; ++c) qb[s][c] = as_bf16x8(ld16(src + 16 * c));
-    } else {
-#pragma unroll
-      for (int c = 0; c < NK; ++c) qb[s][c] = zero_bf16x8();
-    }
-  }
+      for (int i = 0; i < CPT; ++i) {
+        const int P = tid + 256 * i;
+        st16(dst + 16 * T::swz(P / CPR, P % CPR), regs[i]);
+      }
+    };
 
-  const int64_t kstride = (int64_t)G * DI;
-  const uint16_t *kbase = k_idx + (sq.kv0 * G + g) * (int64_t)DI;
-  u32x4 pre[CPT];
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CPR, c = ci - (ci / CPR) * CPR;
-      const int64_t s = (int64_t)j * BS + r;
-      if (s < sq.lkv) pre[i] = ld16(kbase + s * kstride + 8 * c);
-      else pre[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  fetch(j0);
-  for (int j = j0; j < jc_end; ++j) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CPR, c = ci - (ci / CPR) * CPR;
-      st16(ks + r * KROW + 8 * c, pre[i]);
-    }
-    __syncthreads();
-    if (j + 1 < jc_end) fetch(j + 1);
-
-    const bool need_mask = j >= jmask;
-    float m0 = neg_inf(), m1 = neg_inf();
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      f32x16 a0 = {}, a1 = {};
-      const uint16_t *arow = ks + (kt * 32 + (lane & 31)) * KROW + 8 * half;
+    // MFMAs of one key tile of the staged block `cur` (32 keys x 2 x 32 queries)
+    auto mma = [&](const uint8_t *cur, int kt, f32x16 (&a)[2]) {
+      const int r = kt * 32 + col;
+      a[0] = f32x16{};
+      a[1] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NK; ++c) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(arow + 16 * c));
-        a0 = mfma32x32x16(a, qb[0][c], a0);
-        a1 = mfma32x32x16(a, qb[1][c], a1);
+        const bf16x8 op = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+            cur + 16 * T::swz(r, 2 * c + half)));
+        a[0] = mfma32x32x16(op, qb[0][c], a[0]);
+        a[1] = mfma32x32x16(op, qb[1][c], a[1]);
       }
-      if (need_mask) {
+    };
+    auto put = [&](int it, float m0, float m1) {
+      m0 = fmaxf(m0, shfl_xor_f(m0, 32));
+      m1 = fmaxf(m1, shfl_xor_f(m1, 32));
+      if (half == 0) {
+        res[it * RSTR + wave * 64 + col] = m0;
+        res[it * RSTR + wave * 64 + 32 + col] = m1;
+      }
+    };
+
+    // Blocks below jmask are causal for every query of the tile: a pipelined
+    // loop without masking.  The block being computed sits in LDS stage
+    // `cur`; block it+1 (registers `nxt`) goes to the other stage and block
+    // it+3 is fetched into `nxt`, so two blocks are in flight.
+    const int nfull = min(nblk, max(0, jmask - j0));
+    auto step = [&](int it, const uint8_t *cur, uint8_t *other, u32x4 (&nxt)[CPT]) {
+      __syncthreads();  // block it visible; every wave is done with `other`
+      if (it + 1 < nfull) store(nxt, other);
+      if (it + 3 < nfull) fetch(it + 3, nxt);
+      float m0 = neg_inf(), m1 = neg_inf();
+      f32x16 acc[2][2];
+      auto reduce = [&](f32x16 (&a)[2]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t s = (int64_t)j * BS + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (s > pos[0]) a0[r] = neg_inf();
-          if (s > pos[1]) a1[r] = neg_inf();
+        for (int e = 0; e < 16; ++e) {
+          m0 = fmaxf(m0, a[0][e]);
+          m1 = fmaxf(m1, a[1][e]);
+        }
+      };
+      // software pipeline: MFMAs of key tile kt overlap the max of tile kt-1
+      mma(cur, 0, acc[0]);
+#pragma unroll
+      for (int kt = 1; kt < KT; ++kt) {
+        mma(cur, kt, acc[kt & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        reduce(acc[(kt - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      reduce(acc[(KT - 1) & 1]);
+      put(it, m0, m1);
+    };
+    if (nfull > 0) {
+      u32x4 ra[CPT], rb[CPT];
+      fetch(0, ra);
+      store(ra, stage[0]);              // block 0 -> stage 0
+      if (1 < nfull) fetch(1, ra);      // block 1 in ra
+      if (2 < nfull) fetch(2, rb);      // block 2 in rb
+      for (int it = 0; it < nfull; it += 2) {
+        step(it, stage[0], stage[1], ra);                          // stores it+1, fetches it+3
+        if (it + 1 < nfull) step(it + 1, stage[1], stage[0], rb);  // stores it+2, fetches it+4
+      }
+    }
+
+    // The tile's last blocks (its current blocks): causal mask, plain staging.
+    for (int it = nfull; it < nblk; ++it) {
+      u32x4 rr[CPT];
+      fetch(it, rr);
+      __syncthreads();  // every wave is done with stage 0
+      store(rr, stage[0]);
+      __syncthreads();
+      const int l0 = lim0[0] - it * BS, l1 = lim0[1] - it * BS;
+      float m0 = neg_inf(), m1 = neg_inf();
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x16 a[2];
+        mma(stage[0], kt, a);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          m0 = fmaxf(m0, key > l0 ? neg_inf() : a[0][e]);
+          m1 = fmaxf(m1, key > l1 ? neg_inf() : a[1][e]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        m0 = fmaxf(m0, a0[r]);
-        m1 = fmaxf(m1, a1[r]);
-      }
-    }
-    m0 = fmaxf(m0, shfl_xor_f(m0, 32));
-    m1 = fmaxf(m1, shfl_xor_f(m1, 32));
-    if (lane < 32) {
-      res[(j - j0) * RSTR + wave * 64 + lane] = m0;
-      res[(j - j0) * RSTR + wave * 64 + 32 + lane] = m1;
+      put(it, m0, m1);
     }
   }
-  for (int i = tid; i < (j1 - jc_end) * QT; i += 256)
-    res[(jc_end - j0 + i / QT) * RSTR + (i % QT)] = neg_inf();
+  // blocks of the chunk that no query of the tile reaches
+  for (int i = tid; i < (ncol - nblk) * QT; i += 256)
+    res[(nblk + i / QT) * RSTR + (i % QT)] = neg_inf();
   __syncthreads();
   for (int i = tid; i < nq * ncol; i += 256) {
     const int r = i / ncol, c = i - (i / ncol) * ncol;
