@@ -54,6 +54,72 @@ def algorithmic_work(w, len_q, len_kv):
     return f_idx, f_attn, nbytes
 
 
+def kvmajor_partial_work(w, len_q, len_kv, block_idx):
+    """FLOPs of the current (diagonal) blocks, and the algorithmic bytes of the
+    KV-major partial kernel: per (query, group, kept non-current block) it
+    reads the group's H/G query rows and writes H/G partial rows (bf16 O and
+    an fp32 log-sum-exp); each distinct kept (group, block) pair is staged
+    once (K and V)."""
+    import torch
+    G, H, d, B = w.num_kv_groups, w.num_q_heads, w.head_dim, w.block_size
+    hpg = H // G
+    f_diag = 0.0
+    for lq, lkv in zip(len_q, len_kv):
+        base = lkv - lq
+        f_diag += 4.0 * H * d * sum(p % B + 1 for p in range(base, lkv))
+    # entries = kept blocks strictly below the query's current block
+    cu = [0]
+    for lq in len_q:
+        cu.append(cu[-1] + lq)
+    n_entries = 0
+    n_buckets = 0
+    for si, (lq, lkv) in enumerate(zip(len_q, len_kv)):
+        if lq == 0:
+            continue
+        bi = block_idx[:, cu[si]:cu[si + 1], :]
+        pos = torch.arange(lkv - lq, lkv, device=bi.device)
+        J = (pos // B).view(1, -1, 1)
+        valid = (bi >= 0) & (bi < J)
+        n_entries += int(valid.sum().item())
+        nb = -(-lkv // B)
+        keyed = torch.where(valid, bi + nb * torch.arange(G, device=bi.device).view(-1, 1, 1),
+                            torch.full_like(bi, -1))
+        n_buckets += int(torch.unique(keyed[keyed >= 0]).numel())
+    part_bytes = n_entries * hpg * (d * 2 + d * 2 + 4) + n_buckets * 2 * B * d * 2
+    return f_diag, part_bytes
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain copy of known size: reads and writes exactly mib MiB per launch."""
+    import torch
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary for this kernel
+    and workload, or None if there is none or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm-traffic.json")
+    src = {"kv_partial": "attn_kvmajor.hip", "index_score_mfma": "index_score.hip",
+           "index_score_decode": "index_score.hip"}.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, "block_sparse_long_msa_amd", "csrc", src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,7 +129,12 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "query_major", "kv_major"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -91,7 +162,17 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sid = stream.cuda_stream
 
-    def step(ev=None):
+    decode = prob.max_q_len == 1
+    if decode:
+        attn_kernels = ["attn_qmajor", "combine_splits"] if prob.top_k > 4 else ["attn_qmajor"]
+    elif prob.dtype == "bf16" and args.schedule != "query_major":
+        attn_kernels = ["kv_clear", "kv_count", "kv_scan", "kv_scatter", "kv_partial",
+                        "kv_diag", "kv_merge"]
+    else:
+        attn_kernels = ["attn_qmajor"]
+    index_kernel = "index_score_decode" if decode else "index_score_mfma"
+
+    def step(ev=None, pev=None):
         if ev is not None:
             ev[0].record(stream)
         msa.index_score(prob, inp["q_idx"], inp["k_idx"], scores, stream=sid)
@@ -100,8 +181,13 @@ def main():
         msa.topk_select(prob, scores, block_idx, stream=sid)
         if ev is not None:
             ev[2].record(stream)
-        msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
-                            workspace=workspace, stream=sid)
+        if pev is not None:
+            with pev:
+                msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
+                                    workspace=workspace, stream=sid)
+        else:
+            msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
+                                workspace=workspace, stream=sid)
         if ev is not None:
             ev[3].record(stream)
 
@@ -109,12 +195,14 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(events[i])
+        step(events[i], pevents[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -122,9 +210,17 @@ def main():
     ms_per_step = total_ms / args.steps
     st_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
              for i, name in enumerate(("index_score", "topk_select", "sparse_attn_fwd"))}
+    # per-kernel averages: kernel i of the attention call ends at its profile event i
+    kern_ms = {index_kernel: st_ms["index_score"], "topk": st_ms["topk_select"]}
+    for i, name in enumerate(attn_kernels):
+        vals = []
+        for e, pe in zip(events, pevents):
+            prev = e[2] if i == 0 else pe.events[i - 1]
+            vals.append(prev.elapsed_time(pe.events[i]))
+        kern_ms[name] = float(np.mean(vals))
 
     f_idx, f_attn, nbytes = algorithmic_work(w, lq, lkv)
-    decode = prob.max_q_len == 1
+    f_diag, part_bytes = kvmajor_partial_work(w, lq, lkv, block_idx)
     tokens = prob.total_q
     res = {"metric": METRIC}
     stages = {
@@ -135,29 +231,43 @@ def main():
     }
     for s in ("index_score", "sparse_attn_fwd"):
         stages[s]["pct_mfma_peak"] = 100.0 * stages[s]["tflops"] / PEAK_BF16_TFLOPS
-    if decode:
-        value = nbytes / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        dom = "index_score"
+    dom = max(kern_ms, key=lambda k: kern_ms[k])
+    dom_s = kern_ms[dom] * 1e-3
+    if dom == "index_score_mfma":
+        achieved = f_idx / dom_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": f_idx}
+    elif dom == "kv_partial":
+        achieved = part_bytes / dom_s / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": part_bytes,
+                "tflops": (f_attn - f_diag) / dom_s / 1e12}
+    elif dom == "index_score_decode":
         dom_bytes = sum(x * w.num_kv_groups * w.idx_dim * 2 for x in lkv)
-        achieved = dom_bytes / (st_ms[dom] * 1e-3) / 1e9
+        achieved = dom_bytes / dom_s / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                 "algorithmic_bytes_per_launch": dom_bytes}
+    else:
+        achieved = f_attn / dom_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": f_attn}
+    if decode:
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
         extra = {"gbps_step": value, "pct_hbm_peak": 100.0 * value / PEAK_HBM_GBS,
                  "bytes_per_step": nbytes}
     else:
         value = tokens / (ms_per_step * 1e-3)
         unit = "tokens/s"
-        dom = max(("index_score", "sparse_attn_fwd"), key=lambda s: st_ms[s])
-        flops = f_idx if dom == "index_score" else f_attn
-        achieved = flops / (st_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "algorithmic_flops_per_launch": flops}
         extra = {"tflops_effective_attention": f_attn / (st_ms["sparse_attn_fwd"] * 1e-3) / 1e12,
                  "tflops_pipeline": (f_idx + f_attn) / (ms_per_step * 1e-3) / 1e12,
                  "flops_index": f_idx, "flops_attention": f_attn}
+    extra["kernels_ms"] = kern_ms
+    roof["traffic"] = measured_traffic(dom, w.name)
     res.update({"value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
                 "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",

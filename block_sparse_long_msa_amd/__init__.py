@@ -29,8 +29,8 @@ STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHA
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
-            "msa_sparse_attn_fwd", "msa_status_string", "msa_last_error_message",
-            "msa_abi_version")
+            "msa_sparse_attn_fwd", "msa_set_profile_events", "msa_status_string",
+            "msa_last_error_message", "msa_abi_version")
 
 
 class MsaError(RuntimeError):
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_last_error_message.restype = ctypes.c_char_p
     lib.msa_abi_version.argtypes = []
     lib.msa_abi_version.restype = ctypes.c_int
+    lib.msa_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.msa_set_profile_events.restype = None
     _lib_handle = lib
     return lib
 
@@ -215,6 +217,28 @@ def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                                               _ptr(block_idx), _ptr(out), _ptr(lse),
                                               _ptr(workspace), wbytes, s))
     return out, lse
+
+
+class ProfileEvents:
+    """Per-kernel timing via msa_set_profile_events: `with ProfileEvents(n) as ev:`
+    around one library call; afterwards ev.events[i] was recorded right after
+    the call's i-th kernel launch (torch.cuda.Event objects)."""
+
+    def __init__(self, n: int, device=None):
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        stream = torch.cuda.current_stream(dev)
+        for e in self.events:          # torch creates the HIP event on first record
+            e.record(stream)
+        self._arr = (ctypes.c_void_p * n)(*[e.cuda_event for e in self.events])
+
+    def __enter__(self):
+        load_library().msa_set_profile_events(self._arr, len(self.events))
+        return self
+
+    def __exit__(self, *exc):
+        load_library().msa_set_profile_events(None, 0)
+        return False
 
 
 def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):

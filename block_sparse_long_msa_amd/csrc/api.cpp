@@ -38,6 +38,7 @@ constexpr int kMaxHpg = 16;             // heads of a group are MFMA columns (16
 constexpr int kDecodeBlocksPerSplit = 4;
 
 msa_status_t check_problem(const msa_problem_t *p, msa::Dims *d) {
+  msa::profile_begin_call();
   if (p == nullptr) return fail(MSA_ERR_NULL_POINTER, "problem descriptor is NULL");
   if (p->num_seqs < 1) return fail(MSA_ERR_BAD_SHAPE, "num_seqs must be >= 1 (got %d)", p->num_seqs);
   if (p->num_q_heads < 1 || p->num_kv_groups < 1)

@@ -560,26 +560,33 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   const float sl2 = p.scale * kLog2e;
   hipLaunchKernelGGL(kv_clear_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
                      w.counts, w.cursor, w.nbk);
+  profile_mark(s);
   const int64_t per_g = p.total_q * p.top_k;
   const dim3 tiles((unsigned)((per_g + kEntTile - 1) / kEntTile), p.G);
   const size_t hist_bytes = sizeof(int32_t) * p.nb_max;
   hipLaunchKernelGGL(kv_count_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.counts,
                      p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q, p.top_k, p.B, p.nb_max);
+  profile_mark(s);
   hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, w.entry_off,
                      w.item_off, w.nbk, qch);
+  profile_mark(s);
   hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
                      w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
                      p.top_k, p.B, p.nb_max);
+  profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s, q,
                      k, v, w.counts, w.entry_off, w.item_off, w.entries, w.part_o, w.part_lse,
                      p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
+  profile_mark(s);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(256), 0, s,
                      q, k, v, block_idx, w.part_o, w.part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H,
                      p.G, p.top_k, p.nb_max, p.total_q, sl2);
+  profile_mark(s);
   const size_t merge_lds = sizeof(float) * ((size_t)p.top_k * p.H + p.H);
   hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), merge_lds, s, block_idx,
                      w.part_o, w.part_lse, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
                      p.top_k, p.B, p.total_q);
+  profile_mark(s);
   return hipGetLastError();
 }
 

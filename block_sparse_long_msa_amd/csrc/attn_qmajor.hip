@@ -310,6 +310,7 @@ hipError_t launch_attn_qmajor_bf16(const Dims &p, const uint16_t *q, const uint1
     hipLaunchKernelGGL((attn_qmajor_bf16_kernel<D_, BS_>), grid, dim3(64), 0, s, q, k, v,     \
                        block_idx, out, lse, part_o, part_lse, p.cu_q, p.cu_kv, p.num_seqs,   \
                        p.H, p.G, p.top_k, p.total_q, sl2, n_split, bps);                     \
+    profile_mark(s);                                                                          \
     return hipGetLastError();                                                                 \
   }
   MSA_QM_CASE(64, 64) MSA_QM_CASE(64, 128) MSA_QM_CASE(128, 64) MSA_QM_CASE(128, 128)
@@ -327,10 +328,12 @@ hipError_t launch_attn_qmajor_f32(const Dims &p, const float *q, const float *k,
     hipLaunchKernelGGL((attn_qmajor_f32_kernel<64>), grid, dim3(64), 0, s, q, k, v, block_idx,
                        out, lse, part_o, part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.B,
                        p.top_k, p.total_q, p.scale, n_split, bps);
+    profile_mark(s);
   } else if (p.d == 128) {
     hipLaunchKernelGGL((attn_qmajor_f32_kernel<128>), grid, dim3(64), 0, s, q, k, v, block_idx,
                        out, lse, part_o, part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.B,
                        p.top_k, p.total_q, p.scale, n_split, bps);
+    profile_mark(s);
   } else {
     return hipErrorInvalidValue;
   }
@@ -345,6 +348,7 @@ hipError_t launch_combine_splits(const Dims &p, int n_split, const float *part_o
   dim3 grid((unsigned)((n + 3) / 4));
   hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, s, part_o, part_lse, out,
                      out_bf16 ? 1 : 0, lse, p.total_q, p.H, p.d, n_split);
+  profile_mark(s);
   return hipGetLastError();
 }
 

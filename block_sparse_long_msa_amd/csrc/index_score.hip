@@ -314,6 +314,7 @@ hipError_t launch_mfma(const Dims &p, const uint16_t *q_idx, const uint16_t *k_i
   dim3 grid((p.nb_max + kKC - 1) / kKC, (p.max_q_len + kQT - 1) / kQT, p.num_seqs * p.G);
   hipLaunchKernelGGL((index_score_mfma_kernel<DI, BS>), grid, dim3(256), 0, s, q_idx, k_idx,
                      scores, p.cu_q, p.cu_kv, p.G, p.nb_max, p.total_q);
+  profile_mark(s);
   return hipGetLastError();
 }
 
@@ -323,6 +324,7 @@ hipError_t launch_decode(const Dims &p, const uint16_t *q_idx, const uint16_t *k
   dim3 grid((p.nb_max + 3) / 4, p.num_seqs);
   hipLaunchKernelGGL((index_score_decode_kernel<DI, KPS>), grid, dim3(256), 0, s, q_idx, k_idx,
                      scores, p.cu_q, p.cu_kv, p.G, p.B, p.nb_max, p.total_q);
+  profile_mark(s);
   return hipGetLastError();
 }
 
@@ -364,6 +366,7 @@ hipError_t launch_index_score_f32(const Dims &p, const float *q_idx, const float
   dim3 grid((unsigned)((n + 255) / 256), p.G);
   hipLaunchKernelGGL(index_score_f32_kernel, grid, dim3(256), 0, s, q_idx, k_idx, scores, p.cu_q,
                      p.cu_kv, p.num_seqs, p.G, p.d_idx, p.B, p.nb_max, p.total_q);
+  profile_mark(s);
   return hipGetLastError();
 }
 

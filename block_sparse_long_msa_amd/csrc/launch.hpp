@@ -9,6 +9,11 @@
 
 namespace msa {
 
+// Timing hook (profile.cpp): reset at the start of each public call, marked
+// after every kernel launch.
+void profile_begin_call();
+void profile_mark(hipStream_t s);
+
 struct Dims {
   int num_seqs, H, G, d, d_idx, B, top_k;
   int max_q_len;

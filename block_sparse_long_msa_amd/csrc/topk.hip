@@ -191,6 +191,7 @@ hipError_t launch_nch(const Dims &p, const float *scores, int32_t *block_idx, hi
   dim3 grid((unsigned)((rows + 3) / 4));
   hipLaunchKernelGGL((topk_kernel<NCH>), grid, dim3(256), 0, s, scores, block_idx, p.cu_q,
                      p.cu_kv, p.num_seqs, p.G, p.total_q, p.nb_max, p.B, p.top_k);
+  profile_mark(s);
   return hipGetLastError();
 }
 

@@ -141,6 +141,14 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Kernel timing hook (diagnostics).  After this call, every msa_* call on
+ * the calling thread records events[i] (each a hipEvent_t created by the
+ * caller) on its stream right after launching its i-th kernel, for i <
+ * num_events; the count restarts at each call.  Pass NULL / 0 to turn it
+ * off.  The caller keeps ownership of the events and of the array, which
+ * must stay valid while the hook is set. */
+void msa_set_profile_events(void *const *events, int num_events);
+
 /* Static text for a status code. */
 const char *msa_status_string(msa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
