@@ -166,8 +166,8 @@ def main():
     if decode:
         attn_kernels = ["attn_qmajor", "combine_splits"] if prob.top_k > 4 else ["attn_qmajor"]
     elif prob.dtype == "bf16" and args.schedule != "query_major":
-        attn_kernels = ["kv_clear", "kv_count", "kv_scan", "kv_scatter", "kv_partial",
-                        "kv_diag", "kv_merge"]
+        attn_kernels = ["kv_clear", "kv_count", "kv_scan", "kv_scatter", "kv_items",
+                        "kv_partial", "kv_diag", "kv_merge"]
     else:
         attn_kernels = ["attn_qmajor"]
     index_kernel = "index_score_decode" if decode else "index_score_mfma"

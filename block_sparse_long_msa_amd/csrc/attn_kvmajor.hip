@@ -17,6 +17,7 @@
 //   kv_count        entries per bucket (integer atomics: only counting)
 //   kv_scan         exclusive scans -> entry offsets and work-item offsets
 //   kv_scatter      entry lists (t << 6 | slot) per bucket
+//   kv_items        work-item descriptors (bucket, first entry, count)
 //   kv_partial      one work item = one bucket chunk of <= 256/hpg queries
 //   kv_diag         the current (diagonal) block of every query, causal mask
 //   kv_merge        per query: LSE-weighted merge of its slots -> out, lse
@@ -33,6 +34,7 @@ constexpr int kWaves = 4;
 
 struct KvWs {
   int32_t *counts, *cursor, *entry_off, *item_off, *entries;
+  int32_t *item_desc;    // per work item: bucket, first entry, entry count, 0
   float *part_lse;     // [total_q][K][H]      log2-sum-exp of each slot
   uint16_t *part_o;    // [total_q][K][H][d]   O / l of each slot, bf16
   int64_t nbk, max_entries, max_items;
@@ -59,6 +61,7 @@ KvWs carve(const Dims &p, void *base) {
   w.entry_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
   w.item_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
   w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_entries));
+  w.item_desc = reinterpret_cast<int32_t *>(take(4 * sizeof(int32_t) * w.max_items));
   w.part_lse = reinterpret_cast<float *>(take(sizeof(float) * p.total_q * p.top_k * p.H));
   w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * p.total_q * p.top_k * p.H * p.d));
   w.total_bytes = off;
@@ -240,6 +243,24 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t *__restrict
   }
 }
 
+// Thread per bucket: writes the descriptors of the bucket's work items
+// (bucket, first entry, entry count), so a work item starts after one load.
+__global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict__ counts,
+                                                       const int32_t *__restrict__ entry_off,
+                                                       const int32_t *__restrict__ item_off,
+                                                       int32_t *__restrict__ item_desc,
+                                                       int64_t nbk, int qch) {
+  const int64_t bkt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (bkt >= nbk) return;
+  const int cnt = counts[bkt];
+  const int e0 = entry_off[bkt];
+  const int first = item_off[bkt];
+  for (int i = 0; i * qch < cnt; ++i) {
+    u32x4 d = {(uint32_t)bkt, (uint32_t)(e0 + i * qch), (uint32_t)min(qch, cnt - i * qch), 0u};
+    st16(item_desc + 4 * (int64_t)(first + i), d);
+  }
+}
+
 // LDS tile of one K/V block: K row-major [key][d] (stride D+8) and V
 // transposed [d][key] (stride BS+4); both strides keep the MFMA operand reads
 // free of LDS bank conflicts.
@@ -286,23 +307,37 @@ __device__ __forceinline__ void stage_kv(KvTile<D, BS> &t, const uint16_t *__res
   }
 }
 
+// Q^T operands of one lane's row (B operand of S^T = K . Q^T): 16 values of
+// d per MFMA step, lanes 0-31 and 32-63 taking the two halves of each step.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, bool valid) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qb[c] = valid ? as_bf16x8(ld16(qrow + 16 * c + 8 * half)) : zero_bf16x8();
+}
+
+// Partial O rows are stored with d permuted to the MFMA result layout, so a
+// lane writes its 16 values of a 32-wide dv tile as 32 contiguous bytes:
+// stored position 32*dt + 16*half + 4*i + e holds dv = 32*dt + 8*i + 4*half + e.
+__device__ __forceinline__ int partial_dv(int pos) {
+  const int dt = pos >> 5, half = (pos >> 4) & 1, i = (pos >> 2) & 3, e = pos & 3;
+  return 32 * dt + 8 * i + 4 * half + e;
+}
+
 // One wave, 32 rows (MFMA columns) against the staged block:
 //   S^T (keys x rows) = K . Q^T, softmax per row (log2 domain), O^T = V^T . P^T.
-// Row r of the tile is valid if `valid`; its query head is `qh` and position
-// `pos` (keys s0 + key > pos are masked when MASK).  Writes O / l (bf16) and
-// log2-sum-exp to `o_dst` / `lse_dst` (per-lane row pointers; null = skip).
+// Row r of the tile is valid if `valid`; its Q operands are `qb` and its
+// position `pos` (keys s0 + key > pos are masked when MASK).  Writes O / l
+// (bf16, permuted d) and log2-sum-exp to `o_dst` / `lse_dst` (null = skip).
 template <int D, int BS, bool MASK>
-__device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16_t *qrow,
+__device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8 (&qb)[D / 16],
                                             bool valid, int64_t s0, int64_t pos,
                                             float scale_log2, uint16_t *o_dst, float *lse_dst) {
   constexpr int NC = D / 16;     // MFMA steps over d
   constexpr int KT = BS / 32;    // 32-key tiles
   constexpr int DT = D / 32;     // 32-wide dv tiles
   const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
-  bf16x8 qb[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    qb[c] = valid ? as_bf16x8(ld16(qrow + 16 * c + 8 * half)) : zero_bf16x8();
   f32x16 s[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
@@ -313,21 +348,21 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16
       s[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + 16 * c)), qb[c], s[kt]);
     __builtin_amdgcn_sched_barrier(0);  // keep one key tile's operands live at a time
   }
-  float m = neg_inf();
+  // max over the raw logits (the scale is positive), masked keys at -inf
+  float mraw = neg_inf();
   // causal limit inside the block: keys with local index > lim are masked
   const int lim = MASK ? (int)min<int64_t>(max<int64_t>(pos - s0, -1), BS) : BS;
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float z = s[kt][r] * scale_log2;
-      if (MASK && kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) > lim) z = neg_inf();
-      s[kt][r] = z;
-      m = fmaxf(m, z);
+      if (MASK && kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) > lim) s[kt][r] = neg_inf();
+      mraw = fmaxf(mraw, s[kt][r]);
     }
   }
-  m = fmaxf(m, shfl_xor_f(m, 32));
-  const float msafe = m == neg_inf() ? 0.f : m;
+  mraw = fmaxf(mraw, shfl_xor_f(mraw, 32));
+  const float m = mraw * scale_log2;  // max of the log2-domain logits
+  const float msafe = mraw == neg_inf() ? 0.f : m;
   // P in bf16, one 16-key MFMA step at a time: step ks takes registers
   // 8*(ks&1) .. +7 of S^T tile ks/2, i.e. keys 16ks + 4*half + {0..3} and
   // 16ks + 8 + 4*half + {0..3}; V^T is read below with the same key order.
@@ -339,7 +374,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      e[i] = __builtin_amdgcn_exp2f(s[ks >> 1][r0 + i] - msafe);
+      e[i] = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][r0 + i], scale_log2, -msafe));
       l += e[i];
     }
     pk[ks] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
@@ -359,15 +394,17 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const uint16
       u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
       o = mfma32x32x16(as_bf16x8(aw), as_bf16x8(pk[ks]), o);
     }
-    __builtin_amdgcn_sched_barrier(0);
     if (store) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w2 = {pack_bf16x2(o[4 * i] * inv, o[4 * i + 1] * inv),
-                    pack_bf16x2(o[4 * i + 2] * inv, o[4 * i + 3] * inv)};
-        *reinterpret_cast<u32x2 *>(o_dst + 32 * dt + 8 * i + 4 * half) = w2;
-      }
+      // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
+      uint16_t *dst = o_dst + 32 * dt + 16 * half;
+      u32x4 w0 = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                  pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+      u32x4 w1 = {pack_bf16x2(o[8] * inv, o[9] * inv), pack_bf16x2(o[10] * inv, o[11] * inv),
+                  pack_bf16x2(o[12] * inv, o[13] * inv), pack_bf16x2(o[14] * inv, o[15] * inv)};
+      st16(dst, w0);
+      st16(dst + 8, w1);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (!store) return;
   if (half == 0) *lse_dst = l > 0.f ? m + log2f(l) : neg_inf();
@@ -378,46 +415,52 @@ __global__ __launch_bounds__(256, 2) void kv_partial_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ entry_off, const int32_t *__restrict__ item_off,
-    const int32_t *__restrict__ entries, uint16_t *__restrict__ part_o,
-    float *__restrict__ part_lse, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
-    int64_t nbk, int qch, float scale_log2) {
+    const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
+    uint16_t *__restrict__ part_o, float *__restrict__ part_lse,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
+    int G, int K, int nb_max, int64_t nbk, int qch, float scale_log2) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
   const int item = blockIdx.x;
   if (item >= item_off[nbk]) return;
-  int64_t lo = 0, hi = nbk - 1;  // last bucket with item_off <= item
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (item_off[mid] <= item) lo = mid; else hi = mid - 1;
-  }
-  const int64_t bkt = lo;
+  const u32x4 desc = ld16(item_desc + 4 * (int64_t)item);
+  const int64_t bkt = desc[0];
   const int g = (int)(bkt / ((int64_t)num_seqs * nb_max));
   const int64_t rem = bkt - (int64_t)g * num_seqs * nb_max;
   const int b = (int)(rem / nb_max);
   const int j = (int)(rem - (int64_t)b * nb_max);
-  const int first = (item - item_off[bkt]) * qch;
-  const int n = min(qch, counts[bkt] - first);
-  const int32_t *ent = entries + entry_off[bkt] + first;
+  const int n = (int)desc[2];
+  const int32_t *ent = entries + desc[1];
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
   const int64_t s0 = (int64_t)j * BS;
-  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
-  __syncthreads();
   const int hpg = H / G;
   const int nrows = n * hpg;
   const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
-  for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
-    const int r = rt * 32 + col;
-    const bool valid = r < nrows;
-    const int qi = valid ? r / hpg : 0;
-    const int hh = valid ? r - qi * hpg : 0;
-    const int32_t e = valid ? ent[qi] : 0;
+  // Each wave owns row tiles wave and wave + 4 (an item has <= 256 rows);
+  // their gathered Q rows are requested before the K/V block is staged.
+  constexpr int kTiles = kRowsPerItem / 32 / kWaves;
+  bf16x8 qb[kTiles][D / 16];
+  bool valid[kTiles];
+  int64_t ps[kTiles];
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    const int r = (wave + kWaves * u) * 32 + col;
+    valid[u] = r < nrows;
+    const int qi = valid[u] ? r / hpg : 0;
+    const int hh = valid[u] ? r - qi * hpg : 0;
+    const int32_t e = valid[u] ? ent[qi] : 0;
     const int64_t row = e >> 6;
     const int slot = e & 63;
     const int h = g * hpg + hh;
-    const uint16_t *qrow = q + (row * H + h) * (int64_t)D;
-    const int64_t ps = (row * K + slot) * H + h;
-    attend_rows<D, BS, false>(tile, qrow, valid, s0, 0, scale_log2, part_o + ps * D,
-                              part_lse + ps);
+    load_q<D>(qb[u], q + (row * H + h) * (int64_t)D, valid[u]);
+    ps[u] = (row * K + slot) * H + h;
+  }
+  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    if ((wave + kWaves * u) * 32 >= nrows) break;
+    attend_rows<D, BS, false>(tile, qb[u], valid[u], s0, 0, scale_log2, part_o + ps[u] * D,
+                              part_lse + ps[u]);
   }
 }
 
@@ -440,30 +483,49 @@ __global__ __launch_bounds__(256, 2) void kv_diag_kernel(
   const int64_t i1 = min<int64_t>(sq.lq, (int64_t)(J + 1) * BS - sq.base);
   if (i1 <= i0) return;
   const int64_t s0 = (int64_t)J * BS;
-  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
-  __syncthreads();
   const int hpg = H / G;
   const int nrows = (int)(i1 - i0) * hpg;
   const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
-  for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
+  // row tile rt -> (valid, Q operands, slot of J, position); the next tile's
+  // Q rows are requested while the current tile computes
+  struct RowT {
+    bool valid;
+    int64_t row, pos;
+    int h;
+  };
+  auto row_of = [&](int rt) {
+    RowT x;
     const int r = rt * 32 + col;
-    bool valid = r < nrows;
-    const int qi = valid ? r / hpg : 0;
-    const int hh = valid ? r - qi * hpg : 0;
-    const int64_t row = sq.q0 + i0 + qi;
-    const int64_t pos = sq.base + i0 + qi;
-    const int h = g * hpg + hh;
+    x.valid = r < nrows;
+    const int qi = x.valid ? r / hpg : 0;
+    const int hh = x.valid ? r - qi * hpg : 0;
+    x.row = sq.q0 + i0 + qi;
+    x.pos = sq.base + i0 + qi;
+    x.h = g * hpg + hh;
+    return x;
+  };
+  bf16x8 qa[D / 16];
+  RowT cur = row_of(wave);
+  load_q<D>(qa, q + (cur.row * H + cur.h) * (int64_t)D, cur.valid);
+  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
+  __syncthreads();
+  for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
+    bf16x8 qn[D / 16];
+    const RowT nxt = row_of(rt + kWaves);
+    load_q<D>(qn, q + (nxt.row * H + nxt.h) * (int64_t)D, nxt.valid);
     int slot = -1;
-    if (valid) {
-      const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
+    if (cur.valid) {
+      const int32_t *br = block_idx + ((int64_t)g * total_q + cur.row) * K;
       for (int s = 0; s < K; ++s)
         if (br[s] == J) slot = s;
     }
-    const bool write = valid && slot >= 0;
-    const int64_t ps = (row * K + (slot < 0 ? 0 : slot)) * H + h;
-    const uint16_t *qrow = q + (row * H + h) * (int64_t)D;
-    attend_rows<D, BS, true>(tile, qrow, valid, s0, pos, scale_log2,
+    const bool write = cur.valid && slot >= 0;
+    const int64_t ps = (cur.row * K + (slot < 0 ? 0 : slot)) * H + cur.h;
+    attend_rows<D, BS, true>(tile, qa, cur.valid, s0, cur.pos, scale_log2,
                              write ? part_o + ps * D : nullptr, part_lse + ps);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qa[c] = qn[c];
+    cur = nxt;
   }
 }
 
@@ -510,7 +572,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     if (lse != nullptr) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
   }
   __syncthreads();
-  constexpr int OPH = D / 8;  // octets per head
+  constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
   const uint16_t *base = part_o + row * (int64_t)K * H * D;
   for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
     const int h = oc / OPH;
@@ -544,9 +606,14 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
       }
     }
     const float inv = winv[h];
-    u32x4 r = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-               pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-    st16(out + row * (int64_t)H * D + (int64_t)oc * 8, r);
+    // the 8 stored positions 8*o8 .. +7 are two runs of 4 consecutive dv
+    const int o8 = oc - h * OPH;
+    const int dv0 = partial_dv(8 * o8), dv1 = partial_dv(8 * o8 + 4);
+    uint16_t *orow = out + row * (int64_t)H * D + (int64_t)h * D;
+    u32x2 r0 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    u32x2 r1 = {pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    *reinterpret_cast<u32x2 *>(orow + dv0) = r0;
+    *reinterpret_cast<u32x2 *>(orow + dv1) = r1;
   }
 }
 
@@ -574,8 +641,11 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
                      w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
                      p.top_k, p.B, p.nb_max);
   profile_mark(s);
+  hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
+                     w.counts, w.entry_off, w.item_off, w.item_desc, w.nbk, qch);
+  profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s, q,
-                     k, v, w.counts, w.entry_off, w.item_off, w.entries, w.part_o, w.part_lse,
+                     k, v, w.counts, w.entry_off, w.item_off, w.entries, w.item_desc, w.part_o, w.part_lse,
                      p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
   profile_mark(s);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(256), 0, s,
