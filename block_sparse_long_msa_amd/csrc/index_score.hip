@@ -5,8 +5,8 @@
 // <q_idx[row, g], k_idx[s, g]>, and -inf where block j holds no causal key.
 //
 // Three kernels:
-//  * index_score_mfma_kernel  - bf16 prefill.  A work-group owns 256 queries
-//    x 32 key blocks of one (sequence, group).  The 256 index queries stay in
+//  * index_score_mfma_kernel  - bf16 prefill.  A work-group (8 waves) owns 512
+//    queries x 16 key blocks of one (sequence, group).  The index queries stay in
 //    registers as MFMA B operands for the whole work-group; key blocks stream
 //    through a 2-3 stage LDS ring filled by direct global->LDS loads (no
 //    register staging; an XOR swizzle applied through the source addresses
@@ -26,7 +26,9 @@
 namespace msa {
 namespace {
 
-constexpr int kQT = 256;  // queries per work-group (4 waves x 2 x 32 columns)
+constexpr int kIdxWaves = 8;
+constexpr int kIdxThreads = 64 * kIdxWaves;
+constexpr int kQT = 64 * kIdxWaves;  // queries per work-group (each wave 2 x 32 columns)
 constexpr int kKC = 16;   // key blocks per work-group
 
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
@@ -40,17 +42,17 @@ template <int DI, int BS>
 struct IdxTile {
   static constexpr int CPR = DI / 8;                 // 16-byte chunks per key row
   static constexpr int CHUNKS = BS * CPR;            // chunks per key block
-  static constexpr int CPT = CHUNKS / 256;           // chunks per thread per block
+  static constexpr int CPT = (CHUNKS + kIdxThreads - 1) / kIdxThreads;  // chunks per thread
   static constexpr int STAGE = CHUNKS * 16;          // bytes per staged block
   static constexpr int RPB = 16 / CPR;               // rows sharing one 64-bank line
-  static_assert(CHUNKS % 256 == 0, "a block must split evenly over 256 threads");
+  static_assert(CHUNKS % kIdxThreads == 0 || CHUNKS < kIdxThreads, "uneven block split");
   // LDS position of 16-byte chunk q of key row r: chunks are XOR-swizzled so
   // the 32 rows read by one MFMA operand load hit distinct banks.
   __device__ static __forceinline__ int swz(int r, int q) { return r * CPR + (q ^ ((r / RPB) % CPR)); }
 };
 
 template <int DI, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_score_mfma_kernel(
+__global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI >= 128 ? 2 : 4, DI >= 128 ? 2 : 4))) void index_score_mfma_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     float *__restrict__ scores, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int G, int nb_max, int64_t total_q) {
@@ -64,7 +66,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
-  const int kc = blockIdx.x, qt = blockIdx.y, bg = blockIdx.z;
+  // Query tiles are dispatched last-first: the late tiles see the most causal
+  // blocks, so the heavy work-groups start first and the tail is light.  The
+  // key chunk kc varies fastest, so chunk kc stays on one XCD (and its L2).
+  const int kc = blockIdx.x, qt = gridDim.y - 1 - blockIdx.y, bg = blockIdx.z;
   const int b = bg / G, g = bg - b * G;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
   const int64_t t0 = (int64_t)qt * QT;
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
-    // Staging: thread tid moves chunks tid + 256*i of each block; chunk P is
+    // Staging: thread tid moves chunks tid + 512*i of each block; chunk P is
     // key row P / CPR, 16-byte column P % CPR, stored at its swizzled place.
     const int64_t kstride = (int64_t)G * DI;
     const uint16_t *kbase = k_idx + ((sq.kv0 + (int64_t)j0 * BS) * G + g) * (int64_t)DI;
@@ -109,7 +114,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto fetch = [&](int it, u32x4 (&regs)[CPT]) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int P = tid + 256 * i;
+        const int P = tid + kIdxThreads * i;
+        if (P >= T::CHUNKS) break;
         const int r = P / CPR, c = P % CPR;
         // rows past the sequence end are read from its last row (masked later)
         const int64_t row = min<int64_t>((int64_t)it * BS + r, rows_left - 1);
@@ -119,7 +125,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto store = [&](const u32x4 (&regs)[CPT], uint8_t *dst) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int P = tid + 256 * i;
+        const int P = tid + kIdxThreads * i;
+        if (P >= T::CHUNKS) break;
         st16(dst + 16 * T::swz(P / CPR, P % CPR), regs[i]);
       }
     };
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (it + 1 < nfull) store(nxt, other);
       if (it + 3 < nfull) fetch(it + 3, nxt);
       float m0 = neg_inf(), m1 = neg_inf();
-      f32x16 acc[2][2];
+      f32x16 acc[1][2];
       auto reduce = [&](f32x16 (&a)[2]) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -164,16 +171,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           m1 = fmaxf(m1, a[1][e]);
         }
       };
-      // software pipeline: MFMAs of key tile kt overlap the max of tile kt-1
-      mma(cur, 0, acc[0]);
 #pragma unroll
-      for (int kt = 1; kt < KT; ++kt) {
-        mma(cur, kt, acc[kt & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        reduce(acc[(kt - 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        mma(cur, kt, acc[0]);
+        reduce(acc[0]);
       }
-      reduce(acc[(KT - 1) & 1]);
       put(it, m0, m1);
     };
     if (nfull > 0) {
@@ -212,10 +214,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   // blocks of the chunk that no query of the tile reaches
-  for (int i = tid; i < (ncol - nblk) * QT; i += 256)
+  for (int i = tid; i < (ncol - nblk) * QT; i += kIdxThreads)
     res[(nblk + i / QT) * RSTR + (i % QT)] = neg_inf();
   __syncthreads();
-  for (int i = tid; i < nq * ncol; i += 256) {
+  for (int i = tid; i < nq * ncol; i += kIdxThreads) {
     const int r = i / ncol, c = i - (i / ncol) * ncol;
     out_rows[(int64_t)r * nb_max + c] = res[c * RSTR + r];
   }
@@ -312,7 +314,7 @@ template <int DI, int BS>
 hipError_t launch_mfma(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx, float *scores,
                        hipStream_t s) {
   dim3 grid((p.nb_max + kKC - 1) / kKC, (p.max_q_len + kQT - 1) / kQT, p.num_seqs * p.G);
-  hipLaunchKernelGGL((index_score_mfma_kernel<DI, BS>), grid, dim3(256), 0, s, q_idx, k_idx,
+  hipLaunchKernelGGL((index_score_mfma_kernel<DI, BS>), grid, dim3(kIdxThreads), 0, s, q_idx, k_idx,
                      scores, p.cu_q, p.cu_kv, p.G, p.nb_max, p.total_q);
   profile_mark(s);
   return hipGetLastError();
