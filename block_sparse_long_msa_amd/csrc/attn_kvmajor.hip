@@ -30,7 +30,8 @@ namespace msa {
 namespace {
 
 constexpr int kRowsPerItem = 256;  // gathered (query, head) rows per work item
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;          // one 32-row tile per wave
+constexpr int kThreads = 64 * kWaves;
 
 struct KvWs {
   int32_t *counts, *cursor, *entry_off, *item_off, *entries;
@@ -282,13 +283,13 @@ __device__ __forceinline__ void stage_kv(KvTile<D, BS> &t, const uint16_t *__res
   const int64_t rs = (int64_t)G * D;
   const uint16_t *kb = k + ((kv0 + s0) * G + g) * (int64_t)D;
   const uint16_t *vb = v + ((kv0 + s0) * G + g) * (int64_t)D;
-  for (int c = tid; c < BS * OCT; c += kWaves * 64) {
+  for (int c = tid; c < BS * OCT; c += kThreads) {
     const int key = c / OCT, o = c - (c / OCT) * OCT;
     const u32x4 w = s0 + key < lkv ? ld16(kb + key * rs + 8 * o) : u32x4{0u, 0u, 0u, 0u};
     st16(t.k + key * KvTile<D, BS>::KSTR + 8 * o, w);
   }
   constexpr int KQ = BS / 4;
-  for (int task = tid; task < KQ * OCT; task += kWaves * 64) {
+  for (int task = tid; task < KQ * OCT; task += kThreads) {
     const int kq = task % KQ, o = task / KQ;
     u32x4 w[4];
 #pragma unroll
@@ -411,7 +412,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void kv_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kv_partial_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ entry_off, const int32_t *__restrict__ item_off,
@@ -435,8 +436,8 @@ __global__ __launch_bounds__(256, 2) void kv_partial_kernel(
   const int hpg = H / G;
   const int nrows = n * hpg;
   const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
-  // Each wave owns row tiles wave and wave + 4 (an item has <= 256 rows);
-  // their gathered Q rows are requested before the K/V block is staged.
+  // Each wave owns row tile `wave` (+ kWaves*u); its gathered Q rows are
+  // requested before the K/V block is staged.
   constexpr int kTiles = kRowsPerItem / 32 / kWaves;
   bf16x8 qb[kTiles][D / 16];
   bool valid[kTiles];
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(256, 2) void kv_partial_kernel(
 // The current block of each 128-query block of positions, with the causal
 // mask; its partial goes to the slot holding that block (if listed).
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void kv_diag_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kv_diag_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ block_idx,
     uint16_t *__restrict__ part_o, float *__restrict__ part_lse,
@@ -486,8 +487,7 @@ __global__ __launch_bounds__(256, 2) void kv_diag_kernel(
   const int hpg = H / G;
   const int nrows = (int)(i1 - i0) * hpg;
   const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
-  // row tile rt -> (valid, Q operands, slot of J, position); the next tile's
-  // Q rows are requested while the current tile computes
+  // row tile rt -> (valid, query row, position, head)
   struct RowT {
     bool valid;
     int64_t row, pos;
@@ -504,15 +504,12 @@ __global__ __launch_bounds__(256, 2) void kv_diag_kernel(
     x.h = g * hpg + hh;
     return x;
   };
-  bf16x8 qa[D / 16];
-  RowT cur = row_of(wave);
-  load_q<D>(qa, q + (cur.row * H + cur.h) * (int64_t)D, cur.valid);
   stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
   __syncthreads();
   for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
-    bf16x8 qn[D / 16];
-    const RowT nxt = row_of(rt + kWaves);
-    load_q<D>(qn, q + (nxt.row * H + nxt.h) * (int64_t)D, nxt.valid);
+    const RowT cur = row_of(rt);
+    bf16x8 qa[D / 16];
+    load_q<D>(qa, q + (cur.row * H + cur.h) * (int64_t)D, cur.valid);
     int slot = -1;
     if (cur.valid) {
       const int32_t *br = block_idx + ((int64_t)g * total_q + cur.row) * K;
@@ -523,9 +520,6 @@ __global__ __launch_bounds__(256, 2) void kv_diag_kernel(
     const int64_t ps = (cur.row * K + (slot < 0 ? 0 : slot)) * H + cur.h;
     attend_rows<D, BS, true>(tile, qa, cur.valid, s0, cur.pos, scale_log2,
                              write ? part_o + ps * D : nullptr, part_lse + ps);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) qa[c] = qn[c];
-    cur = nxt;
   }
 }
 
@@ -644,11 +638,11 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
                      w.counts, w.entry_off, w.item_off, w.item_desc, w.nbk, qch);
   profile_mark(s);
-  hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s, q,
+  hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, q,
                      k, v, w.counts, w.entry_off, w.item_off, w.entries, w.item_desc, w.part_o, w.part_lse,
                      p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
   profile_mark(s);
-  hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(256), 0, s,
+  hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(kThreads), 0, s,
                      q, k, v, block_idx, w.part_o, w.part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H,
                      p.G, p.top_k, p.nb_max, p.total_q, sl2);
   profile_mark(s);
