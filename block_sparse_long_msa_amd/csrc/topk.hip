@@ -12,9 +12,12 @@
 // candidates in index order with ballot prefix counts emits them ascending;
 // J (larger than every candidate) comes last.  The candidate keys of a row
 // stay in registers (NCH chunks of 64 per lane).  Long rows first cut the
-// search down: the (k-1)-th largest of the 64 lane maxima is a lower bound
-// of the answer, and the few keys at or above it (kept in index order in
-// LDS) hold every selected key; the exact search then runs on those only.
+// search down: the (k-1)-th largest of the 64 lane maxima (128 half-lane
+// maxima when k-1 > 31) is a lower bound of the answer, and the few keys at
+// or above it (kept in index order in LDS) hold every selected key; the
+// exact search then runs on those only.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "msa_common.hpp"
 
@@ -22,7 +25,6 @@ namespace msa {
 namespace {
 
 constexpr int kCandCap = 512;  // candidates kept for the exact search (8 per lane)
-constexpr int kGroups = 4;     // key groups per lane for the lower bound (256 group maxima)
 constexpr int kPruneMinChunks = 8;  // rows of fewer chunks go straight to the exact search
 
 // Exact need-th largest key among NC chunks of 64 keys (0 = absent).
@@ -119,13 +121,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     }
   }
   if (NCH == 0 || NCH >= kPruneMinChunks) {
-    // Lower bound: the need-th largest of 256 group maxima (group r of a lane
-    // = its chunks c with c % 4 == r).  More than `need` groups hold a
-    // candidate, so at least `need` keys are >= it; hence every selected key,
-    // and every key tied with the last one, is >= it.
-    uint32_t gmax[kGroups] = {0u, 0u, 0u, 0u};
-    for (int c = 0; c < nch; ++c) gmax[c & 3] = max(gmax[c & 3], key_at(c));
-    const uint32_t lb = kth_largest<kGroups>(gmax, need);
+    // Lower bound: the need-th largest of the group maxima (group r of a lane
+    // = its chunks c with c % GPL == r; 64*GPL groups).  More than `need`
+    // groups hold a candidate, so at least `need` keys are >= it; hence
+    // every selected key, and every key tied with the last one, is >= it.
+    // One group per lane leaves ~42 expected candidates for need = 31 on
+    // i.i.d. scores, two per lane ~87 for need = 63.
+    uint32_t lb;
+    if (need <= 31) {
+      uint32_t gmax[1] = {0u};
+      for (int c = 0; c < nch; ++c) gmax[0] = max(gmax[0], key_at(c));
+      lb = kth_largest<1>(gmax, need);
+    } else {
+      uint32_t gmax[2] = {0u, 0u};
+      for (int c = 0; c < nch; ++c) gmax[c & 1] = max(gmax[c & 1], key_at(c));
+      lb = kth_largest<2>(gmax, need);
+    }
     int n_cand = 0;
     for (int c = 0; c < nch; ++c) n_cand += __popcll(ballot64(key_at(c) >= lb));
     if (n_cand <= kCandCap) {
@@ -141,16 +152,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         base += __popcll(m);
       }
       wave_lds_sync();
-      constexpr int CC = kCandCap / 64;
-      uint32_t ck[CC];
-      int ci[CC];
+      auto finish = [&](auto tag) {
+        constexpr int CC = decltype(tag)::value;
+        uint32_t ck[CC];
+        int ci[CC];
 #pragma unroll
-      for (int c = 0; c < CC; ++c) {
-        const int i = 64 * c + lane;
-        ck[c] = i < n_cand ? cand_key[i] : 0u;
-        ci[c] = i < n_cand ? cand_idx[i] : 0;
-      }
-      emit_selected<CC>(ck, [&](int c) { return ci[c]; }, kth_largest<CC>(ck, need), need, dst);
+        for (int c = 0; c < CC; ++c) {
+          const int i = 64 * c + lane;
+          ck[c] = i < n_cand ? cand_key[i] : 0u;
+          ci[c] = i < n_cand ? cand_idx[i] : 0;
+        }
+        emit_selected<CC>(ck, [&](int c) { return ci[c]; }, kth_largest<CC>(ck, need), need, dst);
+      };
+      if (n_cand <= 128) finish(std::integral_constant<int, 2>());
+      else finish(std::integral_constant<int, kCandCap / 64>());
       if (lane == 0) dst[need] = J;
       return;
     }
