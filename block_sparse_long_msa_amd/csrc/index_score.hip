@@ -265,11 +265,13 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
   const int nslab = (nkeys + KPS - 1) / KPS;
   const uint16_t *base = k_idx + (sq.kv0 + s_begin) * (int64_t)rowlen + e;
   float mx = neg_inf();
-#pragma unroll 4
+#pragma unroll 8
   for (int i = 0; i < nslab; ++i) {
     const int key = i * KPS + key_in_slab;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (key < nkeys) w = ld16(base + (int64_t)i * 512);
+    // the index-key cache is streamed once per step: non-temporal loads
+    if (key < nkeys)
+      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)i * 512));
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
