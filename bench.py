@@ -85,7 +85,7 @@ def kvmajor_partial_work(w, len_q, len_kv, block_idx):
         keyed = torch.where(valid, bi + nb * torch.arange(G, device=bi.device).view(-1, 1, 1),
                             torch.full_like(bi, -1))
         n_buckets += int(torch.unique(keyed[keyed >= 0]).numel())
-    part_bytes = n_entries * hpg * (d * 2 + d * 2 + 4) + n_buckets * 2 * B * d * 2
+    part_bytes = n_entries * hpg * (d * 2 + d * 2 + 8) + n_buckets * 2 * B * d * 2
     return f_diag, part_bytes
 
 

@@ -119,7 +119,8 @@ AttnPath attn_path(const msa_problem_t *p, const msa::Dims &d, int *n_split) {
     *n_split = (d.top_k + kDecodeBlocksPerSplit - 1) / kDecodeBlocksPerSplit;
     return AttnPath::kDecodeSplit;
   }
-  if (p->dtype == MSA_BF16 && p->schedule != MSA_SCHED_QUERY_MAJOR && d.total_q < (1 << 25))
+  if (p->dtype == MSA_BF16 && p->schedule != MSA_SCHED_QUERY_MAJOR &&
+      d.total_kv <= (int64_t)INT32_MAX && msa::kvmajor_fits(d))
     return AttnPath::kKvMajor;
   return AttnPath::kQueryMajor;
 }

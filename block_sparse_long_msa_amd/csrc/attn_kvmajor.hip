@@ -8,21 +8,27 @@
 // loop is inverted: every kept (group, block) pair is one bucket holding the
 // (query, slot) entries that kept it, and a work item stages ONE block in LDS
 // and runs it against up to 256 gathered (query, head) rows with MFMA.  Each
-// item writes a normalised partial result (O / l in bf16 and its log2-sum-exp)
-// into the slot of the query's kept-block list; a merge kernel then combines
-// the slots of every (query, head) in slot order (deterministic, no atomics).
+// item writes an unnormalised partial result (sum of exp2(z - m) v in bf16,
+// with the row's log2-domain max m and its sum l) into the slot of the
+// query's kept-block list; a merge kernel then combines the slots of every
+// (query, head) in slot order (deterministic, no atomics).
 //
 // Kernels, in launch order:
 //   kv_clear        counts and cursors <- 0
 //   kv_count        entries per bucket (integer atomics: only counting)
 //   kv_scan         exclusive scans -> entry offsets and work-item offsets
 //   kv_scatter      entry lists (t << 6 | slot) per bucket
-//   kv_items        work-item descriptors (bucket, first entry, count)
-//   kv_partial      one work item = one bucket chunk of <= 256/hpg queries
+//   kv_items        work-item descriptors (group, block, first entry, count, sequence)
+//   kv_partial      persistent: one work-group per CU walks a contiguous range
+//                   of work items (one bucket chunk of <= 256/hpg queries each),
+//                   loading the next item while it computes the current one
 //   kv_diag         the current (diagonal) block of every query, causal mask
 //   kv_merge        per query: LSE-weighted merge of its slots -> out, lse
 // Buckets never hold a query's current block: that block is shared by the
 // whole 128-query block of positions, so kv_diag runs it densely.
+#include <algorithm>
+#include <atomic>
+
 #include "launch.hpp"
 #include "msa_common.hpp"
 
@@ -35,9 +41,11 @@ constexpr int kThreads = 64 * kWaves;
 
 struct KvWs {
   int32_t *counts, *cursor, *entry_off, *item_off, *entries;
-  int32_t *item_desc;    // per work item: bucket, first entry, entry count, 0
-  float *part_lse;     // [total_q][K][H]      log2-sum-exp of each slot
-  uint16_t *part_o;    // [total_q][K][H][d]   O / l of each slot, bf16
+  int32_t *item_desc;  // per work item: g << 16 | j, first entry, entry count, first KV row
+  float2 *part_ml;     // [total_q][K][H]      (m, l) of each slot
+  uint16_t *part_o;    // [total_q][K][H][d]   unnormalised O of each slot, bf16
+  uint16_t *trash_o;   // [64][d]  write target of lanes without a row (never read)
+  float2 *trash_ml;    // [64]
   int64_t nbk, max_entries, max_items;
   size_t total_bytes;
 };
@@ -61,10 +69,13 @@ KvWs carve(const Dims &p, void *base) {
   w.cursor = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
   w.entry_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
   w.item_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
-  w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_entries));
+  // item-major with qch slots per item (a bucket's last item is padded)
+  w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_items * qch));
   w.item_desc = reinterpret_cast<int32_t *>(take(4 * sizeof(int32_t) * w.max_items));
-  w.part_lse = reinterpret_cast<float *>(take(sizeof(float) * p.total_q * p.top_k * p.H));
+  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * p.total_q * p.top_k * p.H));
   w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * p.total_q * p.top_k * p.H * p.d));
+  w.trash_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * 64 * p.d));
+  w.trash_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * 64));
   w.total_bytes = off;
   return w;
 }
@@ -156,11 +167,13 @@ __global__ __launch_bounds__(256) void kv_count_kernel(
     if (hist[i] != 0) atomicAdd(&counts[bbase + i], hist[i]);
 }
 
+// Entries are laid out item-major: the bucket's entry of rank `pos` goes to
+// item_off[bucket] * qch + pos, so work item t owns entries [t*qch, t*qch + qch).
 __global__ __launch_bounds__(256) void kv_scatter_kernel(
     const int32_t *__restrict__ block_idx, int32_t *__restrict__ cursor,
-    const int32_t *__restrict__ entry_off, int32_t *__restrict__ entries,
+    const int32_t *__restrict__ item_off, int32_t *__restrict__ entries,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
-    int64_t total_q, int K, int BS, int nb_max) {
+    int64_t total_q, int K, int BS, int nb_max, int qch) {
   extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
   const int g = blockIdx.y;
   const int64_t e0 = (int64_t)g * total_q * K + (int64_t)blockIdx.x * kEntTile;
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
       } else if (r.bkt >= 0) {
         const int pos = atomicAdd(&cursor[r.bkt], 1);
         const int64_t row = e / K - (int64_t)g * total_q;
-        entries[entry_off[r.bkt] + pos] = (int32_t)((row << 6) | (int)(e % K));
+        entries[item_off[r.bkt] * qch + pos] = (int32_t)((row << 6) | (int)(e % K));
       }
     }
   }
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
   const int64_t bbase = ((int64_t)g * num_seqs + b0) * nb_max;
   for (int i = threadIdx.x; i < nb_max; i += 256) {
     const int c = hist[i];
-    hist[i] = c != 0 ? entry_off[bbase + i] + atomicAdd(&cursor[bbase + i], c) : 0;
+    hist[i] = c != 0 ? item_off[bbase + i] * qch + atomicAdd(&cursor[bbase + i], c) : 0;
   }
   __syncthreads();
 #pragma unroll
@@ -245,21 +258,32 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t *__restrict
 }
 
 // Thread per bucket: writes the descriptors of the bucket's work items
-// (bucket, first entry, entry count), so a work item starts after one load.
+// (g << 16 | block, 0, entry count, packed row of the block's first key), so a
+// work item starts after one 16-byte load and no divisions, and fills the
+// unused entry slots of the bucket's last item with row 0 / slot 0 (a valid
+// row to load; the partial kernel never stores for those lanes).
 __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict__ counts,
-                                                       const int32_t *__restrict__ entry_off,
                                                        const int32_t *__restrict__ item_off,
+                                                       int32_t *__restrict__ entries,
                                                        int32_t *__restrict__ item_desc,
-                                                       int64_t nbk, int qch) {
+                                                       const int64_t *__restrict__ cu_kv,
+                                                       int64_t nbk, int num_seqs, int nb_max,
+                                                       int BS, int qch) {
   const int64_t bkt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (bkt >= nbk) return;
   const int cnt = counts[bkt];
-  const int e0 = entry_off[bkt];
+  if (cnt == 0) return;
   const int first = item_off[bkt];
+  const int64_t gb = bkt / nb_max;
+  const uint32_t j = (uint32_t)(bkt - gb * nb_max);
+  const uint32_t g = (uint32_t)(gb / num_seqs);
+  const uint32_t b = (uint32_t)(gb - (int64_t)g * num_seqs);
+  const uint32_t kvrow = (uint32_t)(cu_kv[b] + (int64_t)j * BS);
   for (int i = 0; i * qch < cnt; ++i) {
-    u32x4 d = {(uint32_t)bkt, (uint32_t)(e0 + i * qch), (uint32_t)min(qch, cnt - i * qch), 0u};
+    u32x4 d = {g << 16 | j, 0u, (uint32_t)min(qch, cnt - i * qch), kvrow};
     st16(item_desc + 4 * (int64_t)(first + i), d);
   }
+  for (int pos = cnt; pos % qch != 0; ++pos) entries[(int64_t)first * qch + pos] = 0;
 }
 
 // LDS tile of one K/V block: K row-major [key][d] (stride D+8) and V
@@ -273,35 +297,76 @@ struct KvTile {
   uint16_t vt[D * VSTR];
 };
 
-// Stage block rows [s0, s0 + BS) of group g (rows >= lkv become zeros).
+// One thread's share of a K/V block on its way from HBM to LDS.  K moves as
+// 16-byte octets (8 consecutive d of one key); V moves as groups of 4 keys at
+// one octet, transposed in registers.  Both mappings put consecutive lanes on
+// consecutive octets of a row, so every load instruction reads whole rows.
 template <int D, int BS>
-__device__ __forceinline__ void stage_kv(KvTile<D, BS> &t, const uint16_t *__restrict__ k,
+struct KvRegs {
+  static constexpr int OCT = D / 8;
+  static constexpr int KTASKS = BS * OCT;        // K octets
+  static constexpr int VTASKS = BS / 4 * OCT;    // V (4-key group, octet) pairs
+  static constexpr int KN = (KTASKS + kThreads - 1) / kThreads;
+  static constexpr int VN = (VTASKS + kThreads - 1) / kThreads;
+  u32x4 k[KN];
+  u32x4 v[VN][4];
+};
+
+// Loads block rows [s0, s0 + BS) of group g into registers.  With GUARD, rows
+// at or past lkv read as zeros; without it every row must exist.
+template <int D, int BS, bool GUARD>
+__device__ __forceinline__ void fetch_kv(KvRegs<D, BS> &r, const uint16_t *__restrict__ k,
                                          const uint16_t *__restrict__ v, int64_t kv0, int64_t s0,
                                          int64_t lkv, int G, int g) {
-  constexpr int OCT = D / 8;
+  using R = KvRegs<D, BS>;
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)G * D;
   const uint16_t *kb = k + ((kv0 + s0) * G + g) * (int64_t)D;
   const uint16_t *vb = v + ((kv0 + s0) * G + g) * (int64_t)D;
-  for (int c = tid; c < BS * OCT; c += kThreads) {
-    const int key = c / OCT, o = c - (c / OCT) * OCT;
-    const u32x4 w = s0 + key < lkv ? ld16(kb + key * rs + 8 * o) : u32x4{0u, 0u, 0u, 0u};
-    st16(t.k + key * KvTile<D, BS>::KSTR + 8 * o, w);
-  }
-  constexpr int KQ = BS / 4;
-  for (int task = tid; task < KQ * OCT; task += kThreads) {
-    const int kq = task % KQ, o = task / KQ;
-    u32x4 w[4];
+  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 4 * kq + r;
-      w[r] = s0 + key < lkv ? ld16(vb + key * rs + 8 * o) : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < R::KN; ++i) {
+    const int c = tid + i * kThreads;
+    const int key = c / R::OCT, o = c % R::OCT;
+    const bool ok = (R::KTASKS % kThreads == 0 || c < R::KTASKS) && (!GUARD || s0 + key < lkv);
+    r.k[i] = ok ? ld16(kb + key * rs + 8 * o) : z;
+  }
+#pragma unroll
+  for (int i = 0; i < R::VN; ++i) {
+    const int task = tid + i * kThreads;
+    const int kq = task / R::OCT, o = task % R::OCT;
+    const bool in = R::VTASKS % kThreads == 0 || task < R::VTASKS;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 4 * kq + e;
+      const bool ok = in && (!GUARD || s0 + key < lkv);
+      r.v[i][e] = ok ? ld16(vb + key * rs + 8 * o) : z;
     }
+  }
+}
+
+template <int D, int BS>
+__device__ __forceinline__ void store_kv(KvTile<D, BS> &t, const KvRegs<D, BS> &r) {
+  using R = KvRegs<D, BS>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < R::KN; ++i) {
+    const int c = tid + i * kThreads;
+    if (R::KTASKS % kThreads != 0 && c >= R::KTASKS) break;
+    const int key = c / R::OCT, o = c % R::OCT;
+    st16(t.k + key * KvTile<D, BS>::KSTR + 8 * o, r.k[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < R::VN; ++i) {
+    const int task = tid + i * kThreads;
+    if (R::VTASKS % kThreads != 0 && task >= R::VTASKS) break;
+    const int kq = task / R::OCT, o = task % R::OCT;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // d = 8o + e of keys 4kq .. 4kq+3: the e-th bf16 of each key's octet
       const int sh = (e & 1) * 16;
-      const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu, a1 = (w[1][e >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu, a3 = (w[3][e >> 1] >> sh) & 0xffffu;
+      const uint32_t a0 = (r.v[i][0][e >> 1] >> sh) & 0xffffu, a1 = (r.v[i][1][e >> 1] >> sh) & 0xffffu;
+      const uint32_t a2 = (r.v[i][2][e >> 1] >> sh) & 0xffffu, a3 = (r.v[i][3][e >> 1] >> sh) & 0xffffu;
       u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
       *reinterpret_cast<u32x2 *>(t.vt + (8 * o + e) * KvTile<D, BS>::VSTR + 4 * kq) = pk;
     }
@@ -328,26 +393,48 @@ __device__ __forceinline__ int partial_dv(int pos) {
 
 // One wave, 32 rows (MFMA columns) against the staged block:
 //   S^T (keys x rows) = K . Q^T, softmax per row (log2 domain), O^T = V^T . P^T.
-// Row r of the tile is valid if `valid`; its Q operands are `qb` and its
-// position `pos` (keys s0 + key > pos are masked when MASK).  Writes O / l
-// (bf16, permuted d) and log2-sum-exp to `o_dst` / `lse_dst` (null = skip).
-template <int D, int BS, bool MASK>
+// The lane's row has Q operands `qb` and position `pos` (keys s0 + key > pos
+// are masked when MASK).  Writes the unnormalised O = sum_s exp2(z_s - m) v_s
+// (bf16, permuted d) and (m, l) to `o_dst` / `ml_dst`, where z_s are the
+// log2-domain logits, m their max and l = sum_s exp2(z_s - m).  Every lane
+// stores (lanes without a row of their own point at scratch rows): stores
+// outside divergent branches keep the memory counters' waits exact.
+// WIDE keeps more operands in flight (independent accumulators for the four
+// key tiles of S^T, a whole dv tile of V^T read ahead of its MFMAs) for
+// kernels with a 256-register budget; the narrow form fits 128 registers.
+template <int D, int BS, bool MASK, bool WIDE>
 __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8 (&qb)[D / 16],
-                                            bool valid, int64_t s0, int64_t pos,
-                                            float scale_log2, uint16_t *o_dst, float *lse_dst) {
+                                            int64_t s0, int64_t pos, float scale_log2,
+                                            uint16_t *o_dst, float2 *ml_dst) {
   constexpr int NC = D / 16;     // MFMA steps over d
   constexpr int KT = BS / 32;    // 32-key tiles
   constexpr int DT = D / 32;     // 32-wide dv tiles
   const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+  // S^T: the four key tiles accumulate independently, so consecutive MFMAs
+  // never wait on each other.
   f32x16 s[KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    s[kt] = f32x16{};
-    const uint16_t *ar = t.k + (kt * 32 + col) * KvTile<D, BS>::KSTR + 8 * half;
+  for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+  const uint16_t *ar = t.k + col * KvTile<D, BS>::KSTR + 8 * half;
+  if constexpr (WIDE) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      s[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + 16 * c)), qb[c], s[kt]);
-    __builtin_amdgcn_sched_barrier(0);  // keep one key tile's operands live at a time
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        s[kt] = mfma32x32x16(
+            as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c)),
+            qb[c], s[kt]);
+    }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        s[kt] = mfma32x32x16(
+            as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c)),
+            qb[c], s[kt]);
+      __builtin_amdgcn_sched_barrier(0);  // one key tile's operands live at a time
+    }
   }
   // max over the raw logits (the scale is positive), masked keys at -inf
   float mraw = neg_inf();
@@ -382,86 +469,165 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
                    pack_bf16x2(e[6], e[7])};
   }
   l += shfl_xor_f(l, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const bool store = valid && o_dst != nullptr;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     f32x16 o = {};
     const uint16_t *vr = t.vt + (32 * dt + col) * KvTile<D, BS>::VSTR + 4 * half;
-#pragma unroll
-    for (int ks = 0; ks < BS / 16; ++ks) {
+    auto vt_op = [&](int ks) {
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 16 * ks);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 * ks + 8);
-      u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
-      o = mfma32x32x16(as_bf16x8(aw), as_bf16x8(pk[ks]), o);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    if constexpr (WIDE) {
+      u32x4 aw[BS / 16];
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) aw[ks] = vt_op(ks);
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(aw[ks]), as_bf16x8(pk[ks]), o);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(vt_op(ks)), as_bf16x8(pk[ks]), o);
     }
-    if (store) {
-      // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
-      uint16_t *dst = o_dst + 32 * dt + 16 * half;
-      u32x4 w0 = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
-                  pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
-      u32x4 w1 = {pack_bf16x2(o[8] * inv, o[9] * inv), pack_bf16x2(o[10] * inv, o[11] * inv),
-                  pack_bf16x2(o[12] * inv, o[13] * inv), pack_bf16x2(o[14] * inv, o[15] * inv)};
-      st16(dst, w0);
-      st16(dst + 8, w1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
+    uint16_t *dst = o_dst + 32 * dt + 16 * half;
+    u32x4 w0 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                pack_bf16x2(o[6], o[7])};
+    u32x4 w1 = {pack_bf16x2(o[8], o[9]), pack_bf16x2(o[10], o[11]), pack_bf16x2(o[12], o[13]),
+                pack_bf16x2(o[14], o[15])};
+    st16(dst, w0);
+    st16(dst + 8, w1);
+    if constexpr (!WIDE) __builtin_amdgcn_sched_barrier(0);
   }
-  if (!store) return;
-  if (half == 0) *lse_dst = l > 0.f ? m + log2f(l) : neg_inf();
+  // both halves hold the same (m, l) and store it to the same place
+  *ml_dst = l > 0.f ? float2{m, l} : float2{neg_inf(), 0.f};
 }
 
+// Decoded work-item descriptor (see kv_items_kernel).
+struct ItemDesc {
+  int g, n;
+  int64_t kvrow;  // packed K/V row of the block's first key
+};
+
+// A zero the compiler cannot see through: addresses built from it are
+// per-lane, so loads through them stay vector loads (counted by vmcnt, in
+// order with the other vector memory traffic) instead of scalar loads.
+__device__ __forceinline__ int opaque_lane_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// Pins a value in place: instructions that read it cannot be scheduled above
+// this point (the empty asm "rewrites" it), and the value must be ready here.
+__device__ __forceinline__ void pin(u32x4 &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int32_t &x) { asm volatile("" : "+v"(x)); }
+
+// Persistent partial attention.  Work items are split into one contiguous
+// range per XCD (work-groups are dealt to the XCDs round-robin, so work-group
+// w runs on XCD w % 8); the work-groups of an XCD walk its range with a
+// stride, so the items of a bucket, which share one K/V block, meet in the
+// same L2.  Each work-group double-buffers the K/V tile in LDS: while it
+// computes item t from one buffer, the Q rows and K/V block of item t+1 are in
+// flight to registers and the descriptor and entries of item t+2 too; after
+// the compute the K/V registers go to the other buffer and one barrier hands
+// it over.  Every lane owns one (query, head) row of each item.
+//
+// The loop is unrolled by two so that the two sets of Q registers and item
+// metadata trade roles instead of being copied (a copy of a register that a
+// load is still filling would make the compute wait for that load), and it
+// has no data-dependent branch around a memory access: lanes past an item's
+// rows load a valid row and store to scratch rows, and a work-group with an
+// odd item count runs its last item twice (same values to the same places).
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kv_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_partial_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ entry_off, const int32_t *__restrict__ item_off,
+    const uint16_t *__restrict__ v, const int32_t *__restrict__ item_off,
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_lse,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int K, int nb_max, int64_t nbk, int qch, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
-  const int item = blockIdx.x;
-  if (item >= item_off[nbk]) return;
-  const u32x4 desc = ld16(item_desc + 4 * (int64_t)item);
-  const int64_t bkt = desc[0];
-  const int g = (int)(bkt / ((int64_t)num_seqs * nb_max));
-  const int64_t rem = bkt - (int64_t)g * num_seqs * nb_max;
-  const int b = (int)(rem / nb_max);
-  const int j = (int)(rem - (int64_t)b * nb_max);
-  const int n = (int)desc[2];
-  const int32_t *ent = entries + desc[1];
-  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
-  const int64_t s0 = (int64_t)j * BS;
-  const int hpg = H / G;
-  const int nrows = n * hpg;
-  const int wave = threadIdx.x >> 6, col = threadIdx.x & 31;
-  // Each wave owns row tile `wave` (+ kWaves*u); its gathered Q rows are
-  // requested before the K/V block is staged.
-  constexpr int kTiles = kRowsPerItem / 32 / kWaves;
-  bf16x8 qb[kTiles][D / 16];
-  bool valid[kTiles];
-  int64_t ps[kTiles];
-#pragma unroll
-  for (int u = 0; u < kTiles; ++u) {
-    const int r = (wave + kWaves * u) * 32 + col;
-    valid[u] = r < nrows;
-    const int qi = valid[u] ? r / hpg : 0;
-    const int hh = valid[u] ? r - qi * hpg : 0;
-    const int32_t e = valid[u] ? ent[qi] : 0;
-    const int64_t row = e >> 6;
-    const int slot = e & 63;
-    const int h = g * hpg + hh;
-    load_q<D>(qb[u], q + (row * H + h) * (int64_t)D, valid[u]);
-    ps[u] = (row * K + slot) * H + h;
+    uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
+    float2 *__restrict__ trash_ml, int H, int G, int K, int64_t nbk, int qch, float scale_log2) {
+  static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
+  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tiles[2];
+  const int nitems = item_off[nbk];
+  int lo = 0, hi = nitems, first = blockIdx.x, step = gridDim.x;
+  if (gridDim.x % 8 == 0) {
+    const int x = blockIdx.x % 8;
+    lo = (int)((int64_t)nitems * x / 8);
+    hi = (int)((int64_t)nitems * (x + 1) / 8);
+    first = lo + blockIdx.x / 8;
+    step = gridDim.x / 8;
   }
-  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
-  __syncthreads();
+  if (first >= hi) return;
+  const int last = first + (hi - 1 - first) / step * step;  // this work-group's last item
+  const int hpg = H / G;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, col = lane & 31;
+  const int r = wave * 32 + col;   // this lane's row of every item
+  const int qi = r / hpg;          // query of the item
+  const int hh = r - qi * hpg;     // head inside the group
+  const int qs = min(qi, qch - 1); // entry slot read by this lane
+  const int32_t *desc_base = item_desc + opaque_lane_zero();
+  auto meta_at = [&](int it, u32x4 &w, int32_t &e) {
+    const int64_t i = min(it, last);
+    w = ld16(desc_base + 4 * i);
+    e = entries[i * qch + qs];
+  };
+  auto decode = [&](const u32x4 &w) {
+    ItemDesc d;
+    d.g = (int)(__builtin_amdgcn_readfirstlane(w[0]) >> 16);
+    d.n = (int)__builtin_amdgcn_readfirstlane(w[2]);
+    d.kvrow = (int64_t)__builtin_amdgcn_readfirstlane(w[3]);
+    return d;
+  };
+  auto q_of = [&](bf16x8 (&qb)[D / 16], const ItemDesc &d, int32_t e) {
+    const int half = lane >> 5;
+    const uint16_t *qrow = q + ((int64_t)(e >> 6) * H + d.g * hpg + hh) * (int64_t)D + 8 * half;
 #pragma unroll
-  for (int u = 0; u < kTiles; ++u) {
-    if ((wave + kWaves * u) * 32 >= nrows) break;
-    attend_rows<D, BS, false>(tile, qb[u], valid[u], s0, 0, scale_log2, part_o + ps[u] * D,
-                              part_lse + ps[u]);
+    for (int c = 0; c < D / 16; ++c) qb[c] = as_bf16x8(ld16(qrow + 16 * c));
+  };
+  KvRegs<D, BS> kv;
+  // One item: prefetch the next item's data (metadata wn / en) and the
+  // metadata of the one after (into wc / ec, free once the current item's
+  // store addresses are formed), then compute the current item from tile tc.
+  auto run_item = [&](int it, bf16x8 (&qc)[D / 16], bf16x8 (&qn)[D / 16], u32x4 &wc,
+                      int32_t &ec, u32x4 &wn, int32_t &en, KvTile<D, BS> &tc,
+                      KvTile<D, BS> &tn) {
+    // the next item's metadata is read from here on, not earlier (where it
+    // would make the previous compute wait for its load)
+    pin(wn);
+    pin(en);
+    const ItemDesc dc = decode(wc);
+    const bool own = qi < dc.n;
+    const int64_t ps = ((int64_t)(ec >> 6) * K + (ec & 63)) * H + dc.g * hpg + hh;
+    uint16_t *od = own ? part_o + ps * D : trash_o + lane * D;
+    float2 *md = own ? part_ml + ps : trash_ml + lane;
+    const ItemDesc dn = decode(wn);
+    q_of(qn, dn, en);
+    fetch_kv<D, BS, false>(kv, k, v, dn.kvrow, 0, 0, G, dn.g);
+    meta_at(it + 2 * step, wc, ec);
+    // keep the loads above ahead of the compute (the scheduler would
+    // otherwise sink them next to their first use, after it)
+    __builtin_amdgcn_sched_barrier(0);
+    attend_rows<D, BS, false, true>(tc, qc, 0, 0, scale_log2, od, md);
+    store_kv<D, BS>(tn, kv);
+    __syncthreads();
+  };
+
+  u32x4 wa, wb;
+  int32_t ea, eb;
+  meta_at(first, wa, ea);
+  meta_at(first + step, wb, eb);
+  bf16x8 qa[D / 16], qb[D / 16];
+  {
+    const ItemDesc d = decode(wa);
+    q_of(qa, d, ea);
+    fetch_kv<D, BS, false>(kv, k, v, d.kvrow, 0, 0, G, d.g);
+  }
+  store_kv<D, BS>(tiles[0], kv);
+  __syncthreads();
+  for (int it = first;; it += 2 * step) {
+    run_item(it, qa, qb, wa, ea, wb, eb, tiles[0], tiles[1]);
+    run_item(it + step, qb, qa, wb, eb, wa, ea, tiles[1], tiles[0]);
+    if (it + 2 * step > last) break;
   }
 }
 
@@ -471,9 +637,10 @@ template <int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kv_diag_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ block_idx,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_lse,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int K, int nb_max, int64_t total_q, float scale_log2) {
+    uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
+    float2 *__restrict__ trash_ml, const int64_t *__restrict__ cu_q,
+    const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
+    int64_t total_q, float scale_log2) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
   const int J = blockIdx.x;
   const int g = blockIdx.y;
@@ -504,7 +671,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     x.h = g * hpg + hh;
     return x;
   };
-  stage_kv<D, BS>(tile, k, v, sq.kv0, s0, sq.lkv, G, g);
+  {
+    KvRegs<D, BS> kv;
+    fetch_kv<D, BS, true>(kv, k, v, sq.kv0, s0, sq.lkv, G, g);
+    store_kv<D, BS>(tile, kv);
+  }
   __syncthreads();
   for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
     const RowT cur = row_of(rt);
@@ -518,52 +689,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
     const bool write = cur.valid && slot >= 0;
     const int64_t ps = (cur.row * K + (slot < 0 ? 0 : slot)) * H + cur.h;
-    attend_rows<D, BS, true>(tile, qa, cur.valid, s0, cur.pos, scale_log2,
-                             write ? part_o + ps * D : nullptr, part_lse + ps);
+    const int lane = threadIdx.x & 63;
+    attend_rows<D, BS, true, false>(tile, qa, s0, cur.pos, scale_log2,
+                             write ? part_o + ps * D : trash_o + lane * D,
+                             write ? part_ml + ps : trash_ml + lane);
   }
 }
 
 // Per query row: merge the slots whose block is causal (0 <= j <= J).
-// Phase 1 turns the slots' log2-sum-exps into merge weights in LDS (w = 0 for
-// unused slots); phase 2 streams the bf16 partials, each thread owning 8
+// Phase 1 spreads the (slot, head) pairs over the work-group: each loads its
+// slot's (m, l) (m = -inf for unused slots) into LDS; then one thread per
+// head forms M = max m, the weights w = exp2(m - M) (0 for unused slots) and
+// 1 / sum(w l).  Phase 2 streams the bf16 partials, each thread owning 8
 // consecutive output values of one head, with the slot loop unrolled so
 // several 16-byte loads are in flight.  Unused slots are never multiplied
 // (their memory may hold anything): the select below drops them.
 template <int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(
     const int32_t *__restrict__ block_idx, const uint16_t *__restrict__ part_o,
-    const float *__restrict__ part_lse, uint16_t *__restrict__ out, float *__restrict__ lse,
+    const float2 *__restrict__ part_ml, uint16_t *__restrict__ out, float *__restrict__ lse,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
     int G, int K, int BS, int64_t total_q) {
-  extern __shared__ float wsh[];  // [K][H] weights, then [H] 1/sum
+  extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum
+  float *lsh = wsh + K * H;
+  float *winv = lsh + K * H;
   const int64_t row = blockIdx.x;
   const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
   const int64_t J = ri.p < 0 ? -1 : ri.p / BS;
   const int hpg = H / G;
-  float *winv = wsh + K * H;
+  for (int t = threadIdx.x; t < K * H; t += 256) {
+    const int sl = t / H, h = t - sl * H;
+    const int32_t *br = block_idx + ((int64_t)(h / hpg) * total_q + row) * K;
+    const int j = br[sl];
+    bool use = j >= 0 && j < J;
+    if (j == J) {  // the last slot listing J is the one the diagonal kernel wrote
+      use = true;
+      for (int s2 = sl + 1; s2 < K; ++s2)
+        if (br[s2] == J) use = false;
+    }
+    const float2 ml = use ? part_ml[(row * K + sl) * H + h] : float2{neg_inf(), 0.f};
+    wsh[t] = ml.y > 0.f ? ml.x : neg_inf();
+    lsh[t] = ml.y;
+  }
+  __syncthreads();
   for (int h = threadIdx.x; h < H; h += 256) {
-    const int g = h / hpg;
-    const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
-    int diag_slot = -1;  // the last slot listing J is the one the diagonal kernel wrote
-    for (int s = 0; s < K; ++s)
-      if (br[s] == J) diag_slot = s;
     float M = neg_inf();
-    for (int s = 0; s < K; ++s) {
-      const int j = br[s];
-      const bool use = (j >= 0 && j < J) || s == diag_slot;
-      const float ls = use ? part_lse[(row * K + s) * H + h] : neg_inf();
-      wsh[s * H + h] = ls;
-      M = fmaxf(M, ls);
+    for (int sl = 0; sl < K; ++sl) M = fmaxf(M, wsh[sl * H + h]);
+    float L = 0.f;
+    for (int sl = 0; sl < K; ++sl) {
+      const float ms = wsh[sl * H + h];
+      const float w = (M == neg_inf() || ms == neg_inf()) ? 0.f : exp2f(ms - M);
+      wsh[sl * H + h] = w;
+      L += w * lsh[sl * H + h];
     }
-    float W = 0.f;
-    for (int s = 0; s < K; ++s) {
-      const float ls = wsh[s * H + h];
-      const float w = (M == neg_inf() || ls == neg_inf()) ? 0.f : exp2f(ls - M);
-      wsh[s * H + h] = w;
-      W += w;
-    }
-    winv[h] = W > 0.f ? 1.f / W : 0.f;
-    if (lse != nullptr) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
+    winv[h] = L > 0.f ? 1.f / L : 0.f;
+    if (lse != nullptr) lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : neg_inf();
   }
   __syncthreads();
   constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
@@ -611,6 +791,21 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
   }
 }
 
+// Work-groups of the persistent partial kernel: one per compute unit (its
+// two LDS tiles take most of a CU's 160 KiB), never more than the items.
+int persistent_grid(int64_t max_items) {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return (int)std::max<int64_t>(1, std::min<int64_t>(n, max_items));
+}
+
 template <int D, int BS>
 hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       const int32_t *block_idx, uint16_t *out, float *lse, void *workspace,
@@ -632,29 +827,38 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
                      w.item_off, w.nbk, qch);
   profile_mark(s);
   hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
-                     w.entry_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
-                     p.top_k, p.B, p.nb_max);
+                     w.item_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
+                     p.top_k, p.B, p.nb_max, qch);
   profile_mark(s);
   hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
-                     w.counts, w.entry_off, w.item_off, w.item_desc, w.nbk, qch);
+                     w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.num_seqs,
+                     p.nb_max, p.B, qch);
   profile_mark(s);
-  hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, q,
-                     k, v, w.counts, w.entry_off, w.item_off, w.entries, w.item_desc, w.part_o, w.part_lse,
-                     p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, w.nbk, qch, sl2);
+  hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
+                     dim3(kThreads), 0, s, q, k, v, w.item_off, w.entries, w.item_desc, w.part_o,
+                     w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, w.nbk, qch, sl2);
   profile_mark(s);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(kThreads), 0, s,
-                     q, k, v, block_idx, w.part_o, w.part_lse, p.cu_q, p.cu_kv, p.num_seqs, p.H,
+                     q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv, p.num_seqs, p.H,
                      p.G, p.top_k, p.nb_max, p.total_q, sl2);
   profile_mark(s);
-  const size_t merge_lds = sizeof(float) * ((size_t)p.top_k * p.H + p.H);
+  const size_t merge_lds = sizeof(float) * (2 * (size_t)p.top_k * p.H + p.H);
   hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), merge_lds, s, block_idx,
-                     w.part_o, w.part_lse, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
+                     w.part_o, w.part_ml, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
                      p.top_k, p.B, p.total_q);
   profile_mark(s);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool kvmajor_fits(const Dims &p) {
+  if (p.total_q >= (int64_t)1 << 25) return false;  // entries pack the query row above 6 slot bits
+  // the merge keeps (m, l) of every (slot, head) of a row in LDS
+  if ((2 * (int64_t)p.top_k * p.H + p.H) * (int64_t)sizeof(float) > 64 * 1024) return false;
+  const KvWs w = carve(p, nullptr);
+  return w.max_items * (kRowsPerItem / (p.H / p.G)) < (int64_t)INT32_MAX;
+}
 
 size_t kvmajor_workspace_bytes(const Dims &p) { return carve(p, nullptr).total_bytes; }
 

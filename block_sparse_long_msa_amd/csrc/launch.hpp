@@ -51,6 +51,8 @@ hipError_t launch_combine_splits(const Dims &p, int n_split, const float *part_o
                                  hipStream_t s);
 
 // Attention, KV-major prefill (bf16): see attn_kvmajor.hip.
+// True if the KV-major schedule's 32-bit entry and item indices hold this problem.
+bool kvmajor_fits(const Dims &p);
 size_t kvmajor_workspace_bytes(const Dims &p);
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,

@@ -84,7 +84,11 @@ typedef enum {
   MSA_SCHED_AUTO = 0,        /* library choice (KV-major for bf16 prefill) */
   MSA_SCHED_QUERY_MAJOR = 1, /* one work item per (query, group): gathers its k blocks */
   MSA_SCHED_KV_MAJOR = 2     /* one work item per (group, kept block, query chunk),
-                                then a per-query merge (bf16 only) */
+                                then a per-query merge (bf16 only; used while
+                                total_q < 2^25, total_kv < 2^31,
+                                top_k * H <= 8000 and the (query, group, kept
+                                block) entries number fewer than about 2^31;
+                                query-major beyond) */
 } msa_schedule_t;
 
 typedef struct {

@@ -96,7 +96,11 @@ def test_topk_exact_on_synthetic_scores():
 
 
 def test_closed_forms_constant_v_and_zero_q():
-    """Constant V gives that constant; Q = 0 gives the mean of V over the kept keys."""
+    """Constant V gives that constant; Q = 0 gives the mean of V over the kept keys.
+
+    Partial results are held in bf16 before the merge, so the constant comes
+    back within one bf16 step of it (2^-6 for |c| in [2, 4)); the bound is the
+    bf16 output tolerance, 2e-2."""
     lq, lkv, H, G, d, di, B, k = [900], [1300], 8, 2, 128, 64, 128, 4
     inp = W.random_case(21, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
     prob = C.problem_for(inp, H, G, d, di, B, k, "bf16")
@@ -107,7 +111,7 @@ def test_closed_forms_constant_v_and_zero_q():
     for sched in ("query_major", "kv_major"):
         p2 = prob.with_schedule(sched)
         out, _ = msa.sparse_attn_fwd(p2, inp["q"], inp["k"], v_const, idx)
-        assert (out.float() - c.float()).abs().max().item() <= 1e-2
+        assert (out.float() - c.float()).abs().max().item() <= 2e-2
         q0 = torch.zeros_like(inp["q"])
         out0, lse0 = msa.sparse_attn_fwd(p2, q0, inp["k"], inp["v"], idx, return_lse=True)
         idx_h = idx.cpu().numpy()
