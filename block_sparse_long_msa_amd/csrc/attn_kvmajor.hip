@@ -288,7 +288,10 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
 
 // LDS tile of one K/V block: K row-major [key][d] (stride D+8) and V
 // transposed [d][key] (stride BS+4); both strides keep the MFMA operand reads
-// free of LDS bank conflicts.
+// free of LDS bank conflicts.  In V^T the groups of 4 keys of row d are
+// stored XOR-swizzled by the row's 32-wide dv tile (group kq at kq ^ 4*dt):
+// the staging writes of 16 consecutive d-octets then spread over all banks,
+// and for the MFMA reads the swizzle only renames 16-key steps (ks ^ dt).
 template <int D, int BS>
 struct KvTile {
   static constexpr int KSTR = D + 8;
@@ -296,6 +299,7 @@ struct KvTile {
   uint16_t k[BS * KSTR];
   uint16_t vt[D * VSTR];
 };
+__device__ __forceinline__ int vt_group(int d, int kq) { return kq ^ (4 * ((d >> 5) & 3)); }
 
 // One thread's share of a K/V block on its way from HBM to LDS.  K moves as
 // 16-byte octets (8 consecutive d of one key); V moves as groups of 4 keys at
@@ -368,7 +372,8 @@ __device__ __forceinline__ void store_kv(KvTile<D, BS> &t, const KvRegs<D, BS> &
       const uint32_t a0 = (r.v[i][0][e >> 1] >> sh) & 0xffffu, a1 = (r.v[i][1][e >> 1] >> sh) & 0xffffu;
       const uint32_t a2 = (r.v[i][2][e >> 1] >> sh) & 0xffffu, a3 = (r.v[i][3][e >> 1] >> sh) & 0xffffu;
       u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
-      *reinterpret_cast<u32x2 *>(t.vt + (8 * o + e) * KvTile<D, BS>::VSTR + 4 * kq) = pk;
+      const int d = 8 * o + e;
+      *reinterpret_cast<u32x2 *>(t.vt + d * KvTile<D, BS>::VSTR + 4 * vt_group(d, kq)) = pk;
     }
   }
 }
@@ -416,23 +421,22 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
   const uint16_t *ar = t.k + col * KvTile<D, BS>::KSTR + 8 * half;
+  auto k_op = [&](int kt, int c) {
+    return *reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c);
+  };
   if constexpr (WIDE) {
+    // the four key tiles accumulate independently, so consecutive MFMAs
+    // never wait on each other
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-        s[kt] = mfma32x32x16(
-            as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c)),
-            qb[c], s[kt]);
+      for (int kt = 0; kt < KT; ++kt) s[kt] = mfma32x32x16(as_bf16x8(k_op(kt, c)), qb[c], s[kt]);
     }
   } else {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        s[kt] = mfma32x32x16(
-            as_bf16x8(*reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c)),
-            qb[c], s[kt]);
+      for (int c = 0; c < NC; ++c) s[kt] = mfma32x32x16(as_bf16x8(k_op(kt, c)), qb[c], s[kt]);
       __builtin_amdgcn_sched_barrier(0);  // one key tile's operands live at a time
     }
   }
@@ -469,26 +473,16 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
                    pack_bf16x2(e[6], e[7])};
   }
   l += shfl_xor_f(l, 32);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    f32x16 o = {};
-    const uint16_t *vr = t.vt + (32 * dt + col) * KvTile<D, BS>::VSTR + 4 * half;
-    auto vt_op = [&](int ks) {
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 16 * ks);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 * ks + 8);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-    if constexpr (WIDE) {
-      u32x4 aw[BS / 16];
-#pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks) aw[ks] = vt_op(ks);
-#pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(aw[ks]), as_bf16x8(pk[ks]), o);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(vt_op(ks)), as_bf16x8(pk[ks]), o);
-    }
-    // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
+  // V^T fragment of dv tile dt and 16-key step ks (keys in the order of pk)
+  auto vt_op = [&](int dt, int ks) {
+    const int ksw = ks ^ dt;  // the V^T swizzle renames the 16-key steps
+    const uint16_t *vr = t.vt + (32 * dt + col) * KvTile<D, BS>::VSTR + 16 * ksw + 4 * half;
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 8);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
+  auto store_o = [&](int dt, const f32x16 &o) {
     uint16_t *dst = o_dst + 32 * dt + 16 * half;
     u32x4 w0 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                 pack_bf16x2(o[6], o[7])};
@@ -496,7 +490,29 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
                 pack_bf16x2(o[14], o[15])};
     st16(dst, w0);
     st16(dst + 8, w1);
-    if constexpr (!WIDE) __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (WIDE) {
+    // a whole dv tile of V^T fragments is read ahead of its MFMA chain
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x4 aw[BS / 16];
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) aw[ks] = vt_op(dt, ks);
+      f32x16 o = {};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(aw[ks]), as_bf16x8(pk[ks]), o);
+      store_o(dt, o);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x16 o = {};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks)
+        o = mfma32x32x16(as_bf16x8(vt_op(dt, ks)), as_bf16x8(pk[ks]), o);
+      store_o(dt, o);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // both halves hold the same (m, l) and store it to the same place
   *ml_dst = l > 0.f ? float2{m, l} : float2{neg_inf(), 0.f};
