@@ -16,8 +16,8 @@
 // Kernels, in launch order:
 //   kv_clear        counts and cursors <- 0
 //   kv_count        entries per bucket (integer atomics: only counting)
-//   kv_scan         exclusive scans -> entry offsets and work-item offsets
-//   kv_scatter      entry lists (t << 6 | slot) per bucket
+//   kv_scan_*       exclusive scan of the per-bucket work-item counts
+//   kv_scatter      entry lists (t << 6 | slot) per bucket, item-major
 //   kv_items        work-item descriptors (group, block, first entry, count, sequence)
 //   kv_partial      persistent: one work-group per CU walks a contiguous range
 //                   of work items (one bucket chunk of <= 256/hpg queries each),
@@ -39,14 +39,21 @@ constexpr int kRowsPerItem = 256;  // gathered (query, head) rows per work item
 constexpr int kWaves = 8;          // one 32-row tile per wave
 constexpr int kThreads = 64 * kWaves;
 
+// Buckets: one per (sequence, group, kept block), numbered
+// (b * G + g) * nb_max + j.  (Splitting a bucket further by query chunk, so
+// that a chunk's gathered Q rows stay in L2, was measured slower on the long
+// prefill shapes: a chunk's bucket holds too few queries to fill work items,
+// and every chunk re-reads the K/V block.)
+constexpr int kScanTile = 4096;  // buckets per block of the item-count scan
+
 struct KvWs {
-  int32_t *counts, *cursor, *entry_off, *item_off, *entries;
-  int32_t *item_desc;  // per work item: g << 16 | j, first entry, entry count, first KV row
+  int32_t *counts, *cursor, *item_off, *entries, *scan_blk;
+  int32_t *item_desc;  // per work item: g << 16 | j, 0, entry count, first KV row
   float2 *part_ml;     // [total_q][K][H]      (m, l) of each slot
   uint16_t *part_o;    // [total_q][K][H][d]   unnormalised O of each slot, bf16
   uint16_t *trash_o;   // [64][d]  write target of lanes without a row (never read)
   float2 *trash_ml;    // [64]
-  int64_t nbk, max_entries, max_items;
+  int64_t nbk, nscan, max_entries, max_items;
   size_t total_bytes;
 };
 
@@ -54,10 +61,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 KvWs carve(const Dims &p, void *base) {
   KvWs w;
-  w.nbk = (int64_t)p.G * p.num_seqs * p.nb_max;
+  w.nbk = (int64_t)p.num_seqs * p.G * p.nb_max;
+  w.nscan = (w.nbk + kScanTile - 1) / kScanTile;
   w.max_entries = (int64_t)p.G * p.total_q * p.top_k;
   const int qch = kRowsPerItem / (p.H / p.G);
-  w.max_items = w.max_entries / qch + w.nbk + 1;
+  // every bucket adds at most one partly filled item
+  w.max_items = w.max_entries / qch + std::min(w.nbk, w.max_entries) + 1;
   size_t off = 0;
   char *c = static_cast<char *>(base);
   auto take = [&](size_t bytes) {
@@ -67,8 +76,8 @@ KvWs carve(const Dims &p, void *base) {
   };
   w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
   w.cursor = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
-  w.entry_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
   w.item_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
+  w.scan_blk = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nscan + 1)));
   // item-major with qch slots per item (a bucket's last item is padded)
   w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_items * qch));
   w.item_desc = reinterpret_cast<int32_t *>(take(4 * sizeof(int32_t) * w.max_items));
@@ -104,84 +113,103 @@ __global__ __launch_bounds__(256) void kv_clear_kernel(int32_t *a, int32_t *b, i
 
 // Count and scatter work on tiles of kEntTile consecutive (row, slot) entries
 // of one group.  Entries are kept blocks strictly below the query's current
-// block (all their keys are causal).  Buckets of the tile's first sequence are
-// counted in an LDS histogram first, so a tile issues one global atomic per
-// touched bucket instead of one per entry; rows of other sequences (tiles that
-// straddle a sequence boundary) go straight to global atomics.  The order of
-// entries inside a bucket is not fixed, but every entry's result is computed
-// independently of its neighbours, so outputs do not depend on it.
+// block (all their keys are causal).  Buckets of the tile's first sequence
+// are counted in an LDS histogram over the block index first, so a tile
+// issues one global atomic per touched bucket instead of one per entry; rows
+// of another sequence (tiles that straddle a boundary) go straight to global
+// atomics.  The order of entries inside a bucket is not
+// fixed, but every entry's result is computed independently of its
+// neighbours, so outputs do not depend on it.
 constexpr int kEntPerThread = 32;
 constexpr int kEntTile = 256 * kEntPerThread;
 
 struct EntryRef {
   int64_t bkt;   // bucket, or -1 if the entry is not a partial-attention entry
-  int bin;       // LDS bin (block index) if the entry belongs to the tile's first sequence, else -1
+  int bin;       // LDS bin (block index) if the entry is in the tile's first sequence, else -1
 };
 
-__device__ __forceinline__ EntryRef entry_ref(const int32_t *__restrict__ block_idx,
-                                              int64_t e, int g, int64_t total_q, int K, int BS,
-                                              int nb_max, int num_seqs, int b0,
+// Geometry shared by the count and scatter kernels.
+struct EntGeom {
+  int G, K, BS, nb_max, num_seqs;
+  int64_t total_q;
+};
+
+__device__ __forceinline__ EntryRef entry_ref(const int32_t *__restrict__ block_idx, int64_t e,
+                                              int g, const EntGeom &cg, int b0,
                                               const SeqGeom &s0, const int64_t *cu_q,
                                               const int64_t *cu_kv) {
   EntryRef r{-1, -1};
-  const int64_t gr = e / K;
-  const int64_t row = gr - (int64_t)g * total_q;
+  const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
   const int j = block_idx[e];
   if (j < 0) return r;
   int b = b0;
-  int64_t p;
-  if (row >= s0.q0 && row < s0.q0 + s0.lq) {
-    p = s0.base + (row - s0.q0);
-  } else {
-    const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
-    b = ri.b;
-    p = ri.p;
+  SeqGeom sq = s0;
+  if (row < s0.q0 || row >= s0.q0 + s0.lq) {
+    b = find_seq(cu_q, cg.num_seqs, row);
+    sq = seq_geom(cu_q, cu_kv, b);
   }
-  if (p < 0 || (int64_t)j >= p / BS) return r;
-  r.bkt = ((int64_t)g * num_seqs + b) * nb_max + j;
+  const int64_t p = sq.base + (row - sq.q0);
+  if (p < 0 || (int64_t)j >= p / cg.BS) return r;
+  r.bkt = ((int64_t)b * cg.G + g) * cg.nb_max + j;
   r.bin = b == b0 ? j : -1;
   return r;
 }
 
-__global__ __launch_bounds__(256) void kv_count_kernel(
-    const int32_t *__restrict__ block_idx, int32_t *__restrict__ counts,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
-    int64_t total_q, int K, int BS, int nb_max) {
+// First sequence of a count/scatter tile and its bucket base.
+struct TileStart {
+  int b0;
+  int64_t bbase;
+  SeqGeom s0;
+};
+__device__ __forceinline__ TileStart tile_start(int64_t e0, int g, const EntGeom &cg,
+                                                const int64_t *cu_q, const int64_t *cu_kv) {
+  TileStart t;
+  const int64_t row0 = e0 / cg.K - (int64_t)g * cg.total_q;
+  t.b0 = find_seq(cu_q, cg.num_seqs, row0);
+  t.s0 = seq_geom(cu_q, cu_kv, t.b0);
+  t.bbase = ((int64_t)t.b0 * cg.G + g) * cg.nb_max;
+  return t;
+}
+
+__global__ __launch_bounds__(256) void kv_count_kernel(const int32_t *__restrict__ block_idx,
+                                                       int32_t *__restrict__ counts,
+                                                       const int64_t *__restrict__ cu_q,
+                                                       const int64_t *__restrict__ cu_kv,
+                                                       EntGeom cg) {
   extern __shared__ int32_t hist[];  // nb_max bins
   const int g = blockIdx.y;
-  const int64_t e0 = (int64_t)g * total_q * K + (int64_t)blockIdx.x * kEntTile;
-  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * total_q * K);
+  const int64_t e0 = (int64_t)g * cg.total_q * cg.K + (int64_t)blockIdx.x * kEntTile;
+  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * cg.total_q * cg.K);
   if (e0 >= e_end) return;
-  const int b0 = find_seq(cu_q, num_seqs, (e0 / K) - (int64_t)g * total_q);
-  const SeqGeom s0 = seq_geom(cu_q, cu_kv, b0);
-  for (int i = threadIdx.x; i < nb_max; i += 256) hist[i] = 0;
+  const TileStart ts = tile_start(e0, g, cg, cu_q, cu_kv);
+  for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   for (int64_t e = e0 + threadIdx.x; e < e_end; e += 256) {
-    const EntryRef r = entry_ref(block_idx, e, g, total_q, K, BS, nb_max, num_seqs, b0, s0, cu_q, cu_kv);
+    const EntryRef r = entry_ref(block_idx, e, g, cg, ts.b0, ts.s0, cu_q, cu_kv);
     if (r.bin >= 0) atomicAdd(&hist[r.bin], 1);
     else if (r.bkt >= 0) atomicAdd(&counts[r.bkt], 1);
   }
   __syncthreads();
-  const int64_t bbase = ((int64_t)g * num_seqs + b0) * nb_max;
-  for (int i = threadIdx.x; i < nb_max; i += 256)
-    if (hist[i] != 0) atomicAdd(&counts[bbase + i], hist[i]);
+  for (int i = threadIdx.x; i < cg.nb_max; i += 256)
+    if (hist[i] != 0) atomicAdd(&counts[ts.bbase + i], hist[i]);
 }
 
 // Entries are laid out item-major: the bucket's entry of rank `pos` goes to
 // item_off[bucket] * qch + pos, so work item t owns entries [t*qch, t*qch + qch).
-__global__ __launch_bounds__(256) void kv_scatter_kernel(
-    const int32_t *__restrict__ block_idx, int32_t *__restrict__ cursor,
-    const int32_t *__restrict__ item_off, int32_t *__restrict__ entries,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G,
-    int64_t total_q, int K, int BS, int nb_max, int qch) {
+__global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restrict__ block_idx,
+                                                         int32_t *__restrict__ cursor,
+                                                         const int32_t *__restrict__ item_off,
+                                                         int32_t *__restrict__ entries,
+                                                         const int64_t *__restrict__ cu_q,
+                                                         const int64_t *__restrict__ cu_kv,
+                                                         EntGeom cg, int qch) {
   extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
   const int g = blockIdx.y;
-  const int64_t e0 = (int64_t)g * total_q * K + (int64_t)blockIdx.x * kEntTile;
-  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * total_q * K);
+  const int64_t e0 = (int64_t)g * cg.total_q * cg.K + (int64_t)blockIdx.x * kEntTile;
+  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * cg.total_q * cg.K);
   if (e0 >= e_end) return;
-  const int b0 = find_seq(cu_q, num_seqs, (e0 / K) - (int64_t)g * total_q);
-  const SeqGeom s0 = seq_geom(cu_q, cu_kv, b0);
-  for (int i = threadIdx.x; i < nb_max; i += 256) hist[i] = 0;
+  const TileStart ts = tile_start(e0, g, cg, cu_q, cu_kv);
+  for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   int rank[kEntPerThread];
 #pragma unroll
@@ -189,21 +217,20 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
     const int64_t e = e0 + threadIdx.x + 256 * i;
     rank[i] = -1;
     if (e < e_end) {
-      const EntryRef r = entry_ref(block_idx, e, g, total_q, K, BS, nb_max, num_seqs, b0, s0, cu_q, cu_kv);
+      const EntryRef r = entry_ref(block_idx, e, g, cg, ts.b0, ts.s0, cu_q, cu_kv);
       if (r.bin >= 0) {
         rank[i] = atomicAdd(&hist[r.bin], 1);
       } else if (r.bkt >= 0) {
         const int pos = atomicAdd(&cursor[r.bkt], 1);
-        const int64_t row = e / K - (int64_t)g * total_q;
-        entries[item_off[r.bkt] * qch + pos] = (int32_t)((row << 6) | (int)(e % K));
+        const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
+        entries[(int64_t)item_off[r.bkt] * qch + pos] = (int32_t)((row << 6) | (int)(e % cg.K));
       }
     }
   }
   __syncthreads();
-  const int64_t bbase = ((int64_t)g * num_seqs + b0) * nb_max;
-  for (int i = threadIdx.x; i < nb_max; i += 256) {
+  for (int i = threadIdx.x; i < cg.nb_max; i += 256) {
     const int c = hist[i];
-    hist[i] = c != 0 ? item_off[bbase + i] * qch + atomicAdd(&cursor[bbase + i], c) : 0;
+    hist[i] = c != 0 ? item_off[ts.bbase + i] * qch + atomicAdd(&cursor[ts.bbase + i], c) : 0;
   }
   __syncthreads();
 #pragma unroll
@@ -211,50 +238,79 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
     if (rank[i] < 0) continue;
     const int64_t e = e0 + threadIdx.x + 256 * i;
     const int j = block_idx[e];
-    const int64_t row = e / K - (int64_t)g * total_q;
-    entries[hist[j] + rank[i]] = (int32_t)((row << 6) | (int)(e % K));
+    const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
+    entries[hist[j] + rank[i]] = (int32_t)((row << 6) | (int)(e % cg.K));
   }
 }
 
-// Single work-group exclusive scans of the bucket counts (entries) and of the
-// per-bucket work-item counts ceil(count / qch).
-__global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t *__restrict__ counts,
-                                                       int32_t *__restrict__ entry_off,
-                                                       int32_t *__restrict__ item_off,
-                                                       int64_t nbk, int qch) {
-  __shared__ int32_t sa[1024], sb[1024];
+// Exclusive scan of the per-bucket work-item counts ceil(count / qch) into
+// item_off (item_off[nbk] = total), in three passes: per block of kScanTile
+// buckets a local scan and the block's total; a single work-group scan of the
+// block totals; then each block adds its offset.
+__device__ __forceinline__ int32_t block_excl_scan256(int32_t v, int32_t *sh, int32_t *total) {
   const int tid = threadIdx.x;
-  const int64_t per = (nbk + 1023) / 1024;
-  const int64_t lo = min<int64_t>(nbk, tid * per), hi = min<int64_t>(nbk, lo + per);
-  int32_t a = 0, b = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t c = counts[i];
-    a += c;
-    b += (c + qch - 1) / qch;
-  }
-  sa[tid] = a;
-  sb[tid] = b;
+  sh[tid] = v;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int32_t va = tid >= off ? sa[tid - off] : 0;
-    const int32_t vb = tid >= off ? sb[tid - off] : 0;
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t add = tid >= off ? sh[tid - off] : 0;
     __syncthreads();
-    sa[tid] += va;
-    sb[tid] += vb;
+    sh[tid] += add;
     __syncthreads();
   }
-  int32_t ra = sa[tid] - a, rb = sb[tid] - b;  // exclusive prefix of this segment
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t c = counts[i];
-    entry_off[i] = ra;
-    item_off[i] = rb;
-    ra += c;
-    rb += (c + qch - 1) / qch;
+  const int32_t incl = sh[tid];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(256) void kv_scan_local_kernel(const int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ item_off,
+                                                            int32_t *__restrict__ scan_blk,
+                                                            int64_t nbk, int qch) {
+  __shared__ int32_t sh[256];
+  constexpr int PER = kScanTile / 256;
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * PER;
+  int32_t v[PER];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t bk = base + i;
+    const int32_t c = bk < nbk ? counts[bk] : 0;
+    v[i] = (c + qch - 1) / qch;
+    sum += v[i];
   }
-  if (tid == 1023) {
-    entry_off[nbk] = sa[1023];
-    item_off[nbk] = sb[1023];
+  int32_t total;
+  int32_t run = block_excl_scan256(sum, sh, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t bk = base + i;
+    if (bk < nbk) item_off[bk] = run;
+    run += v[i];
   }
+  if (threadIdx.x == 0) scan_blk[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(256) void kv_scan_top_kernel(int32_t *__restrict__ scan_blk,
+                                                          int64_t nscan) {
+  __shared__ int32_t sh[256];
+  int32_t carry = 0;
+  for (int64_t b0 = 0; b0 < nscan; b0 += 256) {
+    const int64_t i = b0 + threadIdx.x;
+    const int32_t v = i < nscan ? scan_blk[i] : 0;
+    int32_t total;
+    const int32_t ex = block_excl_scan256(v, sh, &total);
+    if (i < nscan) scan_blk[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) scan_blk[nscan] = carry;
+}
+
+__global__ __launch_bounds__(256) void kv_scan_add_kernel(int32_t *__restrict__ item_off,
+                                                          const int32_t *__restrict__ scan_blk,
+                                                          int64_t nbk, int64_t nscan) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nbk) item_off[i] += scan_blk[i / kScanTile];
+  if (i == 0) item_off[nbk] = scan_blk[nscan];
 }
 
 // Thread per bucket: writes the descriptors of the bucket's work items
@@ -267,17 +323,17 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
                                                        int32_t *__restrict__ entries,
                                                        int32_t *__restrict__ item_desc,
                                                        const int64_t *__restrict__ cu_kv,
-                                                       int64_t nbk, int num_seqs, int nb_max,
-                                                       int BS, int qch) {
+                                                       int64_t nbk, int G, int nb_max, int BS,
+                                                       int qch) {
   const int64_t bkt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (bkt >= nbk) return;
   const int cnt = counts[bkt];
   if (cnt == 0) return;
   const int first = item_off[bkt];
-  const int64_t gb = bkt / nb_max;
-  const uint32_t j = (uint32_t)(bkt - gb * nb_max);
-  const uint32_t g = (uint32_t)(gb / num_seqs);
-  const uint32_t b = (uint32_t)(gb - (int64_t)g * num_seqs);
+  const int64_t t = bkt / nb_max;
+  const uint32_t j = (uint32_t)(bkt - t * nb_max);
+  const int64_t b = t / G;
+  const uint32_t g = (uint32_t)(t - b * G);
   const uint32_t kvrow = (uint32_t)(cu_kv[b] + (int64_t)j * BS);
   for (int i = 0; i * qch < cnt; ++i) {
     u32x4 d = {g << 16 | j, 0u, (uint32_t)min(qch, cnt - i * qch), kvrow};
@@ -286,96 +342,131 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
   for (int pos = cnt; pos % qch != 0; ++pos) entries[(int64_t)first * qch + pos] = 0;
 }
 
-// LDS tile of one K/V block: K row-major [key][d] (stride D+8) and V
-// transposed [d][key] (stride BS+4); both strides keep the MFMA operand reads
-// free of LDS bank conflicts.  In V^T the groups of 4 keys of row d are
-// stored XOR-swizzled by the row's 32-wide dv tile (group kq at kq ^ 4*dt):
-// the staging writes of 16 consecutive d-octets then spread over all banks,
-// and for the MFMA reads the swizzle only renames 16-key steps (ks ^ dt).
+// LDS tile of one K/V block, both row-major [key][d] without padding.  The
+// 16-byte chunks of each row are XOR-swizzled (chunk c of row r sits at
+// c ^ swz(r)) so that the MFMA operand reads spread over all LDS banks:
+//   K: swz = r mod (D/8); the S^T operand read takes 32 consecutive rows at
+//      one chunk.
+//   V: swz = 2 (r mod 4) + 8 ((r / 4) mod 2) (D = 128; D = 64 drops the
+//      second term); the transposed read takes 4 consecutive rows x 32 bytes
+//      per 16 lanes.
+// The tile is filled by direct HBM -> LDS loads (16 bytes per lane, lane L
+// of a load writing LDS bytes [16L, 16L + 16) of the load's base), so the
+// swizzle is applied by choosing which global chunk each lane fetches.
 template <int D, int BS>
 struct KvTile {
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = BS + 4;
-  uint16_t k[BS * KSTR];
-  uint16_t vt[D * VSTR];
+  uint16_t k[BS * D];
+  uint16_t v[BS * D];
 };
-__device__ __forceinline__ int vt_group(int d, int kq) { return kq ^ (4 * ((d >> 5) & 3)); }
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 2 * (r & 3) + 8 * ((r >> 2) & 1) : 2 * (r & 3);
+}
 
-// One thread's share of a K/V block on its way from HBM to LDS.  K moves as
-// 16-byte octets (8 consecutive d of one key); V moves as groups of 4 keys at
-// one octet, transposed in registers.  Both mappings put consecutive lanes on
-// consecutive octets of a row, so every load instruction reads whole rows.
-template <int D, int BS>
-struct KvRegs {
-  static constexpr int OCT = D / 8;
-  static constexpr int KTASKS = BS * OCT;        // K octets
-  static constexpr int VTASKS = BS / 4 * OCT;    // V (4-key group, octet) pairs
-  static constexpr int KN = (KTASKS + kThreads - 1) / kThreads;
-  static constexpr int VN = (VTASKS + kThreads - 1) / kThreads;
-  u32x4 k[KN];
-  u32x4 v[VN][4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-// Loads block rows [s0, s0 + BS) of group g into registers.  With GUARD, rows
-// at or past lkv read as zeros; without it every row must exist.
-template <int D, int BS, bool GUARD>
-__device__ __forceinline__ void fetch_kv(KvRegs<D, BS> &r, const uint16_t *__restrict__ k,
-                                         const uint16_t *__restrict__ v, int64_t kv0, int64_t s0,
-                                         int64_t lkv, int G, int g) {
-  using R = KvRegs<D, BS>;
-  const int tid = threadIdx.x;
+// Issues the direct loads of block rows [key0, key0 + BS) of group g (packed
+// row kvrow0 + key) into tile t.  With CLAMP, keys at or past nvalid read
+// key nvalid - 1 instead (their scores are masked; V then holds finite
+// values that are multiplied by zero).  Completion is waited for by the
+// caller (vmcnt, then a barrier before other waves read the tile).
+template <int D, int BS, bool CLAMP>
+__device__ __forceinline__ void dma_kv(KvTile<D, BS> &t, const uint16_t *__restrict__ k,
+                                       const uint16_t *__restrict__ v, int64_t kvrow0,
+                                       int nvalid, int G, int g) {
+  constexpr int CPR = D / 8;              // chunks per row
+  constexpr int NCH = BS * CPR;           // chunks per tensor
+  constexpr int PER_WAVE = NCH / kWaves;  // chunks per wave, a multiple of 64
+  static_assert(PER_WAVE % 64 == 0, "whole 64-lane loads per wave");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t rs = (int64_t)G * D;
-  const uint16_t *kb = k + ((kv0 + s0) * G + g) * (int64_t)D;
-  const uint16_t *vb = v + ((kv0 + s0) * G + g) * (int64_t)D;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  const uint16_t *kb = k + (kvrow0 * G + g) * (int64_t)D;
+  const uint16_t *vb = v + (kvrow0 * G + g) * (int64_t)D;
 #pragma unroll
-  for (int i = 0; i < R::KN; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = c / R::OCT, o = c % R::OCT;
-    const bool ok = (R::KTASKS % kThreads == 0 || c < R::KTASKS) && (!GUARD || s0 + key < lkv);
-    r.k[i] = ok ? ld16(kb + key * rs + 8 * o) : z;
-  }
-#pragma unroll
-  for (int i = 0; i < R::VN; ++i) {
-    const int task = tid + i * kThreads;
-    const int kq = task / R::OCT, o = task % R::OCT;
-    const bool in = R::VTASKS % kThreads == 0 || task < R::VTASKS;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = 4 * kq + e;
-      const bool ok = in && (!GUARD || s0 + key < lkv);
-      r.v[i][e] = ok ? ld16(vb + key * rs + 8 * o) : z;
-    }
+  for (int i = 0; i < PER_WAVE / 64; ++i) {
+    const int p0 = wave * PER_WAVE + i * 64;  // first chunk of this load (wave-uniform)
+    const int p = p0 + lane;
+    const int row = p / CPR, cp = p % CPR;
+    const int key = CLAMP ? min(row, nvalid - 1) : row;
+    __builtin_amdgcn_global_load_lds(kb + key * rs + 8 * (cp ^ k_swz<D>(row)),
+                                     (lds_void *)(t.k + 8 * p0), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + key * rs + 8 * (cp ^ v_swz<D>(row)),
+                                     (lds_void *)(t.v + 8 * p0), 16, 0, 0);
   }
 }
 
+// Reads back one element of this wave's own part of tile t and pins it: the
+// compiler then waits for this wave's loads into t right here (and no later
+// than here), so a barrier placed after this call publishes the tile.
 template <int D, int BS>
-__device__ __forceinline__ void store_kv(KvTile<D, BS> &t, const KvRegs<D, BS> &r) {
-  using R = KvRegs<D, BS>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < R::KN; ++i) {
-    const int c = tid + i * kThreads;
-    if (R::KTASKS % kThreads != 0 && c >= R::KTASKS) break;
-    const int key = c / R::OCT, o = c % R::OCT;
-    st16(t.k + key * KvTile<D, BS>::KSTR + 8 * o, r.k[i]);
+__device__ __forceinline__ void dma_settle(const KvTile<D, BS> &t) {
+  constexpr int PER_WAVE = BS * D / 8 / kWaves;
+  const int wave = threadIdx.x >> 6;
+  uint32_t x = *reinterpret_cast<const volatile uint16_t *>(t.k + 8 * (wave * PER_WAVE + PER_WAVE - 1)) +
+               *reinterpret_cast<const volatile uint16_t *>(t.v + 8 * (wave * PER_WAVE + PER_WAVE - 1));
+  asm volatile("" : "+v"(x));
+}
+
+// All V^T fragments of one dv tile: for 16-key step ks, the transposed reads
+// at key rows 16ks (+ 4 half + l/4, folded into `addr`) and 16ks + 8, as
+// immediate offsets from `addr` (an LDS byte address).  One asm block issues
+// every read and waits for them before it ends.  The tile being read was
+// published by a barrier before this point, while the direct loads in flight
+// target the other tile: written as builtins, these reads would make the
+// compiler wait for those loads, as it cannot tell the two tiles apart.
+#define MSA_TR(i) "ds_read_b64_tr_b16 %" #i ", %[a] offset:%[o" #i "]\n"
+template <int D, int BS>
+__device__ __forceinline__ void vt_tile_read(u32x4 (&aw)[BS / 16], uint32_t addr) {
+  constexpr int R = 2 * D;  // bytes per V row
+  u32x2 x[BS / 8];
+  if constexpr (BS == 128) {
+    asm volatile(MSA_TR(0) MSA_TR(1) MSA_TR(2) MSA_TR(3) MSA_TR(4) MSA_TR(5) MSA_TR(6) MSA_TR(7)
+                 MSA_TR(8) MSA_TR(9) MSA_TR(10) MSA_TR(11) MSA_TR(12) MSA_TR(13) MSA_TR(14)
+                 MSA_TR(15) "s_waitcnt lgkmcnt(0)"
+                 : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]),
+                   "=v"(x[6]), "=v"(x[7]), "=v"(x[8]), "=v"(x[9]), "=v"(x[10]), "=v"(x[11]),
+                   "=v"(x[12]), "=v"(x[13]), "=v"(x[14]), "=v"(x[15])
+                 : [a] "v"(addr), [o0] "n"(0 * R), [o1] "n"(8 * R), [o2] "n"(16 * R),
+                   [o3] "n"(24 * R), [o4] "n"(32 * R), [o5] "n"(40 * R), [o6] "n"(48 * R),
+                   [o7] "n"(56 * R), [o8] "n"(64 * R), [o9] "n"(72 * R), [o10] "n"(80 * R),
+                   [o11] "n"(88 * R), [o12] "n"(96 * R), [o13] "n"(104 * R), [o14] "n"(112 * R),
+                   [o15] "n"(120 * R));
+  } else {
+    static_assert(BS == 64, "block size 64 or 128");
+    asm volatile(MSA_TR(0) MSA_TR(1) MSA_TR(2) MSA_TR(3) MSA_TR(4) MSA_TR(5) MSA_TR(6) MSA_TR(7)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]),
+                   "=v"(x[6]), "=v"(x[7])
+                 : [a] "v"(addr), [o0] "n"(0 * R), [o1] "n"(8 * R), [o2] "n"(16 * R),
+                   [o3] "n"(24 * R), [o4] "n"(32 * R), [o5] "n"(40 * R), [o6] "n"(48 * R),
+                   [o7] "n"(56 * R));
   }
 #pragma unroll
-  for (int i = 0; i < R::VN; ++i) {
-    const int task = tid + i * kThreads;
-    if (R::VTASKS % kThreads != 0 && task >= R::VTASKS) break;
-    const int kq = task / R::OCT, o = task % R::OCT;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // d = 8o + e of keys 4kq .. 4kq+3: the e-th bf16 of each key's octet
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (r.v[i][0][e >> 1] >> sh) & 0xffffu, a1 = (r.v[i][1][e >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (r.v[i][2][e >> 1] >> sh) & 0xffffu, a3 = (r.v[i][3][e >> 1] >> sh) & 0xffffu;
-      u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
-      const int d = 8 * o + e;
-      *reinterpret_cast<u32x2 *>(t.vt + d * KvTile<D, BS>::VSTR + 4 * vt_group(d, kq)) = pk;
-    }
-  }
+  for (int ks = 0; ks < BS / 16; ++ks)
+    aw[ks] = u32x4{x[2 * ks][0], x[2 * ks][1], x[2 * ks + 1][0], x[2 * ks + 1][1]};
+}
+#undef MSA_TR
+
+// K fragments of MFMA step c for the four 32-key tiles of a 128-key block
+// (rows kt*32 + col, kt = 0..3): the K swizzle depends on col mod 16 only, so
+// the four reads share one LDS byte address `addr` and differ by immediate
+// offsets; one asm block issues them and waits before it ends (same reason
+// as vt_tile_read).
+template <int D>
+__device__ __forceinline__ void k_step_read4(u32x4 (&kf)[4], uint32_t addr) {
+  constexpr int T = 32 * 2 * D;  // bytes per 32-key tile
+  asm volatile(
+      "ds_read_b128 %0, %[a] offset:%[o0]\n"
+      "ds_read_b128 %1, %[a] offset:%[o1]\n"
+      "ds_read_b128 %2, %[a] offset:%[o2]\n"
+      "ds_read_b128 %3, %[a] offset:%[o3]\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(kf[0]), "=v"(kf[1]), "=v"(kf[2]), "=v"(kf[3])
+      : [a] "v"(addr), [o0] "n"(0), [o1] "n"(T), [o2] "n"(2 * T), [o3] "n"(3 * T));
 }
 
 // Q^T operands of one lane's row (B operand of S^T = K . Q^T): 16 values of
@@ -420,13 +511,22 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
   f32x16 s[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
-  const uint16_t *ar = t.k + col * KvTile<D, BS>::KSTR + 8 * half;
+  // K fragment of key tile kt, MFMA step c: row kt*32 + col, chunk 2c + half
   auto k_op = [&](int kt, int c) {
-    return *reinterpret_cast<const u32x4 *>(ar + kt * 32 * KvTile<D, BS>::KSTR + 16 * c);
+    const int r = kt * 32 + col;
+    return *reinterpret_cast<const u32x4 *>(t.k + r * D + 8 * ((2 * c + half) ^ k_swz<D>(r)));
   };
-  if constexpr (WIDE) {
-    // the four key tiles accumulate independently, so consecutive MFMAs
-    // never wait on each other
+  if constexpr (WIDE && KT == 4) {
+    // the four key tiles accumulate independently; the fragments of step c
+    // are read in one block while the MFMAs of step c - 1 run
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 kf[4];
+      k_step_read4<D>(kf, (uint32_t)(uintptr_t)(t.k + col * D + 8 * ((2 * c + half) ^ k_swz<D>(col))));
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] = mfma32x32x16(as_bf16x8(kf[kt]), qb[c], s[kt]);
+    }
+  } else if constexpr (WIDE) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -473,13 +573,18 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
                    pack_bf16x2(e[6], e[7])};
   }
   l += shfl_xor_f(l, 32);
-  // V^T fragment of dv tile dt and 16-key step ks (keys in the order of pk)
-  auto vt_op = [&](int dt, int ks) {
-    const int ksw = ks ^ dt;  // the V^T swizzle renames the 16-key steps
-    const uint16_t *vr = t.vt + (32 * dt + col) * KvTile<D, BS>::VSTR + 16 * ksw + 4 * half;
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 8);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  // V^T fragments of dv tile dt, read transposed from the row-major V tile:
+  // within each 16-lane group, lane l points at key row r0 + l/4 and dv
+  // 4(l%4) .. +3 of its group's 16 dv; lane i then receives V[r0 .. r0+3][dv
+  // of lane i].  Step ks takes rows r0 = 16ks + 4half and 16ks + 8 + 4half,
+  // the key order of pk.  Along a lane's reads only r0 changes by multiples
+  // of 8 and the V swizzle of its rows stays 2 (l/4) + 8 half, so all of a
+  // tile's reads share one address and differ by immediate offsets.
+  const int lq = lane & 15;
+  auto vt_base = [&](int dt) {
+    const int dv = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lq & 3);
+    const int r = 4 * half + (lq >> 2);
+    return (uint32_t)(uintptr_t)(t.v + r * D + 8 * ((dv >> 3) ^ v_swz<D>(r)) + (dv & 7));
   };
   // o[4i + e] is dv = 32dt + 8i + 4half + e: stored at 32dt + 16half + 4i + e
   auto store_o = [&](int dt, const f32x16 &o) {
@@ -492,12 +597,10 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
     st16(dst + 8, w1);
   };
   if constexpr (WIDE) {
-    // a whole dv tile of V^T fragments is read ahead of its MFMA chain
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       u32x4 aw[BS / 16];
-#pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks) aw[ks] = vt_op(dt, ks);
+      vt_tile_read<D, BS>(aw, vt_base(dt));
       f32x16 o = {};
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(aw[ks]), as_bf16x8(pk[ks]), o);
@@ -506,10 +609,11 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
   } else {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      u32x4 aw[BS / 16];
+      vt_tile_read<D, BS>(aw, vt_base(dt));
       f32x16 o = {};
 #pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks)
-        o = mfma32x32x16(as_bf16x8(vt_op(dt, ks)), as_bf16x8(pk[ks]), o);
+      for (int ks = 0; ks < BS / 16; ++ks) o = mfma32x32x16(as_bf16x8(aw[ks]), as_bf16x8(pk[ks]), o);
       store_o(dt, o);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -543,10 +647,10 @@ __device__ __forceinline__ void pin(int32_t &x) { asm volatile("" : "+v"(x)); }
 // w runs on XCD w % 8); the work-groups of an XCD walk its range with a
 // stride, so the items of a bucket, which share one K/V block, meet in the
 // same L2.  Each work-group double-buffers the K/V tile in LDS: while it
-// computes item t from one buffer, the Q rows and K/V block of item t+1 are in
-// flight to registers and the descriptor and entries of item t+2 too; after
-// the compute the K/V registers go to the other buffer and one barrier hands
-// it over.  Every lane owns one (query, head) row of each item.
+// computes item t from one tile, the K/V block of item t+1 streams straight
+// into the other tile, its Q rows into registers, and the descriptor and
+// entries of item t+2 too; one barrier per item hands the tiles over.  Every
+// lane owns one (query, head) row of each item.
 //
 // The loop is unrolled by two so that the two sets of Q registers and item
 // metadata trade roles instead of being copied (a copy of a register that a
@@ -562,7 +666,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
     float2 *__restrict__ trash_ml, int H, int G, int K, int64_t nbk, int qch, float scale_log2) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
-  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tiles[2];
+  // two separate objects, so the compiler can tell the tile being loaded
+  // from the tile being read
+  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile_a;
+  __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile_b;
   const int nitems = item_off[nbk];
   int lo = 0, hi = nitems, first = blockIdx.x, step = gridDim.x;
   if (gridDim.x % 8 == 0) {
@@ -600,10 +707,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qb[c] = as_bf16x8(ld16(qrow + 16 * c));
   };
-  KvRegs<D, BS> kv;
-  // One item: prefetch the next item's data (metadata wn / en) and the
-  // metadata of the one after (into wc / ec, free once the current item's
-  // store addresses are formed), then compute the current item from tile tc.
+  // One item: prefetch the next item's data (metadata wn / en: Q rows to
+  // registers, K/V block straight into tile tn) and the metadata of the one
+  // after (into wc / ec, free once the current item's store addresses are
+  // formed), then compute the current item from tile tc.
   auto run_item = [&](int it, bf16x8 (&qc)[D / 16], bf16x8 (&qn)[D / 16], u32x4 &wc,
                       int32_t &ec, u32x4 &wn, int32_t &en, KvTile<D, BS> &tc,
                       KvTile<D, BS> &tn) {
@@ -618,13 +725,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float2 *md = own ? part_ml + ps : trash_ml + lane;
     const ItemDesc dn = decode(wn);
     q_of(qn, dn, en);
-    fetch_kv<D, BS, false>(kv, k, v, dn.kvrow, 0, 0, G, dn.g);
+    dma_kv<D, BS, false>(tn, k, v, dn.kvrow, BS, G, dn.g);
     meta_at(it + 2 * step, wc, ec);
     // keep the loads above ahead of the compute (the scheduler would
     // otherwise sink them next to their first use, after it)
     __builtin_amdgcn_sched_barrier(0);
     attend_rows<D, BS, false, true>(tc, qc, 0, 0, scale_log2, od, md);
-    store_kv<D, BS>(tn, kv);
+    dma_settle<D, BS>(tn);
     __syncthreads();
   };
 
@@ -636,13 +743,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   {
     const ItemDesc d = decode(wa);
     q_of(qa, d, ea);
-    fetch_kv<D, BS, false>(kv, k, v, d.kvrow, 0, 0, G, d.g);
+    dma_kv<D, BS, false>(tile_a, k, v, d.kvrow, BS, G, d.g);
   }
-  store_kv<D, BS>(tiles[0], kv);
+  dma_settle<D, BS>(tile_a);
   __syncthreads();
   for (int it = first;; it += 2 * step) {
-    run_item(it, qa, qb, wa, ea, wb, eb, tiles[0], tiles[1]);
-    run_item(it + step, qb, qa, wb, eb, wa, ea, tiles[1], tiles[0]);
+    run_item(it, qa, qb, wa, ea, wb, eb, tile_a, tile_b);
+    run_item(it + step, qb, qa, wb, eb, wa, ea, tile_b, tile_a);
     if (it + 2 * step > last) break;
   }
 }
@@ -687,11 +794,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     x.h = g * hpg + hh;
     return x;
   };
-  {
-    KvRegs<D, BS> kv;
-    fetch_kv<D, BS, true>(kv, k, v, sq.kv0, s0, sq.lkv, G, g);
-    store_kv<D, BS>(tile, kv);
-  }
+  dma_kv<D, BS, true>(tile, k, v, sq.kv0 + s0, (int)min<int64_t>(BS, sq.lkv - s0), G, g);
+  dma_settle<D, BS>(tile);
   __syncthreads();
   for (int rt = wave; rt * 32 < nrows; rt += kWaves) {
     const RowT cur = row_of(rt);
@@ -833,21 +937,24 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   hipLaunchKernelGGL(kv_clear_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
                      w.counts, w.cursor, w.nbk);
   profile_mark(s);
+  const EntGeom cg{p.G, p.top_k, p.B, p.nb_max, p.num_seqs, p.total_q};
   const int64_t per_g = p.total_q * p.top_k;
   const dim3 tiles((unsigned)((per_g + kEntTile - 1) / kEntTile), p.G);
   const size_t hist_bytes = sizeof(int32_t) * p.nb_max;
   hipLaunchKernelGGL(kv_count_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.counts,
-                     p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q, p.top_k, p.B, p.nb_max);
+                     p.cu_q, p.cu_kv, cg);
   profile_mark(s);
-  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, w.entry_off,
-                     w.item_off, w.nbk, qch);
+  hipLaunchKernelGGL(kv_scan_local_kernel, dim3((unsigned)w.nscan), dim3(256), 0, s, w.counts,
+                     w.item_off, w.scan_blk, w.nbk, qch);
+  hipLaunchKernelGGL(kv_scan_top_kernel, dim3(1), dim3(256), 0, s, w.scan_blk, w.nscan);
+  hipLaunchKernelGGL(kv_scan_add_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
+                     w.item_off, w.scan_blk, w.nbk, w.nscan);
   profile_mark(s);
   hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
-                     w.item_off, w.entries, p.cu_q, p.cu_kv, p.num_seqs, p.G, p.total_q,
-                     p.top_k, p.B, p.nb_max, qch);
+                     w.item_off, w.entries, p.cu_q, p.cu_kv, cg, qch);
   profile_mark(s);
   hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
-                     w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.num_seqs,
+                     w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.G,
                      p.nb_max, p.B, qch);
   profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
