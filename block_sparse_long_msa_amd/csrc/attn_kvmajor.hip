@@ -622,6 +622,23 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
   *ml_dst = l > 0.f ? float2{m, l} : float2{neg_inf(), 0.f};
 }
 
+// Hands the tile that this wave has been loading over to the other waves:
+// waits until this wave's direct loads into it have landed and meets them at
+// a barrier.  The vector memory counter completes in issue order, and the
+// last NAFTER vector memory operations issued before this point (the current
+// item's partial-result stores) come after those loads, so vmcnt <= NAFTER
+// is enough; the stores keep draining.  There is no memory fence: the LDS
+// tile is all that is exchanged, and a fence would wait for the stores.  The
+// LDS reads of the current tile waited for themselves (asm blocks).
+template <int NAFTER>
+__device__ __forceinline__ void tile_handover() {
+  static_assert(NAFTER >= 0 && NAFTER < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((NAFTER & 15) | (7 << 4) | (15 << 8) | ((NAFTER >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Decoded work-item descriptor (see kv_items_kernel).
 struct ItemDesc {
   int g, n;
@@ -731,8 +748,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // otherwise sink them next to their first use, after it)
     __builtin_amdgcn_sched_barrier(0);
     attend_rows<D, BS, false, true>(tc, qc, 0, 0, scale_log2, od, md);
-    dma_settle<D, BS>(tn);
-    __syncthreads();
+    // the item's stores: two 16-byte stores per 32-wide dv tile, then (m, l)
+    tile_handover<2 * (D / 32) + 1>();
   };
 
   u32x4 wa, wb;
