@@ -8,13 +8,13 @@
 //  * index_score_mfma_kernel  - bf16 prefill.  A work-group (8 waves) owns 512
 //    queries x 16 key blocks of one (sequence, group).  The index queries stay in
 //    registers as MFMA B operands for the whole work-group; key blocks stream
-//    through a 2-3 stage LDS ring filled by direct global->LDS loads (no
-//    register staging; an XOR swizzle applied through the source addresses
-//    keeps the operand reads free of bank conflicts); each wave computes
-//    S^T = K * Q^T tiles (keys x queries) with 32x32x16 bf16 MFMA so a lane
-//    holds 16 keys of ONE query column and the block max is an in-lane max
-//    chain plus one cross-half step.  Causal masking is applied only to
-//    blocks that can hold keys past a query's position.
+//    through a two-stage LDS ring, fed from registers that are loaded two
+//    blocks ahead (XOR-swizzled 16-byte chunks keep the operand reads free of
+//    bank conflicts); each wave computes S^T = K * Q^T tiles (keys x queries)
+//    with 32x32x16 bf16 MFMA so a lane holds 16 keys of ONE query column and
+//    the block max is an in-lane max chain plus one cross-half step.  Causal
+//    masking is applied only to blocks that can hold keys past a query's
+//    position, in a separate loop.
 //  * index_score_decode_kernel - bf16, one query per sequence: a streaming
 //    scan of the index-key cache (HBM-bound).  Lanes read consecutive 16-byte
 //    chunks of 1 KiB slabs, dot them against the matching slice of the query
@@ -30,13 +30,6 @@ constexpr int kIdxWaves = 8;
 constexpr int kIdxThreads = 64 * kIdxWaves;
 constexpr int kQT = 64 * kIdxWaves;  // queries per work-group (each wave 2 x 32 columns)
 constexpr int kKC = 16;   // key blocks per work-group
-
-// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <int DI, int BS>
 struct IdxTile {
