@@ -11,7 +11,7 @@
 // is every key above it plus the lowest-index keys equal to it.  Scanning the
 // candidates in index order with ballot prefix counts emits them ascending;
 // J (larger than every candidate) comes last.  The candidate keys of a row
-// stay in registers (NCH chunks of 64 per lane).  Long rows first cut the
+// stay in registers (NCH chunks of 64 per lane, up to 128).  Long rows first cut the
 // search down: the (k-1)-th largest of the 64 lane maxima (128 half-lane
 // maxima when k-1 > 31) is a lower bound of the answer, and the few keys at
 // or above it (kept in index order in LDS) hold every selected key; the
@@ -41,16 +41,46 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[NC], int n
   return tau;
 }
 
-// Emits, in index order, every key > tau plus the first (need - #{> tau})
-// keys == tau.  index_of(c) is the block index of key[c]; writes dst[0..need).
-template <int NC, typename IndexOf>
-__device__ __forceinline__ void emit_selected(const uint32_t (&key)[NC], IndexOf index_of,
-                                              uint32_t tau, int need, int32_t *dst) {
-  int gt = 0;
+// The same when the answer is known to lie in [lo, hi] (at least `need` keys
+// are >= lo and none is above hi): it shares the bits of lo and hi above
+// their highest differing bit, so the search starts there.
+template <int NC>
+__device__ __forceinline__ uint32_t kth_largest_in(const uint32_t (&key)[NC], int need, uint32_t lo,
+                                                   uint32_t hi) {
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0u) return lo;
+  const int top = 31 - __builtin_clz(diff);
+  uint32_t tau = lo & ~((2u << top) - 1u);  // common prefix, lower bits 0
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) gt += __popcll(ballot64(key[c] > tau));
-  const int take_eq = need - gt;
-  int out_pos = 0, eq_seen = 0;
+    for (int c = 0; c < NC; ++c) cnt += __popcll(ballot64(key[c] >= cand));
+    if (cnt >= need) tau = cand;
+  }
+  return tau;
+}
+
+// Maximum key over the wave (all lanes get it).
+template <int NC>
+__device__ __forceinline__ uint32_t wave_max_key(const uint32_t (&key)[NC]) {
+  uint32_t m = key[0];
+#pragma unroll
+  for (int c = 1; c < NC; ++c) m = max(m, key[c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return m;
+}
+
+// Emits, in index order, every key > tau plus keys == tau while fewer than
+// take_eq equal keys have been taken overall; eq_seen0 equal keys come
+// before this wave's keys in index order, and the wave's first selected key
+// goes to dst[out0].
+template <int NC, typename IndexOf>
+__device__ __forceinline__ void emit_from(const uint32_t (&key)[NC], IndexOf index_of,
+                                          uint32_t tau, int take_eq, int out0, int eq_seen0,
+                                          int32_t *dst) {
+  int out_pos = out0, eq_seen = eq_seen0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const bool is_gt = key[c] > tau, is_eq = key[c] == tau;
@@ -63,6 +93,17 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&key)[NC], IndexOf
   }
 }
 
+// Emits, in index order, every key > tau plus the first (need - #{> tau})
+// keys == tau.  index_of(c) is the block index of key[c]; writes dst[0..need).
+template <int NC, typename IndexOf>
+__device__ __forceinline__ void emit_selected(const uint32_t (&key)[NC], IndexOf index_of,
+                                              uint32_t tau, int need, int32_t *dst) {
+  int gt = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) gt += __popcll(ballot64(key[c] > tau));
+  emit_from<NC>(key, index_of, tau, need - gt, 0, 0, dst);
+}
+
 // LDS written and read back by lanes of the same wave: the wave's LDS
 // operations complete in issue order; this keeps the compiler from moving
 // them across each other.
@@ -72,9 +113,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per (group, query row), four rows per work-group.  NCH > 0: the
-// row's keys stay in registers (NCH chunks of 64 per lane).  NCH == 0: long
-// rows; keys are streamed from the score row (L2-resident after one pass).
+// One wave per (group, query row), four rows per work-group.  The row's
+// candidate keys stay in registers: NCH chunks of 64 per lane, key j of the
+// row in chunk j / 64, lane j % 64 (0 past the candidates: it ranks below
+// every real key).  NCH = 128 covers the longest supported row (8192 blocks).
 template <int NCH>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores,
                                                    int32_t *__restrict__ block_idx,
@@ -105,22 +147,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     return;
   }
   const float *src = scores + grow * nb_max;
-  const int nch = (J + 63) / 64;  // chunks holding candidates
-  constexpr int R = NCH > 0 ? NCH : 1;
-  uint32_t key[R];
-  auto key_at = [&](int c) -> uint32_t {  // c < nch
-    if (NCH > 0) return key[c];
-    const int j = 64 * c + lane;
-    return j < J ? ordered_key(src[j]) : 0u;
-  };
-  if (NCH > 0) {
+  uint32_t key[NCH];
 #pragma unroll
-    for (int c = 0; c < R; ++c) {
-      const int j = 64 * c + lane;
-      key[c] = j < J ? ordered_key(src[j]) : 0u;  // 0 ranks below every real key
-    }
+  for (int c = 0; c < NCH; ++c) {
+    const int j = 64 * c + lane;
+    key[c] = j < J ? ordered_key(src[j]) : 0u;
   }
-  if (NCH == 0 || NCH >= kPruneMinChunks) {
+  if (NCH >= kPruneMinChunks) {
     // Lower bound: the need-th largest of the group maxima (group r of a lane
     // = its chunks c with c % GPL == r; 64*GPL groups).  More than `need`
     // groups hold a candidate, so at least `need` keys are >= it; hence
@@ -130,23 +163,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     uint32_t lb;
     if (need <= 31) {
       uint32_t gmax[1] = {0u};
-      for (int c = 0; c < nch; ++c) gmax[0] = max(gmax[0], key_at(c));
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) gmax[0] = max(gmax[0], key[c]);
       lb = kth_largest<1>(gmax, need);
     } else {
       uint32_t gmax[2] = {0u, 0u};
-      for (int c = 0; c < nch; ++c) gmax[c & 1] = max(gmax[c & 1], key_at(c));
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) gmax[c & 1] = max(gmax[c & 1], key[c]);
       lb = kth_largest<2>(gmax, need);
     }
     int n_cand = 0;
-    for (int c = 0; c < nch; ++c) n_cand += __popcll(ballot64(key_at(c) >= lb));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) n_cand += __popcll(ballot64(key[c] >= lb));
     if (n_cand <= kCandCap) {
       int base = 0;
-      for (int c = 0; c < nch; ++c) {
-        const uint32_t kc = key_at(c);
-        const bool in = kc >= lb;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const bool in = key[c] >= lb;
         const uint64_t m = ballot64(in);
         if (in) {
-          cand_key[base + mbcnt64(m)] = kc;
+          cand_key[base + mbcnt64(m)] = key[c];
           cand_idx[base + mbcnt64(m)] = 64 * c + lane;
         }
         base += __popcll(m);
@@ -162,42 +198,170 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
           ck[c] = i < n_cand ? cand_key[i] : 0u;
           ci[c] = i < n_cand ? cand_idx[i] : 0;
         }
-        emit_selected<CC>(ck, [&](int c) { return ci[c]; }, kth_largest<CC>(ck, need), need, dst);
+        const uint32_t tau = kth_largest_in<CC>(ck, need, lb, wave_max_key<CC>(ck));
+        emit_selected<CC>(ck, [&](int c) { return ci[c]; }, tau, need, dst);
       };
       if (n_cand <= 128) finish(std::integral_constant<int, 2>());
+      else if (n_cand <= 256) finish(std::integral_constant<int, 4>());
       else finish(std::integral_constant<int, kCandCap / 64>());
       if (lane == 0) dst[need] = J;
       return;
     }
+    // more keys tie at the bound than the candidate slice holds: exact
+    // search over the whole row below
   }
-  if (NCH > 0) {
-    emit_selected<R>(key, [&](int c) { return 64 * c + lane; }, kth_largest<R>(key, need), need,
+  emit_selected<NCH>(key, [&](int c) { return 64 * c + lane; }, kth_largest<NCH>(key, need), need,
                      dst);
-  } else {
-    // Too many keys tie at the lower bound: exact search with streamed keys.
-    uint32_t tau = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      int cnt = 0;
-      for (int c = 0; c < nch; ++c) cnt += __popcll(ballot64(key_at(c) >= cand));
-      if (cnt >= need) tau = cand;
-    }
-    int gt = 0;
-    for (int c = 0; c < nch; ++c) gt += __popcll(ballot64(key_at(c) > tau));
-    const int take_eq = need - gt;
-    int out_pos = 0, eq_seen = 0;
-    for (int c = 0; c < nch; ++c) {
-      const uint32_t kc = key_at(c);
-      const bool is_gt = kc > tau, is_eq = kc == tau;
-      const uint64_t eqm = ballot64(is_eq);
-      const bool sel = is_gt || (is_eq && eq_seen + mbcnt64(eqm) < take_eq);
-      const uint64_t selm = ballot64(sel);
-      if (sel) dst[out_pos + mbcnt64(selm)] = 64 * c + lane;
-      out_pos += __popcll(selm);
-      eq_seen += __popcll(eqm);
-    }
-  }
   if (lane == 0) dst[need] = J;
+}
+
+// Long rows (more than 2048 candidate blocks): one 4-wave work-group per
+// row, wave w holding keys [w*64*NCW, (w+1)*64*NCW) in registers (NCW chunks
+// of 64).  The waves share their lane maxima for the lower bound, compact
+// their candidates at offsets given by the counts of the waves before them,
+// so the list stays in index order, and wave 0 runs the exact search on the
+// list.  If more keys tie at the bound than the list
+// holds, the four waves run the bitwise search together and emit their keys
+// at offsets given by the selected counts of the waves before them.
+template <int NCW>
+__global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict__ scores,
+                                                        int32_t *__restrict__ block_idx,
+                                                        const int64_t *__restrict__ cu_q,
+                                                        const int64_t *__restrict__ cu_kv,
+                                                        int num_seqs, int64_t total_q, int nb_max,
+                                                        int BS, int K) {
+  __shared__ uint32_t gmax_sh[4 * 64];
+  __shared__ int cnt_sh[2][4];
+  __shared__ uint32_t cand_key[kCandCap];
+  __shared__ int32_t cand_idx[kCandCap];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t grow = blockIdx.x;  // g * total_q + row
+  const int64_t row = grow % total_q;
+  const int b = find_seq(cu_q, num_seqs, row);
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  const int64_t p = sq.base + (row - sq.q0);
+  int32_t *dst = block_idx + grow * K;
+  if (p < 0) {
+    for (int i = threadIdx.x; i < K; i += 256) dst[i] = -1;
+    return;
+  }
+  const int J = (int)(p / BS);
+  const int need = K - 1;
+  if (J <= need) {
+    for (int i = threadIdx.x; i < K; i += 256) dst[i] = i <= J ? i : -1;
+    return;
+  }
+  const float *src = scores + grow * nb_max;
+  const int j0 = wave * 64 * NCW;
+  uint32_t key[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    const int j = j0 + 64 * c + lane;
+    key[c] = j < J ? ordered_key(src[j]) : 0u;
+  }
+  // Lower bound: the need-th largest of the maxima of the 64 residue classes
+  // j mod 64 (lane l of every wave holds class l).  The first J keys fall in
+  // min(J, 64) > need classes, so at least `need` keys are >= it.
+  uint32_t gm = 0u;
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) gm = max(gm, key[c]);
+  gmax_sh[wave * 64 + lane] = gm;
+  __syncthreads();
+  uint32_t cls[1] = {max(max(gmax_sh[lane], gmax_sh[64 + lane]),
+                         max(gmax_sh[128 + lane], gmax_sh[192 + lane]))};
+  const uint32_t lb = kth_largest<1>(cls, need);
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) n += __popcll(ballot64(key[c] >= lb));
+  if (lane == 0) cnt_sh[0][wave] = n;
+  __syncthreads();
+  int total = 0, off = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int cw = cnt_sh[0][w];
+    off += w < wave ? cw : 0;
+    total += cw;
+  }
+  if (total <= kCandCap) {
+    int base = off;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+      const bool in = key[c] >= lb;
+      const uint64_t m = ballot64(in);
+      if (in) {
+        cand_key[base + mbcnt64(m)] = key[c];
+        cand_idx[base + mbcnt64(m)] = j0 + 64 * c + lane;
+      }
+      base += __popcll(m);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    auto finish = [&](auto tag) {
+      constexpr int CC = decltype(tag)::value;
+      uint32_t ck[CC];
+      int ci[CC];
+#pragma unroll
+      for (int c = 0; c < CC; ++c) {
+        const int i = 64 * c + lane;
+        ck[c] = i < total ? cand_key[i] : 0u;
+        ci[c] = i < total ? cand_idx[i] : 0;
+      }
+      const uint32_t tau = kth_largest_in<CC>(ck, need, lb, wave_max_key<CC>(ck));
+      emit_selected<CC>(ck, [&](int c) { return ci[c]; }, tau, need, dst);
+    };
+    if (total <= 128) finish(std::integral_constant<int, 2>());
+    else if (total <= 256) finish(std::integral_constant<int, 4>());
+    else finish(std::integral_constant<int, kCandCap / 64>());
+    if (lane == 0) dst[need] = J;
+    return;
+  }
+  // Cooperative exact search: bit by bit, the four waves' counts are summed
+  // through LDS (two count slots alternate, so one barrier per bit is enough).
+  uint32_t tau = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) cnt += __popcll(ballot64(key[c] >= cand));
+    if (lane == 0) cnt_sh[bit & 1][wave] = cnt;
+    __syncthreads();
+    const int tot = cnt_sh[bit & 1][0] + cnt_sh[bit & 1][1] + cnt_sh[bit & 1][2] + cnt_sh[bit & 1][3];
+    if (tot >= need) tau = cand;
+  }
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    gt += __popcll(ballot64(key[c] > tau));
+    eq += __popcll(ballot64(key[c] == tau));
+  }
+  __syncthreads();  // every wave is done reading the count slots
+  if (lane == 0) {
+    cnt_sh[0][wave] = gt;
+    cnt_sh[1][wave] = eq;
+  }
+  __syncthreads();
+  int GT = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) GT += cnt_sh[0][w];
+  const int take_eq = need - GT;
+  int out0 = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int e = cnt_sh[1][w];
+    out0 += cnt_sh[0][w] + min(max(take_eq - eq_before, 0), e);
+    eq_before += e;
+  }
+  emit_from<NCW>(key, [&](int c) { return j0 + 64 * c + lane; }, tau, take_eq, out0, eq_before,
+                 dst);
+  if (threadIdx.x == 0) dst[need] = J;
+}
+
+template <int NCW>
+hipError_t launch_long(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s) {
+  const int64_t rows = (int64_t)p.G * p.total_q;
+  hipLaunchKernelGGL((topk_long_kernel<NCW>), dim3((unsigned)rows), dim3(256), 0, s, scores,
+                     block_idx, p.cu_q, p.cu_kv, p.num_seqs, p.total_q, p.nb_max, p.B, p.top_k);
+  profile_mark(s);
+  return hipGetLastError();
 }
 
 template <int NCH>
@@ -220,7 +384,11 @@ hipError_t launch_topk(const Dims &p, const float *scores, int32_t *block_idx, h
   if (nch <= 4) return launch_nch<4>(p, scores, block_idx, s);
   if (nch <= 8) return launch_nch<8>(p, scores, block_idx, s);
   if (nch <= 16) return launch_nch<16>(p, scores, block_idx, s);
-  return launch_nch<0>(p, scores, block_idx, s);  // long rows: streamed keys
+  if (nch <= 32) return launch_nch<32>(p, scores, block_idx, s);
+  // rows of up to 4096 / 8192 blocks: four waves per row
+  if (nch <= 64) return launch_long<16>(p, scores, block_idx, s);
+  if (nch <= 128) return launch_long<32>(p, scores, block_idx, s);
+  return hipErrorInvalidValue;  // rows are at most 8192 blocks (checked at the API)
 }
 
 }  // namespace msa
