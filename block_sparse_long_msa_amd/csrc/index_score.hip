@@ -48,7 +48,7 @@ template <int DI, int BS>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI >= 128 ? 2 : 4, DI >= 128 ? 2 : 4))) void index_score_mfma_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     float *__restrict__ scores, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, int G, int nb_max, int64_t total_q) {
+    const int64_t *__restrict__ cu_kv, int G, int nb_max, int64_t total_q, int nqt, int nkcl) {
   using T = IdxTile<DI, BS>;
   constexpr int QT = kQT, KC = kKC, CPR = T::CPR, CPT = T::CPT;
   constexpr int KT = BS / 32;  // 32-key tiles per block
@@ -59,10 +59,20 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
-  // Query tiles are dispatched last-first: the late tiles see the most causal
-  // blocks, so the heavy work-groups start first and the tail is light.  The
-  // key chunk kc varies fastest, so chunk kc stays on one XCD (and its L2).
-  const int kc = blockIdx.x, qt = gridDim.y - 1 - blockIdx.y, bg = blockIdx.z;
+  // Work-groups are dealt to the 8 XCDs round-robin (w runs on XCD w % 8).
+  // Each XCD owns whole key chunks and runs the query tiles of one chunk back
+  // to back, so the chunk's index keys are read from HBM once into that XCD's
+  // L2 and reused by every query tile.  Chunks go to XCDs in snake order
+  // (slot s of XCD x is chunk 8s + x for even s, 8s + 7 - x for odd s), which
+  // balances the causal triangle's uneven chunks across XCDs.
+  const int x = blockIdx.x & 7;
+  int local = blockIdx.x >> 3;
+  const int qt = nqt - 1 - local % nqt;
+  local /= nqt;
+  const int slot = local % nkcl;
+  const int bg = local / nkcl;
+  const int kc = 8 * slot + ((slot & 1) ? 7 - x : x);
+  if (kc * KC >= nb_max) return;
   const int b = bg / G, g = bg - b * G;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
   const int64_t t0 = (int64_t)qt * QT;
@@ -308,9 +318,14 @@ __global__ __launch_bounds__(256) void index_score_f32_kernel(
 template <int DI, int BS>
 hipError_t launch_mfma(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx, float *scores,
                        hipStream_t s) {
-  dim3 grid((p.nb_max + kKC - 1) / kKC, (p.max_q_len + kQT - 1) / kQT, p.num_seqs * p.G);
-  hipLaunchKernelGGL((index_score_mfma_kernel<DI, BS>), grid, dim3(kIdxThreads), 0, s, q_idx, k_idx,
-                     scores, p.cu_q, p.cu_kv, p.G, p.nb_max, p.total_q);
+  const int nkc = (p.nb_max + kKC - 1) / kKC;   // key chunks
+  const int nkcl = (nkc + 7) / 8;                // chunk slots per XCD
+  const int nqt = (p.max_q_len + kQT - 1) / kQT; // query tiles
+  const int64_t nwg = (int64_t)8 * nkcl * nqt * p.num_seqs * p.G;
+  if (nwg > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((index_score_mfma_kernel<DI, BS>), dim3((unsigned)nwg), dim3(kIdxThreads), 0,
+                     s, q_idx, k_idx, scores, p.cu_q, p.cu_kv, p.G, p.nb_max, p.total_q, nqt,
+                     nkcl);
   profile_mark(s);
   return hipGetLastError();
 }
