@@ -114,6 +114,22 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
     const int64_t kstride = (int64_t)G * DI;
     const uint16_t *kbase = k_idx + ((sq.kv0 + (int64_t)j0 * BS) * G + g) * (int64_t)DI;
     const int64_t rows_left = sq.lkv - (int64_t)j0 * BS;  // key rows of the chunk that exist
+    // Blocks of the pipelined loop lie below every query's position, so all
+    // their rows exist: a per-thread pointer stepped by one block per block.
+    const uint16_t *kthr[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int P = min(tid + kIdxThreads * i, T::CHUNKS - 1);
+      kthr[i] = kbase + (P / CPR) * kstride + 8 * (P % CPR);
+    }
+    const int64_t kblock = (int64_t)BS * kstride;
+    auto fetch_full = [&](int it, u32x4 (&regs)[CPT]) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        if (tid + kIdxThreads * i >= T::CHUNKS) break;
+        regs[i] = ld16(kthr[i] + it * kblock);
+      }
+    };
     auto fetch = [&](int it, u32x4 (&regs)[CPT]) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
     auto step = [&](int it, const uint8_t *cur, uint8_t *other, u32x4 (&nxt)[CPT]) {
       __syncthreads();  // block it visible; every wave is done with `other`
       if (it + 1 < nfull) store(nxt, other);
-      if (it + 3 < nfull) fetch(it + 3, nxt);
+      if (it + 3 < nfull) fetch_full(it + 3, nxt);
       float m0 = neg_inf(), m1 = neg_inf();
       f32x16 acc[1][2];
       auto reduce = [&](f32x16 (&a)[2]) {
@@ -183,10 +199,10 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
     };
     if (nfull > 0) {
       u32x4 ra[CPT], rb[CPT];
-      fetch(0, ra);
-      store(ra, stage[0]);              // block 0 -> stage 0
-      if (1 < nfull) fetch(1, ra);      // block 1 in ra
-      if (2 < nfull) fetch(2, rb);      // block 2 in rb
+      fetch_full(0, ra);
+      store(ra, stage[0]);                   // block 0 -> stage 0
+      if (1 < nfull) fetch_full(1, ra);      // block 1 in ra
+      if (2 < nfull) fetch_full(2, rb);      // block 2 in rb
       for (int it = 0; it < nfull; it += 2) {
         step(it, stage[0], stage[1], ra);                          // stores it+1, fetches it+3
         if (it + 1 < nfull) step(it + 1, stage[1], stage[0], rb);  // stores it+2, fetches it+4
@@ -220,9 +236,21 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
   for (int i = tid; i < (ncol - nblk) * QT; i += kIdxThreads)
     res[(nblk + i / QT) * RSTR + (i % QT)] = neg_inf();
   __syncthreads();
-  for (int i = tid; i < nq * ncol; i += kIdxThreads) {
-    const int r = i / ncol, c = i - (i / ncol) * ncol;
-    out_rows[(int64_t)r * nb_max + c] = res[c * RSTR + r];
+  if (ncol == KC && nb_max % 4 == 0) {
+    // full chunk: 4 consecutive blocks of one query row per 16-byte store
+    // (rows start 16-byte aligned: nb_max and j0 are multiples of 4)
+    constexpr int QPR = KC / 4;  // 16-byte pieces per query row
+    for (int i = tid; i < nq * QPR; i += kIdxThreads) {
+      const int r = i / QPR, c4 = 4 * (i % QPR);
+      const float4 v = {res[c4 * RSTR + r], res[(c4 + 1) * RSTR + r], res[(c4 + 2) * RSTR + r],
+                        res[(c4 + 3) * RSTR + r]};
+      *reinterpret_cast<float4 *>(out_rows + (int64_t)r * nb_max + c4) = v;
+    }
+  } else {
+    for (int i = tid; i < nq * ncol; i += kIdxThreads) {
+      const int r = i / ncol, c = i - (i / ncol) * ncol;
+      out_rows[(int64_t)r * nb_max + c] = res[c * RSTR + r];
+    }
   }
 }
 
