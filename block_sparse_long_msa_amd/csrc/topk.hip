@@ -25,7 +25,7 @@ namespace msa {
 namespace {
 
 constexpr int kCandCap = 512;  // candidates kept for the exact search (8 per lane)
-constexpr int kPruneMinChunks = 8;  // rows of fewer chunks go straight to the exact search
+constexpr int kPruneMinChunks = 4;  // rows of fewer chunks go straight to the exact search
 
 // Exact need-th largest key among NC chunks of 64 keys (0 = absent).
 template <int NC>

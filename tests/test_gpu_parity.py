@@ -78,10 +78,15 @@ def test_tiny_fp32_workload_every_row():
 
 
 def test_topk_exact_on_synthetic_scores():
-    """Selection alone, on generated score rows with many exact ties: bit-exact."""
-    for nb, lq, levels in ((16, 1024, 3), (300, 300 * 64, 2), (1100, 70000, 0), (8192, 2048, 5)):
-        B = 64 if nb != 8192 else 128
-        k = 13 if nb < 8192 else 64
+    """Selection alone, on generated score rows with many exact ties: bit-exact.
+
+    Row lengths reach every kernel variant: one wave per row with 1, 8 and 32
+    chunks of 64 keys in registers, and four waves per row (up to 4096 and
+    8192 blocks); every 17th row is constant, which forces the exact search
+    over the whole row."""
+    for nb, lq, levels, B, k in ((16, 1024, 3, 64, 13), (300, 300 * 64, 2, 64, 13),
+                                 (1100, 70000, 0, 64, 13), (3000, 4000, 2, 64, 13),
+                                 (3000, 3000, 1, 64, 64), (8192, 2048, 5, 128, 64)):
         lkv = nb * B
         lq = min(lq, lkv)
         G = 2
