@@ -659,11 +659,10 @@ __device__ __forceinline__ int opaque_lane_zero() {
 __device__ __forceinline__ void pin(u32x4 &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(int32_t &x) { asm volatile("" : "+v"(x)); }
 
-// Persistent partial attention.  Work items are split into one contiguous
-// range per XCD (work-groups are dealt to the XCDs round-robin, so work-group
-// w runs on XCD w % 8); the work-groups of an XCD walk its range with a
-// stride, so the items of a bucket, which share one K/V block, meet in the
-// same L2.  Each work-group double-buffers the K/V tile in LDS: while it
+// Persistent partial attention.  Work-groups are dealt to the XCDs
+// round-robin (work-group w runs on XCD w % 8); the item order is described
+// at the top of the kernel.  Each work-group double-buffers the K/V tile in
+// LDS: while it
 // computes item t from one tile, the K/V block of item t+1 streams straight
 // into the other tile, its Q rows into registers, and the descriptor and
 // entries of item t+2 too; one barrier per item hands the tiles over.  Every
@@ -681,23 +680,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t *__restrict__ v, const int32_t *__restrict__ item_off,
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
-    float2 *__restrict__ trash_ml, int H, int G, int K, int64_t nbk, int qch, float scale_log2) {
+    float2 *__restrict__ trash_ml, int H, int G, int K, int nseg, int nb_max, int qch,
+    float scale_log2) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
   // two separate objects, so the compiler can tell the tile being loaded
   // from the tile being read
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile_a;
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile_b;
-  const int nitems = item_off[nbk];
-  int lo = 0, hi = nitems, first = blockIdx.x, step = gridDim.x;
+  // Item order.  Items come in segments, one per (sequence, group) pair (its
+  // buckets, block by block).  Every XCD takes its eighth of segment 0, then
+  // its eighth of segment 1, and so on, and the XCD's work-groups stride
+  // through that eighth: at any time the whole GPU gathers Q rows of the
+  // same group (a working set that stays in the Infinity Cache between the
+  // many reads of each row), and consecutive items of an XCD still share
+  // buckets (the K/V block stays in its L2).
+  int xcd = 0, parts = 1, nw = gridDim.x, w = blockIdx.x;
   if (gridDim.x % 8 == 0) {
-    const int x = blockIdx.x % 8;
-    lo = (int)((int64_t)nitems * x / 8);
-    hi = (int)((int64_t)nitems * (x + 1) / 8);
-    first = lo + blockIdx.x / 8;
-    step = gridDim.x / 8;
+    xcd = blockIdx.x % 8;
+    parts = 8;
+    nw = gridDim.x / 8;
+    w = blockIdx.x / 8;
   }
-  if (first >= hi) return;
-  const int last = first + (hi - 1 - first) / step * step;  // this work-group's last item
+  auto part_of = [&](int sg, int &plo, int &phi) {
+    const int a = item_off[(int64_t)sg * nb_max], b = item_off[(int64_t)(sg + 1) * nb_max];
+    plo = a + (int)((int64_t)(b - a) * xcd / parts);
+    phi = a + (int)((int64_t)(b - a) * (xcd + 1) / parts);
+  };
+  int total = 0;  // items of this work-group
+  for (int sg = 0; sg < nseg; ++sg) {
+    int plo, phi;
+    part_of(sg, plo, phi);
+    if (plo + w < phi) total += (phi - plo - w + nw - 1) / nw;
+  }
+  if (total == 0) return;
+  // Cursor over this work-group's items; once they run out it repeats the
+  // last one (a work-group with an odd count runs its last item twice,
+  // writing the same values to the same places).
+  int cur_sg = 0, cur_it = 0, cur_end = 0, cur_last = 0;
+  auto next_item = [&]() {
+    while (cur_it >= cur_end && cur_sg < nseg) {
+      int plo, phi;
+      part_of(cur_sg, plo, phi);
+      ++cur_sg;
+      cur_it = plo + w;
+      cur_end = phi;
+    }
+    if (cur_it < cur_end) {
+      cur_last = cur_it;
+      cur_it += nw;
+    }
+    return cur_last;
+  };
   const int hpg = H / G;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, col = lane & 31;
@@ -706,10 +739,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int hh = r - qi * hpg;     // head inside the group
   const int qs = min(qi, qch - 1); // entry slot read by this lane
   const int32_t *desc_base = item_desc + opaque_lane_zero();
-  auto meta_at = [&](int it, u32x4 &w, int32_t &e) {
-    const int64_t i = min(it, last);
-    w = ld16(desc_base + 4 * i);
-    e = entries[i * qch + qs];
+  auto meta_at = [&](int it, u32x4 &wd, int32_t &e) {
+    wd = ld16(desc_base + 4 * (int64_t)it);
+    e = entries[(int64_t)it * qch + qs];
   };
   auto decode = [&](const u32x4 &w) {
     ItemDesc d;
@@ -728,7 +760,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // registers, K/V block straight into tile tn) and the metadata of the one
   // after (into wc / ec, free once the current item's store addresses are
   // formed), then compute the current item from tile tc.
-  auto run_item = [&](int it, bf16x8 (&qc)[D / 16], bf16x8 (&qn)[D / 16], u32x4 &wc,
+  auto run_item = [&](int it_after_next, bf16x8 (&qc)[D / 16], bf16x8 (&qn)[D / 16], u32x4 &wc,
                       int32_t &ec, u32x4 &wn, int32_t &en, KvTile<D, BS> &tc,
                       KvTile<D, BS> &tn) {
     // the next item's metadata is read from here on, not earlier (where it
@@ -743,7 +775,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const ItemDesc dn = decode(wn);
     q_of(qn, dn, en);
     dma_kv<D, BS, false>(tn, k, v, dn.kvrow, BS, G, dn.g);
-    meta_at(it + 2 * step, wc, ec);
+    meta_at(it_after_next, wc, ec);
     // keep the loads above ahead of the compute (the scheduler would
     // otherwise sink them next to their first use, after it)
     __builtin_amdgcn_sched_barrier(0);
@@ -754,8 +786,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   u32x4 wa, wb;
   int32_t ea, eb;
-  meta_at(first, wa, ea);
-  meta_at(first + step, wb, eb);
+  meta_at(next_item(), wa, ea);
+  meta_at(next_item(), wb, eb);
   bf16x8 qa[D / 16], qb[D / 16];
   {
     const ItemDesc d = decode(wa);
@@ -764,10 +796,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   dma_settle<D, BS>(tile_a);
   __syncthreads();
-  for (int it = first;; it += 2 * step) {
-    run_item(it, qa, qb, wa, ea, wb, eb, tile_a, tile_b);
-    run_item(it + step, qb, qa, wb, eb, wa, ea, tile_b, tile_a);
-    if (it + 2 * step > last) break;
+  for (int done = 0; done < total; done += 2) {
+    run_item(next_item(), qa, qb, wa, ea, wb, eb, tile_a, tile_b);
+    run_item(next_item(), qb, qa, wb, eb, wa, ea, tile_b, tile_a);
   }
 }
 
@@ -976,7 +1007,8 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
                      dim3(kThreads), 0, s, q, k, v, w.item_off, w.entries, w.item_desc, w.part_o,
-                     w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, w.nbk, qch, sl2);
+                     w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, p.num_seqs * p.G,
+                     p.nb_max, qch, sl2);
   profile_mark(s);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(kThreads), 0, s,
                      q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv, p.num_seqs, p.H,
