@@ -927,7 +927,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         w[u] = wsh[(s + u) * H + h];
-        x[u] = ld16(src + (int64_t)(s + u) * H * D);
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (int64_t)(s + u) * H * D));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -940,7 +940,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     }
     for (; s < K; ++s) {
       const float w = wsh[s * H + h];
-      const u32x4 x = ld16(src + (int64_t)s * H * D);
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (int64_t)s * H * D));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += w > 0.f ? w * bf16_lo(x[i]) : 0.f;
