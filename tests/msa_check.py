@@ -107,8 +107,12 @@ def check_attention(out_gpu: np.ndarray, lse_gpu: Optional[np.ndarray], out_ref:
 
 def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int, dtype: str,
                   rows_per_seq: Optional[Sequence[Sequence[int]]] = None,
-                  schedule: str = "auto") -> Dict[str, float]:
-    """Run the whole path on the GPU and check sampled rows (all rows if None)."""
+                  schedule: str = "auto", shuffle_slots: bool = False) -> Dict[str, float]:
+    """Run the whole path on the GPU and check sampled rows (all rows if None).
+
+    With shuffle_slots, the attention gets every row's kept-block list in a
+    seeded random order (the -1 padding included): the result must not
+    depend on the order of the list."""
     prob = problem_for(inp, H, G, d, d_idx, B, k, dtype, schedule)
     dev = inp["q"].device
     scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
@@ -145,6 +149,10 @@ def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int,
         if r is not None:
             gr = torch.from_numpy(r["global_rows"]).to(dev)
             idx_in[:, gr, :] = torch.from_numpy(r["block_idx"]).to(dev)
+    if shuffle_slots:
+        gen = torch.Generator(device="cpu").manual_seed(1234)
+        perm = torch.rand(idx_in.shape, generator=gen).argsort(dim=-1).to(dev)
+        idx_in = torch.gather(idx_in, -1, perm).contiguous()
     out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], idx_in, return_lse=True)
     torch.cuda.synchronize()
     stats = {"score_ratio": 0.0, "unseparated": 0, "out_err": 0.0, "rows": 0}

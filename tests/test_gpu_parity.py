@@ -59,6 +59,19 @@ def test_small_kv_major_schedule(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1]], ids=[SMALL[0][0], SMALL[1][0]])
+def test_unsorted_block_lists(case, dtype):
+    """The kept-block lists are sets: any order of a row's entries gives the oracle's result."""
+    name, lq, lkv, H, G, d, di, B, k = case
+    inp = W.random_case(40 + SMALL.index(case), lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+    for sched in ("query_major", "kv_major"):
+        if sched == "kv_major" and dtype == "f32":
+            continue
+        _log(f"unsorted lists {name} {sched} {dtype}")
+        C.run_and_check(inp, H, G, d, di, B, k, dtype, schedule=sched, shuffle_slots=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_small_decode_batch(dtype):
     """max_q_len == 1: streaming index kernel and split-KV attention."""
     lkv = [1, 127, 128, 129, 5000, 64, 3000]
