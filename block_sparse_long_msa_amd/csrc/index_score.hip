@@ -181,20 +181,45 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
       __syncthreads();  // block it visible; every wave is done with `other`
       if (it + 1 < nfull) store(nxt, other);
       if (it + 3 < nfull) fetch_full(it + 3, nxt);
+      // Skewed schedule: the max over query half 0 of key tile kt runs while
+      // the MFMAs of half 1 execute, and the max over half 1 while the MFMAs
+      // of half 0 of tile kt+1 execute, so the block-max VALU work overlaps
+      // the matrix pipe instead of following it.
       float m0 = neg_inf(), m1 = neg_inf();
-      f32x16 acc[1][2];
-      auto reduce = [&](f32x16 (&a)[2]) {
+      f32x16 a0, a1;
+      auto mfma_half = [&](f32x16 &a, const u32x4 (&kf)[NK], int sq) {
+        a = f32x16{};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          m0 = fmaxf(m0, a[0][e]);
-          m1 = fmaxf(m1, a[1][e]);
+        for (int c = 0; c < NK; ++c) a = mfma32x32x16(as_bf16x8(kf[c]), qb[sq][c], a);
+      };
+      auto max_into = [&](float &m, const f32x16 &a) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, a[e]);
+      };
+      // interleave: one MFMA, then two VALU ops (the 16-value max of the other
+      // half is 8 v_max3), for the NK MFMAs just issued
+      auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
       };
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        mma(cur, kt, acc[0]);
-        reduce(acc[0]);
+        u32x4 kf[NK];
+        const int r = kt * 32 + col;
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+          kf[c] = *reinterpret_cast<const u32x4 *>(cur + 16 * T::swz(r, 2 * c + half));
+        mfma_half(a0, kf, 0);
+        if (kt > 0) max_into(m1, a1);  // half 1 of tile kt-1
+        interleave();
+        mfma_half(a1, kf, 1);
+        max_into(m0, a0);              // half 0 of tile kt
+        interleave();
       }
+      max_into(m1, a1);
       put(it, m0, m1);
     };
     if (nfull > 0) {
