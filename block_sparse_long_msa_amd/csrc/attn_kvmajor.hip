@@ -802,6 +802,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Last slot of a kept-block list (K <= 64 entries) that holds block J, or
+// -1.  When the list is 16-byte aligned (K a multiple of 4) all of its loads
+// are issued, 16 bytes at a time, before any is compared.
+__device__ __forceinline__ int last_slot_of(const int32_t *__restrict__ br, int K, int J) {
+  int slot = -1;
+  if ((K & 3) == 0) {
+    u32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (4 * i < K) v[i] = ld16(br + 4 * i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * i < K && (int)v[i][e] == J) slot = 4 * i + e;
+  } else {
+#pragma unroll 8
+    for (int i = 0; i < K; ++i)
+      if (br[i] == J) slot = i;
+  }
+  return slot;
+}
+
 // The current block of each 128-query block of positions, with the causal
 // mask; its partial goes to the slot holding that block (if listed).
 template <int D, int BS>
@@ -849,12 +872,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const RowT cur = row_of(rt);
     bf16x8 qa[D / 16];
     load_q<D>(qa, q + (cur.row * H + cur.h) * (int64_t)D, cur.valid);
-    int slot = -1;
-    if (cur.valid) {
-      const int32_t *br = block_idx + ((int64_t)g * total_q + cur.row) * K;
-      for (int s = 0; s < K; ++s)
-        if (br[s] == J) slot = s;
-    }
+    const int slot = cur.valid ? last_slot_of(block_idx + ((int64_t)g * total_q + cur.row) * K, K, J)
+                               : -1;
     const bool write = cur.valid && slot >= 0;
     const int64_t ps = (cur.row * K + (slot < 0 ? 0 : slot)) * H + cur.h;
     const int lane = threadIdx.x & 63;
