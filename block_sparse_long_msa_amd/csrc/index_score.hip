@@ -279,67 +279,117 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
   }
 }
 
-// One wave per key block; lane l reads 16-byte chunk l of each 1 KiB slab of
-// the packed [key][group][d_idx] index-key rows.  KPS keys share a slab.
+// Sum over aligned groups of LPD lanes (4, 8 or 16) with DPP lane moves:
+// swap neighbours, swap pairs, then fold the mirrored half of the 8-lane and
+// 16-lane row.  Every lane of a group ends with the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int LPD>
+__device__ __forceinline__ float lane_group_sum(float a) {
+  a += dpp_mov<0xB1>(a);                       // quad_perm(1,0,3,2)
+  a += dpp_mov<0x4E>(a);                       // quad_perm(2,3,0,1)
+  if constexpr (LPD >= 8) a += dpp_mov<0x141>(a);   // row_half_mirror
+  if constexpr (LPD >= 16) a += dpp_mov<0x140>(a);  // row_mirror
+  return a;
+}
+
+// One work-group per key block.  Lane l reads 16-byte chunk l of each 1 KiB
+// slab of the packed [key][group][d_idx] index-key rows (KPS keys share a
+// slab), and wave w takes slabs w, w+4, ..., so the four waves stream 4 KiB of
+// contiguous keys per step.  The block index is uniform, so the slab loop over
+// a full block keeps eight loads per wave in flight; only a block cut by the
+// causal end takes a predicated last slab.
 template <int DI, int KPS>
 __global__ __launch_bounds__(256) void index_score_decode_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     float *__restrict__ scores, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int G, int BS, int nb_max, int64_t total_q) {
   constexpr int LPD = DI / 8;  // lanes per (key, group) dot product
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float wave_max[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int rowlen = 512 / KPS;  // G * DI elements per key
   const int b = blockIdx.y;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
-  if (sq.lq <= 0) return;
-  const int j = blockIdx.x * 4 + wave;
-  if (j >= nb_max) return;
+  const int j = blockIdx.x;
   const int64_t row = sq.q0;
   const int64_t p = sq.base;  // the query's position: len_kv - 1
-  const int rowlen = G * DI;
   const int e = lane * 8;
   const int key_in_slab = e / rowlen;
-  const int g = (e - key_in_slab * rowlen) / DI;
-  const int dof = e - key_in_slab * rowlen - g * DI;
-  const bool writer = key_in_slab == 0 && dof == 0;
+  const int g = (e % rowlen) / DI;
+  const int dof = e % DI;
+  const bool writer = wave == 0 && key_in_slab == 0 && dof == 0;
   float *dst = scores + ((int64_t)g * total_q + row) * nb_max + j;
-  const int64_t jmax = p < 0 ? -1 : p / BS;
-  if ((int64_t)j > jmax) {
-    if (writer) *dst = neg_inf();
+  const int64_t s_begin = (int64_t)j * BS;
+  // One branch for both exits: a sequence with no query row, and a block that
+  // starts past the query (also p < 0: an empty cache).
+  if (sq.lq <= 0 || s_begin > p) {
+    if (sq.lq > 0 && writer) *dst = neg_inf();
     return;
   }
+  const u32x4 qw = ld16(q_idx + (row * G + g) * (int64_t)DI + dof);
   float qf[8];
-  {
-    const u32x4 w = ld16(q_idx + (row * G + g) * (int64_t)DI + dof);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qf[2 * i] = bf16_lo(w[i]);
-      qf[2 * i + 1] = bf16_hi(w[i]);
-    }
-  }
-  const int64_t s_begin = (int64_t)j * BS;
-  const int nkeys = (int)(min<int64_t>(s_begin + BS, p + 1) - s_begin);
-  const int nslab = (nkeys + KPS - 1) / KPS;
-  const uint16_t *base = k_idx + (sq.kv0 + s_begin) * (int64_t)rowlen + e;
-  float mx = neg_inf();
-#pragma unroll 8
-  for (int i = 0; i < nslab; ++i) {
-    const int key = i * KPS + key_in_slab;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    // the index-key cache is streamed once per step: non-temporal loads
-    if (key < nkeys)
-      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)i * 512));
+  auto dot = [&](const u32x4 w) {
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       acc = fmaf(qf[2 * t], bf16_lo(w[t]), acc);
       acc = fmaf(qf[2 * t + 1], bf16_hi(w[t]), acc);
     }
+    return lane_group_sum<LPD>(acc);
+  };
+  const int nkeys = (int)(min<int64_t>(s_begin + BS, p + 1) - s_begin);
+  const int nfull = nkeys / KPS;  // slabs whose keys are all causal
+  const int nslab = nfull + (nfull * KPS < nkeys ? 1 : 0);  // incl. a causally cut slab
+  const uint16_t *blk = k_idx + (sq.kv0 + s_begin) * (int64_t)rowlen;
+  const int in_row = e - key_in_slab * rowlen;  // this lane's offset within a key row
+  // Wave w reads slabs w, w+4, ..., w+28 of a batch; rows past the block's
+  // last causal key are clamped to it (those loads stay in bounds and their
+  // values are never used).  The index-key cache is streamed once per step:
+  // non-temporal loads.
+  u32x4 w[8];
+  auto load_batch = [&](int i0) {
 #pragma unroll
-    for (int off = 1; off < LPD; off <<= 1) acc += shfl_xor_f(acc, off);
-    if (key < nkeys) mx = fmaxf(mx, acc);
+    for (int u = 0; u < 8; ++u) {
+      const int r = min((i0 + 4 * u) * KPS + key_in_slab, nkeys - 1);
+      w[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(blk + (int64_t)r * rowlen + in_row));
+    }
+  };
+  float mx = neg_inf();
+  int i = wave;
+  // The first batch is in flight before the query slice is waited for, and it
+  // is used on every path, so it is not moved behind a branch.
+  load_batch(i);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    qf[2 * t] = bf16_lo(qw[t]);
+    qf[2 * t + 1] = bf16_hi(qw[t]);
+  }
+  while (i + 28 < nfull) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mx = fmaxf(mx, dot(w[u]));
+    i += 32;
+    if (i < nslab) load_batch(i);
+  }
+  // Fewer than eight of this wave's slabs are left, all in w.
+  if (i < nslab) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sl = i + 4 * u;
+      const bool live = sl < nfull || (sl == nfull && nfull * KPS + key_in_slab < nkeys);
+      const float acc = dot(w[u]);
+      if (live) mx = fmaxf(mx, acc);
+    }
   }
   for (int off = rowlen / 8; off < 64; off <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
-  if (writer) *dst = mx;
+  wave_max[wave][lane] = mx;
+  __syncthreads();
+  if (writer)
+    *dst = fmaxf(fmaxf(wave_max[0][lane], wave_max[1][lane]),
+                 fmaxf(wave_max[2][lane], wave_max[3][lane]));
 }
 
 __global__ __launch_bounds__(256) void index_score_f32_kernel(
@@ -386,7 +436,7 @@ hipError_t launch_mfma(const Dims &p, const uint16_t *q_idx, const uint16_t *k_i
 template <int DI, int KPS>
 hipError_t launch_decode(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx,
                          float *scores, hipStream_t s) {
-  dim3 grid((p.nb_max + 3) / 4, p.num_seqs);
+  dim3 grid(p.nb_max, p.num_seqs);
   hipLaunchKernelGGL((index_score_decode_kernel<DI, KPS>), grid, dim3(256), 0, s, q_idx, k_idx,
                      scores, p.cu_q, p.cu_kv, p.G, p.B, p.nb_max, p.total_q);
   profile_mark(s);
