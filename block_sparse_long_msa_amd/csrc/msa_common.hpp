@@ -67,6 +67,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+// DPP lane move within 16-lane rows (CTRL: 0xB1 swaps neighbours, 0x4E swaps
+// pairs, 0x141 mirrors each 8-lane half row, 0x140 mirrors the row).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// Wave-uniform maximum / minimum of one value per lane: DPP steps reduce each
+// 16-lane row, then the four row results are read into scalar registers.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = max(m, dpp_u32<0xB1>(m));
+  m = max(m, dpp_u32<0x4E>(m));
+  m = max(m, dpp_u32<0x141>(m));
+  m = max(m, dpp_u32<0x140>(m));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t m) {
+  m = min(m, dpp_u32<0xB1>(m));
+  m = min(m, dpp_u32<0x4E>(m));
+  m = min(m, dpp_u32<0x141>(m));
+  m = min(m, dpp_u32<0x140>(m));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+}
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int mbcnt64(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -41,35 +41,66 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[NC], int n
   return tau;
 }
 
-// The same when the answer is known to lie in [lo, hi] (at least `need` keys
-// are >= lo and none is above hi): it shares the bits of lo and hi above
-// their highest differing bit, so the search starts there.
+// One step of the bitwise search: keep `bit` in tau if at least `need` keys
+// are >= tau | bit.  Bits HI..LO of the search, unrolled (no loop overhead on
+// the scalar unit, which carries the counts).
 template <int NC>
-__device__ __forceinline__ uint32_t kth_largest_in(const uint32_t (&key)[NC], int need, uint32_t lo,
-                                                   uint32_t hi) {
-  const uint32_t diff = lo ^ hi;
-  if (diff == 0u) return lo;
-  const int top = 31 - __builtin_clz(diff);
-  uint32_t tau = lo & ~((2u << top) - 1u);  // common prefix, lower bits 0
-  for (int bit = top; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int cnt = 0;
+__device__ __forceinline__ uint32_t search_step(const uint32_t (&key)[NC], int need, uint32_t tau,
+                                                uint32_t bit) {
+  const uint32_t cand = tau | bit;
+  int cnt = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) cnt += __popcll(ballot64(key[c] >= cand));
-    if (cnt >= need) tau = cand;
-  }
+  for (int c = 0; c < NC; ++c) cnt += __popcll(ballot64(key[c] >= cand));
+  return cnt >= need ? cand : tau;
+}
+template <int NC, int HI, int LO>
+__device__ __forceinline__ uint32_t search_bits(const uint32_t (&key)[NC], int need, uint32_t tau) {
+#pragma unroll
+  for (int b = HI; b >= LO; --b) tau = search_step<NC>(key, need, tau, 1u << b);
   return tau;
 }
 
-// Maximum key over the wave (all lanes get it).
+// The need-th largest key when the answer is known to lie in [lo, hi] (at
+// least `need` keys are >= lo and none is above hi), with bits below LOW left
+// 0: for LOW > 0 the result is a lower bound that at least `need` keys still
+// reach.  The answer shares the bits of lo and hi above their highest
+// differing bit, so the search enters the unrolled bit sequence at bit 31, 23,
+// 15 or 7, whichever is the first at or above that bit.
+template <int NC, int LOW = 0>
+__device__ __forceinline__ uint32_t kth_largest_in(const uint32_t (&key)[NC], int need, uint32_t lo,
+                                                   uint32_t hi) {
+  // lo and hi are wave-uniform: the search runs on scalar registers
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  const uint32_t low_mask = ~((1u << LOW) - 1u);
+  const uint32_t diff = lo ^ hi;
+  if (diff < (1u << LOW)) return lo & low_mask;
+  if (diff >= (1u << 24)) return search_bits<NC, 31, LOW>(key, need, 0u);
+  if constexpr (LOW <= 23) {
+    if (diff >= (1u << 16)) return search_bits<NC, 23, LOW>(key, need, lo & 0xff000000u);
+  }
+  if constexpr (LOW <= 15) {
+    if (diff >= (1u << 8)) return search_bits<NC, 15, LOW>(key, need, lo & 0xffff0000u);
+  }
+  if constexpr (LOW <= 7) return search_bits<NC, 7, LOW>(key, need, lo & 0xffffff00u);
+  return lo & low_mask;  // not reached: diff < 2^LOW was handled above
+}
+
+// Maximum key over the wave, wave-uniform.
 template <int NC>
 __device__ __forceinline__ uint32_t wave_max_key(const uint32_t (&key)[NC]) {
   uint32_t m = key[0];
 #pragma unroll
   for (int c = 1; c < NC; ++c) m = max(m, key[c]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  return m;
+  return wave_max_u32(m);
+}
+
+// A lower bound for the need-th largest of one value per lane (need <= 63):
+// that value's top 16 bits, low bits 0.  At least `need` lanes are at or
+// above it, and it is within 2^-7 (relative) of the exact value.
+__device__ __forceinline__ uint32_t kth_largest_lanes_lb(uint32_t v, int need) {
+  const uint32_t one[1] = {v};
+  return kth_largest_in<1, 16>(one, need, wave_min_u32(v), wave_max_u32(v));
 }
 
 // Emits, in index order, every key > tau plus keys == tau while fewer than
@@ -113,10 +144,11 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per (group, query row), four rows per work-group.  The row's
-// candidate keys stay in registers: NCH chunks of 64 per lane, key j of the
-// row in chunk j / 64, lane j % 64 (0 past the candidates: it ranks below
-// every real key).  NCH = 128 covers the longest supported row (8192 blocks).
+// One wave per (group, query row), four rows of one group per work-group
+// (grid: query rows / 4 x groups).  Row, position and block index are
+// wave-uniform scalars.  The row's candidate keys stay in registers: NCH
+// chunks of 64 per lane, key j of the row in chunk j / 64, lane j % 64 (0 past
+// the candidates: it ranks below every real key).
 template <int NCH>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores,
                                                    int32_t *__restrict__ block_idx,
@@ -126,12 +158,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
                                                    int nb_max, int BS, int K) {
   __shared__ uint32_t cand_key_all[4][kCandCap];
   __shared__ int32_t cand_idx_all[4][kCandCap];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t *cand_key = cand_key_all[wave];
   int32_t *cand_idx = cand_idx_all[wave];
-  const int64_t grow = (int64_t)blockIdx.x * 4 + wave;  // g * total_q + row
-  if (grow >= (int64_t)G * total_q) return;
-  const int64_t row = grow % total_q;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= total_q) return;
+  const int64_t grow = (int64_t)blockIdx.y * total_q + row;  // g * total_q + row
   const int b = find_seq(cu_q, num_seqs, row);
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
   const int64_t p = sq.base + (row - sq.q0);
@@ -140,18 +173,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     for (int i = lane; i < K; i += 64) dst[i] = -1;
     return;
   }
-  const int J = (int)(p / BS);
+  const int J = (int)(p >> (31 - __builtin_clz(BS)));  // BS is a power of two
   const int need = K - 1;
   if (J <= need) {
     for (int i = lane; i < K; i += 64) dst[i] = i <= J ? i : -1;
     return;
   }
   const float *src = scores + grow * nb_max;
+  // all chunks load at once: lanes past the candidates read block J - 1
+  // (in the row) and take key 0
   uint32_t key[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int j = 64 * c + lane;
-    key[c] = j < J ? ordered_key(src[j]) : 0u;
+    key[c] = ordered_key(src[min(j, J - 1)]) & (j < J ? 0xffffffffu : 0u);
   }
   if (NCH >= kPruneMinChunks) {
     // Lower bound: the need-th largest of the group maxima (group r of a lane
@@ -162,15 +197,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     // i.i.d. scores, two per lane ~87 for need = 63.
     uint32_t lb;
     if (need <= 31) {
-      uint32_t gmax[1] = {0u};
+      uint32_t gmax = 0u;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) gmax[0] = max(gmax[0], key[c]);
-      lb = kth_largest<1>(gmax, need);
+      for (int c = 0; c < NCH; ++c) gmax = max(gmax, key[c]);
+      lb = kth_largest_lanes_lb(gmax, need);
     } else {
       uint32_t gmax[2] = {0u, 0u};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) gmax[c & 1] = max(gmax[c & 1], key[c]);
-      lb = kth_largest<2>(gmax, need);
+      lb = kth_largest_in<2, 16>(gmax, need, wave_min_u32(min(gmax[0], gmax[1])),
+                                 wave_max_u32(max(gmax[0], gmax[1])));
     }
     int n_cand = 0;
 #pragma unroll
@@ -234,9 +270,10 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
   __shared__ int cnt_sh[2][4];
   __shared__ uint32_t cand_key[kCandCap];
   __shared__ int32_t cand_idx[kCandCap];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t grow = blockIdx.x;  // g * total_q + row
-  const int64_t row = grow % total_q;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const int64_t grow = (int64_t)blockIdx.y * total_q + row;  // g * total_q + row
   const int b = find_seq(cu_q, num_seqs, row);
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
   const int64_t p = sq.base + (row - sq.q0);
@@ -245,7 +282,7 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
     for (int i = threadIdx.x; i < K; i += 256) dst[i] = -1;
     return;
   }
-  const int J = (int)(p / BS);
+  const int J = (int)(p >> (31 - __builtin_clz(BS)));  // BS is a power of two
   const int need = K - 1;
   if (J <= need) {
     for (int i = threadIdx.x; i < K; i += 256) dst[i] = i <= J ? i : -1;
@@ -257,7 +294,7 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
 #pragma unroll
   for (int c = 0; c < NCW; ++c) {
     const int j = j0 + 64 * c + lane;
-    key[c] = j < J ? ordered_key(src[j]) : 0u;
+    key[c] = ordered_key(src[min(j, J - 1)]) & (j < J ? 0xffffffffu : 0u);
   }
   // Lower bound: the need-th largest of the maxima of the 64 residue classes
   // j mod 64 (lane l of every wave holds class l).  The first J keys fall in
@@ -267,9 +304,9 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
   for (int c = 0; c < NCW; ++c) gm = max(gm, key[c]);
   gmax_sh[wave * 64 + lane] = gm;
   __syncthreads();
-  uint32_t cls[1] = {max(max(gmax_sh[lane], gmax_sh[64 + lane]),
-                         max(gmax_sh[128 + lane], gmax_sh[192 + lane]))};
-  const uint32_t lb = kth_largest<1>(cls, need);
+  const uint32_t cls = max(max(gmax_sh[lane], gmax_sh[64 + lane]),
+                           max(gmax_sh[128 + lane], gmax_sh[192 + lane]));
+  const uint32_t lb = kth_largest_lanes_lb(cls, need);
   int n = 0;
 #pragma unroll
   for (int c = 0; c < NCW; ++c) n += __popcll(ballot64(key[c] >= lb));
@@ -357,8 +394,7 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
 
 template <int NCW>
 hipError_t launch_long(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s) {
-  const int64_t rows = (int64_t)p.G * p.total_q;
-  hipLaunchKernelGGL((topk_long_kernel<NCW>), dim3((unsigned)rows), dim3(256), 0, s, scores,
+  hipLaunchKernelGGL((topk_long_kernel<NCW>), dim3((unsigned)p.total_q, p.G), dim3(256), 0, s, scores,
                      block_idx, p.cu_q, p.cu_kv, p.num_seqs, p.total_q, p.nb_max, p.B, p.top_k);
   profile_mark(s);
   return hipGetLastError();
@@ -366,8 +402,7 @@ hipError_t launch_long(const Dims &p, const float *scores, int32_t *block_idx, h
 
 template <int NCH>
 hipError_t launch_nch(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s) {
-  const int64_t rows = (int64_t)p.G * p.total_q;
-  dim3 grid((unsigned)((rows + 3) / 4));
+  dim3 grid((unsigned)((p.total_q + 3) / 4), p.G);
   hipLaunchKernelGGL((topk_kernel<NCH>), grid, dim3(256), 0, s, scores, block_idx, p.cu_q,
                      p.cu_kv, p.num_seqs, p.G, p.total_q, p.nb_max, p.B, p.top_k);
   profile_mark(s);
