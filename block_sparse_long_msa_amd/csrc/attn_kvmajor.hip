@@ -128,44 +128,63 @@ struct EntryRef {
   int bin;       // LDS bin (block index) if the entry is in the tile's first sequence, else -1
 };
 
-// Geometry shared by the count and scatter kernels.
+// Geometry shared by the count and scatter kernels.  kmagic = ceil(2^32 / K)
+// splits a tile-local entry offset x < 2^16 into (row, slot) exactly:
+// x / K = (x * kmagic) >> 32 (the rounding error of kmagic is below K, and
+// x * K < 2^32).  Block sizes are powers of two: J = p >> lg_bs.
 struct EntGeom {
-  int G, K, BS, nb_max, num_seqs;
+  int G, K, lg_bs, nb_max, num_seqs;
+  uint32_t kmagic_lo, kmagic_hi;  // ceil(2^32 / K) as two words (it is 2^32 for K = 1)
   int64_t total_q;
 };
 
+// Entries of one tile: group-local entry index el = row * K + slot runs over
+// [el0, el0 + kEntTile); thread entry i of the tile is el0 + tid + 256 i.
+struct TileStart {
+  int64_t el0, row0;  // the tile's first entry and its row
+  int off0;           // its slot
+  int b0;             // sequence of row0
+  int64_t bbase;      // first bucket of (b0, g)
+  SeqGeom s0;
+};
+struct EntPos {
+  int64_t row;
+  int slot;
+};
+__device__ __forceinline__ EntPos entry_pos(const TileStart &t, const EntGeom &cg, int local) {
+  const uint32_t x = (uint32_t)(t.off0 + local);  // < K + kEntTile < 2^16
+  const uint64_t magic = ((uint64_t)cg.kmagic_hi << 32) | cg.kmagic_lo;
+  const uint32_t q = (uint32_t)(((uint64_t)x * magic) >> 32);
+  return EntPos{t.row0 + q, (int)(x - q * (uint32_t)cg.K)};
+}
+
 __device__ __forceinline__ EntryRef entry_ref(const int32_t *__restrict__ block_idx, int64_t e,
-                                              int g, const EntGeom &cg, int b0,
-                                              const SeqGeom &s0, const int64_t *cu_q,
+                                              const EntPos &ep, int g, const EntGeom &cg,
+                                              const TileStart &t, const int64_t *cu_q,
                                               const int64_t *cu_kv) {
   EntryRef r{-1, -1};
-  const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
   const int j = block_idx[e];
   if (j < 0) return r;
-  int b = b0;
-  SeqGeom sq = s0;
-  if (row < s0.q0 || row >= s0.q0 + s0.lq) {
-    b = find_seq(cu_q, cg.num_seqs, row);
+  int b = t.b0;
+  SeqGeom sq = t.s0;
+  if (ep.row < t.s0.q0 || ep.row >= t.s0.q0 + t.s0.lq) {
+    b = find_seq(cu_q, cg.num_seqs, ep.row);
     sq = seq_geom(cu_q, cu_kv, b);
   }
-  const int64_t p = sq.base + (row - sq.q0);
-  if (p < 0 || (int64_t)j >= p / cg.BS) return r;
+  const int64_t p = sq.base + (ep.row - sq.q0);
+  if (p < 0 || (int64_t)j >= (p >> cg.lg_bs)) return r;
   r.bkt = ((int64_t)b * cg.G + g) * cg.nb_max + j;
-  r.bin = b == b0 ? j : -1;
+  r.bin = b == t.b0 ? j : -1;
   return r;
 }
 
-// First sequence of a count/scatter tile and its bucket base.
-struct TileStart {
-  int b0;
-  int64_t bbase;
-  SeqGeom s0;
-};
-__device__ __forceinline__ TileStart tile_start(int64_t e0, int g, const EntGeom &cg,
-                                                const int64_t *cu_q, const int64_t *cu_kv) {
+__device__ __forceinline__ TileStart tile_start(int g, const EntGeom &cg, const int64_t *cu_q,
+                                                const int64_t *cu_kv) {
   TileStart t;
-  const int64_t row0 = e0 / cg.K - (int64_t)g * cg.total_q;
-  t.b0 = find_seq(cu_q, cg.num_seqs, row0);
+  t.el0 = (int64_t)blockIdx.x * kEntTile;
+  t.row0 = t.el0 / cg.K;  // once per work-group
+  t.off0 = (int)(t.el0 - t.row0 * cg.K);
+  t.b0 = find_seq(cu_q, cg.num_seqs, t.row0);
   t.s0 = seq_geom(cu_q, cu_kv, t.b0);
   t.bbase = ((int64_t)t.b0 * cg.G + g) * cg.nb_max;
   return t;
@@ -178,14 +197,15 @@ __global__ __launch_bounds__(256) void kv_count_kernel(const int32_t *__restrict
                                                        EntGeom cg) {
   extern __shared__ int32_t hist[];  // nb_max bins
   const int g = blockIdx.y;
-  const int64_t e0 = (int64_t)g * cg.total_q * cg.K + (int64_t)blockIdx.x * kEntTile;
-  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * cg.total_q * cg.K);
-  if (e0 >= e_end) return;
-  const TileStart ts = tile_start(e0, g, cg, cu_q, cu_kv);
+  const int64_t per_g = cg.total_q * cg.K;
+  const TileStart ts = tile_start(g, cg, cu_q, cu_kv);
+  const int n = (int)min<int64_t>(kEntTile, per_g - ts.el0);
+  if (n <= 0) return;
+  const int32_t *bi = block_idx + (int64_t)g * per_g + ts.el0;
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
-  for (int64_t e = e0 + threadIdx.x; e < e_end; e += 256) {
-    const EntryRef r = entry_ref(block_idx, e, g, cg, ts.b0, ts.s0, cu_q, cu_kv);
+  for (int local = threadIdx.x; local < n; local += 256) {
+    const EntryRef r = entry_ref(bi, local, entry_pos(ts, cg, local), g, cg, ts, cu_q, cu_kv);
     if (r.bin >= 0) atomicAdd(&hist[r.bin], 1);
     else if (r.bkt >= 0) atomicAdd(&counts[r.bkt], 1);
   }
@@ -196,6 +216,7 @@ __global__ __launch_bounds__(256) void kv_count_kernel(const int32_t *__restrict
 
 // Entries are laid out item-major: the bucket's entry of rank `pos` goes to
 // item_off[bucket] * qch + pos, so work item t owns entries [t*qch, t*qch + qch).
+// An entry is stored as row << 6 | slot.
 __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restrict__ block_idx,
                                                          int32_t *__restrict__ cursor,
                                                          const int32_t *__restrict__ item_off,
@@ -205,25 +226,26 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
                                                          EntGeom cg, int qch) {
   extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
   const int g = blockIdx.y;
-  const int64_t e0 = (int64_t)g * cg.total_q * cg.K + (int64_t)blockIdx.x * kEntTile;
-  const int64_t e_end = min<int64_t>(e0 + kEntTile, (int64_t)(g + 1) * cg.total_q * cg.K);
-  if (e0 >= e_end) return;
-  const TileStart ts = tile_start(e0, g, cg, cu_q, cu_kv);
+  const int64_t per_g = cg.total_q * cg.K;
+  const TileStart ts = tile_start(g, cg, cu_q, cu_kv);
+  const int n = (int)min<int64_t>(kEntTile, per_g - ts.el0);
+  if (n <= 0) return;
+  const int32_t *bi = block_idx + (int64_t)g * per_g + ts.el0;
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   int rank[kEntPerThread];
 #pragma unroll
   for (int i = 0; i < kEntPerThread; ++i) {
-    const int64_t e = e0 + threadIdx.x + 256 * i;
+    const int local = threadIdx.x + 256 * i;
     rank[i] = -1;
-    if (e < e_end) {
-      const EntryRef r = entry_ref(block_idx, e, g, cg, ts.b0, ts.s0, cu_q, cu_kv);
+    if (local < n) {
+      const EntPos ep = entry_pos(ts, cg, local);
+      const EntryRef r = entry_ref(bi, local, ep, g, cg, ts, cu_q, cu_kv);
       if (r.bin >= 0) {
         rank[i] = atomicAdd(&hist[r.bin], 1);
       } else if (r.bkt >= 0) {
         const int pos = atomicAdd(&cursor[r.bkt], 1);
-        const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
-        entries[(int64_t)item_off[r.bkt] * qch + pos] = (int32_t)((row << 6) | (int)(e % cg.K));
+        entries[(int64_t)item_off[r.bkt] * qch + pos] = (int32_t)((ep.row << 6) | ep.slot);
       }
     }
   }
@@ -236,10 +258,9 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
 #pragma unroll
   for (int i = 0; i < kEntPerThread; ++i) {
     if (rank[i] < 0) continue;
-    const int64_t e = e0 + threadIdx.x + 256 * i;
-    const int j = block_idx[e];
-    const int64_t row = e / cg.K - (int64_t)g * cg.total_q;
-    entries[hist[j] + rank[i]] = (int32_t)((row << 6) | (int)(e % cg.K));
+    const int local = threadIdx.x + 256 * i;
+    const EntPos ep = entry_pos(ts, cg, local);
+    entries[hist[bi[local]] + rank[i]] = (int32_t)((ep.row << 6) | ep.slot);
   }
 }
 
@@ -313,11 +334,12 @@ __global__ __launch_bounds__(256) void kv_scan_add_kernel(int32_t *__restrict__ 
   if (i == 0) item_off[nbk] = scan_blk[nscan];
 }
 
-// Thread per bucket: writes the descriptors of the bucket's work items
-// (g << 16 | block, 0, entry count, packed row of the block's first key), so a
-// work item starts after one 16-byte load and no divisions, and fills the
-// unused entry slots of the bucket's last item with row 0 / slot 0 (a valid
-// row to load; the partial kernel never stores for those lanes).
+// One wave per bucket (four buckets per work-group): the lanes write the
+// descriptors of the bucket's work items (g << 16 | block, 0, entry count,
+// packed row of the block's first key), so a work item starts after one
+// 16-byte load and no divisions, and fill the unused entry slots of the
+// bucket's last item with row 0 / slot 0 (a valid row to load; the partial
+// kernel never stores for those lanes).
 __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict__ counts,
                                                        const int32_t *__restrict__ item_off,
                                                        int32_t *__restrict__ entries,
@@ -325,21 +347,23 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
                                                        const int64_t *__restrict__ cu_kv,
                                                        int64_t nbk, int G, int nb_max, int BS,
                                                        int qch) {
-  const int64_t bkt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t bkt = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (bkt >= nbk) return;
   const int cnt = counts[bkt];
   if (cnt == 0) return;
   const int first = item_off[bkt];
-  const int64_t t = bkt / nb_max;
+  const int64_t t = bkt / nb_max;  // scalar, once per bucket
   const uint32_t j = (uint32_t)(bkt - t * nb_max);
   const int64_t b = t / G;
   const uint32_t g = (uint32_t)(t - b * G);
   const uint32_t kvrow = (uint32_t)(cu_kv[b] + (int64_t)j * BS);
-  for (int i = 0; i * qch < cnt; ++i) {
+  const int nitems = (cnt + qch - 1) / qch;
+  for (int i = lane; i < nitems; i += 64) {
     u32x4 d = {g << 16 | j, 0u, (uint32_t)min(qch, cnt - i * qch), kvrow};
     st16(item_desc + 4 * (int64_t)(first + i), d);
   }
-  for (int pos = cnt; pos % qch != 0; ++pos) entries[(int64_t)first * qch + pos] = 0;
+  for (int i = cnt + lane; i < nitems * qch; i += 64) entries[(int64_t)first * qch + i] = 0;
 }
 
 // LDS tile of one K/V block, both row-major [key][d] without padding.  The
@@ -1004,7 +1028,9 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   hipLaunchKernelGGL(kv_clear_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
                      w.counts, w.cursor, w.nbk);
   profile_mark(s);
-  const EntGeom cg{p.G, p.top_k, p.B, p.nb_max, p.num_seqs, p.total_q};
+  const uint64_t kmagic = ((1ull << 32) + (uint64_t)p.top_k - 1) / (uint64_t)p.top_k;
+  const EntGeom cg{p.G, p.top_k, 31 - __builtin_clz(p.B), p.nb_max, p.num_seqs,
+                   (uint32_t)kmagic, (uint32_t)(kmagic >> 32), p.total_q};
   const int64_t per_g = p.total_q * p.top_k;
   const dim3 tiles((unsigned)((per_g + kEntTile - 1) / kEntTile), p.G);
   const size_t hist_bytes = sizeof(int32_t) * p.nb_max;
@@ -1020,7 +1046,7 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
                      w.item_off, w.entries, p.cu_q, p.cu_kv, cg, qch);
   profile_mark(s);
-  hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 3) / 4)), dim3(256), 0, s,
                      w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.G,
                      p.nb_max, p.B, qch);
   profile_mark(s);
