@@ -860,10 +860,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
     int64_t total_q, float scale_log2) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
-  const int J = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  // blockIdx.x counts the blocks that hold this sequence's queries, from the
+  // block of its first query at a non-negative position
+  const int J = (int)(max<int64_t>(sq.base, 0) / BS) + blockIdx.x;
+  if (J >= nb_max) return;
   // local queries whose position lies in block J
   const int64_t i0 = max<int64_t>(0, (int64_t)J * BS - sq.base);
   const int64_t i1 = min<int64_t>(sq.lq, (int64_t)(J + 1) * BS - sq.base);
@@ -1055,7 +1058,9 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
                      w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, p.num_seqs * p.G,
                      p.nb_max, qch, sl2);
   profile_mark(s);
-  hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(p.nb_max, p.G, p.num_seqs), dim3(kThreads), 0, s,
+  // the blocks holding a sequence's queries: at most ceil(max_q_len / B) + 1
+  const int ndiag = (int)std::min<int64_t>((p.max_q_len + p.B - 1) / p.B + 1, p.nb_max);
+  hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(ndiag, p.G, p.num_seqs), dim3(kThreads), 0, s,
                      q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv, p.num_seqs, p.H,
                      p.G, p.top_k, p.nb_max, p.total_q, sl2);
   profile_mark(s);
