@@ -442,6 +442,9 @@ __device__ __forceinline__ void dma_settle(const KvTile<D, BS> &t) {
 // published by a barrier before this point, while the direct loads in flight
 // target the other tile: written as builtins, these reads would make the
 // compiler wait for those loads, as it cannot tell the two tiles apart.
+// The outputs are early-clobber (=&v): the first read writes its result
+// before the later reads have used `addr`, so no output may share the
+// address register.
 #define MSA_TR(i) "ds_read_b64_tr_b16 %" #i ", %[a] offset:%[o" #i "]\n"
 template <int D, int BS>
 __device__ __forceinline__ void vt_tile_read(u32x4 (&aw)[BS / 16], uint32_t addr) {
@@ -451,9 +454,9 @@ __device__ __forceinline__ void vt_tile_read(u32x4 (&aw)[BS / 16], uint32_t addr
     asm volatile(MSA_TR(0) MSA_TR(1) MSA_TR(2) MSA_TR(3) MSA_TR(4) MSA_TR(5) MSA_TR(6) MSA_TR(7)
                  MSA_TR(8) MSA_TR(9) MSA_TR(10) MSA_TR(11) MSA_TR(12) MSA_TR(13) MSA_TR(14)
                  MSA_TR(15) "s_waitcnt lgkmcnt(0)"
-                 : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]),
-                   "=v"(x[6]), "=v"(x[7]), "=v"(x[8]), "=v"(x[9]), "=v"(x[10]), "=v"(x[11]),
-                   "=v"(x[12]), "=v"(x[13]), "=v"(x[14]), "=v"(x[15])
+                 : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+                   "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+                   "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
                  : [a] "v"(addr), [o0] "n"(0 * R), [o1] "n"(8 * R), [o2] "n"(16 * R),
                    [o3] "n"(24 * R), [o4] "n"(32 * R), [o5] "n"(40 * R), [o6] "n"(48 * R),
                    [o7] "n"(56 * R), [o8] "n"(64 * R), [o9] "n"(72 * R), [o10] "n"(80 * R),
@@ -463,8 +466,8 @@ __device__ __forceinline__ void vt_tile_read(u32x4 (&aw)[BS / 16], uint32_t addr
     static_assert(BS == 64, "block size 64 or 128");
     asm volatile(MSA_TR(0) MSA_TR(1) MSA_TR(2) MSA_TR(3) MSA_TR(4) MSA_TR(5) MSA_TR(6) MSA_TR(7)
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]),
-                   "=v"(x[6]), "=v"(x[7])
+                 : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+                   "=&v"(x[6]), "=&v"(x[7])
                  : [a] "v"(addr), [o0] "n"(0 * R), [o1] "n"(8 * R), [o2] "n"(16 * R),
                    [o3] "n"(24 * R), [o4] "n"(32 * R), [o5] "n"(40 * R), [o6] "n"(48 * R),
                    [o7] "n"(56 * R));
@@ -478,8 +481,8 @@ __device__ __forceinline__ void vt_tile_read(u32x4 (&aw)[BS / 16], uint32_t addr
 // K fragments of MFMA step c for the four 32-key tiles of a 128-key block
 // (rows kt*32 + col, kt = 0..3): the K swizzle depends on col mod 16 only, so
 // the four reads share one LDS byte address `addr` and differ by immediate
-// offsets; one asm block issues them and waits before it ends (same reason
-// as vt_tile_read).
+// offsets; one asm block issues them and waits before it ends (same reason,
+// and the same early-clobber outputs, as vt_tile_read).
 template <int D>
 __device__ __forceinline__ void k_step_read4(u32x4 (&kf)[4], uint32_t addr) {
   constexpr int T = 32 * 2 * D;  // bytes per 32-key tile
@@ -489,7 +492,7 @@ __device__ __forceinline__ void k_step_read4(u32x4 (&kf)[4], uint32_t addr) {
       "ds_read_b128 %2, %[a] offset:%[o2]\n"
       "ds_read_b128 %3, %[a] offset:%[o3]\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(kf[0]), "=v"(kf[1]), "=v"(kf[2]), "=v"(kf[3])
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3])
       : [a] "v"(addr), [o0] "n"(0), [o1] "n"(T), [o2] "n"(2 * T), [o3] "n"(3 * T));
 }
 
