@@ -931,22 +931,53 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
   float *lsh = wsh + K * H;
   float *winv = lsh + K * H;
   const int64_t row = blockIdx.x;
+  constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
+  const uint16_t *base = part_o + row * (int64_t)K * H * D;
+  // The first four slots of this thread's first octet are requested before
+  // the weights are formed, so the partial stream is under way during that
+  // work.  Addresses are clamped into the row (a thread without an octet, or
+  // a row of fewer than four slots, reads data it then ignores).
+  const bool pre_use = (int)threadIdx.x < H * OPH && K >= 4;
+  u32x4 pre[4];
+  {
+    const uint16_t *src = base + (int64_t)min((int)threadIdx.x, H * OPH - 1) * 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pre[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(src + (int64_t)min(u, K - 1) * H * D));
+  }
   const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
   const int64_t J = ri.p < 0 ? -1 : ri.p / BS;
   const int hpg = H / G;
-  for (int t = threadIdx.x; t < K * H; t += 256) {
-    const int sl = t / H, h = t - sl * H;
-    const int32_t *br = block_idx + ((int64_t)(h / hpg) * total_q + row) * K;
-    const int j = br[sl];
-    bool use = j >= 0 && j < J;
-    if (j == J) {  // the last slot listing J is the one the diagonal kernel wrote
-      use = true;
-      for (int s2 = sl + 1; s2 < K; ++s2)
-        if (br[s2] == J) use = false;
+  // (slot, head) pairs in batches of four per thread: the block indices and
+  // the (m, l) of a batch are all requested before any is used; (m, l) of an
+  // unused slot is read too (it may hold anything) and then dropped.
+  for (int t0 = threadIdx.x; t0 < K * H; t0 += 4 * 256) {
+    int j[4], sl[4], h[4];
+    float2 mlr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = min(t0 + 256 * u, K * H - 1);
+      sl[u] = t / H;
+      h[u] = t - sl[u] * H;
+      j[u] = block_idx[((int64_t)(h[u] / hpg) * total_q + row) * K + sl[u]];
+      mlr[u] = part_ml[(row * K + sl[u]) * H + h[u]];
     }
-    const float2 ml = use ? part_ml[(row * K + sl) * H + h] : float2{neg_inf(), 0.f};
-    wsh[t] = ml.y > 0.f ? ml.x : neg_inf();
-    lsh[t] = ml.y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 256 * u;
+      if (t >= K * H) break;
+      bool use = j[u] >= 0 && j[u] < J;
+      if (j[u] == J) {  // the last slot listing J is the one the diagonal kernel wrote
+        const int32_t *br = block_idx + ((int64_t)(h[u] / hpg) * total_q + row) * K;
+        use = true;
+        for (int s2 = sl[u] + 1; s2 < K; ++s2)
+          if (br[s2] == J) use = false;
+      }
+      const float2 ml = use ? mlr[u] : float2{neg_inf(), 0.f};
+      wsh[t] = ml.y > 0.f ? ml.x : neg_inf();
+      lsh[t] = ml.y;
+    }
   }
   __syncthreads();
   for (int h = threadIdx.x; h < H; h += 256) {
@@ -963,13 +994,23 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     if (lse != nullptr) lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : neg_inf();
   }
   __syncthreads();
-  constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
-  const uint16_t *base = part_o + row * (int64_t)K * H * D;
   for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
     const int h = oc / OPH;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const uint16_t *src = base + (int64_t)oc * 8;
     int s = 0;
+    if (pre_use && oc == (int)threadIdx.x) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = wsh[u * H + h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += w > 0.f ? w * bf16_lo(pre[u][i]) : 0.f;
+          acc[2 * i + 1] += w > 0.f ? w * bf16_hi(pre[u][i]) : 0.f;
+        }
+      }
+      s = 4;
+    }
     for (; s + 4 <= K; s += 4) {
       u32x4 x[4];
       float w[4];
