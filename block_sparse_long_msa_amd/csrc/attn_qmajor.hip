@@ -75,18 +75,19 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
     const uint16_t *kblk = k + ((sq.kv0 + s0) * G + g) * (int64_t)D;
     const uint16_t *vblk = v + ((sq.kv0 + s0) * G + g) * (int64_t)D;
 
+    // Keys past the sequence end read its last key instead (their scores are
+    // masked below, and the V rows they stand for get weight 0), so every
+    // load of the block is unconditional and they can all be in flight.
+    const int nkey = (int)min<int64_t>(BS, sq.lkv - s0);
     f32x4 st[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
       st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = kt * 16 + col;
-      const bool kok = s0 + key < sq.lkv;
+      const int key = min(kt * 16 + col, nkey - 1);
       const uint16_t *krow = kblk + key * kvstride + 8 * grp;
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        const bf16x8 a = kok ? as_bf16x8(ld16(krow + 32 * c)) : zero_bf16x8();
-        st[kt] = mfma16x16x32(a, qb[c], st[kt]);
-      }
+      for (int c = 0; c < NDC; ++c)
+        st[kt] = mfma16x16x32(as_bf16x8(ld16(krow + 32 * c)), qb[c], st[kt]);
     }
     float mb = neg_inf();
 #pragma unroll
@@ -126,8 +127,8 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
         u32x4 w[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = ch * 32 + 4 * kq + r;
-          w[r] = s0 + key < sq.lkv ? ld16(vblk + key * kvstride + 8 * o8) : u32x4{0u, 0u, 0u, 0u};
+          const int key = min(ch * 32 + 4 * kq + r, nkey - 1);
+          w[r] = ld16(vblk + key * kvstride + 8 * o8);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
