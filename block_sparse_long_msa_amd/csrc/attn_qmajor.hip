@@ -39,6 +39,8 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
   constexpr int VROW = 36;      // LDS row stride (bf16) of the 32-key V^T chunk
   constexpr int OCT = D / 8;    // 16-byte octets per V row
   constexpr int TASKS = 8 * OCT;  // (key quad, dv octet) transposition tasks per chunk
+  constexpr int TPL = TASKS / 64;  // tasks per lane
+  static_assert(TASKS % 64 == 0, "whole tasks per lane");
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VROW];
 
   const int lane = threadIdx.x;
@@ -66,6 +68,7 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), l = 0.f;
+  u32x4 wv[TPL][4];  // V rows of one 32-key chunk, in flight or being transposed
 
   for (int slot = slot0; slot < slot1; ++slot) {
     const int j = bidx[slot];
@@ -79,6 +82,17 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
     // masked below, and the V rows they stand for get weight 0), so every
     // load of the block is unconditional and they can all be in flight.
     const int nkey = (int)min<int64_t>(BS, sq.lkv - s0);
+    auto load_v = [&](int ch) {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int task = lane + 64 * i, kq = task / OCT, o8 = task - (task / OCT) * OCT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(ch * 32 + 4 * kq + r, nkey - 1);
+          wv[i][r] = ld16(vblk + key * kvstride + 8 * o8);
+        }
+      }
+    };
     f32x4 st[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
@@ -89,6 +103,9 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
       for (int c = 0; c < NDC; ++c)
         st[kt] = mfma16x16x32(as_bf16x8(ld16(krow + 32 * c)), qb[c], st[kt]);
     }
+    // V rows of the block's first 32-key chunk: (key quad, dv octet) tasks,
+    // TPL per lane, loaded while the softmax runs
+    load_v(0);
     float mb = neg_inf();
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
@@ -122,23 +139,20 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
 #pragma unroll
     for (int ch = 0; ch < BS / 32; ++ch) {
       __syncthreads();  // the previous chunk's V^T reads are done
-      for (int task = lane; task < TASKS; task += 64) {
-        const int kq = task / OCT, o8 = task - (task / OCT) * OCT;
-        u32x4 w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = min(ch * 32 + 4 * kq + r, nkey - 1);
-          w[r] = ld16(vblk + key * kvstride + 8 * o8);
-        }
+      for (int i = 0; i < TPL; ++i) {
+        const int task = lane + 64 * i, kq = task / OCT, o8 = task - (task / OCT) * OCT;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int sh = (e & 1) * 16;
-          const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xffffu, k1 = (w[1][e >> 1] >> sh) & 0xffffu;
-          const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xffffu, k3 = (w[3][e >> 1] >> sh) & 0xffffu;
+          const uint32_t k0 = (wv[i][0][e >> 1] >> sh) & 0xffffu, k1 = (wv[i][1][e >> 1] >> sh) & 0xffffu;
+          const uint32_t k2 = (wv[i][2][e >> 1] >> sh) & 0xffffu, k3 = (wv[i][3][e >> 1] >> sh) & 0xffffu;
           u32x2 pk = {k0 | (k1 << 16), k2 | (k3 << 16)};
           *reinterpret_cast<u32x2 *>(vt + (8 * o8 + e) * VROW + 4 * kq) = pk;
         }
       }
+      // the next chunk's V rows load while this chunk's products run
+      if (ch + 1 < BS / 32) load_v(ch + 1);
       __syncthreads();
       const f32x4 &p0 = st[2 * ch], &p1 = st[2 * ch + 1];
       u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
