@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
       const int t = t0 + 256 * u;
       if (t >= K * H) break;
       bool use = j[u] >= 0 && j[u] < J;
-      if (j[u] == J) {  // the last slot listing J is the one the diagonal kernel wrote
+      if (J >= 0 && j[u] == J) {  // the last slot listing J is the one the diagonal kernel wrote
         const int32_t *br = block_idx + ((int64_t)(h[u] / hpg) * total_q + row) * K;
         use = true;
         for (int s2 = sl[u] + 1; s2 < K; ++s2)

@@ -199,3 +199,41 @@ def test_decode_workload_sampled():
     st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
                          w.block_size, w.top_k, w.dtype, rows_per_seq=rows)
     _log(f"  {st}")
+
+
+def test_more_queries_than_keys():
+    """A sequence with len_q > len_kv (the ABI treats its rows at negative
+    positions as having no causal key): those rows get scores -inf, no kept
+    block, output 0 and LSE -inf; every other row equals, bit for bit, the same
+    row of the trimmed problem (the sequence keeps its last len_kv queries),
+    which is checked against the oracle."""
+    H, G, d, di, B, k = 8, 2, 128, 64, 128, 4
+    inp = W.random_case(77, [300, 400], [200, 500], H, G, d, di, B, k, "bf16", device=DEV)
+    cut = 100  # rows 0..99 of sequence 0 sit at positions -100..-1
+    trim = dict(inp)
+    trim["len_q"] = [200, 400]
+    trim["cu_q"] = torch.tensor([0, 200, 600], dtype=torch.int64, device=DEV)
+    for key in ("q_idx", "q"):
+        trim[key] = inp[key][cut:].contiguous()
+    _log("trimmed problem against the oracle")
+    C.run_and_check(trim, H, G, d, di, B, k, "bf16")
+    for sched in ("query_major", "kv_major"):
+        _log(f"more queries than keys, {sched}")
+        res = []
+        for case in (inp, trim):
+            prob = C.problem_for(case, H, G, d, di, B, k, "bf16", sched)
+            scores = msa.index_score(prob, case["q_idx"], case["k_idx"])
+            idx = msa.topk_select(prob, scores)
+            out, lse = msa.sparse_attn_fwd(prob, case["q"], case["k"], case["v"], idx,
+                                           return_lse=True)
+            res.append((scores, idx, out, lse))
+        (s_f, i_f, o_f, l_f), (s_t, i_t, o_t, l_t) = res
+        assert torch.all(s_f[:, :cut, :] == -math.inf)
+        assert torch.all(i_f[:, :cut, :] == -1)
+        assert torch.all(o_f[:cut] == 0)
+        assert torch.all(l_f[:cut] == -math.inf)
+        nb_t = s_t.shape[2]
+        assert torch.equal(s_f[:, cut:, :nb_t], s_t)
+        assert torch.equal(i_f[:, cut:, :], i_t)
+        assert torch.equal(o_f[cut:], o_t)
+        assert torch.equal(l_f[cut:], l_t)
