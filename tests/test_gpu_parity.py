@@ -237,3 +237,38 @@ def test_more_queries_than_keys():
         assert torch.equal(i_f[:, cut:, :], i_t)
         assert torch.equal(o_f[cut:], o_t)
         assert torch.equal(l_f[cut:], l_t)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_arbitrary_kept_lists(dtype):
+    """The attention call on kept-block lists that no selection produced: any
+    number of distinct blocks up to J, the current block present or not, in
+    any slot order, empty rows included (output 0, LSE -inf), against the
+    oracle's attention on the same lists.  Prefill on both schedules, and
+    decode."""
+    H, G, d, di, B, k = 8, 2, 128, 64, 128, 6
+    cases = [("prefill", [700, 1, 300], [900, 513, 300], ("query_major", "kv_major")),
+             ("decode", [1] * 5, [1, 127, 129, 3000, 900], ("auto",))]
+    for name, lq, lkv, scheds in cases:
+        inp = W.random_case(61, lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+        lists = W.random_block_lists(61, lq, lkv, G, B, k)
+        idx = lists.to(DEV)
+        q_h, k_h, v_h = (inp[t].float().cpu() for t in ("q", "k", "v"))
+        refs = []
+        q0 = kv0 = 0
+        for a, b in zip(lq, lkv):
+            pos = O.query_positions(a, b)
+            o, l = O.sparse_attention(q_h[q0:q0 + a], k_h[kv0:kv0 + b], v_h[kv0:kv0 + b],
+                                      lists[:, q0:q0 + a, :].numpy(), pos, B, 1.0 / math.sqrt(d))
+            refs.append((o, l))
+            q0, kv0 = q0 + a, kv0 + b
+        ref_o = np.concatenate([r[0] for r in refs])
+        ref_l = np.concatenate([r[1] for r in refs])
+        for sched in scheds:
+            if sched == "kv_major" and dtype == "f32":
+                continue
+            _log(f"arbitrary lists {name} {sched} {dtype}")
+            prob = C.problem_for(inp, H, G, d, di, B, k, dtype, sched)
+            out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], idx, return_lse=True)
+            err = C.check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, dtype)
+            _log(f"  max |O - O_ref| = {err:.3g}")

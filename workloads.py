@@ -195,3 +195,28 @@ def random_scores(seed: int, G: int, total_q: int, nb: int, levels: int = 0,
         s = torch.randn((G, total_q, nb), generator=g, dtype=torch.float32)
     s[:, ::17, :] = 1.0
     return s.to(device)
+
+
+def random_block_lists(seed: int, len_q: Sequence[int], len_kv: Sequence[int], G: int,
+                       block_size: int, top_k: int) -> torch.Tensor:
+    """Seeded kept-block lists [G, total_q, top_k] int32 that satisfy the
+    attention call's contract without coming from a selection: per (group,
+    row), a random number (0..top_k) of distinct blocks from 0..J (the
+    current block J is included or not at random), in random slot order, the
+    other slots -1.  Rows at negative positions get empty lists."""
+    rng = np.random.default_rng(_seed(seed, "block-lists", top_k))
+    rows = []
+    for lq, lkv in zip(len_q, len_kv):
+        for i in range(lq):
+            p = lkv - lq + i
+            rows.append(-1 if p < 0 else p // block_size)
+    out = np.full((G, len(rows), top_k), -1, dtype=np.int32)
+    for g in range(G):
+        for r, J in enumerate(rows):
+            if J < 0:
+                continue
+            n = int(rng.integers(0, min(top_k, J + 1) + 1))
+            picks = rng.choice(J + 1, size=n, replace=False)
+            slots = rng.choice(top_k, size=n, replace=False)
+            out[g, r, slots] = picks
+    return torch.from_numpy(out)
