@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "query_major", "kv_major"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--layers", type=int, default=1,
+                    help="cross-layer index reuse: one index + Top-k pass, then the attention "
+                         "of this many layers (own q, k, v each) on the same kept-block lists")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -157,6 +160,12 @@ def main():
     scores = torch.empty((prob.G, prob.total_q, prob.nb_max), dtype=torch.float32, device=dev)
     block_idx = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.int32, device=dev)
     out = torch.empty((prob.total_q, prob.H, prob.d), dtype=prob.torch_dtype, device=dev)
+    # further layers reuse the kept-block lists with their own q, k, v
+    layers = [(inp["q"], inp["k"], inp["v"])]
+    for li in range(1, args.layers):
+        lin = W.make_inputs(w, device=dev, seed=1000 + li)
+        layers.append((lin["q"], lin["k"], lin["v"]))
+        del lin
     wbytes = msa.workspace_size(prob)
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -188,6 +197,8 @@ def main():
         else:
             msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
                                 workspace=workspace, stream=sid)
+        for lq_, lk_, lv_ in layers[1:]:
+            msa.sparse_attn_fwd(prob, lq_, lk_, lv_, block_idx, out, workspace=workspace, stream=sid)
         if ev is not None:
             ev[3].record(stream)
 
@@ -227,7 +238,7 @@ def main():
         "index_score": {"ms": st_ms["index_score"], "tflops": f_idx / st_ms["index_score"] / 1e9},
         "topk_select": {"ms": st_ms["topk_select"]},
         "sparse_attn_fwd": {"ms": st_ms["sparse_attn_fwd"],
-                            "tflops": f_attn / st_ms["sparse_attn_fwd"] / 1e9},
+                            "tflops": f_attn * args.layers / st_ms["sparse_attn_fwd"] / 1e9},
     }
     for s in ("index_score", "sparse_attn_fwd"):
         stages[s]["pct_mfma_peak"] = 100.0 * stages[s]["tflops"] / PEAK_BF16_TFLOPS
@@ -263,10 +274,15 @@ def main():
     else:
         value = tokens / (ms_per_step * 1e-3)
         unit = "tokens/s"
-        extra = {"tflops_effective_attention": f_attn / (st_ms["sparse_attn_fwd"] * 1e-3) / 1e12,
-                 "tflops_pipeline": (f_idx + f_attn) / (ms_per_step * 1e-3) / 1e12,
+        extra = {"tflops_effective_attention": f_attn * args.layers / (st_ms["sparse_attn_fwd"] * 1e-3) / 1e12,
+                 "tflops_pipeline": (f_idx + f_attn * args.layers) / (ms_per_step * 1e-3) / 1e12,
                  "flops_index": f_idx, "flops_attention": f_attn}
     extra["kernels_ms"] = kern_ms
+    if args.layers > 1:
+        extra["layers"] = args.layers
+        extra["ms_per_layer"] = ms_per_step / args.layers
+        extra["index_and_topk_share"] = (st_ms["index_score"] + st_ms["topk_select"]) / ms_per_step
+        extra["layer_tokens_per_s"] = tokens * args.layers / (ms_per_step * 1e-3)
     roof["traffic"] = measured_traffic(dom, w.name)
     res.update({"value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -274,7 +290,8 @@ def main():
                 "config": {"workload": w.name, "num_seqs": len(lq), "len_q": max(lq),
                            "len_kv": max(lkv), "total_kv": sum(lkv), "H": w.num_q_heads,
                            "G": w.num_kv_groups, "d": w.head_dim, "d_idx": w.idx_dim,
-                           "block": w.block_size, "top_k": w.top_k, "schedule": args.schedule},
+                           "block": w.block_size, "top_k": w.top_k, "schedule": args.schedule,
+                           **({"layers_per_index": args.layers} if args.layers > 1 else {})},
                 "roofline": roof, "stages": stages, "extra": extra,
                 "wall_s_timed": wall})
 
