@@ -389,7 +389,6 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? 2 * (r & 3) + 8 * ((r >> 2) & 1) : 2 * (r & 3);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -579,7 +578,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
       mraw = fmaxf(mraw, s[kt][r]);
     }
   }
-  mraw = fmaxf(mraw, shfl_xor_f(mraw, 32));
+  mraw = xor32_max_f(mraw);
   const float m = mraw * scale_log2;  // max of the log2-domain logits
   const float msafe = mraw == neg_inf() ? 0.f : m;
   // P in bf16, one 16-key MFMA step at a time: step ks takes registers
@@ -599,7 +598,7 @@ __device__ __forceinline__ void attend_rows(const KvTile<D, BS> &t, const bf16x8
     pk[ks] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                    pack_bf16x2(e[6], e[7])};
   }
-  l += shfl_xor_f(l, 32);
+  l = xor32_sum_f(l);
   // V^T fragments of dv tile dt, read transposed from the row-major V tile:
   // within each 16-lane group, lane l points at key row r0 + l/4 and dv
   // 4(l%4) .. +3 of its group's 16 dv; lane i then receives V[r0 .. r0+3][dv

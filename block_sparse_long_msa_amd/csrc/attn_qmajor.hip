@@ -116,8 +116,7 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
         mb = fmaxf(mb, st[kt][r]);
       }
     }
-    mb = fmaxf(mb, shfl_xor_f(mb, 16));
-    mb = fmaxf(mb, shfl_xor_f(mb, 32));
+    mb = xor32_max_f(xor16_max_f(mb));
     const float m_new = fmaxf(m, mb);  // finite: key s0 <= p is causal
     const float alpha = exp2f(m - m_new);
     float ps = 0.f;
@@ -129,8 +128,7 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
         ps += st[kt][r];
       }
     }
-    ps += shfl_xor_f(ps, 16);
-    ps += shfl_xor_f(ps, 32);
+    ps = xor32_sum_f(xor16_sum_f(ps));
     l = l * alpha + ps;
     m = m_new;
 #pragma unroll

@@ -8,11 +8,11 @@
 //  * index_score_mfma_kernel  - bf16 prefill.  A work-group (8 waves) owns 512
 //    queries x 16 key blocks of one (sequence, group).  The index queries stay in
 //    registers as MFMA B operands for the whole work-group; key blocks stream
-//    through a two-stage LDS ring, fed from registers that are loaded two
-//    blocks ahead (XOR-swizzled 16-byte chunks keep the operand reads free of
+//    through a two-stage LDS ring, filled by direct global-to-LDS loads one
+//    block ahead (XOR-swizzled 16-byte chunks keep the operand reads free of
 //    bank conflicts); each wave computes S^T = K * Q^T tiles (keys x queries)
 //    with 32x32x16 bf16 MFMA so a lane holds 16 keys of ONE query column and
-//    the block max is an in-lane max chain plus one cross-half step.  Causal
+//    the block max is an in-lane max chain plus one cross-half lane swap.  Causal
 //    masking is applied only to blocks that can hold keys past a query's
 //    position, in a separate loop.
 //  * index_score_decode_kernel - bf16, one query per sequence: a streaming
@@ -44,6 +44,13 @@ struct IdxTile {
   __device__ static __forceinline__ int swz(int r, int q) { return r * CPR + (q ^ ((r / RPB) % CPR)); }
 };
 
+// One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds + 16 * l (`lds` is wave-uniform).  Kept out of the kernel body, where
+// the host pass would reject the builtin and drop the kernel's launch stub.
+__device__ __forceinline__ void dma16(const uint16_t *src, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+}
+
 template <int DI, int BS>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI >= 128 ? 2 : 4, DI >= 128 ? 2 : 4))) void index_score_mfma_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
@@ -54,7 +61,8 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
   constexpr int KT = BS / 32;  // 32-key tiles per block
   constexpr int NK = DI / 16;  // MFMA steps over d_idx
   constexpr int RSTR = QT + 1; // result tile row stride (floats)
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[T::STAGE];
   __shared__ float res[KC * RSTR];
 
   const int tid = threadIdx.x;
@@ -109,27 +117,12 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
       }
     }
 
-    // Staging: thread tid moves chunks tid + 512*i of each block; chunk P is
-    // key row P / CPR, 16-byte column P % CPR, stored at its swizzled place.
+    // Register staging (masked blocks only): thread tid moves chunks
+    // tid + 512*i of a block; chunk P is key row P / CPR, 16-byte column
+    // P % CPR, stored at its swizzled place.
     const int64_t kstride = (int64_t)G * DI;
     const uint16_t *kbase = k_idx + ((sq.kv0 + (int64_t)j0 * BS) * G + g) * (int64_t)DI;
     const int64_t rows_left = sq.lkv - (int64_t)j0 * BS;  // key rows of the chunk that exist
-    // Blocks of the pipelined loop lie below every query's position, so all
-    // their rows exist: a per-thread pointer stepped by one block per block.
-    const uint16_t *kthr[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int P = min(tid + kIdxThreads * i, T::CHUNKS - 1);
-      kthr[i] = kbase + (P / CPR) * kstride + 8 * (P % CPR);
-    }
-    const int64_t kblock = (int64_t)BS * kstride;
-    auto fetch_full = [&](int it, u32x4 (&regs)[CPT]) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        if (tid + kIdxThreads * i >= T::CHUNKS) break;
-        regs[i] = ld16(kthr[i] + it * kblock);
-      }
-    };
     auto fetch = [&](int it, u32x4 (&regs)[CPT]) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
@@ -150,6 +143,33 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
       }
     };
 
+    // Direct loads into LDS (global_load_lds_dwordx4) for the unmasked
+    // blocks: a block is NLD wave-loads of 64 16-byte slots, load L filling
+    // slots [64L, 64L + 64) and wave w issuing loads w, w + 8, ...  Lane l of
+    // load L fetches the chunk that the swizzle places in slot 64L + l.  All
+    // rows of these blocks exist, so each lane steps one pointer per load by
+    // a block per block.
+    constexpr int NLD = T::CHUNKS / 64;
+    constexpr int LPW = (NLD + kIdxWaves - 1) / kIdxWaves;  // loads per wave
+    static_assert(T::CHUNKS % 64 == 0, "whole 64-slot loads");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint16_t *kdma[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int S = min(64 * (wave_u + kIdxWaves * i) + lane, T::CHUNKS - 1);
+      const int r = S / CPR;
+      kdma[i] = kbase + r * kstride + 8 * ((S % CPR) ^ ((r / T::RPB) % CPR));
+    }
+    const int64_t kblock = (int64_t)BS * kstride;
+    auto dma = [&](int it, uint8_t *dst) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int L = wave_u + kIdxWaves * i;
+        if (NLD % kIdxWaves != 0 && L >= NLD) break;
+        dma16(kdma[i] + it * kblock, dst + 1024 * L);
+      }
+    };
+
     // MFMAs of one key tile of the staged block `cur` (32 keys x 2 x 32 queries)
     auto mma = [&](const uint8_t *cur, int kt, f32x16 (&a)[2]) {
       const int r = kt * 32 + col;
@@ -163,24 +183,26 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
         a[1] = mfma32x32x16(op, qb[1][c], a[1]);
       }
     };
+    // Lanes l and l + 32 hold different keys of the same query column: after
+    // the cross-half max, lane l stores query wave*64 + l (columns of half 0
+    // from the low lanes, of half 1 from the high lanes).
     auto put = [&](int it, float m0, float m1) {
-      m0 = fmaxf(m0, shfl_xor_f(m0, 32));
-      m1 = fmaxf(m1, shfl_xor_f(m1, 32));
-      if (half == 0) {
-        res[it * RSTR + wave * 64 + col] = m0;
-        res[it * RSTR + wave * 64 + 32 + col] = m1;
-      }
+      res[it * RSTR + wave * 64 + lane] = halves_max_f(m0, m1);
     };
 
     // Blocks below jmask are causal for every query of the tile: a pipelined
-    // loop without masking.  The block being computed sits in LDS stage
-    // `cur`; block it+1 (registers `nxt`) goes to the other stage and block
-    // it+3 is fetched into `nxt`, so two blocks are in flight.
+    // loop without masking.  Block it sits in LDS stage `cur` while block
+    // it+1 streams into `other`.  At the top of each step every wave waits
+    // for its own direct loads (the only vector-memory operations in flight
+    // here), then the barrier publishes the whole block to the work-group;
+    // the work-group fence alone would not wait for loads that write LDS.
+    // The two stages are separate LDS arrays, so the compiler can tell that
+    // operand reads of `cur` need not wait for the loads into `other`.
     const int nfull = min(nblk, max(0, jmask - j0));
-    auto step = [&](int it, const uint8_t *cur, uint8_t *other, u32x4 (&nxt)[CPT]) {
-      __syncthreads();  // block it visible; every wave is done with `other`
-      if (it + 1 < nfull) store(nxt, other);
-      if (it + 3 < nfull) fetch_full(it + 3, nxt);
+    auto step = [&](int it, const uint8_t *cur, uint8_t *other) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // block it in `cur`; every wave is done with `other`
+      if (it + 1 < nfull) dma(it + 1, other);
       // Skewed schedule: the max over query half 0 of key tile kt runs while
       // the MFMAs of half 1 execute, and the max over half 1 while the MFMAs
       // of half 0 of tile kt+1 execute, so the block-max VALU work overlaps
@@ -223,14 +245,10 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
       put(it, m0, m1);
     };
     if (nfull > 0) {
-      u32x4 ra[CPT], rb[CPT];
-      fetch_full(0, ra);
-      store(ra, stage[0]);                   // block 0 -> stage 0
-      if (1 < nfull) fetch_full(1, ra);      // block 1 in ra
-      if (2 < nfull) fetch_full(2, rb);      // block 2 in rb
+      dma(0, stage0);
       for (int it = 0; it < nfull; it += 2) {
-        step(it, stage[0], stage[1], ra);                          // stores it+1, fetches it+3
-        if (it + 1 < nfull) step(it + 1, stage[1], stage[0], rb);  // stores it+2, fetches it+4
+        step(it, stage0, stage1);
+        if (it + 1 < nfull) step(it + 1, stage1, stage0);
       }
     }
 
@@ -239,14 +257,14 @@ __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(DI 
       u32x4 rr[CPT];
       fetch(it, rr);
       __syncthreads();  // every wave is done with stage 0
-      store(rr, stage[0]);
+      store(rr, stage0);
       __syncthreads();
       const int l0 = lim0[0] - it * BS, l1 = lim0[1] - it * BS;
       float m0 = neg_inf(), m1 = neg_inf();
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         f32x16 a[2];
-        mma(stage[0], kt, a);
+        mma(stage0, kt, a);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);

@@ -41,6 +41,9 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return as_bf16x8(z);
 }
 
+// LDS pointer type of the direct global-to-LDS load builtin.
+typedef __attribute__((address_space(3))) void lds_void;
+
 // 16-byte loads (pointer must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
@@ -65,6 +68,39 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 // Cross-lane helpers (wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// max / sum of v over lanes l and l ^ 32, in every lane, with one
+// v_permlane32_swap (a VALU lane swap between the wave's halves) instead of an
+// LDS round trip.  Swapping v with itself leaves v[l] in one result and
+// v[l ^ 32] in the other, whichever way the swap runs, so only the
+// commutative combine of the two is used.
+__device__ __forceinline__ float xor32_max_f(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum_f(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same over lanes l and l ^ 16 with v_permlane16_swap, which exchanges
+// the odd 16-lane rows of one operand with the even rows of the other:
+// swapping v with itself leaves each lane v[l] and v[l ^ 16].
+__device__ __forceinline__ float xor16_max_f(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum_f(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// For two values per lane whose halves hold different parts of one column
+// (lanes l and l + 32 share column l % 32): lane l < 32 gets the max of a over
+// lanes l and l + 32, lane l >= 32 the max of b over lanes l - 32 and l.  One
+// v_permlane32_swap exchanges the upper 32 lanes of a with the lower 32
+// lanes of b; each lane then holds both of its pair's values.
+__device__ __forceinline__ float halves_max_f(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 // DPP lane move within 16-lane rows (CTRL: 0xB1 swaps neighbours, 0x4E swaps

@@ -38,6 +38,19 @@ def test_library_exports_every_declared_symbol():
     assert lib.msa_abi_version() == 1
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """Each kernel's host launch stub is compiled into the library.  If the
+    host pass rejects a kernel body (a gfx950-only builtin written directly
+    in a __global__ function does this without an error), the stub stays an
+    undefined symbol and the library only fails when it is loaded."""
+    nm = subprocess.run(["nm", "-D", "--undefined-only", msa.LIB_PATH],
+                        capture_output=True, text=True)
+    if nm.returncode != 0:
+        pytest.skip("nm not available")
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    assert missing == []
+
+
 def test_problem_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
