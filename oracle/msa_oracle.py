@@ -26,7 +26,13 @@ Readings where the page is silent (each also listed in the design notes):
     -1 when fewer than k blocks are causal;
   * one softmax over the union of the kept keys (not one per block), scaled
     by `scale`; LSE is the natural log-sum-exp of the scaled logits;
-  * query head h belongs to group h // (H / G).
+  * query head h belongs to group h // (H / G);
+  * the indexer's training target (Summary, paragraph 2: a KL objective that
+    matches the group-averaged Main Branch distribution, with the Main Branch
+    detached) is read as: p = the Main Branch's attention mass on each kept
+    block, averaged over the group's heads; q = the softmax of the raw block
+    scores over the same kept blocks; loss KL(p || q) per (group, row); the
+    gradient flows into the scores only.
 
 Everything runs in float64 on exact upcasts of the inputs.  Loops are over
 rows; the inner steps are numpy matrix products and reductions.
@@ -187,3 +193,78 @@ def msa_forward(q, k, v, q_idx, k_idx, len_q: int, len_kv: int, block_size: int,
     idx = select_blocks(S, pos, block_size, top_k)
     out, lse = sparse_attention(q[rows], k, v, idx, pos, block_size, scale)
     return {"scores": S, "block_idx": idx, "out": out, "lse": lse, "pos": pos}
+
+
+def block_mass(q, k, block_idx, pos, block_size: int, scale: float) -> np.ndarray:
+    """Main Branch distribution over the kept blocks, averaged over the heads
+    of each group: the target of the indexer's KL objective (Summary,
+    paragraph 2).
+
+    q: [n, H, d]; k: [len_kv, G, d]; block_idx: [G, n, k]; pos: [n].
+    With a[t,h,s] the attention weight of key s for head h of row t (the
+    softmax of sparse_attention over the union of the kept causal keys),
+      p[g, t, i] = (1/hpg) * sum_{h in g} sum_{s in block block_idx[g,t,i], s <= pos[t]} a[t,h,s].
+    Padding slots (-1) and rows with no causal key get 0.  Returns float64
+    [G, n, k]; each row with a causal key sums to 1.
+    """
+    qf = _f64(q)
+    n, H, _ = qf.shape
+    G, _, K = block_idx.shape
+    hpg = H // G
+    pos = np.asarray(pos, dtype=np.int64)
+    mass = np.zeros((G, n, K))
+    for t in range(n):
+        p = int(pos[t])
+        for g in range(G):
+            slot_keys = []
+            for j in block_idx[g, t]:
+                if j < 0:
+                    slot_keys.append(np.zeros(0, dtype=np.int64))
+                    continue
+                s0 = int(j) * block_size
+                slot_keys.append(np.arange(s0, min(s0 + block_size, p + 1), dtype=np.int64))
+            keys = np.concatenate(slot_keys)
+            if keys.size == 0:
+                continue
+            kg = _gather_f64(k, keys, g)
+            for h in range(g * hpg, (g + 1) * hpg):
+                z = scale * (kg @ qf[t, h])
+                a = np.exp(z - z.max())
+                a /= a.sum()
+                at = 0
+                for i, sk in enumerate(slot_keys):
+                    mass[g, t, i] += a[at:at + sk.size].sum() / hpg
+                    at += sk.size
+    return mass
+
+
+def indexer_kl(S, block_idx, mass):
+    """KL objective of the Index Branch over the kept blocks (Summary,
+    paragraph 2), with the Main Branch detached.
+
+    S: [G, n, NB] block scores; block_idx: [G, n, k]; mass: [G, n, k] (the
+    block_mass target p).  For row (g, t) with kept slots i:
+      q_i  = exp(S[g,t,j_i]) / sum_i' exp(S[g,t,j_i'])    (softmax over the kept blocks)
+      kl   = sum_i p_i (log p_i - log q_i)                 (terms with p_i = 0 are 0)
+      grad_i = d kl / d S[g,t,j_i] = q_i * sum_i' p_i' - p_i   (p held fixed)
+    Padding slots get grad 0; a row without kept blocks gets kl 0.  Returns
+    (kl [G, n], grad [G, n, k]) in float64.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    mass = np.asarray(mass, dtype=np.float64)
+    G, n, K = block_idx.shape
+    kl = np.zeros((G, n))
+    grad = np.zeros((G, n, K))
+    for g in range(G):
+        for t in range(n):
+            slots = [i for i in range(K) if block_idx[g, t, i] >= 0]
+            if not slots:
+                continue
+            s = np.array([S[g, t, block_idx[g, t, i]] for i in slots])
+            p = mass[g, t, slots]
+            logq = s - s.max() - np.log(np.exp(s - s.max()).sum())
+            q = np.exp(logq)
+            pos_p = p > 0
+            kl[g, t] = float((p[pos_p] * (np.log(p[pos_p]) - logq[pos_p])).sum())
+            grad[g, t, slots] = q * p.sum() - p
+    return kl, grad

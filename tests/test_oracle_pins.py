@@ -391,3 +391,148 @@ def test_planted_queries_keep_planted_blocks():
                 assert causal_planted <= set(idx[g, i].tolist())
                 checked += 1
     assert checked > 20
+
+
+# ------------------------------------------- indexer KL target and loss ---
+# Reading of the page's training objective (Summary, paragraph 2): p is the
+# Main Branch's attention mass per kept block averaged over the group's
+# heads; q is the softmax of the raw block scores over the kept blocks; the
+# loss is KL(p || q) with p held fixed.
+
+GOLDEN_KL = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_kl.json")
+
+
+def test_golden_block_mass_and_kl():
+    gd = _golden()
+    a = gd["attention_pow2"]
+    with open(GOLDEN_KL) as f:
+        gk = json.load(f)
+    rows = gk["rows"]
+    pos = O.query_positions(6, 6)[rows]
+    idx = np.array(gk["block_idx"], np.int32)[None]
+    q = np.full((len(rows), 1, 1), math.log(2.0))
+    k = np.array(a["k"], float)[:, None, None]
+    mass = O.block_mass(q, k, idx, pos, gd["block_size"], 1.0)
+    assert np.allclose(mass[0], gk["mass"], rtol=0, atol=1e-15)
+    k_idx = np.array(gd["k_idx"], float)[:, None, :]
+    q_idx = np.array(gd["q_idx"], float)[rows][:, None, :]
+    S = O.block_scores(q_idx, k_idx, pos, gd["block_size"])
+    kl, grad = O.indexer_kl(S, idx, mass)
+    assert np.allclose(kl[0], gk["kl"], rtol=0, atol=1e-14)
+    assert np.allclose(grad[0], gk["grad"], rtol=0, atol=1e-14)
+
+
+def _kl_case(seed, H=4, G=2, L=300, lq=40, B=32, k=3, d=16):
+    rng = np.random.default_rng(seed)
+    q, kk = _rand(rng, lq, H, d), _rand(rng, L, G, d)
+    q_idx, k_idx = _rand(rng, lq, G, 8), _rand(rng, L, G, 8)
+    pos = O.query_positions(lq, L)
+    S = O.block_scores(q_idx, k_idx, pos, B)
+    idx = O.select_blocks(S, pos, B, k)
+    return q, kk, pos, S, idx
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_block_mass_is_one_hot_value_attention(seed):
+    """With V[s] = one-hot of s's block, the attention output of head h is
+    its mass on each block; the group average, read at each kept slot's
+    block, is the block mass (sparse_attention is pinned separately)."""
+    q, kk, pos, S, idx = _kl_case(seed)
+    B, G, H = 32, 2, 4
+    L = kk.shape[0]
+    nb = O.num_blocks(L, B)
+    v = np.zeros((L, G, nb))
+    v[np.arange(L), :, np.arange(L) // B] = 1.0
+    out, _ = O.sparse_attention(q, kk, v, idx, pos, B, 0.25)
+    mass = O.block_mass(q, kk, idx, pos, B, 0.25)
+    hpg = H // G
+    for g in range(G):
+        avg = out[:, g * hpg:(g + 1) * hpg, :].mean(axis=1)          # [n, nb]
+        for t in range(len(pos)):
+            for i, j in enumerate(idx[g, t]):
+                want = 0.0 if j < 0 else avg[t, j]
+                assert abs(mass[g, t, i] - want) < 1e-13
+
+
+def test_block_mass_dense_bruteforce():
+    """k covering every block: the mass is the dense causal softmax of the
+    full score matrix (torch fp64), summed over each block's keys and
+    averaged over the group's heads."""
+    rng = np.random.default_rng(5)
+    L, lq, B, H, G, d = 96, 96, 16, 4, 2, 8
+    q, kk = _rand(rng, lq, H, d), _rand(rng, L, G, d)
+    pos = O.query_positions(lq, L)
+    nb = O.num_blocks(L, B)
+    idx = np.full((G, lq, nb), -1, np.int32)
+    for t, p in enumerate(pos):
+        idx[:, t, :p // B + 1] = np.arange(p // B + 1)
+    mass = O.block_mass(q, kk, idx, pos, B, 0.5)
+    qt, kt = torch.from_numpy(q), torch.from_numpy(kk)
+    for g in range(G):
+        z = 0.5 * torch.einsum("thd,sd->ths", qt[:, 2 * g:2 * g + 2], kt[:, g])
+        z = z.masked_fill(torch.arange(L)[None, None, :] > torch.from_numpy(pos)[:, None, None],
+                          float("-inf"))
+        a = torch.softmax(z, dim=-1).mean(dim=1)                      # [lq, L]
+        per_block = a.reshape(lq, nb, B).sum(dim=-1).numpy()
+        for t in range(lq):
+            for i, j in enumerate(idx[g, t]):
+                want = 0.0 if j < 0 else per_block[t, j]
+                assert abs(mass[g, t, i] - want) < 1e-13
+
+
+def test_block_mass_sums_to_one_and_pads_zero():
+    q, kk, pos, S, idx = _kl_case(3, lq=60, L=200)
+    mass = O.block_mass(q, kk, idx, pos, 32, 0.25)
+    assert np.allclose(mass.sum(axis=2), 1.0, rtol=0, atol=1e-13)
+    assert np.all(mass[idx < 0] == 0.0)
+    assert np.all(mass >= 0.0)
+
+
+def test_kl_matches_scipy_rel_entr():
+    q, kk, pos, S, idx = _kl_case(4)
+    mass = O.block_mass(q, kk, idx, pos, 32, 0.25)
+    kl, _ = O.indexer_kl(S, idx, mass)
+    G, n, _ = idx.shape
+    for g in range(G):
+        for t in range(n):
+            sel = idx[g, t] >= 0
+            qd = scipy.special.softmax(S[g, t, idx[g, t, sel]])
+            want = scipy.special.rel_entr(mass[g, t, sel], qd).sum()
+            assert abs(kl[g, t] - want) < 1e-12
+    assert np.all(kl >= -1e-15)
+
+
+def test_kl_zero_when_scores_are_log_mass():
+    q, kk, pos, S, idx = _kl_case(6)
+    mass = O.block_mass(q, kk, idx, pos, 32, 0.25)
+    S2 = np.full_like(S, -np.inf)
+    G, n, K = idx.shape
+    for g in range(G):
+        for t in range(n):
+            for i in range(K):
+                if idx[g, t, i] >= 0:
+                    S2[g, t, idx[g, t, i]] = math.log(mass[g, t, i]) + 3.0 * g - 0.01 * t
+    kl, grad = O.indexer_kl(S2, idx, mass)
+    assert np.abs(kl).max() < 1e-12
+    assert np.abs(grad).max() < 1e-12
+
+
+def test_kl_gradient_is_finite_difference_of_kl():
+    """Central differences of the loss in each kept block's score."""
+    q, kk, pos, S, idx = _kl_case(7, lq=12)
+    mass = O.block_mass(q, kk, idx, pos, 32, 0.25)
+    _, grad = O.indexer_kl(S, idx, mass)
+    eps = 1e-6
+    G, n, K = idx.shape
+    for g in range(G):
+        for t in range(n):
+            for i in range(K):
+                j = idx[g, t, i]
+                if j < 0:
+                    assert grad[g, t, i] == 0.0
+                    continue
+                Sp, Sm = S.copy(), S.copy()
+                Sp[g, t, j] += eps
+                Sm[g, t, j] -= eps
+                fd = (O.indexer_kl(Sp, idx, mass)[0][g, t] - O.indexer_kl(Sm, idx, mass)[0][g, t]) / (2 * eps)
+                assert abs(fd - grad[g, t, i]) < 1e-8
