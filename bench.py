@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--layers", type=int, default=1,
                     help="cross-layer index reuse: one index + Top-k pass, then the attention "
                          "of this many layers (own q, k, v each) on the same kept-block lists")
+    ap.add_argument("--indexer-kl", action="store_true",
+                    help="training forward: the attention also returns the Main Branch block "
+                         "mass, and the indexer's KL loss and its score gradient follow")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -166,6 +169,11 @@ def main():
         lin = W.make_inputs(w, device=dev, seed=1000 + li)
         layers.append((lin["q"], lin["k"], lin["v"]))
         del lin
+    if args.indexer_kl:
+        lse_buf = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=dev)
+        mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
+        kl = torch.empty((prob.G, prob.total_q), dtype=torch.float32, device=dev)
+        kl_grad = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
     wbytes = msa.workspace_size(prob)
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -181,6 +189,14 @@ def main():
         attn_kernels = ["attn_qmajor"]
     index_kernel = "index_score_decode" if decode else "index_score_mfma"
 
+    def attention():
+        if args.indexer_kl:
+            msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], block_idx, out, lse_buf,
+                                     mass, workspace=workspace, stream=sid)
+        else:
+            msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
+                                workspace=workspace, stream=sid)
+
     def step(ev=None, pev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -192,20 +208,22 @@ def main():
             ev[2].record(stream)
         if pev is not None:
             with pev:
-                msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
-                                    workspace=workspace, stream=sid)
+                attention()
         else:
-            msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
-                                workspace=workspace, stream=sid)
+            attention()
         for lq_, lk_, lv_ in layers[1:]:
             msa.sparse_attn_fwd(prob, lq_, lk_, lv_, block_idx, out, workspace=workspace, stream=sid)
         if ev is not None:
             ev[3].record(stream)
+        if args.indexer_kl:
+            msa.indexer_kl(prob, scores, block_idx, mass, kl, kl_grad, stream=sid)
+            if ev is not None:
+                ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -229,6 +247,8 @@ def main():
             prev = e[2] if i == 0 else pe.events[i - 1]
             vals.append(prev.elapsed_time(pe.events[i]))
         kern_ms[name] = float(np.mean(vals))
+    if args.indexer_kl:
+        kern_ms["indexer_kl"] = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
 
     f_idx, f_attn, nbytes = algorithmic_work(w, lq, lkv)
     f_diag, part_bytes = kvmajor_partial_work(w, lq, lkv, block_idx)
@@ -291,7 +311,8 @@ def main():
                            "len_kv": max(lkv), "total_kv": sum(lkv), "H": w.num_q_heads,
                            "G": w.num_kv_groups, "d": w.head_dim, "d_idx": w.idx_dim,
                            "block": w.block_size, "top_k": w.top_k, "schedule": args.schedule,
-                           **({"layers_per_index": args.layers} if args.layers > 1 else {})},
+                           **({"layers_per_index": args.layers} if args.layers > 1 else {}),
+                           **({"indexer_kl": True} if args.indexer_kl else {})},
                 "roofline": roof, "stages": stages, "extra": extra,
                 "wall_s_timed": wall})
 

@@ -9,6 +9,11 @@ ABI of include/msa.h.  There is no CPU fallback: without the built library
     scores = index_score(prob, q_idx, k_idx)          # msa_index_score
     block_idx = topk_select(prob, scores)             # msa_topk_select
     out, lse = sparse_attn_fwd(prob, q, k, v, block_idx, return_lse=True)
+
+Training support (the indexer's KL objective over the kept blocks):
+
+    out, lse, mass = sparse_attn_fwd_mass(prob, q, k, v, block_idx)   # bf16 prefill
+    kl, grad = indexer_kl(prob, scores, block_idx, mass)    # d kl / d scores
 """
 from __future__ import annotations
 
@@ -29,8 +34,9 @@ STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHA
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
-            "msa_sparse_attn_fwd", "msa_set_profile_events", "msa_status_string",
-            "msa_last_error_message", "msa_abi_version")
+            "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_mass", "msa_indexer_kl",
+            "msa_set_profile_events", "msa_status_string", "msa_last_error_message",
+            "msa_abi_version")
 
 
 class MsaError(RuntimeError):
@@ -82,6 +88,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_workspace_size.restype = st
     lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_sparse_attn_fwd.restype = st
+    lib.msa_sparse_attn_fwd_mass.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msa_sparse_attn_fwd_mass.restype = st
+    lib.msa_indexer_kl.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.msa_indexer_kl.restype = st
     lib.msa_status_string.argtypes = [st]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_last_error_message.argtypes = []
@@ -219,6 +229,60 @@ def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     return out, lse
 
 
+def sparse_attn_fwd_mass(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         block_idx: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream: Optional[int] = None
+                         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """msa_sparse_attn_fwd_mass: (out [total_q, H, d], lse [total_q, H],
+    block_mass [G, total_q, k] fp32)."""
+    dt = prob.torch_dtype
+    _need(q, "q", (prob.total_q, prob.H, prob.d), dt)
+    _need(k, "k", (prob.total_kv, prob.G, prob.d), dt)
+    _need(v, "v", (prob.total_kv, prob.G, prob.d), dt)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    if out is None:
+        out = torch.empty((prob.total_q, prob.H, prob.d), dtype=dt, device=q.device)
+    if lse is None:
+        lse = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=q.device)
+    if mass is None:
+        mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32,
+                           device=q.device)
+    _need(out, "out", (prob.total_q, prob.H, prob.d), dt)
+    _need(lse, "lse", (prob.total_q, prob.H), torch.float32)
+    _need(mass, "block_mass", (prob.G, prob.total_q, prob.top_k), torch.float32)
+    need = workspace_size(prob)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q.device) if stream is None else stream
+    _check(load_library().msa_sparse_attn_fwd_mass(prob.ref(), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(block_idx), _ptr(out), _ptr(lse),
+                                                   _ptr(mass), _ptr(workspace), wbytes, s))
+    return out, lse, mass
+
+
+def indexer_kl(prob: Problem, scores: torch.Tensor, block_idx: torch.Tensor,
+               block_mass: torch.Tensor, kl: Optional[torch.Tensor] = None,
+               grad: Optional[torch.Tensor] = None, stream: Optional[int] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """msa_indexer_kl: (kl [G, total_q], grad [G, total_q, k]) fp32."""
+    _need(scores, "scores", (prob.G, prob.total_q, prob.nb_max), torch.float32)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    _need(block_mass, "block_mass", (prob.G, prob.total_q, prob.top_k), torch.float32)
+    if kl is None:
+        kl = torch.empty((prob.G, prob.total_q), dtype=torch.float32, device=scores.device)
+    if grad is None:
+        grad = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32,
+                           device=scores.device)
+    _need(kl, "kl", (prob.G, prob.total_q), torch.float32)
+    _need(grad, "grad", (prob.G, prob.total_q, prob.top_k), torch.float32)
+    s = _stream(scores.device) if stream is None else stream
+    _check(load_library().msa_indexer_kl(prob.ref(), _ptr(scores), _ptr(block_idx),
+                                         _ptr(block_mass), _ptr(kl), _ptr(grad), s))
+    return kl, grad
+
+
 class ProfileEvents:
     """Per-kernel timing via msa_set_profile_events: `with ProfileEvents(n) as ev:`
     around one library call; afterwards ev.events[i] was recorded right after
@@ -253,3 +317,5 @@ def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):
 msa_index_score = index_score
 msa_topk_select = topk_select
 msa_sparse_attn_fwd = sparse_attn_fwd
+msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass
+msa_indexer_kl = indexer_kl

@@ -140,6 +140,58 @@ size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
   return 0;
 }
 
+msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, const void *v,
+                      const int32_t *block_idx, void *out, float *lse, float *block_mass,
+                      void *workspace, size_t workspace_bytes_given, void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q, "q", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k, "k", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(v, "v", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(MSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const size_t need = workspace_bytes(prob, d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int n_split = 1;
+  const AttnPath path = attn_path(prob, d, &n_split);
+  if (path == AttnPath::kKvMajor)
+    return launched(msa::launch_attn_kvmajor_bf16(d, static_cast<const uint16_t *>(q),
+                                                  static_cast<const uint16_t *>(k),
+                                                  static_cast<const uint16_t *>(v), block_idx,
+                                                  static_cast<uint16_t *>(out), lse, block_mass,
+                                                  workspace, s),
+                    "attn_kvmajor");
+  float *part_o = nullptr, *part_lse = nullptr;
+  if (n_split > 1) {
+    part_o = static_cast<float *>(workspace);
+    part_lse = part_o + (size_t)n_split * d.total_q * d.H * d.d;
+  }
+  hipError_t e;
+  if (prob->dtype == MSA_F32)
+    e = msa::launch_attn_qmajor_f32(d, static_cast<const float *>(q), static_cast<const float *>(k),
+                                    static_cast<const float *>(v), block_idx,
+                                    static_cast<float *>(out), lse, n_split, part_o, part_lse, s);
+  else
+    e = msa::launch_attn_qmajor_bf16(d, static_cast<const uint16_t *>(q),
+                                     static_cast<const uint16_t *>(k),
+                                     static_cast<const uint16_t *>(v), block_idx,
+                                     static_cast<uint16_t *>(out), lse, n_split, part_o, part_lse, s);
+  if (e != hipSuccess || n_split == 1) return launched(e, "attn_query_major");
+  return launched(msa::launch_combine_splits(d, n_split, part_o, part_lse, out,
+                                             prob->dtype == MSA_BF16, lse, s),
+                  "attn_combine_splits");
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,52 +243,47 @@ msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *b
 msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const void *k,
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
                                  void *workspace, size_t workspace_bytes_given, void *stream) {
+  return attn_fwd(prob, q, k, v, block_idx, out, lse, nullptr, workspace, workspace_bytes_given,
+                  stream);
+}
+
+msa_status_t msa_sparse_attn_fwd_mass(const msa_problem_t *prob, const void *q, const void *k,
+                                      const void *v, const int32_t *block_idx, void *out,
+                                      float *lse, float *block_mass, void *workspace,
+                                      size_t workspace_bytes_given, void *stream) {
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);
   if (st != MSA_SUCCESS) return st;
-  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
-  if ((st = check_tensor(q, "q", any_q)) != MSA_SUCCESS) return st;
-  if ((st = check_tensor(k, "k", any_kv)) != MSA_SUCCESS) return st;
-  if ((st = check_tensor(v, "v", any_kv)) != MSA_SUCCESS) return st;
-  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
-  if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
-  if (lse != nullptr && !aligned(lse, 4)) return fail(MSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
-  const size_t need = workspace_bytes(prob, d);
-  if (workspace_bytes_given < need)
-    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
-                workspace_bytes_given);
-  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
-  if (need > 0 && !aligned(workspace, 256))
-    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-  if (!any_q) return ok();
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (prob->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "the block mass is computed by the bf16 KV-major path only");
   int n_split = 1;
-  const AttnPath path = attn_path(prob, d, &n_split);
-  if (path == AttnPath::kKvMajor)
-    return launched(msa::launch_attn_kvmajor_bf16(d, static_cast<const uint16_t *>(q),
-                                                  static_cast<const uint16_t *>(k),
-                                                  static_cast<const uint16_t *>(v), block_idx,
-                                                  static_cast<uint16_t *>(out), lse, workspace, s),
-                    "attn_kvmajor");
-  float *part_o = nullptr, *part_lse = nullptr;
-  if (n_split > 1) {
-    part_o = static_cast<float *>(workspace);
-    part_lse = part_o + (size_t)n_split * d.total_q * d.H * d.d;
-  }
-  hipError_t e;
-  if (prob->dtype == MSA_F32)
-    e = msa::launch_attn_qmajor_f32(d, static_cast<const float *>(q), static_cast<const float *>(k),
-                                    static_cast<const float *>(v), block_idx,
-                                    static_cast<float *>(out), lse, n_split, part_o, part_lse, s);
-  else
-    e = msa::launch_attn_qmajor_bf16(d, static_cast<const uint16_t *>(q),
-                                     static_cast<const uint16_t *>(k),
-                                     static_cast<const uint16_t *>(v), block_idx,
-                                     static_cast<uint16_t *>(out), lse, n_split, part_o, part_lse, s);
-  if (e != hipSuccess || n_split == 1) return launched(e, "attn_query_major");
-  return launched(msa::launch_combine_splits(d, n_split, part_o, part_lse, out,
-                                             prob->dtype == MSA_BF16, lse, s),
-                  "attn_combine_splits");
+  if (d.total_q > 0 && attn_path(prob, d, &n_split) != AttnPath::kKvMajor)
+    return fail(MSA_ERR_BAD_SHAPE,
+                "the block mass needs the KV-major schedule: multi-query rows (max_q_len > 1), "
+                "schedule auto or kv_major, and a problem that schedule holds");
+  if (d.total_q > 0 && block_mass == nullptr) return fail(MSA_ERR_NULL_POINTER, "block_mass is NULL");
+  if (block_mass != nullptr && !aligned(block_mass, 4))
+    return fail(MSA_ERR_MISALIGNED, "block_mass must be 4-byte aligned");
+  return attn_fwd(prob, q, k, v, block_idx, out, lse, block_mass, workspace,
+                  workspace_bytes_given, stream);
+}
+
+msa_status_t msa_indexer_kl(const msa_problem_t *prob, const float *scores, const int32_t *block_idx,
+                            const float *block_mass, float *kl, float *grad, void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any = d.total_q > 0;
+  if ((st = check_tensor(scores, "scores", any && d.nb_max > 0)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_mass, "block_mass", any)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(kl, "kl", any)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(grad, "grad", any)) != MSA_SUCCESS) return st;
+  if (!any) return ok();
+  if (d.nb_max == 0) return fail(MSA_ERR_BAD_SHAPE, "no key blocks: max_kv_len is 0");
+  return launched(msa::launch_indexer_kl(d, scores, block_idx, block_mass, kl, grad,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                  "indexer_kl");
 }
 
 const char *msa_status_string(msa_status_t status) {

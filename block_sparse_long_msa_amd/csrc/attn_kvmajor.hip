@@ -920,10 +920,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 // consecutive output values of one head, with the slot loop unrolled so
 // several 16-byte loads are in flight.  Unused slots are never multiplied
 // (their memory may hold anything): the select below drops them.
+// With block_mass set, the kernel also writes the Main Branch distribution
+// over each group's kept blocks (the target of the indexer's KL objective,
+// "MiniMax Sparse Attention" page, Summary, paragraph 2): head h puts
+// w l / L of its softmax on slot sl, and the group's heads are averaged.
 template <int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(
     const int32_t *__restrict__ block_idx, const uint16_t *__restrict__ part_o,
     const float2 *__restrict__ part_ml, uint16_t *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ block_mass,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
     int G, int K, int BS, int64_t total_q) {
   extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum
@@ -993,6 +998,15 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     if (lse != nullptr) lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : neg_inf();
   }
   __syncthreads();
+  if (block_mass != nullptr) {
+    // unused slots have w = 0 and l = 0; a row without causal keys has 1/L = 0
+    for (int t = threadIdx.x; t < G * K; t += 256) {
+      const int g = t / K, sl = t - g * K;
+      float pm = 0.f;
+      for (int h = g * hpg; h < (g + 1) * hpg; ++h) pm += wsh[sl * H + h] * lsh[sl * H + h] * winv[h];
+      block_mass[((int64_t)g * total_q + row) * K + sl] = pm / (float)hpg;
+    }
+  }
   for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
     const int h = oc / OPH;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1065,8 +1079,8 @@ int persistent_grid(int64_t max_items) {
 
 template <int D, int BS>
 hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                      const int32_t *block_idx, uint16_t *out, float *lse, void *workspace,
-                      hipStream_t s) {
+                      const int32_t *block_idx, uint16_t *out, float *lse, float *block_mass,
+                      void *workspace, hipStream_t s) {
   KvWs w = carve(p, workspace);
   const int hpg = p.H / p.G;
   const int qch = kRowsPerItem / hpg;
@@ -1109,8 +1123,8 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   profile_mark(s);
   const size_t merge_lds = sizeof(float) * (2 * (size_t)p.top_k * p.H + p.H);
   hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), merge_lds, s, block_idx,
-                     w.part_o, w.part_ml, out, lse, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,
-                     p.top_k, p.B, p.total_q);
+                     w.part_o, w.part_ml, out, lse, block_mass, p.cu_q, p.cu_kv, p.num_seqs,
+                     p.H, p.G, p.top_k, p.B, p.total_q);
   profile_mark(s);
   return hipGetLastError();
 }
@@ -1129,10 +1143,12 @@ size_t kvmajor_workspace_bytes(const Dims &p) { return carve(p, nullptr).total_b
 
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
-                                    float *lse, void *workspace, hipStream_t s) {
+                                    float *lse, float *block_mass, void *workspace,
+                                    hipStream_t s) {
   if (p.total_q <= 0) return hipSuccess;
 #define MSA_KV_CASE(D_, BS_) \
-  if (p.d == D_ && p.B == BS_) return launch_all<D_, BS_>(p, q, k, v, block_idx, out, lse, workspace, s);
+  if (p.d == D_ && p.B == BS_)  \
+    return launch_all<D_, BS_>(p, q, k, v, block_idx, out, lse, block_mass, workspace, s);
   MSA_KV_CASE(64, 64) MSA_KV_CASE(64, 128) MSA_KV_CASE(128, 64) MSA_KV_CASE(128, 128)
 #undef MSA_KV_CASE
   return hipErrorInvalidValue;

@@ -54,8 +54,13 @@ hipError_t launch_combine_splits(const Dims &p, int n_split, const float *part_o
 // True if the KV-major schedule's 32-bit entry and item indices hold this problem.
 bool kvmajor_fits(const Dims &p);
 size_t kvmajor_workspace_bytes(const Dims &p);
+// block_mass (may be NULL): [G, total_q, top_k] Main Branch mass per kept slot.
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
-                                    float *lse, void *workspace, hipStream_t s);
+                                    float *lse, float *block_mass, void *workspace, hipStream_t s);
+
+// Indexer KL objective over the kept blocks (indexer_kl.hip).
+hipError_t launch_indexer_kl(const Dims &p, const float *scores, const int32_t *block_idx,
+                             const float *block_mass, float *kl, float *grad, hipStream_t s);
 
 }  // namespace msa

@@ -145,6 +145,48 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Training support: the target and loss of the indexer's KL objective.  The
+ * page (Summary, paragraph 2) trains the Index Branch through a KL
+ * objective matched to the group-averaged Main Branch distribution, with
+ * the Main Branch detached, because Top-k selection has no gradient.  The
+ * two calls below take that objective as: p = the Main Branch's attention
+ * mass on each kept block, averaged over the group's heads; q = the softmax
+ * of the raw block scores over the same kept blocks; loss KL(p || q) per
+ * (group, row); the gradient flows into the scores only. */
+
+/* msa_sparse_attn_fwd plus the Main Branch block mass:
+ *   block_mass[g, r, i] = (1/(H/G)) * sum over heads h of group g of the
+ *                         attention weight head h puts on the causal keys of
+ *                         block block_idx[g, r, i]
+ * (0 for padding slots and for rows without causal keys; each other row
+ * sums to 1).  It comes out of the KV-major combine of the per-block (max,
+ * sum) pairs, so it costs one extra fp32 store per kept slot.  Requirements
+ * beyond msa_sparse_attn_fwd: dtype MSA_BF16 (else
+ * MSA_ERR_UNSUPPORTED_DTYPE); the KV-major schedule, i.e. max_q_len > 1,
+ * schedule AUTO or KV_MAJOR and a problem that schedule holds (else
+ * MSA_ERR_BAD_SHAPE); block_mass [G, total_q, top_k] fp32, 4-byte aligned,
+ * not NULL when total_q > 0.  Same workspace as msa_sparse_attn_fwd. */
+msa_status_t msa_sparse_attn_fwd_mass(const msa_problem_t *prob, const void *q, const void *k,
+                                      const void *v, const int32_t *block_idx, void *out,
+                                      float *lse, float *block_mass, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* KL objective of the Index Branch over the kept blocks, and its gradient
+ * in the block scores with the target held fixed.  For row r of group g,
+ * kept slots i are those with 0 <= block_idx[g, r, i] < NBmax, and
+ * p_i = block_mass[g, r, i]:
+ *   q_i            = exp(s_i) / sum_i' exp(s_i'),  s_i = scores[g, r, block_idx[g, r, i]]
+ *   kl[g, r]       = sum_i p_i (ln p_i - ln q_i)       (terms with p_i = 0 are 0)
+ *   grad[g, r, i]  = q_i * sum_i' p_i' - p_i           (= d kl[g, r] / d s_i)
+ * Padding slots get grad 0; a row without kept blocks gets kl 0.  fp32
+ * throughout (scores from msa_index_score, block_mass from
+ * msa_sparse_attn_fwd_mass, either dtype).  Shapes: scores [G, total_q,
+ * NBmax], block_idx and block_mass and grad [G, total_q, top_k], kl
+ * [G, total_q]. */
+msa_status_t msa_indexer_kl(const msa_problem_t *prob, const float *scores,
+                            const int32_t *block_idx, const float *block_mass, float *kl,
+                            float *grad, void *stream);
+
 /* Kernel timing hook (diagnostics).  After this call, every msa_* call on
  * the calling thread records events[i] (each a hipEvent_t created by the
  * caller) on its stream right after launching its i-th kernel, for i <

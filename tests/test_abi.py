@@ -173,3 +173,52 @@ def test_status_strings():
     for code in range(7):
         assert lib.msa_status_string(code).decode()
     assert lib.msa_status_string(99).decode() == "unknown status"
+
+
+# ------------------------------------------------- indexer KL training calls
+
+def _mass(p, mass=FAKE, q=FAKE, ws=None, wsb=0):
+    lib = msa.load_library()
+    return lib.msa_sparse_attn_fwd_mass(ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, None, mass,
+                                        ws, wsb, None)
+
+
+def _kl(p, sc=FAKE, idx=FAKE, mass=FAKE, kl=FAKE, grad=FAKE):
+    lib = msa.load_library()
+    return lib.msa_indexer_kl(ctypes.byref(p), sc, idx, mass, kl, grad, None)
+
+
+def test_block_mass_call_validation():
+    # bf16 prefill on the KV-major schedule gets past every mass check and
+    # stops at the missing workspace
+    assert _mass(_prob()) == 5
+    assert _mass(_prob(schedule=2)) == 5
+    assert _mass(_prob(dtype=1)) == 3                       # fp32: bf16 path only
+    assert _mass(_prob(schedule=1)) == 2                    # query-major schedule
+    pd = _prob(num_seqs=4, max_q_len=1, total_q=4, max_kv_len=4096, total_kv=16384)
+    assert _mass(pd) == 2                                   # decode rows
+    assert _mass(_prob(), mass=None) == 1
+    assert _mass(_prob(), mass=FAKE + 2) == 4
+    assert _mass(_prob(), q=None) == 1                      # the attention checks still run
+    assert _mass(_prob(num_kv_groups=3)) == 2
+    assert _mass(_prob(max_q_len=0, total_q=0), mass=None, q=None) == 0
+    assert msa.load_library().msa_sparse_attn_fwd_mass(None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                       FAKE, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("which", ["sc", "idx", "mass", "kl", "grad"])
+def test_indexer_kl_pointer_checks(which):
+    p = _prob()
+    args = dict(sc=FAKE, idx=FAKE, mass=FAKE, kl=FAKE, grad=FAKE)
+    args[which] = None
+    assert _kl(p, **args) == 1
+    args[which] = FAKE + 8
+    assert _kl(p, **args) == 4
+
+
+def test_indexer_kl_problem_checks():
+    assert _kl(_prob(top_k=0)) == 2
+    assert _kl(_prob(cu_q=None)) == 1
+    assert _kl(_prob(max_q_len=0, total_q=0), sc=None, idx=None, mass=None, kl=None,
+               grad=None) == 0
+    assert msa.load_library().msa_indexer_kl(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
