@@ -44,18 +44,24 @@ def _check(mass, kl, grad, m_ref, kl_ref, g_ref):
     return em, ek, eg
 
 
-def test_mass_and_kl_on_arbitrary_lists():
+# (H, G, d, d_idx, B, k): k = 6, 20 and 40 take the loss kernel's 16-, 32-
+# and 64-lane row segments; the last case has 16 heads per group and B = 64.
+KL_CASES = [(8, 2, 128, 64, 128, 6), (4, 4, 64, 32, 64, 20), (16, 1, 64, 64, 64, 40)]
+
+
+@pytest.mark.parametrize("case", KL_CASES, ids=[f"k{c[5]}-B{c[4]}-hpg{c[0] // c[1]}" for c in KL_CASES])
+def test_mass_and_kl_on_arbitrary_lists(case):
     """Seeded kept-block lists (any count of distinct blocks up to J, any slot
     order, empty rows and an empty sequence included), every row checked.
     The forward outputs of the mass call equal msa_sparse_attn_fwd's bit for
     bit."""
-    H, G, d, di, B, k = 8, 2, 128, 64, 128, 6
-    lq, lkv = [700, 1, 300, 0], [900, 513, 300, 64]
+    H, G, d, di, B, k = case
+    lq, lkv = [700, 1, 300, 0], [3000, 513, 300, 64]
     inp = W.random_case(91, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
     lists = W.random_block_lists(91, lq, lkv, G, B, k)
     idx = lists.to(DEV)
     prob = C.problem_for(inp, H, G, d, di, B, k, "bf16")
-    _log("arbitrary lists: GPU")
+    _log(f"arbitrary lists {case}: GPU")
     scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
     out_m, lse_m, mass = msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], idx)
     out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], idx, return_lse=True)
