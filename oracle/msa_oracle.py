@@ -268,3 +268,56 @@ def indexer_kl(S, block_idx, mass):
             kl[g, t] = float((p[pos_p] * (np.log(p[pos_p]) - logq[pos_p])).sum())
             grad[g, t, slots] = q * p.sum() - p
     return kl, grad
+
+
+def block_argmax_f32(q_row, k_rows) -> int:
+    """Index of the largest fp32 dot product of q_row with each row of k_rows,
+    ties to the lowest index.  The dot products are summed in fp32 in channel
+    order 0, 1, ..., d-1, one exact product at a time: for bf16 inputs every
+    product is exact in fp32, so this is the value a sequential fp32 FMA chain
+    gives.  The arg-max is an integer decided by floating point; it is taken in
+    that fp32 precision so that both sides decide it the same way."""
+    q = np.asarray(_f64(q_row), dtype=np.float32)
+    kr = np.asarray(_f64(k_rows), dtype=np.float32)
+    acc = np.zeros(kr.shape[0], dtype=np.float32)
+    for c in range(q.shape[0]):
+        acc = (acc + q[c] * kr[:, c]).astype(np.float32)
+    return int(np.argmax(acc))          # first maximum: the lowest index
+
+
+def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
+    """Backward of the Index Branch's max-pooling (Summary, paragraph 2: the
+    scores are max-pooled token-level dot products, so a score's gradient
+    reaches the one causal key that attains the block's maximum).
+
+    q_idx: [n, G, d_idx]; k_idx: [len_kv, G, d_idx]; block_idx, grad: [G, n, k];
+    pos: [n].  For every kept slot (g, t, i) with block j = block_idx[g,t,i] >= 0
+    and causal keys s <= pos[t] of block j, a = the arg-max key
+    (block_argmax_f32), and
+      dq_idx[t, g] += grad[g,t,i] * k_idx[a, g]
+      dk_idx[a, g] += grad[g,t,i] * q_idx[t, g]
+    Slots whose block holds no causal key contribute nothing.  Returns
+    (dq_idx [n, G, d_idx], dk_idx [len_kv, G, d_idx]) in float64.
+    """
+    G, n, K = block_idx.shape
+    L, _, di = k_idx.shape
+    pos = np.asarray(pos, dtype=np.int64)
+    grad = np.asarray(grad, dtype=np.float64)
+    dq = np.zeros((n, G, di))
+    dk = np.zeros((L, G, di))
+    for g in range(G):
+        kg = _f64(k_idx[:, g, :])
+        for t in range(n):
+            qt = _f64(q_idx[t, g, :])
+            for i in range(K):
+                j = int(block_idx[g, t, i])
+                if j < 0:
+                    continue
+                s0 = j * block_size
+                s1 = min(s0 + block_size, int(pos[t]) + 1, L)
+                if s1 <= s0:
+                    continue
+                a = s0 + block_argmax_f32(qt, kg[s0:s1])
+                dq[t, g] += grad[g, t, i] * kg[a]
+                dk[a, g] += grad[g, t, i] * qt
+    return dq, dk

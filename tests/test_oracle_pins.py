@@ -536,3 +536,108 @@ def test_kl_gradient_is_finite_difference_of_kl():
                 Sm[g, t, j] -= eps
                 fd = (O.indexer_kl(Sp, idx, mass)[0][g, t] - O.indexer_kl(Sm, idx, mass)[0][g, t]) / (2 * eps)
                 assert abs(fd - grad[g, t, i]) < 1e-8
+
+
+# --------------------------------------- Index Branch max-pooling backward ---
+
+GOLDEN_IBWD = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_index_bwd.json")
+
+
+def test_golden_index_backward():
+    gd = _golden()
+    with open(GOLDEN_IBWD) as f:
+        gb = json.load(f)
+    rows = gb["rows"]
+    k_idx = np.array(gd["k_idx"], float)[:, None, :]
+    q_idx = np.array(gd["q_idx"], float)[rows][:, None, :]
+    pos = O.query_positions(6, 6)[rows]
+    idx = np.array(gb["block_idx"], np.int32)[None]
+    for r, row in enumerate(gb["argmax"]):
+        for i, a in enumerate(row):
+            s0 = idx[0, r, i] * gd["block_size"]
+            s1 = min(s0 + gd["block_size"], pos[r] + 1)
+            assert s0 + O.block_argmax_f32(q_idx[r, 0], k_idx[s0:s1, 0]) == a
+    dq, dk = O.index_backward(q_idx, k_idx, idx, pos, gd["block_size"],
+                              np.array(gb["grad"], float)[None])
+    assert np.array_equal(dq[:, 0], np.array(gb["dq"], float))
+    assert np.array_equal(dk[:, 0], np.array(gb["dk"], float))
+
+
+def _ibwd_case(seed, L=200, lq=30, G=2, di=8, B=16, k=4):
+    rng = np.random.default_rng(seed)
+    q_idx, k_idx = _rand(rng, lq, G, di), _rand(rng, L, G, di)
+    pos = O.query_positions(lq, L)
+    S = O.block_scores(q_idx, k_idx, pos, B)
+    idx = O.select_blocks(S, pos, B, k)
+    grad = _rand(rng, G, lq, k)
+    grad[idx < 0] = 0.0
+    return q_idx, k_idx, pos, idx, grad
+
+
+def test_index_backward_matches_torch_autograd():
+    """The same loss, sum of grad * S over the kept slots, written with torch
+    (fp64 masked dot products, max over each block's keys) and
+    differentiated by autograd."""
+    B = 16
+    q_idx, k_idx, pos, idx, grad = _ibwd_case(11)
+    dq, dk = O.index_backward(q_idx, k_idx, idx, pos, B, grad)
+    qt = torch.tensor(q_idx, requires_grad=True)
+    kt = torch.tensor(k_idx, requires_grad=True)
+    L, G = k_idx.shape[0], k_idx.shape[1]
+    loss = torch.zeros((), dtype=torch.float64)
+    for g in range(G):
+        dots = qt[:, g, :] @ kt[:, g, :].T                                   # [n, L]
+        dots = dots.masked_fill(torch.arange(L)[None, :] > torch.from_numpy(pos)[:, None],
+                                float("-inf"))
+        for t in range(len(pos)):
+            for i in range(idx.shape[2]):
+                j = idx[g, t, i]
+                if j >= 0:
+                    loss = loss + grad[g, t, i] * dots[t, j * B:(j + 1) * B].max()
+    loss.backward()
+    assert np.allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_index_backward_is_finite_difference_of_scores():
+    """Central differences of sum(grad * S) through block_scores, for a few
+    coordinates of q_idx and k_idx (the max is locally linear)."""
+    B = 16
+    q_idx, k_idx, pos, idx, grad = _ibwd_case(12, L=96, lq=20)
+    dq, dk = O.index_backward(q_idx, k_idx, idx, pos, B, grad)
+
+    def loss(qi, ki):
+        S = O.block_scores(qi, ki, pos, B)
+        tot = 0.0
+        G, n, K = idx.shape
+        for g in range(G):
+            for t in range(n):
+                for i in range(K):
+                    if idx[g, t, i] >= 0:
+                        tot += grad[g, t, i] * S[g, t, idx[g, t, i]]
+        return tot
+
+    eps = 1e-6
+    rng = np.random.default_rng(3)
+    for _ in range(12):
+        t, g, c = rng.integers(20), rng.integers(2), rng.integers(8)
+        qp, qm = q_idx.copy(), q_idx.copy()
+        qp[t, g, c] += eps
+        qm[t, g, c] -= eps
+        assert abs((loss(qp, k_idx) - loss(qm, k_idx)) / (2 * eps) - dq[t, g, c]) < 1e-7
+        s = rng.integers(96)
+        kp, km = k_idx.copy(), k_idx.copy()
+        kp[s, g, c] += eps
+        km[s, g, c] -= eps
+        assert abs((loss(q_idx, kp) - loss(q_idx, km)) / (2 * eps) - dk[s, g, c]) < 1e-7
+
+
+def test_block_argmax_f32_exact_on_small_integers():
+    """Small-integer inputs make every fp32 partial sum exact, so the arg-max
+    is the exact one, ties to the lowest key."""
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        q = rng.integers(-3, 4, 8).astype(float)
+        kr = rng.integers(-3, 4, (16, 8)).astype(float)
+        exact = kr @ q
+        assert O.block_argmax_f32(q, kr) == int(np.flatnonzero(exact == exact.max())[0])
