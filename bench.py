@@ -15,6 +15,7 @@ workload (after the GPU timing).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -133,8 +134,9 @@ def main():
                     help="cross-layer index reuse: one index + Top-k pass, then the attention "
                          "of this many layers (own q, k, v each) on the same kept-block lists")
     ap.add_argument("--indexer-kl", action="store_true",
-                    help="training forward: the attention also returns the Main Branch block "
-                         "mass, and the indexer's KL loss and its score gradient follow")
+                    help="training step of the indexer: the attention also returns the Main "
+                         "Branch block mass, then the indexer's KL loss, its score gradient and "
+                         "the max-pooling backward to q_idx and k_idx follow")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -174,6 +176,9 @@ def main():
         mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
         kl = torch.empty((prob.G, prob.total_q), dtype=torch.float32, device=dev)
         kl_grad = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
+        nbw = ctypes.c_size_t(0)
+        msa._check(msa.load_library().msa_indexer_bwd_workspace_size(prob.ref(), ctypes.byref(nbw)))
+        bwd_ws = torch.empty(max(nbw.value, 1), dtype=torch.uint8, device=dev)
     wbytes = msa.workspace_size(prob)
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -219,11 +224,15 @@ def main():
             msa.indexer_kl(prob, scores, block_idx, mass, kl, kl_grad, stream=sid)
             if ev is not None:
                 ev[4].record(stream)
+            msa.indexer_bwd(prob, inp["q_idx"], inp["k_idx"], block_idx, kl_grad,
+                            workspace=bwd_ws, stream=sid)
+            if ev is not None:
+                ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -249,6 +258,7 @@ def main():
         kern_ms[name] = float(np.mean(vals))
     if args.indexer_kl:
         kern_ms["indexer_kl"] = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+        kern_ms["indexer_bwd"] = float(np.mean([e[4].elapsed_time(e[5]) for e in events]))
 
     f_idx, f_attn, nbytes = algorithmic_work(w, lq, lkv)
     f_diag, part_bytes = kvmajor_partial_work(w, lq, lkv, block_idx)

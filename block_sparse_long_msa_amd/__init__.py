@@ -14,6 +14,7 @@ Training support (the indexer's KL objective over the kept blocks):
 
     out, lse, mass = sparse_attn_fwd_mass(prob, q, k, v, block_idx)   # bf16 prefill
     kl, grad = indexer_kl(prob, scores, block_idx, mass)    # d kl / d scores
+    dq_idx, dk_idx = indexer_bwd(prob, q_idx, k_idx, block_idx, grad)
 """
 from __future__ import annotations
 
@@ -35,6 +36,7 @@ DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_mass", "msa_indexer_kl",
+            "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
             "msa_set_profile_events", "msa_status_string", "msa_last_error_message",
             "msa_abi_version")
 
@@ -92,6 +94,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_fwd_mass.restype = st
     lib.msa_indexer_kl.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.msa_indexer_kl.restype = st
+    lib.msa_indexer_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_indexer_bwd_workspace_size.restype = st
+    lib.msa_indexer_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msa_indexer_bwd.restype = st
     lib.msa_status_string.argtypes = [st]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_last_error_message.argtypes = []
@@ -283,6 +289,31 @@ def indexer_kl(prob: Problem, scores: torch.Tensor, block_idx: torch.Tensor,
     return kl, grad
 
 
+def indexer_bwd(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                block_idx: torch.Tensor, grad: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None, stream: Optional[int] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """msa_indexer_bwd: (dq_idx [total_q, G, d_idx], dk_idx [total_kv, G, d_idx]) fp32,
+    the max-pooling backward of the kept slots' score gradients `grad`."""
+    dt = prob.torch_dtype
+    _need(q_idx, "q_idx", (prob.total_q, prob.G, prob.d_idx), dt)
+    _need(k_idx, "k_idx", (prob.total_kv, prob.G, prob.d_idx), dt)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    _need(grad, "grad", (prob.G, prob.total_q, prob.top_k), torch.float32)
+    dq = torch.empty((prob.total_q, prob.G, prob.d_idx), dtype=torch.float32, device=q_idx.device)
+    dk = torch.empty((prob.total_kv, prob.G, prob.d_idx), dtype=torch.float32, device=q_idx.device)
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_indexer_bwd_workspace_size(prob.ref(), ctypes.byref(n)))
+    if workspace is None and n.value > 0:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q_idx.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q_idx.device) if stream is None else stream
+    _check(load_library().msa_indexer_bwd(prob.ref(), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                                          _ptr(grad), _ptr(dq), _ptr(dk), _ptr(workspace), wbytes,
+                                          s))
+    return dq, dk
+
+
 class ProfileEvents:
     """Per-kernel timing via msa_set_profile_events: `with ProfileEvents(n) as ev:`
     around one library call; afterwards ev.events[i] was recorded right after
@@ -319,3 +350,4 @@ msa_topk_select = topk_select
 msa_sparse_attn_fwd = sparse_attn_fwd
 msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass
 msa_indexer_kl = indexer_kl
+msa_indexer_bwd = indexer_bwd

@@ -286,6 +286,50 @@ msa_status_t msa_indexer_kl(const msa_problem_t *prob, const float *scores, cons
                   "indexer_kl");
 }
 
+msa_status_t msa_indexer_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = msa::index_bwd_workspace_bytes(d);
+  return ok();
+}
+
+msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                             const int32_t *block_idx, const float *grad, float *dq_idx,
+                             float *dk_idx, void *workspace, size_t workspace_bytes_given,
+                             void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q_idx, "q_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k_idx, "k_idx", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(grad, "grad", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dq_idx, "dq_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dk_idx, "dk_idx", any_kv)) != MSA_SUCCESS) return st;
+  if (d.total_q * (int64_t)d.top_k >= (int64_t)INT32_MAX)
+    return fail(MSA_ERR_BAD_SHAPE, "total_q * top_k must be below 2^31");
+  if (msa::index_bwd_hist_bytes(d) > 64 * 1024)
+    return fail(MSA_ERR_BAD_SHAPE,
+                "num_seqs * ceil(max_kv_len / block_size) must be at most 16384 for the "
+                "index backward (one LDS histogram bin per (sequence, block))");
+  const size_t need = msa::index_bwd_workspace_bytes(d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q && !any_kv) return ok();
+  // with no query row every key's gradient is 0: the launch only zero-fills dk_idx
+  return launched(msa::launch_index_bwd(d, prob->dtype == MSA_BF16, q_idx, k_idx, block_idx, grad,
+                                        dq_idx, dk_idx, workspace,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                  "index_bwd");
+}
+
 const char *msa_status_string(msa_status_t status) {
   switch (status) {
     case MSA_SUCCESS: return "success";

@@ -1,0 +1,440 @@
+// Backward of the Index Branch max-pooling ("MiniMax Sparse Attention" page,
+// Summary, paragraph 2: a block's score is the maximum of token-level
+// index-query / index-key dot products, so the gradient of a kept block's
+// score reaches only the causal key that attains that maximum).  Given the
+// gradient c[g, r, i] of every kept slot's score (for instance the indexer KL
+// gradient), with a = the arg-max key of block block_idx[g, r, i] for row r:
+//   dq_idx[r, g] = sum over slots i (in slot order) of c[g,r,i] * k_idx[a, g]
+//   dk_idx[s, g] = sum over (r, i) with a = s (in (r, i) order) of c[g,r,i] * q_idx[r, g]
+// The arg-max is an integer decided by floating point: each key's dot
+// product is summed in fp32 in channel order, every product rounded to fp32
+// before it is added (no fused multiply-add), and ties go to the lower key.
+//
+// Deterministic, without floating-point atomics:
+//   ib_zero      dk_idx <- 0 (keys no slot takes keep 0)
+//   ib_count     per tile of TE consecutive (row, slot) entries of a group:
+//                entries per bucket (sequence, block) in an LDS histogram
+//                (integer atomics, counting only); invalid slots get arg-max -1
+//   ib_colscan   per bucket: exclusive offsets of the tiles, and its total
+//   ib_basescan  exclusive scan of the bucket totals
+//   ib_scatter   per tile, one wave walks its entries in order and writes each
+//                to its bucket's list at tile offset + running count + rank
+//                among equal buckets: every list ends up in (row, slot) order
+//   ib_bucket    per bucket: the block's index keys in LDS; for each entry in
+//                list order the arg-max over the causal keys, then each key
+//                row sums c * q_idx over the entries that chose it, in list
+//                order; the arg-max is stored for ib_dq
+//   ib_dq        per (group, row): dq_idx from the stored arg-max keys
+#include <algorithm>
+
+#include "launch.hpp"
+#include "msa_common.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kTE = 4096;  // entries per counting / scatter tile
+
+struct IbWs {
+  int32_t *cnt;    // [G][ntiles][nbk_g]: tile counts, then exclusive tile offsets
+  int32_t *base;   // [G * nbk_g + 1]: bucket totals, then exclusive starts
+  int32_t *lists;  // [G * total_q * K] entries e = row * K + slot, grouped by bucket
+  int32_t *amax;   // [G][total_q][K] arg-max key (packed key row) or -1
+  int64_t ntiles, nbk_g, nent_g;
+  size_t total_bytes;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+IbWs ib_carve(const Dims &p, void *base) {
+  IbWs w;
+  w.nent_g = p.total_q * (int64_t)p.top_k;
+  w.ntiles = (w.nent_g + kTE - 1) / kTE;
+  w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
+  size_t off = 0;
+  char *c = static_cast<char *>(base);
+  auto take = [&](size_t bytes) {
+    char *r = c == nullptr ? nullptr : c + off;
+    off += al256(bytes);
+    return reinterpret_cast<int32_t *>(r);
+  };
+  w.cnt = take(sizeof(int32_t) * (size_t)p.G * w.ntiles * w.nbk_g);
+  w.base = take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1));
+  w.lists = take(sizeof(int32_t) * (size_t)p.G * w.nent_g);
+  w.amax = take(sizeof(int32_t) * (size_t)p.G * w.nent_g);
+  w.total_bytes = off;
+  return w;
+}
+
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+// One step of an arg-max dot product: acc + q * k with the product rounded
+// to fp32 before the add.  For bf16 inputs the product is exact in fp32, so
+// a fused multiply-add gives the same value; fp32 inputs need the two
+// roundings, so contraction is switched off there.
+__device__ __forceinline__ float dot_step(float acc, float q, float k, uint16_t) {
+  return fmaf(q, k, acc);
+}
+__device__ __forceinline__ float dot_step(float acc, float q, float k, float) {
+#pragma clang fp contract(off)
+  return acc + q * k;
+}
+
+// Bucket of entry e (= row * K + slot) of group g, or -1 when the slot is
+// padding or its block holds no causal key of the row.  The bucket numbers
+// blocks of every sequence: b * nb_max + j.  Also returns the row, the
+// sequence's first key row and the row's position.
+struct EntryInfo {
+  int bucket;
+  int64_t row, kv0, pos;
+};
+__device__ __forceinline__ EntryInfo entry_info(const int32_t *__restrict__ block_idx,
+                                                const int64_t *__restrict__ cu_q,
+                                                const int64_t *__restrict__ cu_kv, int num_seqs,
+                                                int g, int64_t e, int K, int64_t total_q,
+                                                int nb_max, int BS) {
+  EntryInfo r;
+  r.row = e / K;
+  const int j = block_idx[(int64_t)g * total_q * K + e];
+  const int b = find_seq(cu_q, num_seqs, r.row);
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  r.kv0 = sq.kv0;
+  r.pos = sq.base + (r.row - sq.q0);
+  const bool ok = j >= 0 && j < nb_max && r.pos >= 0 && (int64_t)j * BS <= r.pos;
+  r.bucket = ok ? b * nb_max + j : -1;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    x[i] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void ib_count_kernel(
+    const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
+    const int64_t *__restrict__ cu_kv, int32_t *__restrict__ cnt, int32_t *__restrict__ amax,
+    int num_seqs, int K, int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
+  extern __shared__ int32_t hist[];  // [nbk_g]
+  const int g = blockIdx.y;
+  const int64_t tile = blockIdx.x;
+  for (int64_t x = threadIdx.x; x < nbk_g; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int64_t nent = total_q * K;
+  const int64_t e1 = min(nent, (tile + 1) * kTE);
+  for (int64_t e = tile * kTE + threadIdx.x; e < e1; e += 256) {
+    const EntryInfo ei = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS);
+    if (ei.bucket >= 0) atomicAdd(&hist[ei.bucket], 1);
+    else amax[(int64_t)g * nent + e] = -1;
+  }
+  __syncthreads();
+  int32_t *dst = cnt + ((int64_t)g * ntiles + tile) * nbk_g;
+  for (int64_t x = threadIdx.x; x < nbk_g; x += 256) dst[x] = hist[x];
+}
+
+// One thread per (group, bucket): tile counts -> exclusive tile offsets.
+__global__ __launch_bounds__(256) void ib_colscan_kernel(int32_t *__restrict__ cnt,
+                                                         int32_t *__restrict__ total, int G,
+                                                         int64_t ntiles, int64_t nbk_g) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (int64_t)G * nbk_g) return;
+  const int64_t g = x / nbk_g, bk = x - g * nbk_g;
+  int32_t run = 0;
+  for (int64_t t = 0; t < ntiles; ++t) {
+    int32_t *c = cnt + (g * ntiles + t) * nbk_g + bk;
+    const int32_t v = *c;
+    *c = run;
+    run += v;
+  }
+  total[x] = run;
+}
+
+// One work-group: exclusive scan of n bucket totals in place, base[n] = sum.
+__global__ __launch_bounds__(1024) void ib_basescan_kernel(int32_t *__restrict__ base, int64_t n) {
+  __shared__ int32_t part[1024];
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = min(n, (int64_t)threadIdx.x * per), b = min(n, a + per);
+  int32_t s = 0;
+  for (int64_t i = a; i < b; ++i) s += base[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int32_t v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    base[n] = run;
+  }
+  __syncthreads();
+  int32_t run = part[threadIdx.x];
+  for (int64_t i = a; i < b; ++i) {
+    const int32_t v = base[i];
+    base[i] = run;
+    run += v;
+  }
+}
+
+// One wave per (tile, group).  Chunks of 64 entries are placed in order: all
+// lanes holding the same bucket are placed in one step, ranked by lane, after
+// the tile's earlier entries of that bucket (a running count in LDS).
+__global__ __launch_bounds__(64) void ib_scatter_kernel(
+    const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
+    const int64_t *__restrict__ cu_kv, const int32_t *__restrict__ cnt,
+    const int32_t *__restrict__ base, int32_t *__restrict__ lists, int num_seqs, int K,
+    int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
+  extern __shared__ int32_t run[];  // [nbk_g] next list position of each bucket
+  const int g = blockIdx.y;
+  const int64_t tile = blockIdx.x;
+  const int lane = threadIdx.x;
+  // bucket start (global over groups) + this tile's offset in the bucket
+  const int32_t *toff = cnt + ((int64_t)g * ntiles + tile) * nbk_g;
+  const int32_t *gbase = base + (int64_t)g * nbk_g;
+  for (int64_t x = lane; x < nbk_g; x += 64) run[x] = gbase[x] + toff[x];
+  __syncthreads();
+  const int64_t nent = total_q * K;
+  const int64_t e1 = min(nent, (tile + 1) * kTE);
+  for (int64_t c0 = tile * kTE; c0 < e1; c0 += 64) {
+    const int64_t e = c0 + lane;
+    int bk = -1;
+    if (e < e1) bk = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS).bucket;
+    bool active = bk >= 0;
+    uint64_t act = ballot64(active);
+    while (act != 0) {
+      const int leader = (int)__builtin_ctzll(act);
+      const int bl = __builtin_amdgcn_readlane(bk, leader);
+      const uint64_t m = ballot64(active && bk == bl);
+      const int32_t start = __builtin_amdgcn_readfirstlane(run[bl]);
+      if (active && bk == bl) {
+        lists[start + mbcnt64(m)] = (int32_t)e;
+        active = false;
+      }
+      if (lane == 0) run[bl] = start + __popcll(m);
+      act = ballot64(active);
+    }
+  }
+}
+
+// One work-group per (group, bucket).  Threads 4x + part handle entry x of a
+// 64-entry chunk for the arg-max (keys part, part+4, ...); for the key-side
+// sum, thread 4s + part... owns key row s and a quarter-or-more of the
+// channels (TPR threads per row).
+template <typename T, int DI, int BS>
+__global__ __launch_bounds__(256) void ib_bucket_kernel(
+    const T *__restrict__ q_idx, const T *__restrict__ k_idx, const float *__restrict__ grad,
+    const int32_t *__restrict__ base, const int32_t *__restrict__ lists,
+    int32_t *__restrict__ amax, float *__restrict__ dk_idx, const int64_t *__restrict__ cu_q,
+    const int64_t *__restrict__ cu_kv, int num_seqs, int G, int K, int64_t total_q, int nb_max) {
+  constexpr int TPR = 256 / BS;          // threads per key row (2 or 4)
+  constexpr int CPT = DI / TPR;          // channels per thread in the key-side sum
+  constexpr int KS = DI + 1;             // padded LDS row of the staged keys
+  __shared__ float ks[BS * KS];          // the block's index keys, fp32
+  __shared__ float qs[64 * KS];          // index queries of the chunk's entries
+  __shared__ float cs[64];               // their score gradients
+  __shared__ int32_t as_[64];            // their arg-max (block-local key, -1 none)
+  __shared__ float bv[256];              // arg-max candidates of the 4 threads of an entry
+  __shared__ int32_t bs[256];
+  const int g = blockIdx.y;
+  const int64_t bkt = blockIdx.x;        // b * nb_max + j
+  const int64_t gb = (int64_t)g * num_seqs * nb_max + bkt;
+  const int32_t first = base[gb], n = base[gb + 1] - first;
+  if (n == 0) return;
+  const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
+  const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
+  const int64_t q0 = cu_q[b], base_pos = lkv - (cu_q[b + 1] - q0);
+  const int64_t s0 = (int64_t)j * BS;
+  const int nkeys = (int)min<int64_t>(BS, lkv - s0);
+  const int tid = threadIdx.x;
+  for (int x = tid; x < BS * DI; x += 256) {
+    const int s = x / DI, c = x - s * DI;
+    ks[s * KS + c] = s < nkeys ? to_f32(k_idx[((kv0 + s0 + s) * G + g) * (int64_t)DI + c]) : 0.f;
+  }
+  const int srow = tid / TPR, c_lo = (tid % TPR) * CPT;
+  float acc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+  const int64_t nent = total_q * K;
+  for (int32_t c0 = 0; c0 < n; c0 += 64) {
+    const int cn = min(64, n - c0);
+    __syncthreads();  // keys staged; the previous chunk's qs / as_ are consumed
+    for (int x = tid; x < cn * DI; x += 256) {
+      const int xe = x / DI, c = x - xe * DI;
+      const int64_t row = lists[first + c0 + xe] / K;
+      qs[xe * KS + c] = to_f32(q_idx[(row * G + g) * (int64_t)DI + c]);
+    }
+    if (tid < cn) cs[tid] = grad[(int64_t)g * nent + lists[first + c0 + tid]];
+    __syncthreads();
+    // arg-max: entry x = tid / 4 over keys part, part + 4, ... below its
+    // limit, four keys' sums at a time (independent chains); each sum still
+    // runs in channel order
+    {
+      const int x = tid >> 2, part = tid & 3;
+      float best = neg_inf();
+      int bsel = -1;
+      if (x < cn) {
+        const int64_t e = lists[first + c0 + x];
+        const int64_t pos = base_pos + (e / K - q0);
+        const int lim = (int)min<int64_t>(nkeys, pos - s0 + 1);  // causal keys of the block
+        float qr[DI];
+#pragma unroll
+        for (int c = 0; c < DI; ++c) qr[c] = qs[x * KS + c];
+        for (int s = part; s < lim; s += 16) {
+          float d[4] = {0.f, 0.f, 0.f, 0.f};
+          const int sr[4] = {s, min(s + 4, BS - 1), min(s + 8, BS - 1), min(s + 12, BS - 1)};
+#pragma unroll
+          for (int c = 0; c < DI; ++c) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) d[u] = dot_step(d[u], qr[c], ks[sr[u] * KS + c], T());
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {  // keys in increasing order; past the limit ignored
+            if (s + 4 * u < lim && (d[u] > best || bsel < 0)) {
+              best = d[u];
+              bsel = s + 4 * u;
+            }
+          }
+        }
+      }
+      bv[tid] = best;
+      bs[tid] = bsel;
+    }
+    __syncthreads();
+    if (tid < cn) {
+      float best = bv[4 * tid];
+      int bsel = bs[4 * tid];
+      for (int u = 1; u < 4; ++u) {  // the larger value; the lower key on a tie
+        const float v = bv[4 * tid + u];
+        const int s = bs[4 * tid + u];
+        if (s >= 0 && (bsel < 0 || v > best || (v == best && s < bsel))) {
+          best = v;
+          bsel = s;
+        }
+      }
+      as_[tid] = bsel;
+      amax[(int64_t)g * nent + lists[first + c0 + tid]] = bsel < 0 ? -1 : (int32_t)(kv0 + s0 + bsel);
+    }
+    __syncthreads();
+    // key side: row srow adds c * q over the chunk's entries that chose it, in order
+    for (int x = 0; x < cn; ++x) {
+      if (as_[x] == srow) {
+        const float cx = cs[x];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = fmaf(cx, qs[x * KS + c_lo + c], acc[c]);
+      }
+    }
+  }
+  if (srow < nkeys) {
+    float *dst = dk_idx + ((kv0 + s0 + srow) * G + g) * (int64_t)DI + c_lo;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) dst[c] = acc[c];
+  }
+}
+
+// One wave per (group, row): dq_idx[row, g] = sum over slots (in order) of
+// c * k_idx[arg-max key]; lanes hold channels.
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void ib_dq_kernel(const T *__restrict__ k_idx,
+                                                    const float *__restrict__ grad,
+                                                    const int32_t *__restrict__ amax,
+                                                    float *__restrict__ dq_idx, int G, int K,
+                                                    int64_t total_q) {
+  constexpr int CPL = (DI + 63) / 64;  // channels per lane
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= total_q) return;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t rk = ((int64_t)g * total_q + row) * K;
+  float acc[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) acc[u] = 0.f;
+  for (int i = 0; i < K; ++i) {
+    const int32_t a = amax[rk + i];
+    if (a < 0) continue;  // wave-uniform
+    const float c = grad[rk + i];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      if (ch < DI) acc[u] = fmaf(c, to_f32(k_idx[((int64_t)a * G + g) * DI + ch]), acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int ch = lane + 64 * u;
+    if (ch < DI) dq_idx[(row * G + g) * (int64_t)DI + ch] = acc[u];
+  }
+}
+
+template <typename T, int DI, int BS>
+hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_t *block_idx,
+                     const float *grad, float *dq_idx, float *dk_idx, void *workspace,
+                     hipStream_t s) {
+  IbWs w = ib_carve(p, workspace);
+  const int64_t nk = p.total_kv * p.G * (int64_t)DI;
+  if (nk > 0) {
+    const unsigned zg = (unsigned)std::min<int64_t>((nk + 255) / 256, 65536);
+    hipLaunchKernelGGL(ib_zero_kernel, dim3(zg), dim3(256), 0, s, dk_idx, nk);
+  }
+  profile_mark(s);
+  const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
+  hipLaunchKernelGGL(ib_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
+                     block_idx, p.cu_q, p.cu_kv, w.cnt, w.amax, p.num_seqs, p.top_k, p.total_q,
+                     p.nb_max, p.B, w.ntiles, w.nbk_g);
+  profile_mark(s);
+  const int64_t ncol = (int64_t)p.G * w.nbk_g;
+  hipLaunchKernelGGL(ib_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
+                     w.cnt, w.base, p.G, w.ntiles, w.nbk_g);
+  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
+  profile_mark(s);
+  hipLaunchKernelGGL(ib_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
+                     block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
+                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
+  profile_mark(s);
+  hipLaunchKernelGGL((ib_bucket_kernel<T, DI, BS>), dim3((unsigned)w.nbk_g, p.G), dim3(256), 0, s,
+                     q_idx, k_idx, grad, w.base, w.lists, w.amax, dk_idx, p.cu_q, p.cu_kv,
+                     p.num_seqs, p.G, p.top_k, p.total_q, p.nb_max);
+  profile_mark(s);
+  hipLaunchKernelGGL((ib_dq_kernel<T, DI>), dim3((unsigned)((p.total_q + 3) / 4), p.G), dim3(256),
+                     0, s, k_idx, grad, w.amax, dq_idx, p.G, p.top_k, p.total_q);
+  profile_mark(s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t index_bwd_workspace_bytes(const Dims &p) {
+  return p.total_q > 0 ? ib_carve(p, nullptr).total_bytes : 0;
+}
+
+int64_t index_bwd_hist_bytes(const Dims &p) {
+  return (int64_t)sizeof(int32_t) * p.num_seqs * (int64_t)p.nb_max;
+}
+
+hipError_t launch_index_bwd(const Dims &p, bool bf16, const void *q_idx, const void *k_idx,
+                            const int32_t *block_idx, const float *grad, float *dq_idx,
+                            float *dk_idx, void *workspace, hipStream_t s) {
+  if (p.total_q <= 0) {  // no slot: every key's gradient is 0
+    const int64_t nk = p.total_kv * p.G * (int64_t)p.d_idx;
+    if (nk > 0)
+      hipLaunchKernelGGL(ib_zero_kernel, dim3((unsigned)std::min<int64_t>((nk + 255) / 256, 65536)),
+                         dim3(256), 0, s, dk_idx, nk);
+    profile_mark(s);
+    return hipGetLastError();
+  }
+#define MSA_IB_CASE(DI_, BS_)                                                                    \
+  if (p.d_idx == DI_ && p.B == BS_) {                                                            \
+    if (bf16)                                                                                    \
+      return launch_ib<uint16_t, DI_, BS_>(p, static_cast<const uint16_t *>(q_idx),              \
+                                           static_cast<const uint16_t *>(k_idx), block_idx,      \
+                                           grad, dq_idx, dk_idx, workspace, s);                  \
+    return launch_ib<float, DI_, BS_>(p, static_cast<const float *>(q_idx),                      \
+                                      static_cast<const float *>(k_idx), block_idx, grad,        \
+                                      dq_idx, dk_idx, workspace, s);                             \
+  }
+  MSA_IB_CASE(32, 64) MSA_IB_CASE(32, 128) MSA_IB_CASE(64, 64) MSA_IB_CASE(64, 128)
+  MSA_IB_CASE(128, 64) MSA_IB_CASE(128, 128)
+#undef MSA_IB_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -59,6 +59,13 @@ hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
                                     float *lse, float *block_mass, void *workspace, hipStream_t s);
 
+// Backward of the Index Branch max-pooling (index_bwd.hip).
+size_t index_bwd_workspace_bytes(const Dims &p);
+int64_t index_bwd_hist_bytes(const Dims &p);  // LDS of its per-tile bucket histogram
+hipError_t launch_index_bwd(const Dims &p, bool bf16, const void *q_idx, const void *k_idx,
+                            const int32_t *block_idx, const float *grad, float *dq_idx,
+                            float *dk_idx, void *workspace, hipStream_t s);
+
 // Indexer KL objective over the kept blocks (indexer_kl.hip).
 hipError_t launch_indexer_kl(const Dims &p, const float *scores, const int32_t *block_idx,
                              const float *block_mass, float *kl, float *grad, hipStream_t s);

@@ -187,6 +187,30 @@ msa_status_t msa_indexer_kl(const msa_problem_t *prob, const float *scores,
                             const int32_t *block_idx, const float *block_mass, float *kl,
                             float *grad, void *stream);
 
+/* Backward of the Index Branch max-pooling (page: Summary, paragraph 2; the
+ * block score is the maximum of token-level dot products, so a kept block's
+ * score gradient reaches only the causal key that attains that maximum).
+ * grad[g, r, i] is the gradient of the score of kept slot i of row r
+ * (msa_indexer_kl's grad, or any other); with a = the arg-max key of block
+ * block_idx[g, r, i] over the keys s <= p(r) of that block:
+ *   dq_idx[r, g] = sum over slots i (in slot order) of grad[g,r,i] * k_idx[a, g]
+ *   dk_idx[s, g] = sum over (r, i) with a = s (in (r, i) order) of grad[g,r,i] * q_idx[r, g]
+ * Slots that are padding or whose block holds no causal key add nothing;
+ * keys that no slot takes get 0.  The arg-max is an integer decided by
+ * floating point: each dot product is summed in fp32 in channel order
+ * (every product rounded to fp32, then added), ties to the lower key.
+ * Sums are fp32, deterministic (no floating-point atomics).  q_idx, k_idx
+ * have the problem's dtype; grad [G, total_q, top_k], dq_idx [total_q, G,
+ * d_idx] and dk_idx [total_kv, G, d_idx] are fp32, fully written.
+ * Requirements beyond the common ones: total_q * top_k < 2^31 and
+ * num_seqs * NBmax <= 16384 (else MSA_ERR_BAD_SHAPE).  `workspace` must
+ * hold msa_indexer_bwd_workspace_size() bytes, 256-byte aligned. */
+msa_status_t msa_indexer_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes);
+msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                             const int32_t *block_idx, const float *grad, float *dq_idx,
+                             float *dk_idx, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* Kernel timing hook (diagnostics).  After this call, every msa_* call on
  * the calling thread records events[i] (each a hipEvent_t created by the
  * caller) on its stream right after launching its i-th kernel, for i <

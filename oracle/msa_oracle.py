@@ -272,11 +272,11 @@ def indexer_kl(S, block_idx, mass):
 
 def block_argmax_f32(q_row, k_rows) -> int:
     """Index of the largest fp32 dot product of q_row with each row of k_rows,
-    ties to the lowest index.  The dot products are summed in fp32 in channel
-    order 0, 1, ..., d-1, one exact product at a time: for bf16 inputs every
-    product is exact in fp32, so this is the value a sequential fp32 FMA chain
-    gives.  The arg-max is an integer decided by floating point; it is taken in
-    that fp32 precision so that both sides decide it the same way."""
+    ties to the lowest index.  Each dot product is summed in fp32 in channel
+    order 0, 1, ..., d-1: every product is rounded to fp32 (exact for bf16
+    inputs, where a fused multiply-add gives the same value), then added with
+    fp32 rounding.  The arg-max is an integer decided by floating point; it is
+    taken in this fp32 precision so that both sides decide it the same way."""
     q = np.asarray(_f64(q_row), dtype=np.float32)
     kr = np.asarray(_f64(k_rows), dtype=np.float32)
     acc = np.zeros(kr.shape[0], dtype=np.float32)

@@ -222,3 +222,37 @@ def test_indexer_kl_problem_checks():
     assert _kl(_prob(max_q_len=0, total_q=0), sc=None, idx=None, mass=None, kl=None,
                grad=None) == 0
     assert msa.load_library().msa_indexer_kl(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def _ibwd(p, qi=FAKE, ki=FAKE, idx=FAKE, gr=FAKE, dq=FAKE, dk=FAKE, ws=None, wsb=0):
+    lib = msa.load_library()
+    return lib.msa_indexer_bwd(ctypes.byref(p), qi, ki, idx, gr, dq, dk, ws, wsb, None)
+
+
+@pytest.mark.parametrize("which", ["qi", "ki", "idx", "gr", "dq", "dk"])
+def test_indexer_bwd_pointer_checks(which):
+    p = _prob()
+    args = dict(qi=FAKE, ki=FAKE, idx=FAKE, gr=FAKE, dq=FAKE, dk=FAKE)
+    args[which] = None
+    assert _ibwd(p, **args) == 1
+    args[which] = FAKE + 4
+    assert _ibwd(p, **args) == 4
+
+
+def test_indexer_bwd_workspace_and_limits():
+    lib = msa.load_library()
+    n = ctypes.c_size_t(0)
+    p = _prob()
+    assert lib.msa_indexer_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert _ibwd(p, ws=FAKE, wsb=n.value - 1) == 5
+    assert _ibwd(p, ws=None, wsb=n.value) == 1
+    assert _ibwd(p, ws=FAKE + 16, wsb=n.value) == 4
+    # more (sequence, block) histogram bins than the LDS holds
+    wide = _prob(num_seqs=3, max_kv_len=128 * 8000, total_kv=3 * 128 * 8000, max_q_len=1, total_q=3)
+    assert _ibwd(wide, ws=FAKE, wsb=1 << 40) == 2
+    assert _ibwd(_prob(top_k=0)) == 2
+    assert lib.msa_indexer_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
+    # nothing at all to do
+    assert _ibwd(_prob(max_q_len=0, total_q=0, max_kv_len=0, total_kv=0), qi=None, ki=None,
+                 idx=None, gr=None, dq=None, dk=None) == 0

@@ -220,3 +220,10 @@ def random_block_lists(seed: int, len_q: Sequence[int], len_kv: Sequence[int], G
             slots = rng.choice(top_k, size=n, replace=False)
             out[g, r, slots] = picks
     return torch.from_numpy(out)
+
+
+def random_slot_grads(seed: int, G: int, total_q: int, top_k: int) -> torch.Tensor:
+    """Seeded fp32 N(0, 1) gradients for every kept slot [G, total_q, top_k]:
+    the input of the Index Branch backward when it is checked on its own."""
+    g = torch.Generator(device="cpu").manual_seed(_seed(seed, "slot-grads", top_k))
+    return torch.randn((G, total_q, top_k), generator=g, dtype=torch.float32)
