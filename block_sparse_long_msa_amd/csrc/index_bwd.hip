@@ -20,10 +20,15 @@
 //   ib_scatter   per tile, one wave walks its entries in order and writes each
 //                to its bucket's list at tile offset + running count + rank
 //                among equal buckets: every list ends up in (row, slot) order
-//   ib_bucket    per bucket: the block's index keys in LDS; for each entry in
-//                list order the arg-max over the causal keys, then each key
-//                row sums c * q_idx over the entries that chose it, in list
-//                order; the arg-max is stored for ib_dq
+//   ib_item      per work item (at most kIE consecutive entries of one
+//                bucket's list, so popular blocks are shared out): the block's
+//                index keys in LDS; for each entry in list order the arg-max
+//                over the causal keys, then each key row sums c * q_idx over
+//                the entries that chose it, in list order.  A bucket of one
+//                item writes dk_idx; the items of a larger bucket write
+//                partial sums.  The arg-max is stored for ib_dq.
+//   ib_reduce    per bucket of several items: dk_idx = the items' partial
+//                sums added in item order
 //   ib_dq        per (group, row): dq_idx from the stored arg-max keys
 #include <algorithm>
 
@@ -34,13 +39,17 @@ namespace msa {
 namespace {
 
 constexpr int kTE = 4096;  // entries per counting / scatter tile
+constexpr int kIE = 1024;  // entries per work item of the arg-max pass
 
 struct IbWs {
   int32_t *cnt;    // [G][ntiles][nbk_g]: tile counts, then exclusive tile offsets
   int32_t *base;   // [G * nbk_g + 1]: bucket totals, then exclusive starts
   int32_t *lists;  // [G * total_q * K] entries e = row * K + slot, grouped by bucket
   int32_t *amax;   // [G][total_q][K] arg-max key (packed key row) or -1
-  int64_t ntiles, nbk_g, nent_g;
+  int32_t *ibase;  // [G * nbk_g + 1]: items per bucket, then exclusive item starts
+  int32_t *pbase;  // [G * nbk_g + 1]: partial slots per bucket (its items if > 1)
+  float *part;     // [max_parts][BS][d_idx] key-side partial sums of shared buckets
+  int64_t ntiles, nbk_g, nent_g, max_items, max_parts;
   size_t total_bytes;
 };
 
@@ -62,6 +71,14 @@ IbWs ib_carve(const Dims &p, void *base) {
   w.base = take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1));
   w.lists = take(sizeof(int32_t) * (size_t)p.G * w.nent_g);
   w.amax = take(sizeof(int32_t) * (size_t)p.G * w.nent_g);
+  w.ibase = take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1));
+  w.pbase = take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1));
+  // every bucket has one item more than its full kIE-entry items; a bucket
+  // with partial slots has more than kIE entries
+  const int64_t nent = (int64_t)p.G * w.nent_g;
+  w.max_items = nent / kIE + std::min<int64_t>((int64_t)p.G * w.nbk_g, nent) + 1;
+  w.max_parts = 2 * (nent / kIE) + 1;
+  w.part = reinterpret_cast<float *>(take(sizeof(float) * (size_t)w.max_parts * p.B * p.d_idx));
   w.total_bytes = off;
   return w;
 }
@@ -134,7 +151,9 @@ __global__ __launch_bounds__(256) void ib_count_kernel(
 
 // One thread per (group, bucket): tile counts -> exclusive tile offsets.
 __global__ __launch_bounds__(256) void ib_colscan_kernel(int32_t *__restrict__ cnt,
-                                                         int32_t *__restrict__ total, int G,
+                                                         int32_t *__restrict__ total,
+                                                         int32_t *__restrict__ items,
+                                                         int32_t *__restrict__ parts, int G,
                                                          int64_t ntiles, int64_t nbk_g) {
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= (int64_t)G * nbk_g) return;
@@ -147,6 +166,9 @@ __global__ __launch_bounds__(256) void ib_colscan_kernel(int32_t *__restrict__ c
     run += v;
   }
   total[x] = run;
+  const int32_t ni = (run + kIE - 1) / kIE;
+  items[x] = ni;
+  parts[x] = ni > 1 ? ni : 0;
 }
 
 // One work-group: exclusive scan of n bucket totals in place, base[n] = sum.
@@ -216,83 +238,150 @@ __global__ __launch_bounds__(64) void ib_scatter_kernel(
   }
 }
 
-// One work-group per (group, bucket).  Threads 4x + part handle entry x of a
-// 64-entry chunk for the arg-max (keys part, part+4, ...); for the key-side
-// sum, thread 4s + part... owns key row s and a quarter-or-more of the
-// channels (TPR threads per row).
+// One work-group per work item: entries [it * kIE, min(n, (it + 1) * kIE))
+// of one bucket's list.  The item's rows and score gradients are staged in
+// LDS first; the index queries of each 64-entry
+// chunk are loaded into registers while the chunk before it is processed
+// (two LDS buffers), so the only global accesses inside the chunk loop are
+// these prefetches and the arg-max stores.  Lane x handles entry x of a
+// chunk for the arg-max in every wave, the waves splitting the keys; for the
+// key-side sum, the TPR threads of key row s each own DI / TPR of its
+// channels.
 template <typename T, int DI, int BS>
-__global__ __launch_bounds__(256) void ib_bucket_kernel(
+__global__ __launch_bounds__(256) void ib_item_kernel(
     const T *__restrict__ q_idx, const T *__restrict__ k_idx, const float *__restrict__ grad,
-    const int32_t *__restrict__ base, const int32_t *__restrict__ lists,
-    int32_t *__restrict__ amax, float *__restrict__ dk_idx, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, int num_seqs, int G, int K, int64_t total_q, int nb_max) {
+    const int32_t *__restrict__ base, const int32_t *__restrict__ ibase,
+    const int32_t *__restrict__ pbase, const int32_t *__restrict__ lists,
+    int32_t *__restrict__ amax, float *__restrict__ dk_idx, float *__restrict__ part,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G, int K,
+    int64_t total_q, int nb_max, int64_t nbuckets) {
   constexpr int TPR = 256 / BS;          // threads per key row (2 or 4)
   constexpr int CPT = DI / TPR;          // channels per thread in the key-side sum
-  constexpr int KS = DI + 1;             // padded LDS row of the staged keys
-  __shared__ float ks[BS * KS];          // the block's index keys, fp32
-  __shared__ float qs[64 * KS];          // index queries of the chunk's entries
-  __shared__ float cs[64];               // their score gradients
-  __shared__ int32_t as_[64];            // their arg-max (block-local key, -1 none)
-  __shared__ float bv[256];              // arg-max candidates of the 4 threads of an entry
+  constexpr int KS = DI + 4;             // padded LDS row of the chunk's queries (16-byte rows)
+  constexpr int EPP = 16 / (int)sizeof(T);         // elements per 16-byte piece
+  constexpr int PPR = DI / EPP;                    // pieces per query row
+  constexpr int PPT = (64 * PPR + 255) / 256;      // pieces per thread and chunk
+  typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float kq[BS * DI];  // the block's index keys, fp32
+  __shared__ __attribute__((aligned(16))) float qs[2][64 * KS];  // index queries of a chunk's entries
+  __shared__ int32_t ent_row[kIE];       // the item's rows
+  __shared__ float ent_c[kIE];           // and score gradients
+  __shared__ int32_t as_[64];            // arg-max of the chunk's entries (-1 none)
+  __shared__ float bv[256];              // arg-max candidates of the 4 waves
   __shared__ int32_t bs[256];
-  const int g = blockIdx.y;
-  const int64_t bkt = blockIdx.x;        // b * nb_max + j
-  const int64_t gb = (int64_t)g * num_seqs * nb_max + bkt;
-  const int32_t first = base[gb], n = base[gb + 1] - first;
-  if (n == 0) return;
+  const int32_t w = (int32_t)blockIdx.x;
+  if (w >= ibase[nbuckets]) return;      // past the last item
+  // the bucket holding item w: the last one whose first item is <= w
+  int64_t lo = 0, hi = nbuckets - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (ibase[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int64_t gb = lo;                 // g * nbk_g + b * nb_max + j
+  const int32_t it = w - ibase[gb], nit = ibase[gb + 1] - ibase[gb];
+  const int32_t n_b = base[gb + 1] - base[gb];
+  const int32_t first = base[gb] + it * kIE, n = min(kIE, n_b - it * kIE);
+  const int64_t nbk_g = nbuckets / G;
+  const int g = (int)(gb / nbk_g);
+  const int64_t bkt = gb - (int64_t)g * nbk_g;
   const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
   const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
   const int64_t q0 = cu_q[b], base_pos = lkv - (cu_q[b + 1] - q0);
   const int64_t s0 = (int64_t)j * BS;
   const int nkeys = (int)min<int64_t>(BS, lkv - s0);
   const int tid = threadIdx.x;
+  const int64_t nent = total_q * K;
   for (int x = tid; x < BS * DI; x += 256) {
     const int s = x / DI, c = x - s * DI;
-    ks[s * KS + c] = s < nkeys ? to_f32(k_idx[((kv0 + s0 + s) * G + g) * (int64_t)DI + c]) : 0.f;
+    kq[s * DI + c] = s < nkeys ? to_f32(k_idx[((kv0 + s0 + s) * G + g) * (int64_t)DI + c]) : 0.f;
   }
+  for (int x = tid; x < n; x += 256) {
+    const int32_t e = lists[first + x];
+    const int64_t row = e / K;
+    ent_row[x] = (int32_t)row;
+    ent_c[x] = grad[(int64_t)g * nent + e];
+  }
+  __syncthreads();
+  // index-query pieces of chunk c0: piece pc = tid + 256 u is entry pc / PPR,
+  // elements EPP * (pc % PPR) ..; entries past the item read its last entry
+  piece_t pf[PPT];
+  auto prefetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = min(tid + 256 * u, 64 * PPR - 1);
+      const int xe = min(c0 + pc / PPR, n - 1);
+      pf[u] = *reinterpret_cast<const piece_t *>(
+          q_idx + ((int64_t)ent_row[xe] * G + g) * DI + EPP * (pc % PPR));
+    }
+  };
+  auto stash = [&](float *dst) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = tid + 256 * u;
+      if (PPT * 256 != 64 * PPR && pc >= 64 * PPR) break;
+      const int xe = pc / PPR, c = EPP * (pc % PPR);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[xe * KS + c + 2 * i] = bf16_lo(pf[u][i]);
+          dst[xe * KS + c + 2 * i + 1] = bf16_hi(pf[u][i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[xe * KS + c + i] = __uint_as_float(pf[u][i]);
+      }
+    }
+  };
   const int srow = tid / TPR, c_lo = (tid % TPR) * CPT;
   float acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
-  const int64_t nent = total_q * K;
-  for (int32_t c0 = 0; c0 < n; c0 += 64) {
+  prefetch(0);
+  stash(qs[0]);
+  for (int32_t c0 = 0, buf = 0; c0 < n; c0 += 64, buf ^= 1) {
     const int cn = min(64, n - c0);
-    __syncthreads();  // keys staged; the previous chunk's qs / as_ are consumed
-    for (int x = tid; x < cn * DI; x += 256) {
-      const int xe = x / DI, c = x - xe * DI;
-      const int64_t row = lists[first + c0 + xe] / K;
-      qs[xe * KS + c] = to_f32(q_idx[(row * G + g) * (int64_t)DI + c]);
-    }
-    if (tid < cn) cs[tid] = grad[(int64_t)g * nent + lists[first + c0 + tid]];
-    __syncthreads();
-    // arg-max: entry x = tid / 4 over keys part, part + 4, ... below its
-    // limit, four keys' sums at a time (independent chains); each sum still
-    // runs in channel order
+    __syncthreads();  // qs[buf] is filled; the previous chunk's as_ / bv are consumed
+    if (c0 + 64 < n) prefetch(c0 + 64);
+    // arg-max: lane x of every wave holds entry x's index query in registers;
+    // wave wv takes keys wv, wv + 4, ..., so all lanes of a wave read the
+    // same key row (a broadcast LDS read) and each key row is read once per
+    // wave and chunk.  Four keys' sums run at a time as independent chains;
+    // each sum still runs in channel order.  Keys past an entry's causal
+    // limit are computed and ignored.
     {
-      const int x = tid >> 2, part = tid & 3;
+      const int x = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      // causal keys of the block for entry x's row
+      const int lim = x < cn ? (int)min<int64_t>(nkeys, base_pos + (ent_row[c0 + x] - q0) - s0 + 1) : 0;
       float best = neg_inf();
       int bsel = -1;
-      if (x < cn) {
-        const int64_t e = lists[first + c0 + x];
-        const int64_t pos = base_pos + (e / K - q0);
-        const int lim = (int)min<int64_t>(nkeys, pos - s0 + 1);  // causal keys of the block
-        float qr[DI];
+      float qr[DI];
 #pragma unroll
-        for (int c = 0; c < DI; ++c) qr[c] = qs[x * KS + c];
-        for (int s = part; s < lim; s += 16) {
-          float d[4] = {0.f, 0.f, 0.f, 0.f};
-          const int sr[4] = {s, min(s + 4, BS - 1), min(s + 8, BS - 1), min(s + 12, BS - 1)};
+      for (int c = 0; c < DI; c += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c]);
+        qr[c] = v.x;
+        qr[c + 1] = v.y;
+        qr[c + 2] = v.z;
+        qr[c + 3] = v.w;
+      }
+      for (int s = wv; s < nkeys; s += 16) {
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
+        const int sr[4] = {s, min(s + 4, BS - 1), min(s + 8, BS - 1), min(s + 12, BS - 1)};
 #pragma unroll
-          for (int c = 0; c < DI; ++c) {
+        for (int c = 0; c < DI; c += 4) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) d[u] = dot_step(d[u], qr[c], ks[sr[u] * KS + c], T());
+          for (int u = 0; u < 4; ++u) {
+            const float4 kv = *reinterpret_cast<const float4 *>(&kq[sr[u] * DI + c]);
+            d[u] = dot_step(d[u], qr[c], kv.x, T());
+            d[u] = dot_step(d[u], qr[c + 1], kv.y, T());
+            d[u] = dot_step(d[u], qr[c + 2], kv.z, T());
+            d[u] = dot_step(d[u], qr[c + 3], kv.w, T());
           }
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {  // keys in increasing order; past the limit ignored
-            if (s + 4 * u < lim && (d[u] > best || bsel < 0)) {
-              best = d[u];
-              bsel = s + 4 * u;
-            }
+        for (int u = 0; u < 4; ++u) {  // keys in increasing order; past the limit ignored
+          if (s + 4 * u < lim && (d[u] > best || bsel < 0)) {
+            best = d[u];
+            bsel = s + 4 * u;
           }
         }
       }
@@ -301,11 +390,11 @@ __global__ __launch_bounds__(256) void ib_bucket_kernel(
     }
     __syncthreads();
     if (tid < cn) {
-      float best = bv[4 * tid];
-      int bsel = bs[4 * tid];
+      float best = bv[tid];
+      int bsel = bs[tid];
       for (int u = 1; u < 4; ++u) {  // the larger value; the lower key on a tie
-        const float v = bv[4 * tid + u];
-        const int s = bs[4 * tid + u];
+        const float v = bv[64 * u + tid];
+        const int s = bs[64 * u + tid];
         if (s >= 0 && (bsel < 0 || v > best || (v == best && s < bsel))) {
           best = v;
           bsel = s;
@@ -315,19 +404,71 @@ __global__ __launch_bounds__(256) void ib_bucket_kernel(
       amax[(int64_t)g * nent + lists[first + c0 + tid]] = bsel < 0 ? -1 : (int32_t)(kv0 + s0 + bsel);
     }
     __syncthreads();
-    // key side: row srow adds c * q over the chunk's entries that chose it, in order
-    for (int x = 0; x < cn; ++x) {
-      if (as_[x] == srow) {
-        const float cx = cs[x];
+    // key side: row srow adds c * q over the chunk's entries that chose it,
+    // in entry order.  A wave owns rows [wv * 64 / TPR, (wv + 1) * 64 / TPR):
+    // lane x reads entry x's arg-max, and the wave visits only the entries
+    // whose arg-max it owns, lowest first.
+    {
+      const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int my_a = lane < cn ? as_[lane] : -1;
+      const int r_lo = wv * (64 / TPR);
+      uint64_t m = ballot64(my_a >= r_lo && my_a < r_lo + 64 / TPR);
+      while (m != 0) {
+        const int x = (int)__builtin_ctzll(m);
+        m &= m - 1;
+        const int r = __builtin_amdgcn_readlane(my_a, x);
+        if (srow == r) {
+          const float cx = ent_c[c0 + x];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = fmaf(cx, qs[x * KS + c_lo + c], acc[c]);
+          for (int c = 0; c < CPT; c += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c_lo + c]);
+            acc[c] = fmaf(cx, v.x, acc[c]);
+            acc[c + 1] = fmaf(cx, v.y, acc[c + 1]);
+            acc[c + 2] = fmaf(cx, v.z, acc[c + 2]);
+            acc[c + 3] = fmaf(cx, v.w, acc[c + 3]);
+          }
+        }
       }
     }
+    if (c0 + 64 < n) stash(qs[buf ^ 1]);
   }
-  if (srow < nkeys) {
-    float *dst = dk_idx + ((kv0 + s0 + srow) * G + g) * (int64_t)DI + c_lo;
+  if (nit == 1) {
+    if (srow < nkeys) {
+      float *dst = dk_idx + ((kv0 + s0 + srow) * G + g) * (int64_t)DI + c_lo;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) dst[c] = acc[c];
+    }
+  } else {
+    float *dst = part + ((int64_t)(pbase[gb] + it) * BS + srow) * DI + c_lo;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) dst[c] = acc[c];
+  }
+}
+
+// One work-group per bucket; only buckets of several items do work: each
+// key-row channel adds the items' partial sums in item order.
+template <int DI, int BS>
+__global__ __launch_bounds__(256) void ib_reduce_kernel(const int32_t *__restrict__ ibase,
+                                                        const int32_t *__restrict__ pbase,
+                                                        const float *__restrict__ part,
+                                                        float *__restrict__ dk_idx,
+                                                        const int64_t *__restrict__ cu_kv, int G,
+                                                        int num_seqs, int nb_max, int64_t nbk_g) {
+  const int64_t gb = blockIdx.x;
+  const int32_t nit = ibase[gb + 1] - ibase[gb];
+  if (nit <= 1) return;
+  const int g = (int)(gb / nbk_g);
+  const int64_t bkt = gb - (int64_t)g * nbk_g;
+  const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
+  const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
+  const int64_t s0 = (int64_t)j * BS;
+  const int nkeys = (int)min<int64_t>(BS, lkv - s0);
+  const float *src = part + (int64_t)pbase[gb] * BS * DI;
+  for (int x = threadIdx.x; x < nkeys * DI; x += 256) {
+    float acc = 0.f;
+    for (int32_t i = 0; i < nit; ++i) acc += src[(int64_t)i * BS * DI + x];
+    const int s = x / DI, c = x - s * DI;
+    dk_idx[((kv0 + s0 + s) * G + g) * (int64_t)DI + c] = acc;
   }
 }
 
@@ -345,18 +486,31 @@ __global__ __launch_bounds__(256) void ib_dq_kernel(const T *__restrict__ k_idx,
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int64_t rk = ((int64_t)g * total_q + row) * K;
+  // lane i holds slot i's arg-max and gradient; the slots are then taken in
+  // order, four key rows requested before any is used (a slot without an
+  // arg-max reads key row 0 with weight 0)
+  const int32_t am = lane < K ? amax[rk + lane] : -1;
+  const float gc = lane < K ? grad[rk + lane] : 0.f;
   float acc[CPL];
 #pragma unroll
   for (int u = 0; u < CPL; ++u) acc[u] = 0.f;
-  for (int i = 0; i < K; ++i) {
-    const int32_t a = amax[rk + i];
-    if (a < 0) continue;  // wave-uniform
-    const float c = grad[rk + i];
+  for (int i0 = 0; i0 < K; i0 += 4) {
+    float kv[4][CPL], c[4];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      if (ch < DI) acc[u] = fmaf(c, to_f32(k_idx[((int64_t)a * G + g) * DI + ch]), acc[u]);
+    for (int v = 0; v < 4; ++v) {
+      const int i = min(i0 + v, K - 1);
+      const int32_t a = __builtin_amdgcn_readlane(am, i);
+      c[v] = (i0 + v < K && a >= 0) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gc), i)) : 0.f;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int ch = min(lane + 64 * u, DI - 1);
+        kv[v][u] = to_f32(k_idx[((int64_t)max(a, 0) * G + g) * DI + ch]);
+      }
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) acc[u] = fmaf(c[v], kv[v][u], acc[u]);
   }
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
@@ -383,16 +537,21 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   profile_mark(s);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(ib_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
-                     w.cnt, w.base, p.G, w.ntiles, w.nbk_g);
+                     w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g);
   hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
+  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
+  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
   profile_mark(s);
   hipLaunchKernelGGL(ib_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
                      p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
   profile_mark(s);
-  hipLaunchKernelGGL((ib_bucket_kernel<T, DI, BS>), dim3((unsigned)w.nbk_g, p.G), dim3(256), 0, s,
-                     q_idx, k_idx, grad, w.base, w.lists, w.amax, dk_idx, p.cu_q, p.cu_kv,
-                     p.num_seqs, p.G, p.top_k, p.total_q, p.nb_max);
+  hipLaunchKernelGGL((ib_item_kernel<T, DI, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s,
+                     q_idx, k_idx, grad, w.base, w.ibase, w.pbase, w.lists, w.amax, dk_idx, w.part,
+                     p.cu_q, p.cu_kv, p.num_seqs, p.G, p.top_k, p.total_q, p.nb_max, ncol);
+  profile_mark(s);
+  hipLaunchKernelGGL((ib_reduce_kernel<DI, BS>), dim3((unsigned)ncol), dim3(256), 0, s, w.ibase,
+                     w.pbase, w.part, dk_idx, p.cu_kv, p.G, p.num_seqs, p.nb_max, w.nbk_g);
   profile_mark(s);
   hipLaunchKernelGGL((ib_dq_kernel<T, DI>), dim3((unsigned)((p.total_q + 3) / 4), p.G), dim3(256),
                      0, s, k_idx, grad, w.amax, dq_idx, p.G, p.top_k, p.total_q);
@@ -413,11 +572,15 @@ int64_t index_bwd_hist_bytes(const Dims &p) {
 hipError_t launch_index_bwd(const Dims &p, bool bf16, const void *q_idx, const void *k_idx,
                             const int32_t *block_idx, const float *grad, float *dq_idx,
                             float *dk_idx, void *workspace, hipStream_t s) {
-  if (p.total_q <= 0) {  // no slot: every key's gradient is 0
+  if (p.total_q <= 0 || p.total_kv <= 0) {  // no slot takes a key: zero gradients
     const int64_t nk = p.total_kv * p.G * (int64_t)p.d_idx;
+    const int64_t nq = p.total_q * p.G * (int64_t)p.d_idx;
     if (nk > 0)
       hipLaunchKernelGGL(ib_zero_kernel, dim3((unsigned)std::min<int64_t>((nk + 255) / 256, 65536)),
                          dim3(256), 0, s, dk_idx, nk);
+    if (nq > 0)
+      hipLaunchKernelGGL(ib_zero_kernel, dim3((unsigned)std::min<int64_t>((nq + 255) / 256, 65536)),
+                         dim3(256), 0, s, dq_idx, nq);
     profile_mark(s);
     return hipGetLastError();
   }
