@@ -21,12 +21,12 @@
 //                to its bucket's list at tile offset + running count + rank
 //                among equal buckets: every list ends up in (row, slot) order
 //   ib_item      per work item (at most kIE consecutive entries of one
-//                bucket's list, so popular blocks are shared out): the block's
-//                index keys in LDS; for each entry in list order the arg-max
-//                over the causal keys, then each key row sums c * q_idx over
-//                the entries that chose it, in list order.  A bucket of one
-//                item writes dk_idx; the items of a larger bucket write
-//                partial sums.  The arg-max is stored for ib_dq.
+//                bucket's list, so popular blocks are shared out): for each
+//                entry in list order the arg-max over the causal keys (key
+//                operands in scalar registers), then each key row sums
+//                c * q_idx over the entries that chose it, in list order.  A
+//                bucket of one item writes dk_idx; the items of a larger
+//                bucket write partial sums.  The arg-max is stored for ib_dq.
 //   ib_reduce    per bucket of several items: dk_idx = the items' partial
 //                sums added in item order
 //   ib_dq        per (group, row): dq_idx from the stored arg-max keys
@@ -242,8 +242,7 @@ __global__ __launch_bounds__(64) void ib_scatter_kernel(
 // of one bucket's list.  The item's rows and score gradients are staged in
 // LDS first; the index queries of each 64-entry
 // chunk are loaded into registers while the chunk before it is processed
-// (two LDS buffers), so the only global accesses inside the chunk loop are
-// these prefetches and the arg-max stores.  Lane x handles entry x of a
+// (two LDS buffers); the keys are read with scalar loads.  Lane x handles entry x of a
 // chunk for the arg-max in every wave, the waves splitting the keys; for the
 // key-side sum, the TPR threads of key row s each own DI / TPR of its
 // channels.
@@ -262,7 +261,6 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
   constexpr int PPR = DI / EPP;                    // pieces per query row
   constexpr int PPT = (64 * PPR + 255) / 256;      // pieces per thread and chunk
   typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) float kq[BS * DI];  // the block's index keys, fp32
   __shared__ __attribute__((aligned(16))) float qs[2][64 * KS];  // index queries of a chunk's entries
   __shared__ int32_t ent_row[kIE];       // the item's rows
   __shared__ float ent_c[kIE];           // and score gradients
@@ -291,10 +289,6 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
   const int nkeys = (int)min<int64_t>(BS, lkv - s0);
   const int tid = threadIdx.x;
   const int64_t nent = total_q * K;
-  for (int x = tid; x < BS * DI; x += 256) {
-    const int s = x / DI, c = x - s * DI;
-    kq[s * DI + c] = s < nkeys ? to_f32(k_idx[((kv0 + s0 + s) * G + g) * (int64_t)DI + c]) : 0.f;
-  }
   for (int x = tid; x < n; x += 256) {
     const int32_t e = lists[first + x];
     const int64_t row = e / K;
@@ -343,11 +337,11 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
     __syncthreads();  // qs[buf] is filled; the previous chunk's as_ / bv are consumed
     if (c0 + 64 < n) prefetch(c0 + 64);
     // arg-max: lane x of every wave holds entry x's index query in registers;
-    // wave wv takes keys wv, wv + 4, ..., so all lanes of a wave read the
-    // same key row (a broadcast LDS read) and each key row is read once per
-    // wave and chunk.  Four keys' sums run at a time as independent chains;
-    // each sum still runs in channel order.  Keys past an entry's causal
-    // limit are computed and ignored.
+    // wave wv takes keys wv, wv + 4, ..., so all lanes of a wave need the same
+    // key element, which comes from global memory at a wave-uniform address
+    // into scalar registers.  Four keys' sums run at a time as independent
+    // chains; each sum still runs in channel order.  Keys past an entry's
+    // causal limit are computed and ignored.
     {
       const int x = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
       // causal keys of the block for entry x's row
@@ -365,16 +359,38 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
       }
       for (int s = wv; s < nkeys; s += 16) {
         float d[4] = {0.f, 0.f, 0.f, 0.f};
-        const int sr[4] = {s, min(s + 4, BS - 1), min(s + 8, BS - 1), min(s + 12, BS - 1)};
+        // the four key rows, read from global memory at wave-uniform
+        // addresses (scalar loads; rows past the block's end read its last row)
+        const T *kr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kr[u] = k_idx + ((kv0 + s0 + min(s + 4 * u, nkeys - 1)) * G + g) * (int64_t)DI;
+        // 16 channels of the four rows at a time (a scheduling barrier keeps
+        // the compiler from hoisting further scalar loads): a modest number
+        // of scalar registers in flight
 #pragma unroll
         for (int c = 0; c < DI; c += 4) {
+          if (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float4 kv = *reinterpret_cast<const float4 *>(&kq[sr[u] * DI + c]);
-            d[u] = dot_step(d[u], qr[c], kv.x, T());
-            d[u] = dot_step(d[u], qr[c + 1], kv.y, T());
-            d[u] = dot_step(d[u], qr[c + 2], kv.z, T());
-            d[u] = dot_step(d[u], qr[c + 3], kv.w, T());
+            float kv[4];
+            if constexpr (sizeof(T) == 2) {
+              const u32x2 w2 = *reinterpret_cast<const u32x2 *>(kr[u] + c);
+              kv[0] = bf16_lo(w2.x);
+              kv[1] = bf16_hi(w2.x);
+              kv[2] = bf16_lo(w2.y);
+              kv[3] = bf16_hi(w2.y);
+            } else {
+              const float4 w4 = *reinterpret_cast<const float4 *>(kr[u] + c);
+              kv[0] = w4.x;
+              kv[1] = w4.y;
+              kv[2] = w4.z;
+              kv[3] = w4.w;
+            }
+            d[u] = dot_step(d[u], qr[c], kv[0], T());
+            d[u] = dot_step(d[u], qr[c + 1], kv[1], T());
+            d[u] = dot_step(d[u], qr[c + 2], kv[2], T());
+            d[u] = dot_step(d[u], qr[c + 3], kv[3], T());
           }
         }
 #pragma unroll
