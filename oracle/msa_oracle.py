@@ -321,3 +321,46 @@ def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
                 dq[t, g] += grad[g, t, i] * kg[a]
                 dk[a, g] += grad[g, t, i] * qt
     return dq, dk
+
+
+def sparse_attention_backward(q, k, v, block_idx, pos, block_size: int, scale: float, dout):
+    """Gradients of the Main Branch (Summary, paragraph 2: exact softmax
+    attention over the kept blocks) with respect to q, k and v, for an
+    upstream gradient dout of its output.
+
+    Same key sets as sparse_attention.  For row t and head h of group g, with
+    z_s = scale * <q[t,h], k[s,g]>, a = softmax(z), out = sum_s a_s v[s,g]:
+      dv[s,g]  += a_s dout[t,h]
+      dz_s      = a_s (<dout[t,h], v[s,g]> - <dout[t,h], out[t,h]>)
+      dq[t,h]  += scale * sum_s dz_s k[s,g]
+      dk[s,g]  += scale * dz_s q[t,h]
+    Returns (dq [n, H, d], dk [len_kv, G, d], dv [len_kv, G, dv]) in float64.
+    """
+    qf = _f64(q)
+    do = _f64(dout)
+    n, H, d = qf.shape
+    G = block_idx.shape[0]
+    hpg = H // G
+    L = k.shape[0]
+    dq = np.zeros_like(qf)
+    dk = np.zeros((L, G, d))
+    dv = np.zeros((L, G, v.shape[-1]))
+    pos = np.asarray(pos, dtype=np.int64)
+    for t in range(n):
+        for g in range(G):
+            keys = kept_keys(block_idx[g, t], int(pos[t]), block_size)
+            if keys.size == 0:
+                continue
+            kg = _gather_f64(k, keys, g)
+            vg = _gather_f64(v, keys, g)
+            for h in range(g * hpg, (g + 1) * hpg):
+                z = scale * (kg @ qf[t, h])
+                a = np.exp(z - z.max())
+                a /= a.sum()
+                out = a @ vg
+                dp = vg @ do[t, h]
+                dz = a * (dp - do[t, h] @ out)
+                dq[t, h] += scale * (dz @ kg)
+                np.add.at(dk[:, g, :], keys, scale * np.outer(dz, qf[t, h]))
+                np.add.at(dv[:, g, :], keys, np.outer(a, do[t, h]))
+    return dq, dk, dv

@@ -641,3 +641,95 @@ def test_block_argmax_f32_exact_on_small_integers():
         kr = rng.integers(-3, 4, (16, 8)).astype(float)
         exact = kr @ q
         assert O.block_argmax_f32(q, kr) == int(np.flatnonzero(exact == exact.max())[0])
+
+
+# ------------------------------------------------ Main Branch backward ---
+
+def test_attention_backward_matches_torch_autograd():
+    """Autograd of the same attention written with torch (fp64): one masked
+    softmax per (row, head) over the kept causal keys, on kept lists from a
+    real selection."""
+    rng = np.random.default_rng(21)
+    L, lq, H, G, d, B, k = 150, 40, 4, 2, 8, 16, 3
+    q, kk, vv = _rand(rng, lq, H, d), _rand(rng, L, G, d), _rand(rng, L, G, d)
+    q_idx, k_idx = _rand(rng, lq, G, 4), _rand(rng, L, G, 4)
+    pos = O.query_positions(lq, L)
+    idx = O.select_blocks(O.block_scores(q_idx, k_idx, pos, B), pos, B, k)
+    dout = _rand(rng, lq, H, d)
+    dq, dk, dv = O.sparse_attention_backward(q, kk, vv, idx, pos, B, 0.3, dout)
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(kk, requires_grad=True)
+    vt = torch.tensor(vv, requires_grad=True)
+    hpg = H // G
+    loss = torch.zeros((), dtype=torch.float64)
+    for t in range(lq):
+        for g in range(G):
+            mask = torch.zeros(L, dtype=torch.bool)
+            for j in idx[g, t]:
+                if j >= 0:
+                    mask[j * B:min((j + 1) * B, pos[t] + 1)] = True
+            for h in range(g * hpg, (g + 1) * hpg):
+                z = 0.3 * (kt[:, g, :] @ qt[t, h])
+                a = torch.softmax(z.masked_fill(~mask, float("-inf")), dim=0)
+                loss = loss + (torch.tensor(dout[t, h]) * (a @ vt[:, g, :])).sum()
+    loss.backward()
+    assert np.allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_backward_dense_is_sdpa_backward():
+    """k covering every block: the gradients of torch's causal SDPA (fp64),
+    with the GQA head map expanded."""
+    rng = np.random.default_rng(22)
+    L, H, G, d, B = 64, 4, 2, 8, 16
+    q, kk, vv = _rand(rng, L, H, d), _rand(rng, L, G, d), _rand(rng, L, G, d)
+    pos = O.query_positions(L, L)
+    nb = O.num_blocks(L, B)
+    idx = np.full((G, L, nb), -1, np.int32)
+    for t, p in enumerate(pos):
+        idx[:, t, :p // B + 1] = np.arange(p // B + 1)
+    dout = _rand(rng, L, H, d)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = O.sparse_attention_backward(q, kk, vv, idx, pos, B, scale, dout)
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(kk, requires_grad=True)
+    vt = torch.tensor(vv, requires_grad=True)
+    hpg = H // G
+    ke = kt.repeat_interleave(hpg, dim=1).transpose(0, 1)   # [H, L, d]
+    ve = vt.repeat_interleave(hpg, dim=1).transpose(0, 1)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt.transpose(0, 1)[None], ke[None], ve[None], is_causal=True, scale=scale)[0]
+    (out.transpose(0, 1) * torch.tensor(dout)).sum().backward()
+    assert np.allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    """Central differences of sum(dout * out) in a few coordinates of q, k, v."""
+    rng = np.random.default_rng(23)
+    L, lq, H, G, d, B, k = 80, 10, 2, 1, 4, 16, 2
+    q, kk, vv = _rand(rng, lq, H, d), _rand(rng, L, G, d), _rand(rng, L, G, d)
+    pos = O.query_positions(lq, L)
+    idx = O.select_blocks(O.block_scores(_rand(rng, lq, G, 4), _rand(rng, L, G, 4), pos, B),
+                          pos, B, k)
+    dout = _rand(rng, lq, H, d)
+    dq, dk, dv = O.sparse_attention_backward(q, kk, vv, idx, pos, B, 0.5, dout)
+
+    def loss(qq, k2, v2):
+        out, _ = O.sparse_attention(qq, k2, v2, idx, pos, B, 0.5)
+        return float((out * dout).sum())
+
+    eps = 1e-6
+    for (arr, grad, which) in ((q, dq, 0), (kk, dk, 1), (vv, dv, 2)):
+        for flat in rng.choice(arr.size, 6, replace=False):
+            ix = np.unravel_index(flat, arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[ix] += eps
+            am[ix] -= eps
+            args_p = [q, kk, vv]
+            args_m = [q, kk, vv]
+            args_p[which], args_m[which] = ap, am
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[ix]) < 1e-7
