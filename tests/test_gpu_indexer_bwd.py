@@ -115,3 +115,35 @@ def test_index_backward_prefill_32k():
                                grad[:, torch.from_numpy(rows), :].numpy())
     worst = _close(dq[gr].cpu().numpy(), dq_r, "dq_idx")
     _log(f"  sampled dq_idx worst error / tolerance {worst:.3g}")
+
+
+def test_training_calls_with_more_queries_than_keys():
+    """Rows at negative positions (a sequence with len_q > len_kv) have no
+    causal key: their block mass, loss, score gradient and index-query
+    gradient are 0 and they add nothing to dk_idx.  Every other output equals,
+    bit for bit, that of the trimmed problem (the sequence keeps its last
+    len_kv queries), whose rows the small-case tests check against the oracle."""
+    H, G, d, di, B, k = 8, 2, 128, 64, 128, 4
+    inp = W.random_case(78, [300, 400], [200, 500], H, G, d, di, B, k, "bf16", device=DEV)
+    cut = 100
+    trim = dict(inp)
+    trim["len_q"] = [200, 400]
+    trim["cu_q"] = torch.tensor([0, 200, 600], dtype=torch.int64, device=DEV)
+    for key in ("q_idx", "q"):
+        trim[key] = inp[key][cut:].contiguous()
+    res = []
+    for case in (inp, trim):
+        prob = C.problem_for(case, H, G, d, di, B, k, "bf16")
+        scores = msa.index_score(prob, case["q_idx"], case["k_idx"])
+        idx = msa.topk_select(prob, scores)
+        _, _, mass = msa.sparse_attn_fwd_mass(prob, case["q"], case["k"], case["v"], idx)
+        kl, grad = msa.indexer_kl(prob, scores, idx, mass)
+        dq, dk = msa.indexer_bwd(prob, case["q_idx"], case["k_idx"], idx, grad)
+        res.append((mass, kl, grad, dq, dk))
+    torch.cuda.synchronize()
+    (m_f, kl_f, g_f, dq_f, dk_f), (m_t, kl_t, g_t, dq_t, dk_t) = res
+    assert torch.all(m_f[:, :cut] == 0) and torch.all(kl_f[:, :cut] == 0)
+    assert torch.all(g_f[:, :cut] == 0) and torch.all(dq_f[:cut] == 0)
+    assert torch.equal(m_f[:, cut:], m_t) and torch.equal(kl_f[:, cut:], kl_t)
+    assert torch.equal(g_f[:, cut:], g_t) and torch.equal(dq_f[cut:], dq_t)
+    assert torch.equal(dk_f, dk_t)
