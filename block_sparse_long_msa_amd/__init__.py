@@ -37,6 +37,7 @@ SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_mass", "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
+            "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
             "msa_set_profile_events", "msa_status_string", "msa_last_error_message",
             "msa_abi_version")
 
@@ -98,6 +99,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_indexer_bwd_workspace_size.restype = st
     lib.msa_indexer_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_indexer_bwd.restype = st
+    lib.msa_sparse_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_sparse_attn_bwd_workspace_size.restype = st
+    lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+    lib.msa_sparse_attn_bwd.restype = st
     lib.msa_status_string.argtypes = [st]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_last_error_message.argtypes = []
@@ -314,6 +320,38 @@ def indexer_bwd(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
     return dq, dk
 
 
+def sparse_attn_bwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    block_idx: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                    dout: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[int] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """msa_sparse_attn_bwd: (dq [total_q, H, d], dk [total_kv, G, d], dv [total_kv, G, d])
+    fp32, the Main Branch backward for the upstream gradient `dout`, given the
+    forward's `out` and `lse` on the same inputs."""
+    dt = prob.torch_dtype
+    _need(q, "q", (prob.total_q, prob.H, prob.d), dt)
+    _need(k, "k", (prob.total_kv, prob.G, prob.d), dt)
+    _need(v, "v", (prob.total_kv, prob.G, prob.d), dt)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    _need(out, "out", (prob.total_q, prob.H, prob.d), dt)
+    _need(lse, "lse", (prob.total_q, prob.H), torch.float32)
+    _need(dout, "dout", (prob.total_q, prob.H, prob.d), dt)
+    dq = torch.empty((prob.total_q, prob.H, prob.d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((prob.total_kv, prob.G, prob.d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((prob.total_kv, prob.G, prob.d), dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_sparse_attn_bwd_workspace_size(prob.ref(), ctypes.byref(n)))
+    if workspace is None and n.value > 0:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q.device) if stream is None else stream
+    _check(load_library().msa_sparse_attn_bwd(prob.ref(), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(dout),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                              wbytes, s))
+    return dq, dk, dv
+
+
 class ProfileEvents:
     """Per-kernel timing via msa_set_profile_events: `with ProfileEvents(n) as ev:`
     around one library call; afterwards ev.events[i] was recorded right after
@@ -351,3 +389,4 @@ msa_sparse_attn_fwd = sparse_attn_fwd
 msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass
 msa_indexer_kl = indexer_kl
 msa_indexer_bwd = indexer_bwd
+msa_sparse_attn_bwd = sparse_attn_bwd

@@ -330,6 +330,63 @@ msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const
                   "index_bwd");
 }
 
+msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = msa::attn_bwd_workspace_bytes(d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const void *k,
+                                 const void *v, const int32_t *block_idx, const void *out,
+                                 const float *lse, const void *dout, float *dq, float *dk,
+                                 float *dv, void *workspace, size_t workspace_bytes_given,
+                                 void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (prob->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "the attention backward takes bf16 tensors");
+  if (!msa::attn_bwd_supported(d))
+    return fail(MSA_ERR_BAD_SHAPE,
+                "the attention backward needs head_dim 128, block_size 128 and a head count "
+                "per KV group that divides 64");
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q, "q", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k, "k", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(v, "v", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(lse, "lse", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dout, "dout", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dq, "dq", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dk, "dk", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(dv, "dv", any_kv)) != MSA_SUCCESS) return st;
+  if (d.total_q * (int64_t)d.top_k * d.H >= (int64_t)INT32_MAX)
+    return fail(MSA_ERR_BAD_SHAPE, "total_q * top_k * num_q_heads must be below 2^31");
+  if (msa::index_bwd_hist_bytes(d) > 64 * 1024)
+    return fail(MSA_ERR_BAD_SHAPE,
+                "num_seqs * ceil(max_kv_len / block_size) must be at most 16384 for the "
+                "attention backward (one LDS histogram bin per (sequence, block))");
+  const size_t need = msa::attn_bwd_workspace_bytes(d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q && !any_kv) return ok();
+  return launched(msa::launch_attn_bwd_bf16(
+                      d, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                      static_cast<const uint16_t *>(v), block_idx,
+                      static_cast<const uint16_t *>(out), lse,
+                      static_cast<const uint16_t *>(dout), dq, dk, dv, workspace,
+                      reinterpret_cast<hipStream_t>(stream)),
+                  "attn_bwd");
+}
+
 const char *msa_status_string(msa_status_t status) {
   switch (status) {
     case MSA_SUCCESS: return "success";

@@ -1,0 +1,524 @@
+// Backward of the Main Branch ("MiniMax Sparse Attention" page, Summary,
+// paragraph 2: exact softmax attention restricted to the keys of the kept
+// blocks).  For row t and head h of group g, with z_s = scale <q, k_s> over
+// the kept causal keys, P = softmax(z) (rebuilt from the forward's LSE) and
+// an upstream gradient dO of the output:
+//   D        = <dO, O>                       (= sum_s P_s <dO, v_s>)
+//   dS_s     = P_s (<dO, v_s> - D)
+//   dv_s    += P_s dO          dk_s += scale dS_s q          dq += scale dS_s k_s
+//
+// KV-major, like the forward's KV-major schedule (the page's kernels loop
+// KV-outer): every (sequence, group, kept block) bucket lists the (row, slot)
+// entries that kept the block, the current block included (its causal mask
+// is applied per row), in (row, slot) order (buckets.hpp).  A work item is
+// up to kSteps steps of one bucket's list; a step is 64 (query, head) rows.
+// The item keeps its block's K^T in LDS and each wave's share of K and V in
+// registers for all its steps, and accumulates dK, dV of the block in
+// registers; every step writes the rows' dQ contribution of this block into
+// the row's slot (bf16), which a merge then sums in slot order.  No
+// floating-point atomics: every sum has a fixed order.
+//
+// Kernels, in launch order:
+//   ab_zero      dk, dv <- 0 (keys no slot takes keep 0)
+//   ab_dsum      D = rowsum(dO * O) per (row, head)
+//   bk_*         bucket lists and work items (buckets.hpp)
+//   ab_item      per work item: S = Q K^T, dP = dO V^T, P, dS with MFMA; dV^T
+//                += dO^T P, dK^T += Q^T dS, dQ^T = K^T dS^T
+//   ab_reduce    per bucket of several items: dk, dv = the items' partial
+//                sums added in item order
+//   ab_dq        per (row, head): dq = scale * sum of its slots' dQ, in slot order
+#include <algorithm>
+
+#include "buckets.hpp"
+#include "launch.hpp"
+#include "msa_common.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kD = 128;           // head dimension
+constexpr int kBS = 128;          // block size
+constexpr int kRows = 64;         // (query, head) rows per step
+constexpr int kSteps = 32;        // steps per work item
+constexpr int kLd = kD + 8;       // padded LDS row (bf16) of Q, dO, dS and K^T
+constexpr int kLt = kRows + 8;    // padded LDS row of Q^T, dO^T, P^T and dS^T
+constexpr int kItemThreads = 512;  // 8 waves: 4 key groups x 2 halves
+
+struct AbWs {
+  int32_t *cnt, *base, *lists, *ibase, *pbase;
+  float *dsum;        // [total_q][H] rowsum(dO * O)
+  uint16_t *dq_part;  // [total_q * K * H][d] bf16: the dQ of each kept slot, unscaled
+  float *part;        // [max_parts][2][BS][d]: dV, dK (unscaled) of the items of shared buckets
+  int64_t ntiles, nbk_g, nent_g, max_items, max_parts;
+  int32_t per_item;
+  size_t total_bytes;
+};
+
+size_t ab_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+AbWs ab_carve(const Dims &p, void *base) {
+  AbWs w;
+  w.nent_g = p.total_q * (int64_t)p.top_k;
+  w.ntiles = (w.nent_g + kBucketTile - 1) / kBucketTile;
+  w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
+  w.per_item = kSteps * (kRows / (p.H / p.G));
+  const int64_t nent = (int64_t)p.G * w.nent_g;
+  // every bucket has one item more than its full items; a bucket with
+  // partial slots has more than per_item entries
+  w.max_items = nent / w.per_item + std::min<int64_t>((int64_t)p.G * w.nbk_g, nent) + 1;
+  w.max_parts = 2 * (nent / w.per_item) + 1;
+  size_t off = 0;
+  char *c = static_cast<char *>(base);
+  auto take = [&](size_t bytes) {
+    char *r = c == nullptr ? nullptr : c + off;
+    off += ab_align(bytes);
+    return r;
+  };
+  w.cnt = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)p.G * w.ntiles * w.nbk_g));
+  w.base = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1)));
+  w.lists = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)nent));
+  w.ibase = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1)));
+  w.pbase = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * ((size_t)p.G * w.nbk_g + 1)));
+  w.dsum = reinterpret_cast<float *>(take(sizeof(float) * (size_t)p.total_q * p.H));
+  w.dq_part = reinterpret_cast<uint16_t *>(
+      take(sizeof(uint16_t) * (size_t)nent / p.G * p.H * kD));
+  w.part = reinterpret_cast<float *>(take(sizeof(float) * (size_t)w.max_parts * 2 * kBS * kD));
+  w.total_bytes = off;
+  return w;
+}
+
+__global__ __launch_bounds__(256) void ab_zero_kernel(float *__restrict__ x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    x[i] = 0.f;
+}
+
+// 16 lanes per (row, head), 8 channels each, then a 16-lane sum.
+__global__ __launch_bounds__(256) void ab_dsum_kernel(const uint16_t *__restrict__ out,
+                                                      const uint16_t *__restrict__ dout,
+                                                      float *__restrict__ dsum, int64_t nrows) {
+  const int64_t rh = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (rh < nrows) {
+    const u32x4 o = ld16(out + rh * kD + part * 8);
+    const u32x4 g = ld16(dout + rh * kD + part * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc = fmaf(bf16_lo(o[u]), bf16_lo(g[u]), acc);
+      acc = fmaf(bf16_hi(o[u]), bf16_hi(g[u]), acc);
+    }
+  }
+  acc += shfl_xor_f(acc, 8);
+  acc += shfl_xor_f(acc, 4);
+  acc += shfl_xor_f(acc, 2);
+  acc += shfl_xor_f(acc, 1);
+  if (part == 0 && rh < nrows) dsum[rh] = acc;
+}
+
+__device__ __forceinline__ uint16_t lo16(uint32_t w) { return (uint16_t)(w & 0xffffu); }
+__device__ __forceinline__ uint16_t hi16(uint32_t w) { return (uint16_t)(w >> 16); }
+__device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+
+// One work-group per work item, 8 waves; wave wv has kg = wv % 4 and
+// hf = wv / 4.  Per step (64 rows):
+//   phase 1  S = Q K^T and dP = dO V^T for keys 32 kg .. and rows 32 hf ..
+//            (K and V of the wave's keys in registers), then P and dS; P^T
+//            and dS^T go to LDS [key][row], dS also to LDS [row][key]
+//   phase 2  dV^T += dO^T P and dK^T += Q^T dS for channels 64 hf .. 64 hf + 63
+//            and keys 32 kg .. over all 64 rows (each (key, channel) has one
+//            owner, so no cross-wave sum); dQ^T = K^T dS^T for channels
+//            32 kg .. and rows 32 hf .. over all 128 keys -> the rows' slots
+// MFMA 32x32x16 layouts as in msa_common.hpp.  Q and dO rows of the next
+// step are loaded into registers during a step; the row-major copies are
+// written after phase 2 and the transposed ones in phase 1 of their step
+// (no wave reads those in phase 1), so a step needs two barriers.
+__global__ __launch_bounds__(kItemThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+               const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
+               const float *__restrict__ lse, const float *__restrict__ dsum,
+               const int32_t *__restrict__ base, const int32_t *__restrict__ ibase,
+               const int32_t *__restrict__ pbase, const int32_t *__restrict__ lists,
+               uint16_t *__restrict__ dq_part, float *__restrict__ dk, float *__restrict__ dv,
+               float *__restrict__ part, const int64_t *__restrict__ cu_q,
+               const int64_t *__restrict__ cu_kv, int G, int H, int K, int nb_max,
+               int64_t nbuckets, int per_item, float scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kD * kLd];     // K^T [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kRows * kLd];  // Q [row][d]
+  __shared__ __attribute__((aligned(16))) uint16_t os[kRows * kLd];  // dO [row][d]
+  __shared__ __attribute__((aligned(16))) uint16_t ss[kRows * kLd];  // dS [row][key]
+  __shared__ __attribute__((aligned(16))) uint16_t qt[kD * kLt];     // Q^T [d][row]
+  __shared__ __attribute__((aligned(16))) uint16_t ot[kD * kLt];     // dO^T [d][row]
+  __shared__ __attribute__((aligned(16))) uint16_t pt[kBS * kLt];    // P^T [key][row]
+  __shared__ __attribute__((aligned(16))) uint16_t st_[kBS * kLt];   // dS^T [key][row]
+  __shared__ float m_lse[kRows], m_d[kRows];  // log2-domain LSE (+inf: no row), D
+  __shared__ int32_t m_pos[kRows], m_off[kRows];  // position (-1: no row), dQ slot row (-1)
+
+  const int32_t w = (int32_t)blockIdx.x;
+  if (w >= ibase[nbuckets]) return;  // past the last item
+  int64_t lo = 0, hi = nbuckets - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (ibase[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int64_t gb = lo;  // g * nbk_g + b * nb_max + j
+  const int32_t it = w - ibase[gb], nit = ibase[gb + 1] - ibase[gb];
+  const int32_t n_b = base[gb + 1] - base[gb];
+  const int32_t first = base[gb] + it * per_item, n = min(per_item, n_b - it * per_item);
+  const int64_t nbk_g = nbuckets / G;
+  const int g = (int)(gb / nbk_g);
+  const int64_t bkt = gb - (int64_t)g * nbk_g;
+  const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
+  const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
+  const int64_t q0 = cu_q[b], base_pos = lkv - (cu_q[b + 1] - q0);
+  const int64_t s0 = (int64_t)j * kBS;
+  const int nkeys = (int)min<int64_t>(kBS, lkv - s0);
+  const int hpg = H / G, E = kRows / hpg;
+  const int nsteps = (n + E - 1) / E;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kg = wv & 3, hf = wv >> 2;
+  const int li = lane & 31, hh = lane >> 5;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // K^T of the block, zero past the sequence's keys
+  {
+    const int key = tid & 127;
+    const uint16_t *src = k + ((kv0 + s0 + min(key, nkeys - 1)) * G + g) * (int64_t)kD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = (tid >> 7) + 4 * u;
+      const u32x4 x = key < nkeys ? ld16(src + pc * 8) : zero4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        kt[(pc * 8 + 2 * m) * kLd + key] = lo16(x[m]);
+        kt[(pc * 8 + 2 * m + 1) * kLd + key] = hi16(x[m]);
+      }
+    }
+  }
+  // K and V of this wave's 32 keys as B operands of S = Q K^T and dP = dO V^T
+  u32x4 kw[8], vw[8];
+  {
+    const int key = 32 * kg + li;
+    const int64_t roff = ((kv0 + s0 + min(key, nkeys - 1)) * G + g) * (int64_t)kD + 8 * hh;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      kw[x] = key < nkeys ? ld16(k + roff + 16 * x) : zero4;
+      vw[x] = key < nkeys ? ld16(v + roff + 16 * x) : zero4;
+    }
+  }
+
+  // Rows of step st: thread tid loads pieces (tid / 64) and (tid / 64) + 8 of
+  // row tid % 64 of Q and dO; the first wave also loads the row's metadata.
+  u32x4 fq[2], fo[2];
+  float f_lse = 0.f, f_d = 0.f;
+  int f_pos = -1, f_off = -1;
+  auto fetch = [&](int st) {
+    const int r = tid & 63;
+    const int x = st * E + r / hpg;
+    if (x < n) {
+      const int32_t e = lists[first + x];
+      const int64_t t = e / K;
+      const int h = g * hpg + r % hpg;
+      const int64_t roff = (t * H + h) * (int64_t)kD;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pc = (tid >> 6) + 8 * u;
+        fq[u] = ld16(q + roff + pc * 8);
+        fo[u] = ld16(dout + roff + pc * 8);
+      }
+      if (tid < 64) {
+        f_lse = lse[t * H + h] * kLog2e;
+        f_d = dsum[t * H + h];
+        f_pos = (int)(base_pos + (t - q0));
+        f_off = e * H + h;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) fq[u] = fo[u] = zero4;
+      f_lse = __builtin_inff();
+      f_d = 0.f;
+      f_pos = -1;
+      f_off = -1;
+    }
+  };
+  auto stage_rows = [&]() {  // row-major Q, dO and the metadata
+    const int r = tid & 63;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = (tid >> 6) + 8 * u;
+      st16(&qs[r * kLd + pc * 8], fq[u]);
+      st16(&os[r * kLd + pc * 8], fo[u]);
+    }
+    if (tid < 64) {
+      m_lse[r] = f_lse;
+      m_d[r] = f_d;
+      m_pos[r] = f_pos;
+      m_off[r] = f_off;
+    }
+  };
+  auto stage_cols = [&]() {  // transposed Q, dO
+    const int r = tid & 63;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = (tid >> 6) + 8 * u;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        qt[(pc * 8 + 2 * m) * kLt + r] = lo16(fq[u][m]);
+        qt[(pc * 8 + 2 * m + 1) * kLt + r] = hi16(fq[u][m]);
+        ot[(pc * 8 + 2 * m) * kLt + r] = lo16(fo[u][m]);
+        ot[(pc * 8 + 2 * m + 1) * kLt + r] = hi16(fo[u][m]);
+      }
+    }
+  };
+
+  f32x16 acc_v[2], acc_k[2];  // dV^T, dK^T tiles [channel][key] of channels 64 hf ..
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_v[x][r] = acc_k[x][r] = 0.f;
+  const float c2 = scale * kLog2e;
+  const int64_t keypos = s0 + 32 * kg + li;
+
+  if (nsteps > 0) {
+    fetch(0);
+    stage_rows();
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();
+    stage_cols();
+    if (st + 1 < nsteps) fetch(st + 1);
+    // phase 1: S and dP for rows 32 hf .., keys 32 kg ..
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const u32x4 aq = ld16(&qs[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
+      const u32x4 ao = ld16(&os[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
+      sacc = mfma32x32x16(as_bf16x8(aq), as_bf16x8(kw[x]), sacc);
+      pacc = mfma32x32x16(as_bf16x8(ao), as_bf16x8(vw[x]), pacc);
+    }
+    // register r holds row 32 hf + 8 (r / 4) + 4 hh + r % 4 and key keypos
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * hf + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float pv = keypos > (int64_t)m_pos[row] ? 0.f : exp2f(sacc[r] * c2 - m_lse[row]);
+      sacc[r] = pv;
+      pacc[r] = pv * (pacc[r] - m_d[row]);
+    }
+    const int my_off = m_off[32 * hf + li];  // dQ row of this lane, read before it is restaged
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int row = 32 * hf + 8 * q4 + 4 * hh;  // rows row .. row + 3
+      const u32x2 pv = {pack_bf16x2(sacc[4 * q4], sacc[4 * q4 + 1]),
+                        pack_bf16x2(sacc[4 * q4 + 2], sacc[4 * q4 + 3])};
+      const u32x2 dsv = {pack_bf16x2(pacc[4 * q4], pacc[4 * q4 + 1]),
+                         pack_bf16x2(pacc[4 * q4 + 2], pacc[4 * q4 + 3])};
+      *reinterpret_cast<u32x2 *>(&pt[(32 * kg + li) * kLt + row]) = pv;
+      *reinterpret_cast<u32x2 *>(&st_[(32 * kg + li) * kLt + row]) = dsv;
+      ss[row * kLd + 32 * kg + li] = lo16(dsv[0]);
+      ss[(row + 1) * kLd + 32 * kg + li] = hi16(dsv[0]);
+      ss[(row + 2) * kLd + 32 * kg + li] = lo16(dsv[1]);
+      ss[(row + 3) * kLd + 32 * kg + li] = hi16(dsv[1]);
+    }
+    __syncthreads();
+    // phase 2: dV^T += dO^T P, dK^T += Q^T dS (channels 64 hf .., keys 32 kg .., 64 rows)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const u32x4 bp = ld16(&pt[(32 * kg + li) * kLt + 16 * x + 8 * hh]);
+      const u32x4 bs = ld16(&st_[(32 * kg + li) * kLt + 16 * x + 8 * hh]);
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int ch = 64 * hf + 32 * y + li;
+        const u32x4 ao = ld16(&ot[ch * kLt + 16 * x + 8 * hh]);
+        const u32x4 aq = ld16(&qt[ch * kLt + 16 * x + 8 * hh]);
+        acc_v[y] = mfma32x32x16(as_bf16x8(ao), as_bf16x8(bp), acc_v[y]);
+        acc_k[y] = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bs), acc_k[y]);
+      }
+    }
+    // dQ^T = K^T dS^T for channels 32 kg .., rows 32 hf .. (all 128 keys)
+    f32x16 qacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const u32x4 a = ld16(&kt[(32 * kg + li) * kLd + 16 * x + 8 * hh]);
+      const u32x4 bq = ld16(&ss[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
+      qacc = mfma32x32x16(as_bf16x8(a), as_bf16x8(bq), qacc);
+    }
+    // lane holds row 32 hf + li, channels 32 kg + 8 (r / 4) + 4 hh + r % 4
+    if (my_off >= 0) {
+      uint16_t *dst = dq_part + (int64_t)my_off * kD + 32 * kg + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 val = {pack_bf16x2(qacc[4 * q4], qacc[4 * q4 + 1]),
+                           pack_bf16x2(qacc[4 * q4 + 2], qacc[4 * q4 + 3])};
+        *reinterpret_cast<u32x2 *>(dst + 8 * q4) = val;
+      }
+    }
+    if (st + 1 < nsteps) stage_rows();
+  }
+
+  const int key = 32 * kg + li;
+  if (key >= nkeys) return;
+  float *dvp, *dkp;
+  float kscale;
+  if (nit == 1) {
+    dvp = dv + ((kv0 + s0 + key) * G + g) * (int64_t)kD;
+    dkp = dk + ((kv0 + s0 + key) * G + g) * (int64_t)kD;
+    kscale = scale;
+  } else {
+    float *pp = part + (int64_t)(pbase[gb] + it) * 2 * kBS * kD;
+    dvp = pp + key * kD;
+    dkp = pp + (kBS + key) * kD;
+    kscale = 1.f;
+  }
+  // lane holds key 32 kg + li, channels 64 hf + 32 y + 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+  for (int y = 0; y < 2; ++y)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int dc = 64 * hf + 32 * y + 8 * q4 + 4 * hh;
+      const f32x4 vv = {acc_v[y][4 * q4], acc_v[y][4 * q4 + 1], acc_v[y][4 * q4 + 2],
+                        acc_v[y][4 * q4 + 3]};
+      const f32x4 kk = {acc_k[y][4 * q4] * kscale, acc_k[y][4 * q4 + 1] * kscale,
+                        acc_k[y][4 * q4 + 2] * kscale, acc_k[y][4 * q4 + 3] * kscale};
+      *reinterpret_cast<f32x4 *>(dvp + dc) = vv;
+      *reinterpret_cast<f32x4 *>(dkp + dc) = kk;
+    }
+}
+
+// One work-group per bucket of several items: dv, dk = the items' partials
+// added in item order (dk scaled).
+__global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restrict__ ibase,
+                                                        const int32_t *__restrict__ pbase,
+                                                        const float *__restrict__ part,
+                                                        float *__restrict__ dk,
+                                                        float *__restrict__ dv,
+                                                        const int64_t *__restrict__ cu_kv, int G,
+                                                        int nb_max, int64_t nbk_g, float scale) {
+  const int64_t gb = blockIdx.x;
+  const int32_t nit = ibase[gb + 1] - ibase[gb];
+  if (nit <= 1) return;
+  const int g = (int)(gb / nbk_g);
+  const int64_t bkt = gb - (int64_t)g * nbk_g;
+  const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
+  const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
+  const int64_t s0 = (int64_t)j * kBS;
+  const int nkeys = (int)min<int64_t>(kBS, lkv - s0);
+  const float *src = part + (int64_t)pbase[gb] * 2 * kBS * kD;
+  for (int x = threadIdx.x * 4; x < nkeys * kD; x += 256 * 4) {
+    f32x4 av = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t i = 0; i < nit; ++i) {
+      av += *reinterpret_cast<const f32x4 *>(src + (int64_t)i * 2 * kBS * kD + x);
+      ak += *reinterpret_cast<const f32x4 *>(src + (int64_t)i * 2 * kBS * kD + kBS * kD + x);
+    }
+    const int s = x / kD, c = x - s * kD;
+    const int64_t o = ((kv0 + s0 + s) * G + g) * (int64_t)kD + c;
+    *reinterpret_cast<f32x4 *>(dv + o) = av;
+    *reinterpret_cast<f32x4 *>(dk + o) = ak * scale;
+  }
+}
+
+// 16 lanes per (row, head), 8 channels each: dq = scale * sum over the row's
+// kept slots (in slot order) of the slot's dQ.  Slots that are padding or
+// whose block holds no causal key of the row add nothing.
+__global__ __launch_bounds__(256) void ab_dq_kernel(const uint16_t *__restrict__ dq_part,
+                                                    const int32_t *__restrict__ block_idx,
+                                                    float *__restrict__ dq,
+                                                    const int64_t *__restrict__ cu_q,
+                                                    const int64_t *__restrict__ cu_kv,
+                                                    int num_seqs, int H, int G, int K,
+                                                    int64_t total_q, int nb_max, float scale) {
+  const int64_t rh = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (rh >= total_q * H) return;
+  const int part = threadIdx.x & 15;
+  const int64_t row = rh / H;
+  const int h = (int)(rh - row * H);
+  const int g = h / (H / G);
+  const int b = find_seq(cu_q, num_seqs, row);
+  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
+  const int64_t pos = sq.base + (row - sq.q0);
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  const int32_t *bi = block_idx + ((int64_t)g * total_q + row) * K;
+  for (int i = 0; i < K; ++i) {
+    const int jb = bi[i];
+    if (jb < 0 || jb >= nb_max || pos < 0 || (int64_t)jb * kBS > pos) continue;
+    const u32x4 x = ld16(dq_part + (((row * K + i) * H) + h) * (int64_t)kD + part * 8);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] += bf16_lo(x[m]);
+      acc[2 * m + 1] += bf16_hi(x[m]);
+    }
+  }
+  float *dst = dq + rh * kD + part * 8;
+  const f32x4 a = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
+  const f32x4 c = {acc[4] * scale, acc[5] * scale, acc[6] * scale, acc[7] * scale};
+  *reinterpret_cast<f32x4 *>(dst) = a;
+  *reinterpret_cast<f32x4 *>(dst + 4) = c;
+}
+
+void zero_fill(float *x, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  const unsigned zg = (unsigned)std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(ab_zero_kernel, dim3(zg), dim3(256), 0, s, x, n);
+}
+
+}  // namespace
+
+bool attn_bwd_supported(const Dims &p) {
+  const int hpg = p.G > 0 ? p.H / p.G : 0;
+  return p.d == kD && p.B == kBS && hpg > 0 && hpg <= kRows && kRows % hpg == 0;
+}
+
+size_t attn_bwd_workspace_bytes(const Dims &p) { return ab_carve(p, nullptr).total_bytes; }
+
+hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                const uint16_t *v, const int32_t *block_idx, const uint16_t *out,
+                                const float *lse, const uint16_t *dout, float *dq, float *dk,
+                                float *dv, void *workspace, hipStream_t s) {
+  AbWs w = ab_carve(p, workspace);
+  zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
+  zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
+  profile_mark(s);
+  if (p.total_q == 0) return hipGetLastError();
+  if (p.total_kv == 0) {
+    zero_fill(dq, p.total_q * p.H * (int64_t)kD, s);
+    profile_mark(s);
+    return hipGetLastError();
+  }
+  const int64_t nrows = p.total_q * p.H;
+  hipLaunchKernelGGL(ab_dsum_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, out,
+                     dout, w.dsum, nrows);
+  profile_mark(s);
+  const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
+  hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
+                     block_idx, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, p.top_k, p.total_q,
+                     p.nb_max, p.B, w.ntiles, w.nbk_g);
+  const int64_t ncol = (int64_t)p.G * w.nbk_g;
+  hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
+                     w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, w.per_item);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
+  hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
+                     block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
+                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
+  profile_mark(s);
+  hipLaunchKernelGGL(ab_item_kernel, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k,
+                     v, dout, lse, w.dsum, w.base, w.ibase, w.pbase, w.lists, w.dq_part, dk, dv,
+                     w.part, p.cu_q, p.cu_kv, p.G, p.H, p.top_k, p.nb_max, ncol, w.per_item,
+                     p.scale);
+  profile_mark(s);
+  hipLaunchKernelGGL(ab_reduce_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.ibase, w.pbase,
+                     w.part, dk, dv, p.cu_kv, p.G, p.nb_max, w.nbk_g, p.scale);
+  profile_mark(s);
+  hipLaunchKernelGGL(ab_dq_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s,
+                     w.dq_part, block_idx, dq, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k,
+                     p.total_q, p.nb_max, p.scale);
+  profile_mark(s);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -12,14 +12,9 @@
 //
 // Deterministic, without floating-point atomics:
 //   ib_zero      dk_idx <- 0 (keys no slot takes keep 0)
-//   ib_count     per tile of TE consecutive (row, slot) entries of a group:
-//                entries per bucket (sequence, block) in an LDS histogram
-//                (integer atomics, counting only); invalid slots get arg-max -1
-//   ib_colscan   per bucket: exclusive offsets of the tiles, and its total
-//   ib_basescan  exclusive scan of the bucket totals
-//   ib_scatter   per tile, one wave walks its entries in order and writes each
-//                to its bucket's list at tile offset + running count + rank
-//                among equal buckets: every list ends up in (row, slot) order
+//   bk_count, bk_colscan, bk_basescan, bk_scatter (buckets.hpp): the list of
+//                every bucket (sequence, block) in (row, slot) order, split
+//                into items of kIE entries; invalid slots get arg-max -1
 //   ib_item      per work item (at most kIE consecutive entries of one
 //                bucket's list, so popular blocks are shared out): for each
 //                entry in list order the arg-max over the causal keys (key
@@ -33,12 +28,12 @@
 #include <algorithm>
 
 #include "launch.hpp"
+#include "buckets.hpp"
 #include "msa_common.hpp"
 
 namespace msa {
 namespace {
 
-constexpr int kTE = 4096;  // entries per counting / scatter tile
 constexpr int kIE = 1024;  // entries per work item of the arg-max pass
 
 struct IbWs {
@@ -58,7 +53,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 IbWs ib_carve(const Dims &p, void *base) {
   IbWs w;
   w.nent_g = p.total_q * (int64_t)p.top_k;
-  w.ntiles = (w.nent_g + kTE - 1) / kTE;
+  w.ntiles = (w.nent_g + kBucketTile - 1) / kBucketTile;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
   size_t off = 0;
   char *c = static_cast<char *>(base);
@@ -98,144 +93,9 @@ __device__ __forceinline__ float dot_step(float acc, float q, float k, float) {
   return acc + q * k;
 }
 
-// Bucket of entry e (= row * K + slot) of group g, or -1 when the slot is
-// padding or its block holds no causal key of the row.  The bucket numbers
-// blocks of every sequence: b * nb_max + j.  Also returns the row, the
-// sequence's first key row and the row's position.
-struct EntryInfo {
-  int bucket;
-  int64_t row, kv0, pos;
-};
-__device__ __forceinline__ EntryInfo entry_info(const int32_t *__restrict__ block_idx,
-                                                const int64_t *__restrict__ cu_q,
-                                                const int64_t *__restrict__ cu_kv, int num_seqs,
-                                                int g, int64_t e, int K, int64_t total_q,
-                                                int nb_max, int BS) {
-  EntryInfo r;
-  r.row = e / K;
-  const int j = block_idx[(int64_t)g * total_q * K + e];
-  const int b = find_seq(cu_q, num_seqs, r.row);
-  const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
-  r.kv0 = sq.kv0;
-  r.pos = sq.base + (r.row - sq.q0);
-  const bool ok = j >= 0 && j < nb_max && r.pos >= 0 && (int64_t)j * BS <= r.pos;
-  r.bucket = ok ? b * nb_max + j : -1;
-  return r;
-}
-
 __global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     x[i] = 0.f;
-}
-
-__global__ __launch_bounds__(256) void ib_count_kernel(
-    const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, int32_t *__restrict__ cnt, int32_t *__restrict__ amax,
-    int num_seqs, int K, int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
-  extern __shared__ int32_t hist[];  // [nbk_g]
-  const int g = blockIdx.y;
-  const int64_t tile = blockIdx.x;
-  for (int64_t x = threadIdx.x; x < nbk_g; x += 256) hist[x] = 0;
-  __syncthreads();
-  const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * kTE);
-  for (int64_t e = tile * kTE + threadIdx.x; e < e1; e += 256) {
-    const EntryInfo ei = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS);
-    if (ei.bucket >= 0) atomicAdd(&hist[ei.bucket], 1);
-    else amax[(int64_t)g * nent + e] = -1;
-  }
-  __syncthreads();
-  int32_t *dst = cnt + ((int64_t)g * ntiles + tile) * nbk_g;
-  for (int64_t x = threadIdx.x; x < nbk_g; x += 256) dst[x] = hist[x];
-}
-
-// One thread per (group, bucket): tile counts -> exclusive tile offsets.
-__global__ __launch_bounds__(256) void ib_colscan_kernel(int32_t *__restrict__ cnt,
-                                                         int32_t *__restrict__ total,
-                                                         int32_t *__restrict__ items,
-                                                         int32_t *__restrict__ parts, int G,
-                                                         int64_t ntiles, int64_t nbk_g) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (int64_t)G * nbk_g) return;
-  const int64_t g = x / nbk_g, bk = x - g * nbk_g;
-  int32_t run = 0;
-  for (int64_t t = 0; t < ntiles; ++t) {
-    int32_t *c = cnt + (g * ntiles + t) * nbk_g + bk;
-    const int32_t v = *c;
-    *c = run;
-    run += v;
-  }
-  total[x] = run;
-  const int32_t ni = (run + kIE - 1) / kIE;
-  items[x] = ni;
-  parts[x] = ni > 1 ? ni : 0;
-}
-
-// One work-group: exclusive scan of n bucket totals in place, base[n] = sum.
-__global__ __launch_bounds__(1024) void ib_basescan_kernel(int32_t *__restrict__ base, int64_t n) {
-  __shared__ int32_t part[1024];
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t a = min(n, (int64_t)threadIdx.x * per), b = min(n, a + per);
-  int32_t s = 0;
-  for (int64_t i = a; i < b; ++i) s += base[i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    base[n] = run;
-  }
-  __syncthreads();
-  int32_t run = part[threadIdx.x];
-  for (int64_t i = a; i < b; ++i) {
-    const int32_t v = base[i];
-    base[i] = run;
-    run += v;
-  }
-}
-
-// One wave per (tile, group).  Chunks of 64 entries are placed in order: all
-// lanes holding the same bucket are placed in one step, ranked by lane, after
-// the tile's earlier entries of that bucket (a running count in LDS).
-__global__ __launch_bounds__(64) void ib_scatter_kernel(
-    const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, const int32_t *__restrict__ cnt,
-    const int32_t *__restrict__ base, int32_t *__restrict__ lists, int num_seqs, int K,
-    int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
-  extern __shared__ int32_t run[];  // [nbk_g] next list position of each bucket
-  const int g = blockIdx.y;
-  const int64_t tile = blockIdx.x;
-  const int lane = threadIdx.x;
-  // bucket start (global over groups) + this tile's offset in the bucket
-  const int32_t *toff = cnt + ((int64_t)g * ntiles + tile) * nbk_g;
-  const int32_t *gbase = base + (int64_t)g * nbk_g;
-  for (int64_t x = lane; x < nbk_g; x += 64) run[x] = gbase[x] + toff[x];
-  __syncthreads();
-  const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * kTE);
-  for (int64_t c0 = tile * kTE; c0 < e1; c0 += 64) {
-    const int64_t e = c0 + lane;
-    int bk = -1;
-    if (e < e1) bk = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS).bucket;
-    bool active = bk >= 0;
-    uint64_t act = ballot64(active);
-    while (act != 0) {
-      const int leader = (int)__builtin_ctzll(act);
-      const int bl = __builtin_amdgcn_readlane(bk, leader);
-      const uint64_t m = ballot64(active && bk == bl);
-      const int32_t start = __builtin_amdgcn_readfirstlane(run[bl]);
-      if (active && bk == bl) {
-        lists[start + mbcnt64(m)] = (int32_t)e;
-        active = false;
-      }
-      if (lane == 0) run[bl] = start + __popcll(m);
-      act = ballot64(active);
-    }
-  }
 }
 
 // One work-group per work item: entries [it * kIE, min(n, (it + 1) * kIE))
@@ -547,18 +407,18 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   }
   profile_mark(s);
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
-  hipLaunchKernelGGL(ib_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
+  hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.amax, p.num_seqs, p.top_k, p.total_q,
                      p.nb_max, p.B, w.ntiles, w.nbk_g);
   profile_mark(s);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
-  hipLaunchKernelGGL(ib_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
-                     w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g);
-  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
-  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
-  hipLaunchKernelGGL(ib_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
+  hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
+                     w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, kIE);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
+  hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
   profile_mark(s);
-  hipLaunchKernelGGL(ib_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
+  hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
                      p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
   profile_mark(s);

@@ -66,6 +66,14 @@ hipError_t launch_index_bwd(const Dims &p, bool bf16, const void *q_idx, const v
                             const int32_t *block_idx, const float *grad, float *dq_idx,
                             float *dk_idx, void *workspace, hipStream_t s);
 
+// Backward of the Main Branch attention, bf16 (attn_bwd.hip).
+bool attn_bwd_supported(const Dims &p);  // head dim 128, block size 128, 64 % (H/G) == 0
+size_t attn_bwd_workspace_bytes(const Dims &p);
+hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                const uint16_t *v, const int32_t *block_idx, const uint16_t *out,
+                                const float *lse, const uint16_t *dout, float *dq, float *dk,
+                                float *dv, void *workspace, hipStream_t s);
+
 // Indexer KL objective over the kept blocks (indexer_kl.hip).
 hipError_t launch_indexer_kl(const Dims &p, const float *scores, const int32_t *block_idx,
                              const float *block_mass, float *kl, float *grad, hipStream_t s);

@@ -211,6 +211,34 @@ msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const
                              float *dk_idx, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Backward of the Main Branch attention (page: Summary, paragraph 2; exact
+ * softmax attention over the keys of the kept blocks, so its gradient is
+ * that of dense attention restricted to the same keys).  Inputs are those of
+ * msa_sparse_attn_fwd plus its results and the upstream gradient: out
+ * [total_q, H, d] and lse [total_q, H] from msa_sparse_attn_fwd (or
+ * msa_sparse_attn_fwd_mass) on the same q, k, v and block_idx, and dout
+ * [total_q, H, d].  With P the attention weights (rebuilt as
+ * exp(z - lse)), D = <dout, out> and dS_s = P_s (<dout, v_s> - D):
+ *   dq[t, h]  = scale * sum_s dS_s k[s, g]
+ *   dk[s, g]  = scale * sum over (t, h of g) keeping s of dS_s q[t, h]
+ *   dv[s, g]  = sum over (t, h of g) keeping s of P_s dout[t, h]
+ * Rows without a kept causal key get dq 0; keys that no row keeps get dk and
+ * dv 0.  q, k, v, out and dout are bf16 (dtype MSA_BF16, else
+ * MSA_ERR_UNSUPPORTED_DTYPE); dq [total_q, H, d], dk and dv [total_kv, G, d]
+ * are fp32, fully written.  Sums are fp32 and deterministic (no
+ * floating-point atomics); each slot's share of dq is rounded to bf16 before
+ * the slots are added.  Requirements beyond the common ones: head_dim 128,
+ * block_size 128, H/G dividing 64, total_q * top_k * H < 2^31 and
+ * num_seqs * NBmax <= 16384 (else MSA_ERR_BAD_SHAPE).  All tensors 16-byte
+ * aligned; `workspace` must hold msa_sparse_attn_bwd_workspace_size() bytes,
+ * 256-byte aligned. */
+msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes);
+msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const void *k,
+                                 const void *v, const int32_t *block_idx, const void *out,
+                                 const float *lse, const void *dout, float *dq, float *dk,
+                                 float *dv, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Kernel timing hook (diagnostics).  After this call, every msa_* call on
  * the calling thread records events[i] (each a hipEvent_t created by the
  * caller) on its stream right after launching its i-th kernel, for i <

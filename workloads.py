@@ -227,3 +227,12 @@ def random_slot_grads(seed: int, G: int, total_q: int, top_k: int) -> torch.Tens
     the input of the Index Branch backward when it is checked on its own."""
     g = torch.Generator(device="cpu").manual_seed(_seed(seed, "slot-grads", top_k))
     return torch.randn((G, total_q, top_k), generator=g, dtype=torch.float32)
+
+
+def random_out_grad(seed: int, total_q: int, H: int, d: int, dtype: str = "bf16",
+                    device="cpu") -> torch.Tensor:
+    """Seeded N(0, 1) upstream gradient of the attention output [total_q, H, d],
+    drawn in fp32 and cast to the problem's dtype (round to nearest even):
+    the input of the Main Branch backward when it is checked on its own."""
+    g = _seed(seed, "out-grad", H * 1000 + d)
+    return _cast(_randn((total_q, H, d), g, device), dtype).contiguous()
