@@ -137,6 +137,9 @@ def main():
                     help="training step of the indexer: the attention also returns the Main "
                          "Branch block mass, then the indexer's KL loss, its score gradient and "
                          "the max-pooling backward to q_idx and k_idx follow")
+    ap.add_argument("--attn-bwd", action="store_true",
+                    help="training step of the Main Branch: the attention also returns its LSE, "
+                         "then the attention backward for a seeded upstream gradient follows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -171,8 +174,16 @@ def main():
         lin = W.make_inputs(w, device=dev, seed=1000 + li)
         layers.append((lin["q"], lin["k"], lin["v"]))
         del lin
-    if args.indexer_kl:
+    if args.indexer_kl or args.attn_bwd:
         lse_buf = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=dev)
+    if args.attn_bwd:
+        dout = W.random_out_grad(1, prob.total_q, prob.H, prob.d, w.dtype, device=dev)
+        nab = ctypes.c_size_t(0)
+        msa._check(msa.load_library().msa_sparse_attn_bwd_workspace_size(prob.ref(),
+                                                                         ctypes.byref(nab)))
+        ab_ws = torch.empty(max(nab.value, 1), dtype=torch.uint8, device=dev)
+        ab_kernels = ["ab_zero", "ab_dsum", "ab_buckets", "ab_item", "ab_reduce", "ab_dq"]
+    if args.indexer_kl:
         mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
         kl = torch.empty((prob.G, prob.total_q), dtype=torch.float32, device=dev)
         kl_grad = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
@@ -200,9 +211,10 @@ def main():
                                      mass, workspace=workspace, stream=sid)
         else:
             msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out,
-                                workspace=workspace, stream=sid)
+                                workspace=workspace, stream=sid,
+                                lse=lse_buf if args.attn_bwd else None)
 
-    def step(ev=None, pev=None):
+    def step(ev=None, pev=None, bev=None):
         if ev is not None:
             ev[0].record(stream)
         msa.index_score(prob, inp["q_idx"], inp["k_idx"], scores, stream=sid)
@@ -226,21 +238,34 @@ def main():
                 ev[4].record(stream)
             msa.indexer_bwd(prob, inp["q_idx"], inp["k_idx"], block_idx, kl_grad,
                             workspace=bwd_ws, stream=sid)
-            if ev is not None:
-                ev[5].record(stream)
+        if ev is not None:
+            ev[5].record(stream)
+        if args.attn_bwd:
+            def backward():
+                msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out, lse_buf,
+                                    dout, workspace=ab_ws, stream=sid)
+            if bev is not None:
+                with bev:
+                    backward()
+            else:
+                backward()
+        if ev is not None:
+            ev[6].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(args.steps)]
+    bevents = [msa.ProfileEvents(len(ab_kernels), dev) if args.attn_bwd else None
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(events[i], pevents[i])
+        step(events[i], pevents[i], bevents[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -259,6 +284,13 @@ def main():
     if args.indexer_kl:
         kern_ms["indexer_kl"] = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
         kern_ms["indexer_bwd"] = float(np.mean([e[4].elapsed_time(e[5]) for e in events]))
+    if args.attn_bwd:
+        for i, name in enumerate(ab_kernels):
+            vals = []
+            for e, be in zip(events, bevents):
+                prev = e[5] if i == 0 else be.events[i - 1]
+                vals.append(prev.elapsed_time(be.events[i]))
+            kern_ms[name] = float(np.mean(vals))
 
     f_idx, f_attn, nbytes = algorithmic_work(w, lq, lkv)
     f_diag, part_bytes = kvmajor_partial_work(w, lq, lkv, block_idx)
@@ -270,8 +302,14 @@ def main():
         "sparse_attn_fwd": {"ms": st_ms["sparse_attn_fwd"],
                             "tflops": f_attn * args.layers / st_ms["sparse_attn_fwd"] / 1e9},
     }
-    for s in ("index_score", "sparse_attn_fwd"):
-        stages[s]["pct_mfma_peak"] = 100.0 * stages[s]["tflops"] / PEAK_BF16_TFLOPS
+    # backward: S, dP, dV, dK and dQ products over the same kept keys, 5/2 of the forward's
+    f_bwd = 2.5 * f_attn
+    if args.attn_bwd:
+        bwd_ms = float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
+        stages["sparse_attn_bwd"] = {"ms": bwd_ms, "tflops": f_bwd / bwd_ms / 1e9}
+    for s in ("index_score", "sparse_attn_fwd", "sparse_attn_bwd"):
+        if s in stages:
+            stages[s]["pct_mfma_peak"] = 100.0 * stages[s]["tflops"] / PEAK_BF16_TFLOPS
     dom = max(kern_ms, key=lambda k: kern_ms[k])
     dom_s = kern_ms[dom] * 1e-3
     if dom == "index_score_mfma":
@@ -279,6 +317,11 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                 "algorithmic_flops_per_launch": f_idx}
+    elif dom == "ab_item":
+        achieved = f_bwd / dom_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": f_bwd}
     elif dom == "kv_partial":
         achieved = part_bytes / dom_s / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
@@ -322,7 +365,8 @@ def main():
                            "G": w.num_kv_groups, "d": w.head_dim, "d_idx": w.idx_dim,
                            "block": w.block_size, "top_k": w.top_k, "schedule": args.schedule,
                            **({"layers_per_index": args.layers} if args.layers > 1 else {}),
-                           **({"indexer_kl": True} if args.indexer_kl else {})},
+                           **({"indexer_kl": True} if args.indexer_kl else {}),
+                           **({"attn_bwd": True} if args.attn_bwd else {})},
                 "roofline": roof, "stages": stages, "extra": extra,
                 "wall_s_timed": wall})
 

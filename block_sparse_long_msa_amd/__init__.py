@@ -218,8 +218,10 @@ def workspace_size(prob: Problem) -> int:
 def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     block_idx: torch.Tensor, out: Optional[torch.Tensor] = None,
                     return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
-                    stream: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """msa_sparse_attn_fwd: (out [total_q, H, d], lse [total_q, H] or None)."""
+                    stream: Optional[int] = None, lse: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """msa_sparse_attn_fwd: (out [total_q, H, d], lse [total_q, H] or None).
+    The LSE is written when return_lse is set or an `lse` buffer is given."""
     dt = prob.torch_dtype
     _need(q, "q", (prob.total_q, prob.H, prob.d), dt)
     _need(k, "k", (prob.total_kv, prob.G, prob.d), dt)
@@ -228,8 +230,10 @@ def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     if out is None:
         out = torch.empty((prob.total_q, prob.H, prob.d), dtype=dt, device=q.device)
     _need(out, "out", (prob.total_q, prob.H, prob.d), dt)
-    lse = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=q.device) \
-        if return_lse else None
+    if lse is None and return_lse:
+        lse = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", (prob.total_q, prob.H), torch.float32)
     need = workspace_size(prob)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

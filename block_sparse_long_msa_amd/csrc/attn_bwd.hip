@@ -132,6 +132,7 @@ __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<c
 // step are loaded into registers during a step; the row-major copies are
 // written after phase 2 and the transposed ones in phase 1 of their step
 // (no wave reads those in phase 1), so a step needs two barriers.
+template <int HPG>
 __global__ __launch_bounds__(kItemThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
@@ -152,6 +153,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   __shared__ __attribute__((aligned(16))) uint16_t st_[kBS * kLt];   // dS^T [key][row]
   __shared__ float m_lse[kRows], m_d[kRows];  // log2-domain LSE (+inf: no row), D
   __shared__ int32_t m_pos[kRows], m_off[kRows];  // position (-1: no row), dQ slot row (-1)
+  __shared__ int32_t m_ent[2][kRows];  // list entries of the rows of steps st + 1, st + 2
 
   const int32_t w = (int32_t)blockIdx.x;
   if (w >= ibase[nbuckets]) return;  // past the last item
@@ -172,7 +174,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int64_t q0 = cu_q[b], base_pos = lkv - (cu_q[b + 1] - q0);
   const int64_t s0 = (int64_t)j * kBS;
   const int nkeys = (int)min<int64_t>(kBS, lkv - s0);
-  const int hpg = H / G, E = kRows / hpg;
+  constexpr int hpg = HPG, E = kRows / HPG;
   const int nsteps = (n + E - 1) / E;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int kg = wv & 3, hf = wv >> 2;
@@ -206,57 +208,49 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   }
 
-  // Rows of step st: thread tid loads pieces (tid / 64) and (tid / 64) + 8 of
-  // row tid % 64 of Q and dO; the first wave also loads the row's metadata.
+  // Rows of a step: thread tid loads pieces (tid / 64) and (tid / 64) + 8 of
+  // row r = tid % 64 of Q and dO, and the row's LSE and D.  The list entry
+  // naming the row is read one step earlier still (by the first wave, into
+  // the m_ent ring), so no load of a step waits for another; rows past the
+  // item repeat its last entry (valid memory) and are switched off when
+  // staged.
+  const int r_me = tid & 63;
+  auto load_entry = [&](int st) { return lists[first + min(st * E + r_me / hpg, n - 1)]; };
   u32x4 fq[2], fo[2];
   float f_lse = 0.f, f_d = 0.f;
-  int f_pos = -1, f_off = -1;
-  auto fetch = [&](int st) {
-    const int r = tid & 63;
-    const int x = st * E + r / hpg;
-    if (x < n) {
-      const int32_t e = lists[first + x];
-      const int64_t t = e / K;
-      const int h = g * hpg + r % hpg;
-      const int64_t roff = (t * H + h) * (int64_t)kD;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pc = (tid >> 6) + 8 * u;
-        fq[u] = ld16(q + roff + pc * 8);
-        fo[u] = ld16(dout + roff + pc * 8);
-      }
-      if (tid < 64) {
-        f_lse = lse[t * H + h] * kLog2e;
-        f_d = dsum[t * H + h];
-        f_pos = (int)(base_pos + (t - q0));
-        f_off = e * H + h;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) fq[u] = fo[u] = zero4;
-      f_lse = __builtin_inff();
-      f_d = 0.f;
-      f_pos = -1;
-      f_off = -1;
-    }
-  };
-  auto stage_rows = [&]() {  // row-major Q, dO and the metadata
-    const int r = tid & 63;
+  int32_t f_e = 0;
+  auto fetch = [&](int32_t e) {
+    const int64_t t = e / K;
+    const int h = g * hpg + r_me % hpg;
+    const int64_t roff = (t * H + h) * (int64_t)kD;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int pc = (tid >> 6) + 8 * u;
-      st16(&qs[r * kLd + pc * 8], fq[u]);
-      st16(&os[r * kLd + pc * 8], fo[u]);
+      fq[u] = ld16(q + roff + pc * 8);
+      fo[u] = ld16(dout + roff + pc * 8);
+    }
+    f_lse = lse[t * H + h];
+    f_d = dsum[t * H + h];
+    f_e = e;
+  };
+  auto stage_rows = [&](int st) {  // row-major Q, dO and the metadata
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = (tid >> 6) + 8 * u;
+      st16(&qs[r_me * kLd + pc * 8], fq[u]);
+      st16(&os[r_me * kLd + pc * 8], fo[u]);
     }
     if (tid < 64) {
-      m_lse[r] = f_lse;
-      m_d[r] = f_d;
-      m_pos[r] = f_pos;
-      m_off[r] = f_off;
+      const bool ok = st * E + r_me / hpg < n;
+      const int64_t t = f_e / K;
+      m_lse[r_me] = ok ? f_lse * kLog2e : __builtin_inff();
+      m_d[r_me] = ok ? f_d : 0.f;
+      m_pos[r_me] = ok ? (int)(base_pos + (t - q0)) : -1;
+      m_off[r_me] = ok ? f_e * H + g * hpg + r_me % hpg : -1;
     }
   };
   auto stage_cols = [&]() {  // transposed Q, dO
-    const int r = tid & 63;
+    const int r = r_me;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int pc = (tid >> 6) + 8 * u;
@@ -278,14 +272,19 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const float c2 = scale * kLog2e;
   const int64_t keypos = s0 + 32 * kg + li;
 
+  int32_t f_e2 = 0;  // entry of row r_me in step st + 2 (first wave)
   if (nsteps > 0) {
-    fetch(0);
-    stage_rows();
+    if (tid < 64) {
+      m_ent[0][r_me] = load_entry(0);
+      m_ent[1][r_me] = load_entry(1);
+    }
+    __syncthreads();
+    fetch(m_ent[0][r_me]);
+    stage_rows(0);
   }
   for (int st = 0; st < nsteps; ++st) {
     __syncthreads();
     stage_cols();
-    if (st + 1 < nsteps) fetch(st + 1);
     // phase 1: S and dP for rows 32 hf .., keys 32 kg ..
     f32x16 sacc, pacc;
 #pragma unroll
@@ -321,6 +320,10 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       ss[(row + 3) * kLd + 32 * kg + li] = hi16(dsv[1]);
     }
     __syncthreads();
+    if (st + 1 < nsteps) {
+      fetch(m_ent[(st + 1) & 1][r_me]);
+      if (tid < 64) f_e2 = load_entry(st + 2);
+    }
     // phase 2: dV^T += dO^T P, dK^T += Q^T dS (channels 64 hf .., keys 32 kg .., 64 rows)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -355,7 +358,10 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         *reinterpret_cast<u32x2 *>(dst + 8 * q4) = val;
       }
     }
-    if (st + 1 < nsteps) stage_rows();
+    if (st + 1 < nsteps) {
+      stage_rows(st + 1);
+      if (tid < 64) m_ent[st & 1][r_me] = f_e2;  // the slot of step st + 2
+    }
   }
 
   const int key = 32 * kg + li;
@@ -469,7 +475,8 @@ void zero_fill(float *x, int64_t n, hipStream_t s) {
 
 bool attn_bwd_supported(const Dims &p) {
   const int hpg = p.G > 0 ? p.H / p.G : 0;
-  return p.d == kD && p.B == kBS && hpg > 0 && hpg <= kRows && kRows % hpg == 0;
+  return p.d == kD && p.B == kBS &&
+         (hpg == 1 || hpg == 2 || hpg == 4 || hpg == 8 || hpg == 16);
 }
 
 size_t attn_bwd_workspace_bytes(const Dims &p) { return ab_carve(p, nullptr).total_bytes; }
@@ -506,10 +513,18 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
                      p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
   profile_mark(s);
-  hipLaunchKernelGGL(ab_item_kernel, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k,
-                     v, dout, lse, w.dsum, w.base, w.ibase, w.pbase, w.lists, w.dq_part, dk, dv,
-                     w.part, p.cu_q, p.cu_kv, p.G, p.H, p.top_k, p.nb_max, ncol, w.per_item,
-                     p.scale);
+  auto item = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k, v, dout,
+                       lse, w.dsum, w.base, w.ibase, w.pbase, w.lists, w.dq_part, dk, dv, w.part,
+                       p.cu_q, p.cu_kv, p.G, p.H, p.top_k, p.nb_max, ncol, w.per_item, p.scale);
+  };
+  switch (p.H / p.G) {
+    case 1: item(ab_item_kernel<1>); break;
+    case 2: item(ab_item_kernel<2>); break;
+    case 4: item(ab_item_kernel<4>); break;
+    case 8: item(ab_item_kernel<8>); break;
+    default: item(ab_item_kernel<16>); break;
+  }
   profile_mark(s);
   hipLaunchKernelGGL(ab_reduce_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.ibase, w.pbase,
                      w.part, dk, dv, p.cu_kv, p.G, p.nb_max, w.nbk_g, p.scale);
