@@ -12,9 +12,8 @@
 // entries that kept the block, the current block included (its causal mask
 // is applied per row), in (row, slot) order (buckets.hpp).  A work item is
 // up to kSteps steps of one bucket's list; a step is 64 (query, head) rows.
-// The item keeps its block's K^T in LDS and each wave's share of K and V in
-// registers for all its steps, and accumulates dK, dV of the block in
-// registers; every step writes the rows' dQ contribution of this block into
+// The item keeps its block's K and V in LDS for all its steps and
+// accumulates dK, dV of the block in registers; every step writes the rows' dQ contribution of this block into
 // the row's slot (bf16), which a merge then sums in slot order.  No
 // floating-point atomics: every sum has a fixed order.
 //
@@ -40,8 +39,8 @@ constexpr int kD = 128;           // head dimension
 constexpr int kBS = 128;          // block size
 constexpr int kRows = 64;         // (query, head) rows per step
 constexpr int kSteps = 32;        // steps per work item
-constexpr int kLd = kD + 8;       // padded LDS row (bf16) of Q, dO, dS and K^T
-constexpr int kLt = kRows + 8;    // padded LDS row of Q^T, dO^T, P^T and dS^T
+constexpr int kLd = kD + 16;      // padded LDS row (bf16) of K, V, Q and dO
+constexpr int kLt = kRows + 8;    // padded LDS row of P^T and dS^T
 constexpr int kItemThreads = 512;  // 8 waves: 4 key groups x 2 halves
 
 struct AbWs {
@@ -115,23 +114,41 @@ __global__ __launch_bounds__(256) void ab_dsum_kernel(const uint16_t *__restrict
   if (part == 0 && rh < nrows) dsum[rh] = acc;
 }
 
-__device__ __forceinline__ uint16_t lo16(uint32_t w) { return (uint16_t)(w & 0xffffu); }
-__device__ __forceinline__ uint16_t hi16(uint32_t w) { return (uint16_t)(w >> 16); }
-__device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  In each 16-lane group, lane i
+// names a 4-element chunk; lane 4a + b receives element b of the chunks of
+// lanes a, a + 4, a + 8 and a + 12.  So with lane i pointing at
+// X[k0 + i / 4][n0 + 4 (i % 4)] of a row-major X, lane j receives
+// X[k0 .. k0 + 3][n0 + j].
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+// MFMA 32x32x16 operand holding X[k0 + 8 hh .. k0 + 8 hh + 7][n0 + lane % 32]
+// (hh = lane / 32) of a row-major X with row stride ld: two transposing
+// reads of 4 rows each.
+__device__ __forceinline__ u32x4 ld_op_tr(const uint16_t *x, int ld, int k0, int n0, int lane) {
+  const int i = lane & 15, grp = lane >> 4;
+  const uint16_t *p = x + (k0 + 8 * (grp >> 1) + (i >> 2)) * ld + n0 + 16 * (grp & 1) + 4 * (i & 3);
+  const u32x2 a = ld_tr(p), b = ld_tr(p + 4 * ld);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
 
 // One work-group per work item, 8 waves; wave wv has kg = wv % 4 and
-// hf = wv / 4.  Per step (64 rows):
-//   phase 1  S = Q K^T and dP = dO V^T for keys 32 kg .. and rows 32 hf ..
-//            (K and V of the wave's keys in registers), then P and dS; P^T
-//            and dS^T go to LDS [key][row], dS also to LDS [row][key]
+// hf = wv / 4.  K and V of the block stay in LDS (row-major) for the whole
+// item.  Per step (64 rows):
+//   phase 1  S = Q K^T and dP = dO V^T for keys 32 kg .. and rows 32 hf ..,
+//            then P and dS; P^T and dS^T go to LDS [key][row]
 //   phase 2  dV^T += dO^T P and dK^T += Q^T dS for channels 64 hf .. 64 hf + 63
 //            and keys 32 kg .. over all 64 rows (each (key, channel) has one
 //            owner, so no cross-wave sum); dQ^T = K^T dS^T for channels
 //            32 kg .. and rows 32 hf .. over all 128 keys -> the rows' slots
-// MFMA 32x32x16 layouts as in msa_common.hpp.  Q and dO rows of the next
-// step are loaded into registers during a step; the row-major copies are
-// written after phase 2 and the transposed ones in phase 1 of their step
-// (no wave reads those in phase 1), so a step needs two barriers.
+// The transposed operands (dO^T, Q^T, K^T, dS) come from the row-major LDS
+// copies through transposing reads.  MFMA 32x32x16 layouts as in
+// msa_common.hpp.  The next step's Q and dO rows load into registers during
+// phase 2 and are staged after a third barrier (phase 2 still reads qs, os).
 template <int HPG>
 __global__ __launch_bounds__(kItemThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -143,16 +160,16 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                float *__restrict__ part, const int64_t *__restrict__ cu_q,
                const int64_t *__restrict__ cu_kv, int G, int H, int K, int nb_max,
                int64_t nbuckets, int per_item, float scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kD * kLd];     // K^T [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kBS * kLd];    // K [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kBS * kLd];    // V [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t qs[kRows * kLd];  // Q [row][d]
   __shared__ __attribute__((aligned(16))) uint16_t os[kRows * kLd];  // dO [row][d]
-  __shared__ __attribute__((aligned(16))) uint16_t ss[kRows * kLd];  // dS [row][key]
-  __shared__ __attribute__((aligned(16))) uint16_t qt[kD * kLt];     // Q^T [d][row]
-  __shared__ __attribute__((aligned(16))) uint16_t ot[kD * kLt];     // dO^T [d][row]
   __shared__ __attribute__((aligned(16))) uint16_t pt[kBS * kLt];    // P^T [key][row]
   __shared__ __attribute__((aligned(16))) uint16_t st_[kBS * kLt];   // dS^T [key][row]
-  __shared__ float m_lse[kRows], m_d[kRows];  // log2-domain LSE (+inf: no row), D
-  __shared__ int32_t m_pos[kRows], m_off[kRows];  // position (-1: no row), dQ slot row (-1)
+  __shared__ __attribute__((aligned(16))) float m_lse[kRows];  // log2-domain LSE (+inf: no row)
+  __shared__ __attribute__((aligned(16))) float m_d[kRows];    // D
+  __shared__ __attribute__((aligned(16))) int32_t m_pos[kRows];  // position (-1: no row)
+  __shared__ int32_t m_off[kRows];     // dQ slot row (-1: no row)
   __shared__ int32_t m_ent[2][kRows];  // list entries of the rows of steps st + 1, st + 2
 
   const int32_t w = (int32_t)blockIdx.x;
@@ -181,30 +198,15 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int li = lane & 31, hh = lane >> 5;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // K^T of the block, zero past the sequence's keys
+  // K and V of the block, zero past the sequence's keys
   {
     const int key = tid & 127;
-    const uint16_t *src = k + ((kv0 + s0 + min(key, nkeys - 1)) * G + g) * (int64_t)kD;
+    const int64_t roff = ((kv0 + s0 + min(key, nkeys - 1)) * G + g) * (int64_t)kD;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = (tid >> 7) + 4 * u;
-      const u32x4 x = key < nkeys ? ld16(src + pc * 8) : zero4;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        kt[(pc * 8 + 2 * m) * kLd + key] = lo16(x[m]);
-        kt[(pc * 8 + 2 * m + 1) * kLd + key] = hi16(x[m]);
-      }
-    }
-  }
-  // K and V of this wave's 32 keys as B operands of S = Q K^T and dP = dO V^T
-  u32x4 kw[8], vw[8];
-  {
-    const int key = 32 * kg + li;
-    const int64_t roff = ((kv0 + s0 + min(key, nkeys - 1)) * G + g) * (int64_t)kD + 8 * hh;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      kw[x] = key < nkeys ? ld16(k + roff + 16 * x) : zero4;
-      vw[x] = key < nkeys ? ld16(v + roff + 16 * x) : zero4;
+      st16(&ks[key * kLd + pc * 8], key < nkeys ? ld16(k + roff + pc * 8) : zero4);
+      st16(&vs[key * kLd + pc * 8], key < nkeys ? ld16(v + roff + pc * 8) : zero4);
     }
   }
 
@@ -233,7 +235,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     f_d = dsum[t * H + h];
     f_e = e;
   };
-  auto stage_rows = [&](int st) {  // row-major Q, dO and the metadata
+  auto stage_rows = [&](int st) {  // Q, dO and the metadata
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int pc = (tid >> 6) + 8 * u;
@@ -247,20 +249,6 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       m_d[r_me] = ok ? f_d : 0.f;
       m_pos[r_me] = ok ? (int)(base_pos + (t - q0)) : -1;
       m_off[r_me] = ok ? f_e * H + g * hpg + r_me % hpg : -1;
-    }
-  };
-  auto stage_cols = [&]() {  // transposed Q, dO
-    const int r = r_me;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pc = (tid >> 6) + 8 * u;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        qt[(pc * 8 + 2 * m) * kLt + r] = lo16(fq[u][m]);
-        qt[(pc * 8 + 2 * m + 1) * kLt + r] = hi16(fq[u][m]);
-        ot[(pc * 8 + 2 * m) * kLt + r] = lo16(fo[u][m]);
-        ot[(pc * 8 + 2 * m + 1) * kLt + r] = hi16(fo[u][m]);
-      }
     }
   };
 
@@ -284,7 +272,6 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   }
   for (int st = 0; st < nsteps; ++st) {
     __syncthreads();
-    stage_cols();
     // phase 1: S and dP for rows 32 hf .., keys 32 kg ..
     f32x16 sacc, pacc;
 #pragma unroll
@@ -292,17 +279,26 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const u32x4 aq = ld16(&qs[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
+      const u32x4 bk = ld16(&ks[(32 * kg + li) * kLd + 16 * x + 8 * hh]);
       const u32x4 ao = ld16(&os[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
-      sacc = mfma32x32x16(as_bf16x8(aq), as_bf16x8(kw[x]), sacc);
-      pacc = mfma32x32x16(as_bf16x8(ao), as_bf16x8(vw[x]), pacc);
+      const u32x4 bv = ld16(&vs[(32 * kg + li) * kLd + 16 * x + 8 * hh]);
+      sacc = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
+      pacc = mfma32x32x16(as_bf16x8(ao), as_bf16x8(bv), pacc);
     }
-    // register r holds row 32 hf + 8 (r / 4) + 4 hh + r % 4 and key keypos
+    // register 4 q4 + i holds row 32 hf + 8 q4 + 4 hh + i and key keypos
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * hf + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float pv = keypos > (int64_t)m_pos[row] ? 0.f : exp2f(sacc[r] * c2 - m_lse[row]);
-      sacc[r] = pv;
-      pacc[r] = pv * (pacc[r] - m_d[row]);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int row = 32 * hf + 8 * q4 + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&m_lse[row]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&m_d[row]);
+      const u32x4 p4 = ld16(&m_pos[row]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q4 + i;
+        const float pv = keypos > (int64_t)(int32_t)p4[i] ? 0.f : exp2f(sacc[r] * c2 - l4[i]);
+        sacc[r] = pv;
+        pacc[r] = pv * (pacc[r] - d4[i]);
+      }
     }
     const int my_off = m_off[32 * hf + li];  // dQ row of this lane, read before it is restaged
 #pragma unroll
@@ -314,10 +310,6 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                          pack_bf16x2(pacc[4 * q4 + 2], pacc[4 * q4 + 3])};
       *reinterpret_cast<u32x2 *>(&pt[(32 * kg + li) * kLt + row]) = pv;
       *reinterpret_cast<u32x2 *>(&st_[(32 * kg + li) * kLt + row]) = dsv;
-      ss[row * kLd + 32 * kg + li] = lo16(dsv[0]);
-      ss[(row + 1) * kLd + 32 * kg + li] = hi16(dsv[0]);
-      ss[(row + 2) * kLd + 32 * kg + li] = lo16(dsv[1]);
-      ss[(row + 3) * kLd + 32 * kg + li] = hi16(dsv[1]);
     }
     __syncthreads();
     if (st + 1 < nsteps) {
@@ -331,34 +323,38 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       const u32x4 bs = ld16(&st_[(32 * kg + li) * kLt + 16 * x + 8 * hh]);
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
-        const int ch = 64 * hf + 32 * y + li;
-        const u32x4 ao = ld16(&ot[ch * kLt + 16 * x + 8 * hh]);
-        const u32x4 aq = ld16(&qt[ch * kLt + 16 * x + 8 * hh]);
+        const u32x4 ao = ld_op_tr(os, kLd, 16 * x, 64 * hf + 32 * y, lane);
+        const u32x4 aq = ld_op_tr(qs, kLd, 16 * x, 64 * hf + 32 * y, lane);
         acc_v[y] = mfma32x32x16(as_bf16x8(ao), as_bf16x8(bp), acc_v[y]);
         acc_k[y] = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bs), acc_k[y]);
       }
     }
-    // dQ^T = K^T dS^T for channels 32 kg .., rows 32 hf .. (all 128 keys)
-    f32x16 qacc;
+    // dQ^T = K^T dS^T for channels 32 kg .., rows 32 hf .. (all 128 keys), two chains
+    f32x16 qa0, qa1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
+    for (int r = 0; r < 16; ++r) qa0[r] = qa1[r] = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const u32x4 a = ld16(&kt[(32 * kg + li) * kLd + 16 * x + 8 * hh]);
-      const u32x4 bq = ld16(&ss[(32 * hf + li) * kLd + 16 * x + 8 * hh]);
-      qacc = mfma32x32x16(as_bf16x8(a), as_bf16x8(bq), qacc);
+    for (int x = 0; x < 8; x += 2) {
+      const u32x4 a0 = ld_op_tr(ks, kLd, 16 * x, 32 * kg, lane);
+      const u32x4 b0 = ld_op_tr(st_, kLt, 16 * x, 32 * hf, lane);
+      const u32x4 a1 = ld_op_tr(ks, kLd, 16 * x + 16, 32 * kg, lane);
+      const u32x4 b1 = ld_op_tr(st_, kLt, 16 * x + 16, 32 * hf, lane);
+      qa0 = mfma32x32x16(as_bf16x8(a0), as_bf16x8(b0), qa0);
+      qa1 = mfma32x32x16(as_bf16x8(a1), as_bf16x8(b1), qa1);
     }
     // lane holds row 32 hf + li, channels 32 kg + 8 (r / 4) + 4 hh + r % 4
     if (my_off >= 0) {
       uint16_t *dst = dq_part + (int64_t)my_off * kD + 32 * kg + 4 * hh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 val = {pack_bf16x2(qacc[4 * q4], qacc[4 * q4 + 1]),
-                           pack_bf16x2(qacc[4 * q4 + 2], qacc[4 * q4 + 3])};
+        const u32x2 val = {pack_bf16x2(qa0[4 * q4] + qa1[4 * q4], qa0[4 * q4 + 1] + qa1[4 * q4 + 1]),
+                           pack_bf16x2(qa0[4 * q4 + 2] + qa1[4 * q4 + 2],
+                                       qa0[4 * q4 + 3] + qa1[4 * q4 + 3])};
         *reinterpret_cast<u32x2 *>(dst + 8 * q4) = val;
       }
     }
     if (st + 1 < nsteps) {
+      __syncthreads();  // phase 2 reads qs / os (transposed): all waves are past it
       stage_rows(st + 1);
       if (tid < 64) m_ent[st & 1][r_me] = f_e2;  // the slot of step st + 2
     }
