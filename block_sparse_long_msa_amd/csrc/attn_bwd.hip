@@ -48,7 +48,7 @@ struct AbWs {
   float *dsum;        // [total_q][H] rowsum(dO * O)
   uint16_t *dq_part;  // [total_q * K * H][d] bf16: the dQ of each kept slot, unscaled
   float *part;        // [max_parts][2][BS][d]: dV, dK (unscaled) of the items of shared buckets
-  int64_t ntiles, nbk_g, nent_g, max_items, max_parts;
+  int64_t ntiles, nbk_g, nent_g, max_items, max_parts, tile;
   int32_t per_item;
   size_t total_bytes;
 };
@@ -58,7 +58,8 @@ size_t ab_align(size_t x) { return (x + 255) & ~(size_t)255; }
 AbWs ab_carve(const Dims &p, void *base) {
   AbWs w;
   w.nent_g = p.total_q * (int64_t)p.top_k;
-  w.ntiles = (w.nent_g + kBucketTile - 1) / kBucketTile;
+  w.tile = bucket_tile(w.nent_g);
+  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
   w.per_item = kSteps * (kRows / (p.H / p.G));
   const int64_t nent = (int64_t)p.G * w.nent_g;
@@ -389,8 +390,10 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
 }
 
-// One work-group per bucket of several items: dv, dk = the items' partials
-// added in item order (dk scaled).
+// Per bucket of several items, kReduceSplit work-groups (each a share of
+// the block's key rows): dv, dk = the items' partials added in item order
+// (dk scaled).
+constexpr int kReduceSplit = 8;
 __global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restrict__ ibase,
                                                         const int32_t *__restrict__ pbase,
                                                         const float *__restrict__ part,
@@ -408,7 +411,9 @@ __global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restric
   const int64_t s0 = (int64_t)j * kBS;
   const int nkeys = (int)min<int64_t>(kBS, lkv - s0);
   const float *src = part + (int64_t)pbase[gb] * 2 * kBS * kD;
-  for (int x = threadIdx.x * 4; x < nkeys * kD; x += 256 * 4) {
+  constexpr int kShare = kBS * kD / kReduceSplit;  // floats of one work-group
+  const int x0 = blockIdx.y * kShare;
+  for (int x = x0 + threadIdx.x * 4; x < min(x0 + kShare, nkeys * kD); x += 256 * 4) {
     f32x4 av = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
     for (int32_t i = 0; i < nit; ++i) {
       av += *reinterpret_cast<const f32x4 *>(src + (int64_t)i * 2 * kBS * kD + x);
@@ -498,7 +503,7 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
   hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, p.top_k, p.total_q,
-                     p.nb_max, p.B, w.ntiles, w.nbk_g);
+                     p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
                      w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, w.per_item);
@@ -507,7 +512,7 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
-                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
+                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   auto item = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k, v, dout,
@@ -522,7 +527,8 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
     default: item(ab_item_kernel<16>); break;
   }
   profile_mark(s);
-  hipLaunchKernelGGL(ab_reduce_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.ibase, w.pbase,
+  hipLaunchKernelGGL(ab_reduce_kernel, dim3((unsigned)ncol, kReduceSplit), dim3(256), 0, s,
+                     w.ibase, w.pbase,
                      w.part, dk, dv, p.cu_kv, p.G, p.nb_max, w.nbk_g, p.scale);
   profile_mark(s);
   hipLaunchKernelGGL(ab_dq_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s,

@@ -5,7 +5,7 @@
 // b * nb_max + j within the group; padding slots and slots whose block holds
 // no causal key of the row belong to no bucket.  Every bucket's list ends up
 // in (row, slot) order, so sums taken in list order are deterministic:
-//   bk_count     per tile of kBucketTile consecutive entries of a group:
+//   bk_count     per tile of bucket_tile() consecutive entries of a group:
 //                entries per bucket in an LDS histogram (integer atomics,
 //                counting only)
 //   bk_colscan   per bucket: exclusive offsets of the tiles, its total, its
@@ -22,7 +22,15 @@
 namespace msa {
 namespace {
 
-constexpr int kBucketTile = 4096;  // entries per counting / scatter tile
+// Entries per counting / scatter tile: the scatter walks a tile with one
+// wave, so small tiles run more of it in parallel, while the column scan
+// walks the tiles of a bucket in order, so there should not be too many:
+// 1024 entries, doubled up to 4096 while a group has more than 1024 tiles.
+inline int64_t bucket_tile(int64_t nent_g) {
+  int64_t t = 1024;
+  while (t < 4096 && nent_g > t * 1024) t *= 2;
+  return t;
+}
 
 // Bucket of entry e (= row * K + slot) of group g, or -1 when the slot is
 // padding or its block holds no causal key of the row.  The bucket numbers
@@ -52,15 +60,16 @@ __device__ __forceinline__ EntryInfo entry_info(const int32_t *__restrict__ bloc
 __global__ __launch_bounds__(256) void bk_count_kernel(
     const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int32_t *__restrict__ cnt, int32_t *__restrict__ amax,  // may be null
-    int num_seqs, int K, int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
+    int num_seqs, int K, int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g,
+    int64_t tile_len) {
   extern __shared__ int32_t hist[];  // [nbk_g]
   const int g = blockIdx.y;
   const int64_t tile = blockIdx.x;
   for (int64_t x = threadIdx.x; x < nbk_g; x += 256) hist[x] = 0;
   __syncthreads();
   const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * kBucketTile);
-  for (int64_t e = tile * kBucketTile + threadIdx.x; e < e1; e += 256) {
+  const int64_t e1 = min(nent, (tile + 1) * tile_len);
+  for (int64_t e = tile * tile_len + threadIdx.x; e < e1; e += 256) {
     const EntryInfo ei = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS);
     if (ei.bucket >= 0) atomicAdd(&hist[ei.bucket], 1);
     else if (amax != nullptr) amax[(int64_t)g * nent + e] = -1;
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(64) void bk_scatter_kernel(
     const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, const int32_t *__restrict__ cnt,
     const int32_t *__restrict__ base, int32_t *__restrict__ lists, int num_seqs, int K,
-    int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g) {
+    int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g, int64_t tile_len) {
   extern __shared__ int32_t run[];  // [nbk_g] next list position of each bucket
   const int g = blockIdx.y;
   const int64_t tile = blockIdx.x;
@@ -139,8 +148,8 @@ __global__ __launch_bounds__(64) void bk_scatter_kernel(
   for (int64_t x = lane; x < nbk_g; x += 64) run[x] = gbase[x] + toff[x];
   __syncthreads();
   const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * kBucketTile);
-  for (int64_t c0 = tile * kBucketTile; c0 < e1; c0 += 64) {
+  const int64_t e1 = min(nent, (tile + 1) * tile_len);
+  for (int64_t c0 = tile * tile_len; c0 < e1; c0 += 64) {
     const int64_t e = c0 + lane;
     int bk = -1;
     if (e < e1) bk = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS).bucket;

@@ -44,7 +44,7 @@ struct IbWs {
   int32_t *ibase;  // [G * nbk_g + 1]: items per bucket, then exclusive item starts
   int32_t *pbase;  // [G * nbk_g + 1]: partial slots per bucket (its items if > 1)
   float *part;     // [max_parts][BS][d_idx] key-side partial sums of shared buckets
-  int64_t ntiles, nbk_g, nent_g, max_items, max_parts;
+  int64_t ntiles, nbk_g, nent_g, max_items, max_parts, tile;
   size_t total_bytes;
 };
 
@@ -53,7 +53,8 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 IbWs ib_carve(const Dims &p, void *base) {
   IbWs w;
   w.nent_g = p.total_q * (int64_t)p.top_k;
-  w.ntiles = (w.nent_g + kBucketTile - 1) / kBucketTile;
+  w.tile = bucket_tile(w.nent_g);
+  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
   size_t off = 0;
   char *c = static_cast<char *>(base);
@@ -409,7 +410,7 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
   hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.amax, p.num_seqs, p.top_k, p.total_q,
-                     p.nb_max, p.B, w.ntiles, w.nbk_g);
+                     p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
@@ -420,7 +421,7 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   profile_mark(s);
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
-                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g);
+                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   hipLaunchKernelGGL((ib_item_kernel<T, DI, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s,
                      q_idx, k_idx, grad, w.base, w.ibase, w.pbase, w.lists, w.amax, dk_idx, w.part,
