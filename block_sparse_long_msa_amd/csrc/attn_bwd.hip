@@ -480,7 +480,10 @@ bool attn_bwd_supported(const Dims &p) {
          (hpg == 1 || hpg == 2 || hpg == 4 || hpg == 8 || hpg == 16);
 }
 
-size_t attn_bwd_workspace_bytes(const Dims &p) { return ab_carve(p, nullptr).total_bytes; }
+// With no query row the call only clears dk and dv, and needs no workspace.
+size_t attn_bwd_workspace_bytes(const Dims &p) {
+  return p.total_q > 0 ? ab_carve(p, nullptr).total_bytes : 0;
+}
 
 hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                 const uint16_t *v, const int32_t *block_idx, const uint16_t *out,

@@ -256,3 +256,41 @@ def test_indexer_bwd_workspace_and_limits():
     # nothing at all to do
     assert _ibwd(_prob(max_q_len=0, total_q=0, max_kv_len=0, total_kv=0), qi=None, ki=None,
                  idx=None, gr=None, dq=None, dk=None) == 0
+
+
+def _abwd(p, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, out=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE,
+          dv=FAKE, ws=None, wsb=0):
+    lib = msa.load_library()
+    return lib.msa_sparse_attn_bwd(ctypes.byref(p), q, k, v, idx, out, lse, do, dq, dk, dv, ws,
+                                   wsb, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "idx", "out", "lse", "do", "dq", "dk", "dv"])
+def test_attn_bwd_pointer_checks(which):
+    p = _prob()
+    args = {which: None}
+    assert _abwd(p, **args) == 1
+    args[which] = FAKE + 4
+    assert _abwd(p, **args) == 4
+
+
+def test_attn_bwd_shapes_dtype_workspace():
+    lib = msa.load_library()
+    n = ctypes.c_size_t(0)
+    p = _prob()
+    assert lib.msa_sparse_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert _abwd(p, ws=FAKE, wsb=n.value - 1) == 5
+    assert _abwd(p, ws=None, wsb=n.value) == 1
+    assert _abwd(p, ws=FAKE + 16, wsb=n.value) == 4
+    assert _abwd(_prob(dtype=1)) == 3                      # fp32 tensors
+    assert _abwd(_prob(head_dim=64)) == 2
+    assert _abwd(_prob(block_size=64)) == 2
+    assert _abwd(_prob(num_q_heads=6, num_kv_groups=2)) == 2  # 3 heads per group
+    wide = _prob(num_seqs=3, max_kv_len=128 * 8000, total_kv=3 * 128 * 8000, max_q_len=1, total_q=3)
+    assert _abwd(wide, ws=FAKE, wsb=1 << 40) == 2
+    assert lib.msa_sparse_attn_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, None, 0, None) == 1
+    # nothing at all to do
+    assert _abwd(_prob(max_q_len=0, total_q=0, max_kv_len=0, total_kv=0), q=None, k=None, v=None,
+                 idx=None, out=None, lse=None, do=None, dq=None, dk=None, dv=None) == 0

@@ -208,3 +208,18 @@ def test_attn_backward_prefill_32k():
     bound = TOL * dd.abs().view(-1, G, H // G).sum(dim=(0, 2)) / math.sqrt(n_terms)
     assert torch.all((lhs - rhs).abs() <= bound), f"sum <dv, v> {lhs} vs sum <dout, out> {rhs}"
     _log(f"prefill-32k: dq rows {e_q:.2e}, late blocks dk {e_k:.2e} dv {e_v:.2e}")
+
+
+def test_attn_backward_no_query_rows():
+    """No query row at all: the call only clears dk and dv (no workspace)."""
+    H, G, d, di, B, k = 8, 2, 128, 64, 128, 4
+    inp = W.random_case(80, [0], [300], H, G, d, di, B, k, "bf16", device=DEV)
+    prob = C.problem_for(inp, H, G, d, di, B, k, "bf16")
+    empty_idx = torch.empty((G, 0, k), dtype=torch.int32, device=DEV)
+    empty_rows = torch.empty((0, H, d), dtype=torch.bfloat16, device=DEV)
+    empty_lse = torch.empty((0, H), dtype=torch.float32, device=DEV)
+    dq, dk, dv = msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], empty_idx, empty_rows,
+                                     empty_lse, empty_rows)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0
+    assert torch.all(dk == 0) and torch.all(dv == 0)
