@@ -182,7 +182,7 @@ def main():
         msa._check(msa.load_library().msa_sparse_attn_bwd_workspace_size(prob.ref(),
                                                                          ctypes.byref(nab)))
         ab_ws = torch.empty(max(nab.value, 1), dtype=torch.uint8, device=dev)
-        ab_kernels = ["ab_zero", "ab_dsum", "ab_buckets", "ab_item", "ab_reduce", "ab_dq"]
+        ab_kernels = ["ab_dsum", "ab_buckets", "ab_zero_unkept", "ab_item", "ab_reduce", "ab_dq"]
     if args.indexer_kl:
         mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
         kl = torch.empty((prob.G, prob.total_q), dtype=torch.float32, device=dev)

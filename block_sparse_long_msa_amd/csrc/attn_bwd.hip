@@ -18,9 +18,9 @@
 // floating-point atomics: every sum has a fixed order.
 //
 // Kernels, in launch order:
-//   ab_zero      dk, dv <- 0 (keys no slot takes keep 0)
 //   ab_dsum      D = rowsum(dO * O) per (row, head)
 //   bk_*         bucket lists and work items (buckets.hpp)
+//   ab_zero_unkept  dk, dv <- 0 on the keys of blocks no slot keeps
 //   ab_item      per work item: S = Q K^T, dP = dO V^T, P, dS with MFMA; dV^T
 //                += dO^T P, dK^T += Q^T dS, dQ^T = K^T dS^T
 //   ab_reduce    per bucket of several items: dk, dv = the items' partial
@@ -56,9 +56,9 @@ size_t ab_align(size_t x) { return (x + 255) & ~(size_t)255; }
 AbWs ab_carve(const Dims &p, void *base) {
   AbWs w;
   w.nent_g = p.total_q * (int64_t)p.top_k;
-  w.tile = bucket_tile(w.nent_g);
-  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
+  w.tile = bucket_tile(w.nent_g, w.nbk_g);
+  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   w.per_item = kSteps * (kRows / (p.H / p.G));
   const int64_t nent = (int64_t)p.G * w.nent_g;
   // every bucket has one item more than its full items; a bucket with
@@ -88,6 +88,31 @@ AbWs ab_carve(const Dims &p, void *base) {
 __global__ __launch_bounds__(256) void ab_zero_kernel(float *__restrict__ x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     x[i] = 0.f;
+}
+
+// One work-group per (group, sequence, block) bucket that no slot keeps:
+// dk, dv <- 0 on its keys.  The keys of every other bucket are written by
+// ab_item or ab_reduce.
+__global__ __launch_bounds__(256) void ab_zero_unkept_kernel(const int32_t *__restrict__ base,
+                                                             float *__restrict__ dk,
+                                                             float *__restrict__ dv,
+                                                             const int64_t *__restrict__ cu_kv,
+                                                             int G, int nb_max, int64_t nbk_g) {
+  const int64_t gb = blockIdx.x;
+  if (base[gb + 1] != base[gb]) return;
+  const int g = (int)(gb / nbk_g);
+  const int64_t bkt = gb - (int64_t)g * nbk_g;
+  const int b = (int)(bkt / nb_max), j = (int)(bkt - (int64_t)b * nb_max);
+  const int64_t kv0 = cu_kv[b], lkv = cu_kv[b + 1] - kv0;
+  const int64_t s0 = (int64_t)j * kBS;
+  const int nkeys = (int)min<int64_t>(kBS, lkv - s0);  // <= 0 past the sequence's last block
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int x = threadIdx.x * 4; x < nkeys * kD; x += 256 * 4) {
+    const int s = x / kD, c = x - s * kD;
+    const int64_t o = ((kv0 + s0 + s) * G + g) * (int64_t)kD + c;
+    *reinterpret_cast<f32x4 *>(dk + o) = z;
+    *reinterpret_cast<f32x4 *>(dv + o) = z;
+  }
 }
 
 // 16 lanes per (row, head), 8 channels each, then a 16-lane sum.
@@ -509,11 +534,9 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
                                 const float *lse, const uint16_t *dout, float *dq, float *dk,
                                 float *dv, void *workspace, hipStream_t s) {
   AbWs w = ab_carve(p, workspace);
-  zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
-  zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
-  profile_mark(s);
-  if (p.total_q == 0) return hipGetLastError();
-  if (p.total_kv == 0) {
+  if (p.total_q == 0 || p.total_kv == 0) {  // nothing kept: all gradients are 0
+    zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
+    zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
     zero_fill(dq, p.total_q * p.H * (int64_t)kD, s);
     profile_mark(s);
     return hipGetLastError();
@@ -535,6 +558,9 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
                      p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+  profile_mark(s);
+  hipLaunchKernelGGL(ab_zero_unkept_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.base, dk, dv,
+                     p.cu_kv, p.G, p.nb_max, w.nbk_g);
   profile_mark(s);
   auto item = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k, v, dout,

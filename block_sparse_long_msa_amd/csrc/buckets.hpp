@@ -24,11 +24,12 @@ namespace {
 
 // Entries per counting / scatter tile: the scatter walks a tile with one
 // wave, so small tiles run more of it in parallel, while the column scan
-// walks the tiles of a bucket in order, so there should not be too many:
-// 1024 entries, doubled up to 4096 while a group has more than 1024 tiles.
-inline int64_t bucket_tile(int64_t nent_g) {
+// walks the tiles of a bucket in order and every tile has a histogram of all
+// of a group's buckets: 1024 entries, doubled up to 4096 while a group has
+// more than 1024 tiles or more than 2^20 (tile, bucket) counts.
+inline int64_t bucket_tile(int64_t nent_g, int64_t nbk_g) {
   int64_t t = 1024;
-  while (t < 4096 && nent_g > t * 1024) t *= 2;
+  while (t < 4096 && (nent_g > t * 1024 || (nent_g + t - 1) / t * nbk_g > (1 << 20))) t *= 2;
   return t;
 }
 

@@ -53,9 +53,9 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 IbWs ib_carve(const Dims &p, void *base) {
   IbWs w;
   w.nent_g = p.total_q * (int64_t)p.top_k;
-  w.tile = bucket_tile(w.nent_g);
-  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
+  w.tile = bucket_tile(w.nent_g, w.nbk_g);
+  w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
   size_t off = 0;
   char *c = static_cast<char *>(base);
   auto take = [&](size_t bytes) {
