@@ -38,7 +38,7 @@ namespace {
 constexpr int kD = 128;           // head dimension
 constexpr int kBS = 128;          // block size
 constexpr int kRows = 64;         // (query, head) rows per step
-constexpr int kSteps = 32;        // steps per work item
+constexpr int kSteps = 64;        // steps per work item
 constexpr int kItemThreads = 512;  // 8 waves: 4 key groups x 2 halves
 
 struct AbWs {
