@@ -13,9 +13,10 @@
 // is applied per row), in (row, slot) order (buckets.hpp).  A work item is
 // up to kSteps steps of one bucket's list; a step is 64 (query, head) rows.
 // The item keeps its block's K and V in LDS for all its steps and
-// accumulates dK, dV of the block in registers; every step writes the rows' dQ contribution of this block into
-// the row's slot (bf16), which a merge then sums in slot order.  No
-// floating-point atomics: every sum has a fixed order.
+// accumulates dK, dV of the block in registers; every step writes the rows'
+// dQ contribution of this block into the row's slot (bf16), which a merge
+// then sums in slot order.  No floating-point atomics: every sum has a fixed
+// order.
 //
 // Kernels, in launch order:
 //   ab_dsum      D = rowsum(dO * O) per (row, head)
