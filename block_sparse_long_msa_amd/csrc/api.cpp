@@ -330,12 +330,24 @@ msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const
                   "index_bwd");
 }
 
+namespace {
+// The MFMA backward takes bf16 with head_dim 128, block_size 128 and 1, 2, 4,
+// 8 or 16 heads per group; every other problem takes the plain FMA one.
+bool attn_bwd_mfma(const msa_problem_t *prob, const msa::Dims &d) {
+  return prob->dtype == MSA_BF16 && msa::attn_bwd_supported(d);
+}
+size_t attn_bwd_bytes(const msa_problem_t *prob, const msa::Dims &d) {
+  return attn_bwd_mfma(prob, d) ? msa::attn_bwd_workspace_bytes(d)
+                                : msa::attn_bwd_fma_workspace_bytes(d);
+}
+}  // namespace
+
 msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes) {
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);
   if (st != MSA_SUCCESS) return st;
   if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
-  *bytes = msa::attn_bwd_workspace_bytes(d);
+  *bytes = attn_bwd_bytes(prob, d);
   return ok();
 }
 
@@ -347,12 +359,6 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);
   if (st != MSA_SUCCESS) return st;
-  if (prob->dtype != MSA_BF16)
-    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "the attention backward takes bf16 tensors");
-  if (!msa::attn_bwd_supported(d))
-    return fail(MSA_ERR_BAD_SHAPE,
-                "the attention backward needs head_dim 128, block_size 128 and a head count "
-                "per KV group that divides 64");
   const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
   if ((st = check_tensor(q, "q", any_q)) != MSA_SUCCESS) return st;
   if ((st = check_tensor(k, "k", any_kv)) != MSA_SUCCESS) return st;
@@ -370,7 +376,7 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
     return fail(MSA_ERR_BAD_SHAPE,
                 "num_seqs * ceil(max_kv_len / block_size) must be at most 16384 for the "
                 "attention backward (one LDS histogram bin per (sequence, block))");
-  const size_t need = msa::attn_bwd_workspace_bytes(d);
+  const size_t need = attn_bwd_bytes(prob, d);
   if (workspace_bytes_given < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace_bytes_given);
@@ -378,6 +384,11 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
   if (need > 0 && !aligned(workspace, 256))
     return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   if (!any_q && !any_kv) return ok();
+  if (!attn_bwd_mfma(prob, d))
+    return launched(msa::launch_attn_bwd_fma(d, prob->dtype == MSA_BF16, q, k, v, block_idx, out,
+                                             lse, dout, dq, dk, dv, workspace,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "attn_bwd_fma");
   return launched(msa::launch_attn_bwd_bf16(
                       d, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                       static_cast<const uint16_t *>(v), block_idx,

@@ -74,6 +74,14 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
                                 const float *lse, const uint16_t *dout, float *dq, float *dk,
                                 float *dv, void *workspace, hipStream_t s);
 
+// The same backward with plain fp32 FMA for every other shape and dtype
+// (attn_bwd_fma.hip).
+size_t attn_bwd_fma_workspace_bytes(const Dims &p);
+hipError_t launch_attn_bwd_fma(const Dims &p, bool bf16, const void *q, const void *k,
+                               const void *v, const int32_t *block_idx, const void *out,
+                               const float *lse, const void *dout, float *dq, float *dk,
+                               float *dv, void *workspace, hipStream_t s);
+
 // Indexer KL objective over the kept blocks (indexer_kl.hip).
 hipError_t launch_indexer_kl(const Dims &p, const float *scores, const int32_t *block_idx,
                              const float *block_mass, float *kl, float *grad, hipStream_t s);

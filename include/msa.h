@@ -223,15 +223,16 @@ msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const
  *   dk[s, g]  = scale * sum over (t, h of g) keeping s of dS_s q[t, h]
  *   dv[s, g]  = sum over (t, h of g) keeping s of P_s dout[t, h]
  * Rows without a kept causal key get dq 0; keys that no row keeps get dk and
- * dv 0.  q, k, v, out and dout are bf16 (dtype MSA_BF16, else
- * MSA_ERR_UNSUPPORTED_DTYPE); dq [total_q, H, d], dk and dv [total_kv, G, d]
- * are fp32, fully written.  Sums are fp32 and deterministic (no
- * floating-point atomics); each slot's share of dq is rounded to bf16 before
- * the slots are added.  Requirements beyond the common ones: head_dim 128,
- * block_size 128, H/G dividing 64, total_q * top_k * H < 2^31 and
- * num_seqs * NBmax <= 16384 (else MSA_ERR_BAD_SHAPE).  All tensors 16-byte
- * aligned; `workspace` must hold msa_sparse_attn_bwd_workspace_size() bytes,
- * 256-byte aligned. */
+ * dv 0.  q, k, v, out and dout have the problem's dtype; dq [total_q, H, d],
+ * dk and dv [total_kv, G, d] are fp32, fully written.  Sums are fp32 and
+ * deterministic (no floating-point atomics).  bf16 problems with head_dim
+ * 128, block_size 128 and H/G in {1, 2, 4, 8, 16} run on the matrix cores,
+ * rounding P and dS to bf16 for the products that use them and each slot's
+ * share of dq to bf16 before the slots are added; every other problem runs
+ * plain fp32 multiply-adds.  Requirements beyond the common ones:
+ * total_q * top_k * H < 2^31 and num_seqs * NBmax <= 16384 (else
+ * MSA_ERR_BAD_SHAPE).  All tensors 16-byte aligned; `workspace` must hold
+ * msa_sparse_attn_bwd_workspace_size() bytes, 256-byte aligned. */
 msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes);
 msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const void *k,
                                  const void *v, const int32_t *block_idx, const void *out,

@@ -283,10 +283,14 @@ def test_attn_bwd_shapes_dtype_workspace():
     assert _abwd(p, ws=FAKE, wsb=n.value - 1) == 5
     assert _abwd(p, ws=None, wsb=n.value) == 1
     assert _abwd(p, ws=FAKE + 16, wsb=n.value) == 4
-    assert _abwd(_prob(dtype=1)) == 3                      # fp32 tensors
-    assert _abwd(_prob(head_dim=64)) == 2
-    assert _abwd(_prob(block_size=64)) == 2
-    assert _abwd(_prob(num_q_heads=6, num_kv_groups=2)) == 2  # 3 heads per group
+    # fp32, head_dim 64, block_size 64 and 3 heads per group take the FMA
+    # kernels, with a workspace of their own
+    for other in (_prob(dtype=1), _prob(head_dim=64), _prob(block_size=64),
+                  _prob(num_q_heads=6, num_kv_groups=2)):
+        m = ctypes.c_size_t(0)
+        assert lib.msa_sparse_attn_bwd_workspace_size(ctypes.byref(other), ctypes.byref(m)) == 0
+        assert m.value > 0
+        assert _abwd(other, ws=FAKE, wsb=m.value - 1) == 5
     wide = _prob(num_seqs=3, max_kv_len=128 * 8000, total_kv=3 * 128 * 8000, max_q_len=1, total_q=3)
     assert _abwd(wide, ws=FAKE, wsb=1 << 40) == 2
     assert lib.msa_sparse_attn_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,

@@ -37,10 +37,10 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def _close(gpu, ref, name):
+def _close(gpu, ref, name, tol=TOL):
     scale = max(float(np.abs(ref).max()) if ref.size else 0.0, 1e-30)
     err = float(np.abs(gpu - ref).max()) / scale if ref.size else 0.0
-    assert err <= TOL, f"{name}: max error {err:.3g} x max |ref| > {TOL}"
+    assert err <= tol, f"{name}: max error {err:.3g} x max |ref| > {tol}"
     return err
 
 
@@ -51,13 +51,13 @@ def _cu(lengths):
     return cu
 
 
-def _forward_and_backward(inp, H, G, d, di, B, k, block_idx=None, seed=5):
-    prob = C.problem_for(inp, H, G, d, di, B, k, "bf16")
+def _forward_and_backward(inp, H, G, d, di, B, k, block_idx=None, seed=5, dtype="bf16"):
+    prob = C.problem_for(inp, H, G, d, di, B, k, dtype)
     if block_idx is None:
         scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
         block_idx = msa.topk_select(prob, scores)
     out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], block_idx, return_lse=True)
-    dout = W.random_out_grad(seed, prob.total_q, H, d, "bf16", device=DEV)
+    dout = W.random_out_grad(seed, prob.total_q, H, d, dtype, device=DEV)
     dq, dk, dv = msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], block_idx, out, lse, dout)
     torch.cuda.synchronize()
     return prob, block_idx, out, lse, dout, dq, dk, dv
@@ -223,3 +223,33 @@ def test_attn_backward_no_query_rows():
     torch.cuda.synchronize()
     assert dq.numel() == 0
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+FMA_CASES = [
+    # name, len_q, len_kv, H, G, d, B, k, dtype, tolerance (x max |ref|)
+    ("f32-d64-B64", [300, 1, 130], [500, 129, 130], 4, 2, 64, 64, 4, "f32", 1e-4),
+    ("f32-d128-B128", [200, 70], [400, 70], 2, 1, 128, 128, 3, "f32", 1e-4),
+    ("bf16-d64-B64", [250, 100], [600, 100], 8, 2, 64, 64, 5, "bf16", TOL),
+    ("bf16-hpg3", [200], [450], 6, 2, 128, 128, 3, "bf16", TOL),
+]
+
+
+@pytest.mark.parametrize("case", FMA_CASES, ids=[c[0] for c in FMA_CASES])
+def test_attn_backward_fma_path(case):
+    """Problems outside the MFMA kernel's shapes (fp32, head dim 64, block size
+    64, 3 heads per group) take the plain fp32 FMA kernels: every row and key
+    against the oracle; fp32 inputs to 1e-4 of max |ref|.  Deterministic."""
+    name, lq, lkv, H, G, d, B, k, dtype, tol = case
+    di = 64
+    inp = W.random_case(62, lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+    _log(f"{name}: GPU")
+    prob, bi, out, lse, dout, dq, dk, dv = _forward_and_backward(inp, H, G, d, di, B, k,
+                                                                 dtype=dtype)
+    _, _, _, _, _, dq2, dk2, dv2 = _forward_and_backward(inp, H, G, d, di, B, k, block_idx=bi,
+                                                         dtype=dtype)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    _log(f"{name}: oracle")
+    rq, rk, rv = _oracle_all(inp, bi, dout, B, d)
+    e = (_close(dq.cpu().numpy(), rq, "dq", tol), _close(dk.cpu().numpy(), rk, "dk", tol),
+         _close(dv.cpu().numpy(), rv, "dv", tol))
+    _log(f"{name}: errors dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
