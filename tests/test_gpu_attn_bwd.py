@@ -253,3 +253,28 @@ def test_attn_backward_fma_path(case):
     e = (_close(dq.cpu().numpy(), rq, "dq", tol), _close(dk.cpu().numpy(), rk, "dk", tol),
          _close(dv.cpu().numpy(), rv, "dv", tol))
     _log(f"{name}: errors dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
+
+
+@pytest.mark.parametrize("shape", ["query-major-forward", "decode-rows"])
+def test_attn_backward_other_forward_shapes(shape):
+    """The backward from the query-major forward's out and LSE, and on
+    decode-shaped rows (one query per sequence: many single-entry buckets),
+    every row and key against the oracle."""
+    d, di, B = 128, 64, 128
+    if shape == "query-major-forward":
+        lq, lkv, H, G, k, sched = [300, 130], [700, 130], 8, 2, 4, "query_major"
+    else:
+        lq, lkv, H, G, k, sched = [1] * 9, [130, 1000, 257, 64, 1, 700, 384, 129, 2048], 8, 2, 6, "auto"
+    inp = W.random_case(63, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    prob = C.problem_for(inp, H, G, d, di, B, k, "bf16", sched)
+    scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
+    bi = msa.topk_select(prob, scores)
+    out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], bi, return_lse=True)
+    dout = W.random_out_grad(6, prob.total_q, H, d, "bf16", device=DEV)
+    _log(f"{shape}: GPU")
+    dq, dk, dv = msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], bi, out, lse, dout)
+    torch.cuda.synchronize()
+    rq, rk, rv = _oracle_all(inp, bi, dout, B, d)
+    e = (_close(dq.cpu().numpy(), rq, "dq"), _close(dk.cpu().numpy(), rk, "dk"),
+         _close(dv.cpu().numpy(), rv, "dv"))
+    _log(f"{shape}: errors dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
