@@ -341,7 +341,11 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * q4 + i;
-        const float pv = keypos > (int64_t)(int32_t)p4[i] ? 0.f : exp2f(sacc[r] * c2 - l4[i]);
+        // the hardware exp2 (weights below 2^-126 become 0, far below the
+        // bf16 rounding P gets next; exp2(-inf) = 0 for rows past the item)
+        const float pv = keypos > (int64_t)(int32_t)p4[i]
+                             ? 0.f
+                             : __builtin_amdgcn_exp2f(sacc[r] * c2 - l4[i]);
         sacc[r] = pv;
         pacc[r] = pv * (pacc[r] - d4[i]);
       }
