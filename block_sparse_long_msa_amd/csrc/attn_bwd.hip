@@ -251,24 +251,25 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   }
 
-  // Rows of a step: thread tid loads pieces (tid / 64) and (tid / 64) + 8 of
-  // row r = tid % 64 of Q and dO, and the row's LSE and D.  The list entry
+  // Rows of a step: thread tid loads pieces tid % 8 and tid % 8 + 8 of row
+  // tid / 8 of Q and dO, and the row's LSE and D.  The list entry
   // naming the row is read one step earlier still (by the first wave, into
   // the m_ent ring), so no load of a step waits for another; rows past the
   // item repeat its last entry (valid memory) and are switched off when
   // staged.
-  const int r_me = tid & 63;
+  const int r_me = tid & 63;            // row of the entry ring slot this thread fills
+  const int r_ld = tid >> 3, pc0 = tid & 7;  // row and first piece this thread loads
   auto load_entry = [&](int st) { return lists[first + min(st * E + r_me / hpg, n - 1)]; };
   u32x4 fq[2], fo[2];
   float f_lse = 0.f, f_d = 0.f;
   int32_t f_e = 0;
   auto fetch = [&](int32_t e) {
     const int64_t t = e / K;
-    const int h = g * hpg + r_me % hpg;
+    const int h = g * hpg + r_ld % hpg;
     const int64_t roff = (t * H + h) * (int64_t)kD;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int pc = (tid >> 6) + 8 * u;
+      const int pc = pc0 + 8 * u;  // 8 lanes cover 128 contiguous bytes of the row
       fq[u] = ld16(q + roff + pc * 8);
       fo[u] = ld16(dout + roff + pc * 8);
     }
@@ -279,17 +280,17 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   auto stage_rows = [&](int st) {  // Q, dO and the metadata
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int pc = (tid >> 6) + 8 * u;
-      st16(&qs[off256(r_me, pc * 8)], fq[u]);
-      st16(&os[off256(r_me, pc * 8)], fo[u]);
+      const int pc = pc0 + 8 * u;
+      st16(&qs[off256(r_ld, pc * 8)], fq[u]);
+      st16(&os[off256(r_ld, pc * 8)], fo[u]);
     }
-    if (tid < 64) {
-      const bool ok = st * E + r_me / hpg < n;
+    if (pc0 == 0) {  // one of the row's 8 loading threads
+      const bool ok = st * E + r_ld / hpg < n;
       const int64_t t = f_e / K;
-      m_lse[r_me] = ok ? f_lse * kLog2e : __builtin_inff();
-      m_d[r_me] = ok ? f_d : 0.f;
-      m_pos[r_me] = ok ? (int)(base_pos + (t - q0)) : -1;
-      m_off[r_me] = ok ? f_e * H + g * hpg + r_me % hpg : -1;
+      m_lse[r_ld] = ok ? f_lse * kLog2e : __builtin_inff();
+      m_d[r_ld] = ok ? f_d : 0.f;
+      m_pos[r_ld] = ok ? (int)(base_pos + (t - q0)) : -1;
+      m_off[r_ld] = ok ? f_e * H + g * hpg + r_ld % hpg : -1;
     }
   };
 
@@ -308,7 +309,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       m_ent[1][r_me] = load_entry(1);
     }
     __syncthreads();
-    fetch(m_ent[0][r_me]);
+    fetch(m_ent[0][r_ld]);
     stage_rows(0);
   }
   for (int st = 0; st < nsteps; ++st) {
@@ -363,7 +364,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
     __syncthreads();
     if (st + 1 < nsteps) {
-      fetch(m_ent[(st + 1) & 1][r_me]);
+      fetch(m_ent[(st + 1) & 1][r_ld]);
       if (tid < 64) f_e2 = load_entry(st + 2);
     }
     // phase 2: dV^T += dO^T P, dK^T += Q^T dS (channels 64 hf .., keys 32 kg .., 64 rows)
