@@ -393,15 +393,20 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       qa0 = mfma32x32x16(as_bf16x8(a0), as_bf16x8(b0), qa0);
       qa1 = mfma32x32x16(as_bf16x8(a1), as_bf16x8(b1), qa1);
     }
-    // lane holds row 32 hf + li, channels 32 kg + 8 (r / 4) + 4 hh + r % 4
+    // lane holds row 32 hf + li, channels 32 kg + 8 (r / 4) + 4 hh + r % 4; the
+    // slot buffer keeps them in that order (stored position 32 kg + 16 hh + r,
+    // see dq_channel), so the lane's 16 values are 32 contiguous bytes
     if (my_off >= 0) {
-      uint16_t *dst = dq_part + (int64_t)my_off * kD + 32 * kg + 4 * hh;
+      uint16_t *dst = dq_part + (int64_t)my_off * kD + 32 * kg + 16 * hh;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 val = {pack_bf16x2(qa0[4 * q4] + qa1[4 * q4], qa0[4 * q4 + 1] + qa1[4 * q4 + 1]),
-                           pack_bf16x2(qa0[4 * q4 + 2] + qa1[4 * q4 + 2],
-                                       qa0[4 * q4 + 3] + qa1[4 * q4 + 3])};
-        *reinterpret_cast<u32x2 *>(dst + 8 * q4) = val;
+      for (int hv = 0; hv < 2; ++hv) {
+        u32x4 val;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 8 * hv + 2 * m;
+          val[m] = pack_bf16x2(qa0[r] + qa1[r], qa0[r + 1] + qa1[r + 1]);
+        }
+        st16(dst + 8 * hv, val);
       }
     }
     if (st + 1 < nsteps) {
@@ -476,6 +481,13 @@ __global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restric
   }
 }
 
+// Channel of stored position pos of a dQ slot row: position 32 t + 16 h + 4 i
+// + e holds channel 32 t + 8 i + 4 h + e (the MFMA result order of a lane).
+__device__ __forceinline__ int dq_channel(int pos) {
+  const int t = pos >> 5, h = (pos >> 4) & 1, i = (pos >> 2) & 3, e = pos & 3;
+  return 32 * t + 8 * i + 4 * h + e;
+}
+
 // 16 lanes per (row, head), 8 channels each: dq = scale * sum over the row's
 // kept slots (in slot order) of the slot's dQ.  Slots that are padding or
 // whose block holds no causal key of the row add nothing.
@@ -509,11 +521,12 @@ __global__ __launch_bounds__(256) void ab_dq_kernel(const uint16_t *__restrict__
       acc[2 * m + 1] += bf16_hi(x[m]);
     }
   }
-  float *dst = dq + rh * kD + part * 8;
+  // stored positions 8 part .. 8 part + 7 are two runs of 4 channels
+  float *dst = dq + rh * kD;
   const f32x4 a = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
   const f32x4 c = {acc[4] * scale, acc[5] * scale, acc[6] * scale, acc[7] * scale};
-  *reinterpret_cast<f32x4 *>(dst) = a;
-  *reinterpret_cast<f32x4 *>(dst + 4) = c;
+  *reinterpret_cast<f32x4 *>(dst + dq_channel(8 * part)) = a;
+  *reinterpret_cast<f32x4 *>(dst + dq_channel(8 * part + 4)) = c;
 }
 
 void zero_fill(float *x, int64_t n, hipStream_t s) {
