@@ -198,7 +198,9 @@ msa_status_t msa_indexer_kl(const msa_problem_t *prob, const float *scores,
  * Slots that are padding or whose block holds no causal key add nothing;
  * keys that no slot takes get 0.  The arg-max is an integer decided by
  * floating point: each dot product is summed in fp32 in channel order
- * (every product rounded to fp32, then added), ties to the lower key.
+ * (every product rounded to fp32, then added), ties to the lower key; where
+ * two keys' exact dot products lie within that fp32 rounding of each other,
+ * either may be taken.
  * Sums are fp32, deterministic (no floating-point atomics).  q_idx, k_idx
  * have the problem's dtype; grad [G, total_q, top_k], dq_idx [total_q, G,
  * d_idx] and dk_idx [total_kv, G, d_idx] are fp32, fully written.

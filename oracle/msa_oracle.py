@@ -72,7 +72,7 @@ def num_blocks(len_kv: int, block_size: int) -> int:
 
 
 def block_scores(q_idx, k_idx, pos, block_size: int, num_block_cols: int | None = None,
-                 row_chunk: int = 256) -> np.ndarray:
+                 row_chunk: int = 256, workers: int = 1) -> np.ndarray:
     """Index Branch block scores of one sequence (Summary, paragraph 2).
 
     q_idx: [n, G, d_idx] index queries of the rows to score;
@@ -81,7 +81,8 @@ def block_scores(q_idx, k_idx, pos, block_size: int, num_block_cols: int | None 
     Returns S [G, n, NB] with S[g,t,j] = max over keys s of block j with
     s <= pos[t] of <q_idx[t,g], k_idx[s,g]>, and -inf where block j holds no
     such key.  NB defaults to ceil(len_kv / B); a larger num_block_cols pads
-    with -inf columns.
+    with -inf columns.  Row chunks of each group run on `workers` threads
+    (numpy releases the interpreter lock inside the array operations).
     """
     q = _f64(q_idx)
     pos = np.asarray(pos, dtype=np.int64)
@@ -94,12 +95,22 @@ def block_scores(q_idx, k_idx, pos, block_size: int, num_block_cols: int | None 
     row_chunk = max(1, min(row_chunk, (1 << 24) // max(L, 1)))
     for g in range(G):
         kg = _f64(k_idx[:, g, :])
-        for r0 in range(0, n, row_chunk):
+
+        def one_chunk(r0):
             r1 = min(n, r0 + row_chunk)
             dots = np.full((r1 - r0, nb * block_size), NEG_INF)
             dots[:, :L] = q[r0:r1, g, :] @ kg.T           # token-level dot products
             dots[key_pos[None, :] > pos[r0:r1, None]] = NEG_INF   # causal keys only
             S[g, r0:r1, :nb] = dots.reshape(r1 - r0, nb, block_size).max(axis=2)
+
+        chunks = range(0, n, row_chunk)
+        if workers <= 1:
+            for r0 in chunks:
+                one_chunk(r0)
+        else:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(max_workers=workers) as ex:
+                list(ex.map(one_chunk, chunks))
     return S
 
 
@@ -131,6 +142,60 @@ def select_blocks(S, pos, block_size: int, top_k: int) -> np.ndarray:
     return out
 
 
+def select_blocks_vectorised(S, pos, block_size: int, top_k: int,
+                             row_chunk: int = 1024, workers: int = 1) -> np.ndarray:
+    """The rule of select_blocks for many rows at once (same result on every
+    input; pinned against it), for checking whole score tensors.
+
+    Per row with current block J and m = k-1 free picks: if J <= m, keep
+    0..J.  Otherwise let tau be the m-th largest of the candidates 0..J-1;
+    keep every candidate above tau and, of those equal to tau, the lowest
+    indices until m are kept (this is "score descending, then index
+    ascending"); add J.  S may be fp32: comparisons are exact in any
+    precision.  Row chunks run on `workers` threads (numpy releases the
+    interpreter lock inside these array operations).  Returns int32
+    [G, n, k], ascending, padded with -1."""
+    S = np.asarray(S)
+    pos = np.asarray(pos, dtype=np.int64)
+    G, n, nb = S.shape
+    m = top_k - 1
+    out = np.full((G, n, top_k), -1, dtype=np.int32)
+    cols = np.arange(nb)
+
+    def one_chunk(g, r0):
+        r1 = min(n, r0 + row_chunk)
+        J = pos[r0:r1] // block_size
+        keep = cols[None, :] <= J[:, None]            # rows with J <= m keep 0..J
+        big = J > m
+        if m > 0 and big.any():
+            x = S[g, r0:r1][big]
+            cand = cols[None, :] < J[big][:, None]
+            x = np.where(cand, x, -np.inf)
+            tau = -np.partition(-x, m - 1, axis=1)[:, m - 1:m]   # m-th largest
+            gt = x > tau
+            eq = (x == tau) & cand
+            need = m - gt.sum(axis=1, keepdims=True)
+            kb = gt | (eq & (np.cumsum(eq, axis=1) <= need))
+            kb |= cols[None, :] == J[big][:, None]
+            keep[big] = kb
+        elif big.any():                                  # k = 1: only the current block
+            keep[big] = cols[None, :] == J[big][:, None]
+        cnt = keep.sum(axis=1)
+        first = np.argsort(~keep, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+        first[np.arange(top_k)[None, :] >= cnt[:, None]] = -1
+        out[g, r0:r1] = first
+
+    jobs = [(g, r0) for g in range(G) for r0 in range(0, n, row_chunk)]
+    if workers <= 1:
+        for g, r0 in jobs:
+            one_chunk(g, r0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda a: one_chunk(*a), jobs))
+    return out
+
+
 def kept_keys(block_row, p: int, block_size: int) -> np.ndarray:
     """Key positions attended by a query at position p given its kept blocks."""
     keys = []
@@ -151,7 +216,8 @@ def sparse_attention(q, k, v, block_idx, pos, block_size: int, scale: float):
     (s <= pos[t]) of the kept blocks of (g, t).  One softmax over that set:
       z_s = scale * <q[t,h], k[s,g]>,  w = exp(z - max z),
       out[t,h] = sum_s w_s v[s,g] / sum_s w_s,  lse[t,h] = max z + log sum w.
-    Returns (out [n, H, d], lse [n, H]) in float64.
+    The heads of a group share the key set, so they are taken together (one
+    column of z per head).  Returns (out [n, H, d], lse [n, H]) in float64.
     """
     qf = _f64(q)
     n, H, d = qf.shape
@@ -161,35 +227,38 @@ def sparse_attention(q, k, v, block_idx, pos, block_size: int, scale: float):
     out = np.zeros((n, H, dv))
     lse = np.full((n, H), NEG_INF)
     pos = np.asarray(pos, dtype=np.int64)
-    for t in range(n):
-        for g in range(G):
+    for g in range(G):
+        k_all = _f64(k[:, g, :])              # the group's keys and values, upcast once
+        v_all = _f64(v[:, g, :])
+        for t in range(n):
             keys = kept_keys(block_idx[g, t], int(pos[t]), block_size)
             if keys.size == 0:
                 continue
-            kg = _gather_f64(k, keys, g)
-            vg = _gather_f64(v, keys, g)
-            for h in range(g * hpg, (g + 1) * hpg):
-                z = scale * (kg @ qf[t, h])
-                m = z.max()
-                w = np.exp(z - m)
-                l = w.sum()
-                out[t, h] = (w @ vg) / l
-                lse[t, h] = m + np.log(l)
+            kg = k_all[keys]
+            vg = v_all[keys]
+            hs = slice(g * hpg, (g + 1) * hpg)
+            z = scale * (kg @ qf[t, hs].T)           # [keys, heads]
+            m = z.max(axis=0)
+            w = np.exp(z - m)
+            l = w.sum(axis=0)
+            out[t, hs] = (w.T @ vg) / l[:, None]
+            lse[t, hs] = m + np.log(l)
     return out, lse
 
 
 def msa_forward(q, k, v, q_idx, k_idx, len_q: int, len_kv: int, block_size: int,
-                top_k: int, scale: float, rows=None):
+                top_k: int, scale: float, rows=None, workers: int = 1):
     """Whole path for one sequence: scores -> kept blocks -> attention.
 
     `rows` optionally restricts the computation to a subset of the
     sequence's query rows (indices into 0..len_q-1); the inputs are always
-    the whole sequence.  Returns dict(scores, block_idx, out, lse, pos).
+    the whole sequence.  `workers` threads share the scoring.  Returns
+    dict(scores, block_idx, out, lse, pos).
     """
     pos_all = query_positions(len_q, len_kv)
     rows = np.arange(len_q) if rows is None else np.asarray(rows, dtype=np.int64)
     pos = pos_all[rows]
-    S = block_scores(q_idx[rows], k_idx, pos, block_size)
+    S = block_scores(q_idx[rows], k_idx, pos, block_size, workers=workers)
     idx = select_blocks(S, pos, block_size, top_k)
     out, lse = sparse_attention(q[rows], k, v, idx, pos, block_size, scale)
     return {"scores": S, "block_idx": idx, "out": out, "lse": lse, "pos": pos}
@@ -270,22 +339,17 @@ def indexer_kl(S, block_idx, mass):
     return kl, grad
 
 
-def block_argmax_f32(q_row, k_rows) -> int:
-    """Index of the largest fp32 dot product of q_row with each row of k_rows,
-    ties to the lowest index.  Each dot product is summed in fp32 in channel
-    order 0, 1, ..., d-1: every product is rounded to fp32 (exact for bf16
-    inputs, where a fused multiply-add gives the same value), then added with
-    fp32 rounding.  The arg-max is an integer decided by floating point; it is
-    taken in this fp32 precision so that both sides decide it the same way."""
-    q = np.asarray(_f64(q_row), dtype=np.float32)
-    kr = np.asarray(_f64(k_rows), dtype=np.float32)
-    acc = np.zeros(kr.shape[0], dtype=np.float32)
-    for c in range(q.shape[0]):
-        acc = (acc + q[c] * kr[:, c]).astype(np.float32)
-    return int(np.argmax(acc))          # first maximum: the lowest index
+def block_argmax(q_row, k_rows) -> int:
+    """Index of the largest dot product of q_row with each row of k_rows, ties
+    to the lowest index: the key that attains a max-pooled block score
+    (Summary, paragraph 2).  fp64 dot products of the upcast inputs, as every
+    score of this module; no lower precision is imitated."""
+    dots = _f64(k_rows) @ _f64(q_row)
+    return int(np.argmax(dots))          # first maximum: the lowest index
 
 
-def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
+def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad,
+                   return_argmax: bool = False):
     """Backward of the Index Branch's max-pooling (Summary, paragraph 2: the
     scores are max-pooled token-level dot products, so a score's gradient
     reaches the one causal key that attains the block's maximum).
@@ -293,11 +357,13 @@ def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
     q_idx: [n, G, d_idx]; k_idx: [len_kv, G, d_idx]; block_idx, grad: [G, n, k];
     pos: [n].  For every kept slot (g, t, i) with block j = block_idx[g,t,i] >= 0
     and causal keys s <= pos[t] of block j, a = the arg-max key
-    (block_argmax_f32), and
+    (block_argmax: fp64 dot products, ties to the lower key), and
       dq_idx[t, g] += grad[g,t,i] * k_idx[a, g]
       dk_idx[a, g] += grad[g,t,i] * q_idx[t, g]
     Slots whose block holds no causal key contribute nothing.  Returns
-    (dq_idx [n, G, d_idx], dk_idx [len_kv, G, d_idx]) in float64.
+    (dq_idx [n, G, d_idx], dk_idx [len_kv, G, d_idx]) in float64, and with
+    return_argmax also argmax [G, n, k] int64 (the key of each slot, -1 where
+    the slot adds nothing).
     """
     G, n, K = block_idx.shape
     L, _, di = k_idx.shape
@@ -305,6 +371,7 @@ def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
     grad = np.asarray(grad, dtype=np.float64)
     dq = np.zeros((n, G, di))
     dk = np.zeros((L, G, di))
+    amax = np.full((G, n, K), -1, dtype=np.int64)
     for g in range(G):
         kg = _f64(k_idx[:, g, :])
         for t in range(n):
@@ -317,9 +384,12 @@ def index_backward(q_idx, k_idx, block_idx, pos, block_size: int, grad):
                 s1 = min(s0 + block_size, int(pos[t]) + 1, L)
                 if s1 <= s0:
                     continue
-                a = s0 + block_argmax_f32(qt, kg[s0:s1])
+                a = s0 + block_argmax(qt, kg[s0:s1])
+                amax[g, t, i] = a
                 dq[t, g] += grad[g, t, i] * kg[a]
                 dk[a, g] += grad[g, t, i] * qt
+    if return_argmax:
+        return dq, dk, amax
     return dq, dk
 
 

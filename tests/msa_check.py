@@ -18,6 +18,7 @@ Expected values come only from the oracle; the GPU's outputs are never fed to it
 from __future__ import annotations
 
 import math
+import time
 from typing import Dict, Optional, Sequence
 
 import numpy as np
@@ -40,11 +41,27 @@ def problem_for(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int, d
                        k, dtype, 1.0 / math.sqrt(d), schedule)
 
 
-def score_bound(q_idx_rows, k_idx, pos, B: int) -> np.ndarray:
-    """Per-block max of sum_c |q_c k_c| over causal keys (the same pooling as S)."""
-    qa = np.abs(O._f64(q_idx_rows))
-    ka = np.abs(O._f64(k_idx))
-    return O.block_scores(qa, ka, pos, B)
+def score_bound(q_idx_rows, k_idx, pos, B: int, cheap: bool = False) -> np.ndarray:
+    """Per-block max of sum_c |q_c k_c| over causal keys (the same pooling as S).
+
+    cheap: the Cauchy-Schwarz bound |q|_2 * max over the block's keys of
+    |k_s|_2 instead (never smaller, so the acceptance bound only loosens;
+    it costs one norm per key instead of a second scoring pass)."""
+    if not cheap:
+        qa = np.abs(O._f64(q_idx_rows))
+        ka = np.abs(O._f64(k_idx))
+        return O.block_scores(qa, ka, pos, B)
+    q = O._f64(q_idx_rows)
+    n, G, _ = q.shape
+    L = k_idx.shape[0]
+    nb = O.num_blocks(L, B)
+    qn = np.sqrt((q * q).sum(axis=2))                                   # [n, G]
+    kn = np.zeros((nb * B, G))
+    for g in range(G):
+        kg = O._f64(k_idx[:, g, :])
+        kn[:L, g] = np.sqrt((kg * kg).sum(axis=1))
+    kmax = kn.reshape(nb, B, G).max(axis=1)                              # [nb, G]
+    return qn.T[:, :, None] * kmax.T[:, None, :]                         # [G, n, nb]
 
 
 def check_scores(gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, d_idx: int) -> float:
@@ -105,14 +122,41 @@ def check_attention(out_gpu: np.ndarray, lse_gpu: Optional[np.ndarray], out_ref:
     return err
 
 
+def check_topk_every_row(scores, idx_gpu, inp: Dict, B: int, k: int, workers: int = 16) -> int:
+    """The Top-k step on its own, on every row: the library's kept lists must
+    equal the oracle's selection rule applied to the scores the library was
+    given (its own fp32 index scores; the selection is exact on its input).
+    The scores themselves are checked against the oracle's on sampled rows.
+    Returns the number of (group, row) lists checked."""
+    s_h = scores.cpu().numpy()
+    i_h = idx_gpu.cpu().numpy()
+    q0 = 0
+    n = 0
+    for lq, lkv in zip(inp["len_q"], inp["len_kv"]):
+        if lq == 0:
+            continue
+        pos = O.query_positions(lq, lkv)
+        ref = O.select_blocks_vectorised(s_h[:, q0:q0 + lq, :], pos, B, k, workers=workers)
+        bad = np.argwhere(np.any(ref != i_h[:, q0:q0 + lq, :], axis=2))
+        assert bad.size == 0, f"{len(bad)} rows differ from the rule, first (group, row) {bad[0]}"
+        n += ref.shape[0] * ref.shape[1]
+        q0 += lq
+    return n
+
+
 def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int, dtype: str,
                   rows_per_seq: Optional[Sequence[Sequence[int]]] = None,
-                  schedule: str = "auto", shuffle_slots: bool = False) -> Dict[str, float]:
+                  schedule: str = "auto", shuffle_slots: bool = False,
+                  topk_every_row: bool = False, cheap_bound: bool = False,
+                  progress: bool = False) -> Dict[str, float]:
     """Run the whole path on the GPU and check sampled rows (all rows if None).
 
     With shuffle_slots, the attention gets every row's kept-block list in a
     seeded random order (the -1 padding included): the result must not
-    depend on the order of the list."""
+    depend on the order of the list.  With topk_every_row, the selection of
+    every row is also checked against the rule applied to the library's own
+    scores (check_topk_every_row).  cheap_bound takes the Cauchy-Schwarz score
+    bound (score_bound).  progress prints a line per oracle sequence."""
     prob = problem_for(inp, H, G, d, d_idx, B, k, dtype, schedule)
     dev = inp["q"].device
     scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
@@ -137,11 +181,30 @@ def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int,
         k_h = inp["k"][sl_kv].cpu()
         v_h = inp["v"][sl_kv].cpu()
         q_h = inp["q"][sl_q].cpu()
-        r = O.msa_forward(q_h, k_h, v_h, q_idx_h, k_idx_h, lq, lkv, B, k, 1.0 / math.sqrt(d),
-                          rows=rows)
+        t0 = time.perf_counter()
+        if progress and len(rows) > 128:
+            # many rows: upcast K and V once, run the oracle 128 rows at a
+            # time and report each piece
+            k_h, v_h = O._f64(k_h), O._f64(v_h)
+            parts = []
+            for c0 in range(0, len(rows), 128):
+                parts.append(O.msa_forward(q_h, k_h, v_h, q_idx_h, k_idx_h, lq, lkv, B, k,
+                                           1.0 / math.sqrt(d), rows=rows[c0:c0 + 128],
+                                           workers=16))
+                print(f"  oracle: sequence {si}, rows {c0 + len(parts[-1]['pos'])} of "
+                      f"{len(rows)} after {time.perf_counter() - t0:.1f} s", flush=True)
+            r = {key: np.concatenate([p[key] for p in parts], axis=1 if key in
+                                     ("scores", "block_idx") else 0) for key in parts[0]}
+        else:
+            r = O.msa_forward(q_h, k_h, v_h, q_idx_h, k_idx_h, lq, lkv, B, k, 1.0 / math.sqrt(d),
+                              rows=rows, workers=16)
+            if progress:
+                print(f"  oracle: sequence {si}, {len(rows)} rows after "
+                      f"{time.perf_counter() - t0:.1f} s", flush=True)
         r["rows"] = rows
         r["global_rows"] = rows + q0
-        r["bound"] = score_bound(q_idx_h[torch.from_numpy(rows)], k_idx_h, r["pos"], B)
+        r["bound"] = score_bound(q_idx_h[torch.from_numpy(rows)], k_idx_h, r["pos"], B,
+                                 cheap=cheap_bound)
         ref.append(r)
     # attention on the oracle's selection for the sampled rows
     idx_in = idx_gpu.clone()
@@ -156,6 +219,11 @@ def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int,
     out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], idx_in, return_lse=True)
     torch.cuda.synchronize()
     stats = {"score_ratio": 0.0, "unseparated": 0, "out_err": 0.0, "rows": 0}
+    if topk_every_row:
+        t0 = time.perf_counter()
+        stats["topk_rows_checked"] = check_topk_every_row(scores, idx_gpu, inp, B, k)
+        if progress:
+            print(f"  Top-k of every row checked in {time.perf_counter() - t0:.1f} s", flush=True)
     for r in ref:
         if r is None:
             continue
@@ -171,3 +239,43 @@ def run_and_check(inp: Dict, H: int, G: int, d: int, d_idx: int, B: int, k: int,
             out[gr].float().cpu().numpy(), lse[gr].cpu().numpy(), r["out"], r["lse"], dtype))
         stats["rows"] += len(r["rows"])
     return stats
+
+
+def argmax_tie_band(q_idx_rows, k_idx, block_idx: np.ndarray, pos: np.ndarray, B: int,
+                    d_idx: int):
+    """Slots of the max-pooling backward whose arg-max key fp32 rounding may
+    decide either way.
+
+    The oracle takes each kept slot's arg-max from fp64 dot products (ties to
+    the lower key).  The library sums each dot product in fp32, within
+    gamma_{d_idx} * sum_c |q_c k_c| of the exact value.  A slot is ambiguous
+    when some other causal key s of its block comes within the two rounding
+    bounds of the winner a: dot_s + bound_s >= dot_a - bound_a.  Returns
+    (ambiguous [G, n, k] bool, keys: list over groups of the set of keys that
+    an ambiguous slot may pick, its winner included)."""
+    q = O._f64(q_idx_rows)
+    G, n, K = block_idx.shape
+    L = k_idx.shape[0]
+    gam = gamma(d_idx)
+    amb = np.zeros((G, n, K), dtype=bool)
+    keys = [set() for _ in range(G)]
+    for g in range(G):
+        kg = O._f64(k_idx[:, g, :])
+        for t in range(n):
+            for i in range(K):
+                j = int(block_idx[g, t, i])
+                if j < 0:
+                    continue
+                s0 = j * B
+                s1 = min(s0 + B, int(pos[t]) + 1, L)
+                if s1 - s0 < 2:
+                    continue
+                kr = kg[s0:s1]
+                dots = kr @ q[t, g]
+                bound = gam * (np.abs(kr) @ np.abs(q[t, g]))
+                a = int(np.argmax(dots))
+                near = dots + bound >= dots[a] - bound[a]
+                if near.sum() > 1:
+                    amb[g, t, i] = True
+                    keys[g].update((s0 + np.flatnonzero(near)).tolist())
+    return amb, keys

@@ -169,35 +169,54 @@ def test_empty_batch():
 
 # ---------------------------------------------------------- full workloads --
 
-def _sample_rows(lq, planted, seed, n_random=24):
+def _full_size_rows(lq, planted, seed, B=128):
+    """Rows the oracle checks on a long workload (>= 512): the whole first and
+    last 128-query blocks, the whole block holding the most planted queries of
+    group 0 (besides those two), 8 planted rows of every group, both sides of
+    16 block edges and 128 random rows."""
     rng = np.random.default_rng(seed)
-    rows = set([0, 1, 2, 127, 128, 129, lq - 2, lq - 1])
-    rows.update(rng.integers(0, lq, n_random).tolist())
-    for g_rows in planted:
-        if g_rows:
-            rows.update(rng.choice(g_rows, size=min(3, len(g_rows)), replace=False).tolist())
+    rows = set(range(0, min(B, lq)))
+    rows.update(range(max(0, lq - B), lq))
+    if planted and planted[0]:
+        counts = np.bincount(np.asarray(planted[0]) // B, minlength=-(-lq // B))
+        counts[0] = counts[-1] = -1
+        b = int(np.argmax(counts))
+        rows.update(range(b * B, min(lq, (b + 1) * B)))
+        for g_rows in planted:
+            rows.update(rng.choice(g_rows, size=min(8, len(g_rows)), replace=False).tolist())
+    for e in rng.integers(1, max(2, lq // B), 16).tolist():
+        rows.update([e * B - 1, e * B])
+    rows.update(rng.integers(0, lq, 128).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < lq))
 
 
 @pytest.mark.parametrize("name", ["prefill-32k", "prefill-128k", "chunked-prefill-1m"])
-def test_long_prefill_sampled(name):
+def test_long_prefill(name):
+    """The benchmark's workloads at full size: >= 512 rows against the oracle
+    (scores within the rounding bound, delta-valid selection, attention on the
+    oracle's selection), and the Top-k of every row against the selection rule
+    on the library's own scores."""
     w = W.WORKLOADS[name]
     _log(f"workload {name}: generating")
     inp = W.make_inputs(w, device=DEV, seed=0)
-    rows = [_sample_rows(inp["len_q"][0], inp["planted_q"][0] if inp["planted_q"] else [], 1)]
-    _log(f"workload {name}: running + oracle on {len(rows[0])} rows")
+    rows = [_full_size_rows(inp["len_q"][0], inp["planted_q"][0] if inp["planted_q"] else [], 1)]
+    assert len(rows[0]) >= 512
+    _log(f"workload {name}: running + oracle on {len(rows[0])} rows, Top-k on every row")
     st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
-                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows)
+                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows,
+                         topk_every_row=True, cheap_bound=True, progress=True)
     _log(f"  {st}")
 
 
-def test_decode_workload_sampled():
+def test_decode_workload_every_sequence():
     w = W.WORKLOADS["decode-64x256k"]
     _log("decode workload: generating")
     inp = W.make_inputs(w, device=DEV, seed=0)
-    rows = [[0] if i % 8 == 0 else [] for i in range(w.num_seqs)]
+    rows = [[0]] * w.num_seqs
     st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
-                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows)
+                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows, cheap_bound=True,
+                         progress=True)
+    assert st["rows"] == w.num_seqs
     _log(f"  {st}")
 
 

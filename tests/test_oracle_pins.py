@@ -20,6 +20,7 @@ import torch
 from oracle import msa_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_small.json")
+GOLDEN_CHUNK = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_chunk.json")
 
 
 def _rand(rng, *shape):
@@ -76,12 +77,62 @@ def test_golden_attention_pow2():
     assert np.allclose(lse[rows, 0], np.log(a["lse_terms"]), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("levels", [0, 1, 3])
+def test_select_blocks_vectorised_equals_select_blocks(levels):
+    """The whole-tensor form of the selection rule gives the row loop's
+    result, on rows with many exact ties (integer scores), constant rows,
+    rows with J <= k-1, and k = 1."""
+    rng = np.random.default_rng(31 + levels)
+    for nb, n, B, k in ((40, 300, 8, 7), (33, 129, 8, 1), (64, 120, 2, 64), (17, 60, 4, 2)):
+        L = nb * B
+        pos = O.query_positions(n, L)
+        if levels:
+            S = rng.integers(-levels, levels + 1, (2, n, nb)).astype(np.float32)
+        else:
+            S = rng.standard_normal((2, n, nb)).astype(np.float32)
+        S[:, ::11, :] = 0.5
+        ref = O.select_blocks(S, pos, B, k)
+        got = O.select_blocks_vectorised(S, pos, B, k, row_chunk=37)
+        assert np.array_equal(got, ref), (nb, n, B, k)
+
+
 def test_golden_selection_ties():
     gd = _golden()["selection_ties"]
     S = np.array(gd["scores"], float)[None, None, :]
     pos = np.array([gd["position"]])
     for k, expected in gd["cases"]:
         assert O.select_blocks(S, pos, gd["block_size"], k)[0, 0].tolist() == expected
+
+
+@pytest.mark.parametrize("part", ["chunk", "decode"])
+def test_golden_fewer_queries_than_keys(part):
+    """Queries are the LAST len_q tokens: a 2-query chunk and a decode row of
+    a 6-token sequence, worked by hand with their positions written out
+    (hand_worked_chunk.json).  The whole-path call derives the positions from
+    (len_q, len_kv) itself, so an oracle that put the queries at the first
+    len_q positions fails here."""
+    with open(GOLDEN_CHUNK) as f:
+        gd = json.load(f)
+    c = gd[part]
+    B, k = gd["block_size"], gd["top_k"]
+    k_idx = np.array(gd["k_idx"], float)[:, None, :]
+    q_idx = np.array(c["q_idx"], float)[:, None, :]
+    n, L = c["len_q"], c["len_kv"]
+    assert O.query_positions(n, L).tolist() == c["positions"]
+    v = np.arange(L, dtype=float)[:, None, None]
+    kk = np.zeros((L, 1, 1))
+    q0 = np.zeros((n, 1, 1))
+    r = O.msa_forward(q0, kk, v, q_idx, k_idx, n, L, B, k, 1.0)
+    assert r["pos"].tolist() == c["positions"]
+    assert np.array_equal(r["scores"][0], np.array(c["scores"], float))
+    assert r["block_idx"][0].tolist() == c["block_idx"]
+    assert np.allclose(r["out"][:, 0, 0], c["zero_q_out"], rtol=0, atol=1e-15)
+    assert np.allclose(r["lse"][:, 0], np.log(c["zero_q_lse_terms"]), rtol=0, atol=1e-15)
+    # the same rows through the step functions with the hand-written positions
+    pos = np.array(c["positions"])
+    S = O.block_scores(q_idx, k_idx, pos, B)
+    assert np.array_equal(S[0], np.array(c["scores"], float))
+    assert O.select_blocks(S, pos, B, k)[0].tolist() == c["block_idx"]
 
 
 # ------------------------------------------------------------ block scores ---
@@ -556,7 +607,7 @@ def test_golden_index_backward():
         for i, a in enumerate(row):
             s0 = idx[0, r, i] * gd["block_size"]
             s1 = min(s0 + gd["block_size"], pos[r] + 1)
-            assert s0 + O.block_argmax_f32(q_idx[r, 0], k_idx[s0:s1, 0]) == a
+            assert s0 + O.block_argmax(q_idx[r, 0], k_idx[s0:s1, 0]) == a
     dq, dk = O.index_backward(q_idx, k_idx, idx, pos, gd["block_size"],
                               np.array(gb["grad"], float)[None])
     assert np.array_equal(dq[:, 0], np.array(gb["dq"], float))
@@ -632,15 +683,29 @@ def test_index_backward_is_finite_difference_of_scores():
         assert abs((loss(q_idx, kp) - loss(q_idx, km)) / (2 * eps) - dk[s, g, c]) < 1e-7
 
 
-def test_block_argmax_f32_exact_on_small_integers():
-    """Small-integer inputs make every fp32 partial sum exact, so the arg-max
-    is the exact one, ties to the lowest key."""
+def test_block_argmax_is_first_maximum_of_exact_dots():
+    """The arg-max key is the first maximum of the exactly summed dot
+    products (math.fsum of products that are exact in fp64: bf16-valued
+    inputs), with exact ties planted by repeating rows."""
     rng = np.random.default_rng(4)
-    for _ in range(200):
-        q = rng.integers(-3, 4, 8).astype(float)
-        kr = rng.integers(-3, 4, (16, 8)).astype(float)
-        exact = kr @ q
-        assert O.block_argmax_f32(q, kr) == int(np.flatnonzero(exact == exact.max())[0])
+    for it in range(200):
+        q = torch.tensor(rng.standard_normal(8)).to(torch.bfloat16).double().numpy()
+        kr = torch.tensor(rng.standard_normal((16, 8))).to(torch.bfloat16).double().numpy()
+        if it % 2:
+            kr[rng.integers(16)] = kr[rng.integers(16)]      # an exact tie, in either order
+        exact = [math.fsum(float(a) * float(b) for a, b in zip(q, row)) for row in kr]
+        best = max(exact)
+        assert O.block_argmax(q, kr) == exact.index(best)
+
+
+def test_block_argmax_is_not_fp32_channel_order():
+    """A block where fp32 summation in channel order picks the wrong key:
+    key 0 = (2^24, 1, -2^24) dots q = (1, 1, 1) to exactly 1, but fp32 adds
+    2^24 + 1 -> 2^24 and then returns 0; key 1 = (0.5, 0, 0) dots to 0.5.
+    The arg-max of the definition is key 0."""
+    q = np.array([1.0, 1.0, 1.0])
+    kr = np.array([[2.0 ** 24, 1.0, -2.0 ** 24], [0.5, 0.0, 0.0]])
+    assert O.block_argmax(q, kr) == 0
 
 
 # ------------------------------------------------ Main Branch backward ---

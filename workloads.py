@@ -229,6 +229,15 @@ def random_slot_grads(seed: int, G: int, total_q: int, top_k: int) -> torch.Tens
     return torch.randn((G, total_q, top_k), generator=g, dtype=torch.float32)
 
 
+def small_int_tensor(seed: int, shape, bound: int, dtype: str = "bf16") -> torch.Tensor:
+    """Seeded integers drawn uniformly from [-bound, bound] (CPU), in the
+    given dtype: every product and every partial sum of a short dot product
+    of such vectors is exact in fp32, and exact ties are frequent."""
+    g = torch.Generator(device="cpu").manual_seed(_seed(seed, "small-int", bound))
+    x = torch.randint(-bound, bound + 1, tuple(shape), generator=g).to(torch.float32)
+    return _cast(x, dtype).contiguous()
+
+
 def random_out_grad(seed: int, total_q: int, H: int, d: int, dtype: str = "bf16",
                     device="cpu") -> torch.Tensor:
     """Seeded N(0, 1) upstream gradient of the attention output [total_q, H, d],
