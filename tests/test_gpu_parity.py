@@ -291,3 +291,45 @@ def test_arbitrary_kept_lists(dtype):
             out, lse = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], idx, return_lse=True)
             err = C.check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, dtype)
             _log(f"  max |O - O_ref| = {err:.3g}")
+
+
+def test_cross_layer_reuse():
+    """Cross-layer index reuse (LongCat Sparse Attention page, Abstract,
+    strategy (2)): one Index Branch pass selects the kept blocks, and the
+    attention of two layers, each with its own q, k and v, runs on that one
+    kept list.  The library's selection must be delta-valid against the
+    oracle's; each layer's attention on the oracle's kept lists must match the
+    oracle's attention of that layer on the same lists, on both prefill
+    schedules."""
+    lq, lkv, H, G, d, di, B, k = [900, 333], [1300, 333], 8, 2, 128, 64, 128, 4
+    layer1 = W.random_case(71, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    layer2 = W.random_case(72, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    prob = C.problem_for(layer1, H, G, d, di, B, k, "bf16")
+    scores = msa.index_score(prob, layer1["q_idx"], layer1["k_idx"])
+    idx_gpu = msa.topk_select(prob, scores)
+    lists, refs = [], {1: [], 2: []}
+    q0 = kv0 = 0
+    for a, b in zip(lq, lkv):
+        sq, skv = slice(q0, q0 + a), slice(kv0, kv0 + b)
+        r = O.msa_forward(layer1["q"][sq].cpu(), layer1["k"][skv].cpu(), layer1["v"][skv].cpu(),
+                          layer1["q_idx"][sq].cpu(), layer1["k_idx"][skv].cpu(), a, b, B, k,
+                          1.0 / math.sqrt(d))
+        C.check_selection(idx_gpu[:, sq, :].cpu().numpy(), r["block_idx"], r["scores"],
+                          r["pos"], B, k)
+        lists.append(r["block_idx"])
+        refs[1].append((r["out"], r["lse"]))
+        refs[2].append(O.sparse_attention(layer2["q"][sq].cpu(), layer2["k"][skv].cpu(),
+                                          layer2["v"][skv].cpu(), r["block_idx"], r["pos"], B,
+                                          1.0 / math.sqrt(d)))
+        q0, kv0 = q0 + a, kv0 + b
+    kept = torch.from_numpy(np.concatenate(lists, axis=1)).to(DEV).contiguous()
+    for sched in ("kv_major", "query_major"):
+        p2 = prob.with_schedule(sched)
+        for layer, inp in ((1, layer1), (2, layer2)):
+            out, lse = msa.sparse_attn_fwd(p2, inp["q"], inp["k"], inp["v"], kept,
+                                           return_lse=True)
+            ref_o = np.concatenate([x[0] for x in refs[layer]])
+            ref_l = np.concatenate([x[1] for x in refs[layer]])
+            err = C.check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l,
+                                    "bf16")
+            _log(f"cross-layer reuse, {sched}, layer {layer}: max |O - O_ref| = {err:.3g}")
