@@ -35,7 +35,8 @@ STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHA
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
-            "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_mass", "msa_indexer_kl",
+            "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_noalloc", "msa_sparse_attn_fwd_mass",
+            "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
             "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
             "msa_set_profile_events", "msa_status_string", "msa_last_error_message",
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_workspace_size.restype = st
     lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_sparse_attn_fwd.restype = st
+    lib.msa_sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_sparse_attn_fwd_noalloc.restype = st
     lib.msa_sparse_attn_fwd_mass.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_sparse_attn_fwd_mass.restype = st
     lib.msa_indexer_kl.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -245,6 +248,32 @@ def sparse_attn_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     return out, lse
 
 
+def sparse_attn_fwd_noalloc(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            block_idx: torch.Tensor, out: Optional[torch.Tensor] = None,
+                            return_lse: bool = False, stream: Optional[int] = None,
+                            lse: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """msa_sparse_attn_fwd_noalloc: sparse_attn_fwd on the library's fixed
+    device scratch instead of a workspace (the library allocates nothing;
+    outputs are allocated here only when not given)."""
+    dt = prob.torch_dtype
+    _need(q, "q", (prob.total_q, prob.H, prob.d), dt)
+    _need(k, "k", (prob.total_kv, prob.G, prob.d), dt)
+    _need(v, "v", (prob.total_kv, prob.G, prob.d), dt)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    if out is None:
+        out = torch.empty((prob.total_q, prob.H, prob.d), dtype=dt, device=q.device)
+    _need(out, "out", (prob.total_q, prob.H, prob.d), dt)
+    if lse is None and return_lse:
+        lse = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", (prob.total_q, prob.H), torch.float32)
+    s = _stream(q.device) if stream is None else stream
+    _check(load_library().msa_sparse_attn_fwd_noalloc(prob.ref(), _ptr(q), _ptr(k), _ptr(v),
+                                                      _ptr(block_idx), _ptr(out), _ptr(lse), s))
+    return out, lse
+
+
 def sparse_attn_fwd_mass(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          block_idx: torch.Tensor, out: Optional[torch.Tensor] = None,
                          lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None,
@@ -390,6 +419,7 @@ def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):
 msa_index_score = index_score
 msa_topk_select = topk_select
 msa_sparse_attn_fwd = sparse_attn_fwd
+msa_sparse_attn_fwd_noalloc = sparse_attn_fwd_noalloc
 msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass
 msa_indexer_kl = indexer_kl
 msa_indexer_bwd = indexer_bwd

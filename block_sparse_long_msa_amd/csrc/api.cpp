@@ -140,9 +140,13 @@ size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
   return 0;
 }
 
+// With fixed_scratch, `workspace` is ignored: once every argument has been
+// validated, the library's fixed device scratch (noalloc.hip) serves as the
+// workspace, and a problem that needs more than it holds is rejected.
 msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, const void *v,
                       const int32_t *block_idx, void *out, float *lse, float *block_mass,
-                      void *workspace, size_t workspace_bytes_given, void *stream) {
+                      void *workspace, size_t workspace_bytes_given, void *stream,
+                      bool fixed_scratch = false) {
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);
   if (st != MSA_SUCCESS) return st;
@@ -154,6 +158,21 @@ msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, c
   if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
   if (lse != nullptr && !aligned(lse, 4)) return fail(MSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
   const size_t need = workspace_bytes(prob, d);
+  if (fixed_scratch) {
+    const size_t have = msa::noalloc_scratch_bytes();
+    if (need > have)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                  "this problem needs %zu bytes of scratch; the fixed scratch of the "
+                  "no-allocation call holds %zu (use msa_sparse_attn_fwd with a workspace)",
+                  need, have);
+    workspace = nullptr;
+    workspace_bytes_given = have;
+    if (need > 0 && d.total_q > 0) {
+      const hipError_t e = msa::noalloc_scratch(&workspace);
+      if (e != hipSuccess)
+        return fail(MSA_ERR_DEVICE, "no-allocation scratch lookup: %s", hipGetErrorString(e));
+    }
+  }
   if (workspace_bytes_given < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace_bytes_given);
@@ -245,6 +264,12 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
                                  void *workspace, size_t workspace_bytes_given, void *stream) {
   return attn_fwd(prob, q, k, v, block_idx, out, lse, nullptr, workspace, workspace_bytes_given,
                   stream);
+}
+
+msa_status_t msa_sparse_attn_fwd_noalloc(const msa_problem_t *prob, const void *q, const void *k,
+                                         const void *v, const int32_t *block_idx, void *out,
+                                         float *lse, void *stream) {
+  return attn_fwd(prob, q, k, v, block_idx, out, lse, nullptr, nullptr, 0, stream, true);
 }
 
 msa_status_t msa_sparse_attn_fwd_mass(const msa_problem_t *prob, const void *q, const void *k,

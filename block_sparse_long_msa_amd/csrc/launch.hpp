@@ -82,6 +82,12 @@ hipError_t launch_attn_bwd_fma(const Dims &p, bool bf16, const void *q, const vo
                                const float *lse, const void *dout, float *dq, float *dk,
                                float *dv, void *workspace, hipStream_t s);
 
+// Fixed device scratch of the no-allocation attention entry point
+// (noalloc.hip): its size, and its device address on the current device
+// (looked up once per device with hipGetSymbolAddress).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void **ptr);
+
 // Indexer KL objective over the kept blocks (indexer_kl.hip).
 hipError_t launch_indexer_kl(const Dims &p, const float *scores, const int32_t *block_idx,
                              const float *block_mass, float *kl, float *grad, hipStream_t s);

@@ -145,6 +145,21 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* msa_sparse_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, same kernels and same results as
+ * msa_sparse_attn_fwd, without a workspace: the call uses a fixed scratch
+ * array of 64 MiB that the library holds on every GPU it runs on until the
+ * process ends.  It allocates and frees nothing.  A problem whose
+ * msa_sparse_attn_workspace_size() exceeds 64 MiB is rejected with
+ * MSA_ERR_WORKSPACE_TOO_SMALL before anything is launched (use
+ * msa_sparse_attn_fwd for those).  All calls on one GPU share the scratch:
+ * calls that overlap in time on one GPU (on different streams) race and
+ * must be serialised by the caller; consecutive calls need no clearing. */
+msa_status_t msa_sparse_attn_fwd_noalloc(const msa_problem_t *prob, const void *q, const void *k,
+                                         const void *v, const int32_t *block_idx, void *out,
+                                         float *lse, void *stream);
+
 /* Training support: the target and loss of the indexer's KL objective.  The
  * page (Summary, paragraph 2) trains the Index Branch through a KL
  * objective matched to the group-averaged Main Branch distribution, with

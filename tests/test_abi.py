@@ -298,3 +298,26 @@ def test_attn_bwd_shapes_dtype_workspace():
     # nothing at all to do
     assert _abwd(_prob(max_q_len=0, total_q=0, max_kv_len=0, total_kv=0), q=None, k=None, v=None,
                  idx=None, out=None, lse=None, do=None, dq=None, dk=None, dv=None) == 0
+
+
+def test_noalloc_call_validation():
+    """msa_sparse_attn_fwd_noalloc validates like msa_sparse_attn_fwd and rejects,
+    before anything is launched, a problem whose workspace exceeds its fixed
+    64 MiB scratch."""
+    lib = msa.load_library()
+    p = _prob()
+    assert lib.msa_sparse_attn_fwd_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None,
+                                           None) == 1
+    assert lib.msa_sparse_attn_fwd_noalloc(ctypes.byref(p), FAKE + 2, FAKE, FAKE, FAKE, FAKE,
+                                           None, None) == 4
+    big = _prob(max_q_len=65536, total_q=65536, max_kv_len=65536, total_kv=65536, top_k=16)
+    n = ctypes.c_size_t(0)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > 64 << 20
+    assert lib.msa_sparse_attn_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                           None) == 5
+    assert b"fixed scratch" in lib.msa_last_error_message()
+    # an empty batch is a no-op
+    e = _prob(max_q_len=0, total_q=0)
+    assert lib.msa_sparse_attn_fwd_noalloc(ctypes.byref(e), None, FAKE, FAKE, None, None, None,
+                                           None) == 0
