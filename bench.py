@@ -168,6 +168,18 @@ def hbm_roof(kernel, nbytes, ms):
             "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms}
 
 
+class _nullctx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def decode_shape(prob) -> bool:
+    return prob.max_q_len == 1
+
+
 def run_workload(name, steps, warmup, args, keep_state=False):
     """Times `steps` steps of one workload.  Returns (result dict, state);
     state (inputs and the last step's outputs) only when keep_state."""
@@ -212,6 +224,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         bwd_ws = torch.empty(max(nbw.value, 1), dtype=torch.uint8, device=dev)
     wbytes = msa.workspace_size(prob)
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    fused = args.fused_topk and not decode_shape(prob)
+    if fused:
+        itk_ws = torch.empty(max(msa.index_topk_workspace_size(prob), 1), dtype=torch.uint8,
+                             device=dev)
+        del scores
+        scores = None
     stream = torch.cuda.current_stream(dev)
     sid = stream.cuda_stream
 
@@ -236,13 +254,20 @@ def run_workload(name, steps, warmup, args, keep_state=False):
                                 workspace=workspace, stream=sid,
                                 lse=lse_buf if use_bwd else None)
 
-    def step(ev=None, pev=None, bev=None):
+    def step(ev=None, pev=None, bev=None, fev=None):
         if ev is not None:
             ev[0].record(stream)
-        msa.index_score(prob, inp["q_idx"], inp["k_idx"], scores, stream=sid)
-        if ev is not None:
-            ev[1].record(stream)
-        msa.topk_select(prob, scores, block_idx, stream=sid)
+        if fused:
+            with fev if fev is not None else _nullctx():
+                msa.index_topk(prob, inp["q_idx"], inp["k_idx"], block_idx, workspace=itk_ws,
+                               stream=sid)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            msa.index_score(prob, inp["q_idx"], inp["k_idx"], scores, stream=sid)
+            if ev is not None:
+                ev[1].record(stream)
+            msa.topk_select(prob, scores, block_idx, stream=sid)
         if ev is not None:
             ev[2].record(stream)
         if pev is not None:
@@ -282,6 +307,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(steps)]
     bevents = [msa.ProfileEvents(len(ab_kernels), dev) if use_bwd else None
                for _ in range(steps)]
+    fevents = [msa.ProfileEvents(2, dev) if fused else None for _ in range(steps)]
     log(f"[bench] {name}: {steps} timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -289,7 +315,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        step(events[i], pevents[i], bevents[i])
+        step(events[i], pevents[i], bevents[i], fevents[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -299,8 +325,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
              for i, nm in enumerate(("index_score", "topk_select", "sparse_attn_fwd"))}
     # per-kernel durations over the timed steps: kernel i of the attention call
     # ends at its profile event i
-    kern_all = {index_kernel: [e[0].elapsed_time(e[1]) for e in events],
-                "topk": [e[1].elapsed_time(e[2]) for e in events]}
+    if fused:
+        kern_all = {"index_topk": [e[0].elapsed_time(fe.events[0]) for e, fe in zip(events, fevents)],
+                    "index_topk_merge": [fe.events[0].elapsed_time(fe.events[1]) for fe in fevents]}
+    else:
+        kern_all = {index_kernel: [e[0].elapsed_time(e[1]) for e in events],
+                    "topk": [e[1].elapsed_time(e[2]) for e in events]}
     for i, kn in enumerate(attn_kernels):
         kern_all[kn] = [(e[2] if i == 0 else pe.events[i - 1]).elapsed_time(pe.events[i])
                         for e, pe in zip(events, pevents)]
@@ -338,7 +368,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
                                "design_bytes": part_bytes,
                                "design_gbps": part_bytes / (kern_ms["kv_partial"] * 1e-3) / 1e9}
     dom = max(kern_ms, key=lambda kk: kern_ms[kk])
-    if dom == "index_score_mfma":
+    if dom in ("index_score_mfma", "index_topk"):
         roof = mfma_roof(dom, f_idx, kern_ms[dom])
     elif dom == "ab_item":
         roof = mfma_roof(dom, f_bwd, kern_ms[dom])
@@ -371,12 +401,16 @@ def run_workload(name, steps, warmup, args, keep_state=False):
               "schedule": args.schedule,
               **({"layers_per_index": args.layers} if args.layers > 1 else {}),
               **({"indexer_kl": True} if use_kl else {}),
+              **({"fused_topk": True} if fused else {}),
               **({"attn_bwd": True} if use_bwd else {})}
     res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": w.dtype,
            "config": config, "roofline": roof, "stages": stages, "extra": extra,
            "wall_s_timed": wall, "steps": steps, "warmup": warmup}
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step, {value:.4g} {unit}")
     state = None
+    if keep_state and fused:
+        # the fused call leaves no score tensor: the parity leg scores the rows itself
+        scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
     if keep_state:
         state = {"w": w, "inp": inp, "scores": scores, "block_idx": block_idx, "out": out,
                  "decode": decode, "unit": unit}
@@ -499,6 +533,9 @@ def main():
     ap.add_argument("--attn-bwd", action="store_true",
                     help="training step of the Main Branch: the attention also returns its LSE, "
                          "then the attention backward for a seeded upstream gradient follows")
+    ap.add_argument("--fused-topk", action="store_true",
+                    help="index scoring and Top-k in one call (msa_index_topk, no score tensor) "
+                         "instead of msa_index_score + msa_topk_select")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -511,6 +548,10 @@ def main():
         print(msg, file=sys.stderr, flush=True)
         sys.exit(2)
 
+    if args.fused_topk and args.indexer_kl:
+        print("--indexer-kl needs the score tensor, which --fused-topk does not produce",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     import torch
     torch.cuda.set_device(0)
     also = args.also

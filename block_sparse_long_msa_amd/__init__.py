@@ -34,7 +34,8 @@ STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHA
                 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_DEVICE"}
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
-EXPORTED = ("msa_index_score", "msa_topk_select", "msa_sparse_attn_workspace_size",
+EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size",
+            "msa_index_topk", "msa_sparse_attn_workspace_size",
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_noalloc", "msa_sparse_attn_fwd_mass",
             "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_score.restype = st
     lib.msa_topk_select.argtypes = [P, vp, vp, vp]
     lib.msa_topk_select.restype = st
+    lib.msa_index_topk_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_index_topk_workspace_size.restype = st
+    lib.msa_index_topk.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msa_index_topk.restype = st
     lib.msa_sparse_attn_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.msa_sparse_attn_workspace_size.restype = st
     lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -209,6 +214,33 @@ def topk_select(prob: Problem, scores: torch.Tensor, block_idx: Optional[torch.T
     _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
     s = _stream(scores.device) if stream is None else stream
     _check(load_library().msa_topk_select(prob.ref(), _ptr(scores), _ptr(block_idx), s))
+    return block_idx
+
+
+def index_topk_workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_index_topk_workspace_size(prob.ref(), ctypes.byref(n)))
+    return n.value
+
+
+def index_topk(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
+               block_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream: Optional[int] = None) -> torch.Tensor:
+    """msa_index_topk: the kept blocks [G, total_q, k] int32 straight from the
+    index tensors (index scoring and Top-k fused; no score tensor)."""
+    _need(q_idx, "q_idx", (prob.total_q, prob.G, prob.d_idx), prob.torch_dtype)
+    _need(k_idx, "k_idx", (prob.total_kv, prob.G, prob.d_idx), prob.torch_dtype)
+    if block_idx is None:
+        block_idx = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.int32,
+                                device=q_idx.device)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    need = index_topk_workspace_size(prob)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q_idx.device) if stream is None else stream
+    _check(load_library().msa_index_topk(prob.ref(), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                                         _ptr(workspace), wbytes, s))
     return block_idx
 
 
@@ -418,6 +450,7 @@ def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):
 # Names matching the C entry points.
 msa_index_score = index_score
 msa_topk_select = topk_select
+msa_index_topk = index_topk
 msa_sparse_attn_fwd = sparse_attn_fwd
 msa_sparse_attn_fwd_noalloc = sparse_attn_fwd_noalloc
 msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass

@@ -250,6 +250,44 @@ msa_status_t msa_topk_select(const msa_problem_t *prob, const float *scores, int
                   "topk_select");
 }
 
+msa_status_t msa_index_topk_workspace_size(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = msa::index_topk_workspace_bytes(d);
+  return ok();
+}
+
+msa_status_t msa_index_topk(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                            int32_t *block_idx, void *workspace, size_t workspace_bytes_given,
+                            void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (prob->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "the fused index scoring and Top-k takes bf16 inputs");
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q_idx, "q_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k_idx, "k_idx", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if (!msa::index_topk_supported(d))
+    return fail(MSA_ERR_BAD_SHAPE, "the fused index scoring and Top-k holds at most 1024 "
+                                   "candidates per row (segments x list length)");
+  const size_t need = msa::index_topk_workspace_bytes(d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q) return ok();
+  return launched(msa::launch_index_topk(d, static_cast<const uint16_t *>(q_idx),
+                                         static_cast<const uint16_t *>(k_idx), block_idx,
+                                         workspace, reinterpret_cast<hipStream_t>(stream)),
+                  "index_topk");
+}
+
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes) {
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);

@@ -32,6 +32,15 @@ bool decode_index_supported(const Dims &p);
 hipError_t launch_index_score_f32(const Dims &p, const float *q_idx, const float *k_idx,
                                   float *scores, hipStream_t s);
 
+// Index scoring fused with the Top-k (index_topk.hip): per (query tile, key
+// segment) the k-1 best candidates, then a per-row merge.
+int index_topk_segment(const Dims &p);
+int index_topk_nseg(const Dims &p);
+size_t index_topk_workspace_bytes(const Dims &p);
+bool index_topk_supported(const Dims &p);
+hipError_t launch_index_topk(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx,
+                             int32_t *block_idx, void *workspace, hipStream_t s);
+
 // Top-k with the current block forced.
 hipError_t launch_topk(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s);
 

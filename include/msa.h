@@ -127,6 +127,29 @@ msa_status_t msa_index_score(const msa_problem_t *prob, const void *q_idx, const
 msa_status_t msa_topk_select(const msa_problem_t *prob, const float *scores, int32_t *block_idx,
                              void *stream);
 
+/* Steps 1 and 2 fused, without the score tensor: block_idx as msa_topk_select
+ * would produce it from msa_index_score's scores, bit for bit (the same MFMA
+ * arithmetic scores every candidate block, and the same selection rule keeps
+ * them).  The scores themselves are never written to memory: per tile of 512
+ * queries and segment of key blocks, each query keeps its best candidates
+ * (score descending, then block index ascending; at least top_k - 1 of them)
+ * as the blocks stream by, and a merge over the segments lists the final
+ * blocks ascending with the current block appended.  This follows the page's
+ * selection (Summary, paragraph 2) and its comparison-only Top-k (Summary,
+ * paragraph 3), and removes the O(L^2) score round trip that the LongCat
+ * Sparse Attention page names as the indexer's cost (Abstract).  Let L be
+ * top_k - 1 rounded up to a power of two (at least 4): segments are 8 L
+ * blocks long, and ceil(NBmax / (8 L)) * L <= 1024 is required (every
+ * NBmax <= 8192 fits; else MSA_ERR_BAD_SHAPE).  bf16 only (else
+ * MSA_ERR_UNSUPPORTED_DTYPE).  `workspace` must hold
+ * msa_index_topk_workspace_size() bytes (G * total_q * segments * L 8-byte
+ * keys, a quarter of the score tensor), 256-byte aligned; its contents need
+ * no initialisation. */
+msa_status_t msa_index_topk_workspace_size(const msa_problem_t *prob, size_t *bytes);
+msa_status_t msa_index_topk(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                            int32_t *block_idx, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* Bytes of device workspace msa_sparse_attn_fwd needs for this problem and
  * schedule (0 is possible).  Writes the size to *bytes (host). */
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes);

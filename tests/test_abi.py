@@ -321,3 +321,25 @@ def test_noalloc_call_validation():
     e = _prob(max_q_len=0, total_q=0)
     assert lib.msa_sparse_attn_fwd_noalloc(ctypes.byref(e), None, FAKE, FAKE, None, None, None,
                                            None) == 0
+
+
+def test_index_topk_validation():
+    """The fused index scoring + Top-k call: bf16 only, pointer and workspace
+    checks, sizes from the query function."""
+    lib = msa.load_library()
+    p = _prob()
+    n = ctypes.c_size_t(0)
+    assert lib.msa_index_topk_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    # G * total_q * segments * L keys of 8 bytes: k = 4 -> L = 4, segments of 32 blocks, one
+    assert n.value == 2 * 256 * 1 * 4 * 8
+    call = lambda pp, qi=FAKE, ki=FAKE, bi=FAKE, ws=FAKE, wsb=n.value: lib.msa_index_topk(  # noqa: E731
+        ctypes.byref(pp), qi, ki, bi, ws, wsb, None)
+    assert call(_prob(dtype=1)) == 3
+    assert call(p, qi=None) == 1
+    assert call(p, bi=FAKE + 4) == 4
+    assert call(p, wsb=n.value - 1) == 5
+    assert call(p, ws=None) == 1
+    assert call(p, ws=FAKE + 16) == 4
+    big = _prob(max_kv_len=128 * 8192, total_kv=128 * 8192, top_k=64)
+    assert lib.msa_index_topk_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value == 2 * 256 * 16 * 64 * 8
