@@ -434,3 +434,97 @@ def sparse_attention_backward(q, k, v, block_idx, pos, block_size: int, scale: f
                 np.add.at(dk[:, g, :], keys, scale * np.outer(dz, qf[t, h]))
                 np.add.at(dv[:, g, :], keys, np.outer(a, do[t, h]))
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------------
+# Hierarchical (coarse-to-fine) indexing: an approximation of the selection
+# ("LongCat Sparse Attention" page, Abstract, strategy (3): a coarse-to-fine
+# scoring scheme narrows each query's candidate set to cut the indexing
+# computation).  The page gives no formula; the reading taken here:
+#   * chunks of S consecutive blocks; a chunk's coarse key is the mean of
+#     its B*S index keys (a chunk summary, computed once per cache);
+#   * for a query at position p (current block J, current chunk cJ = J // S),
+#     the coarse candidates are the chunks c < cJ, all of whose keys are
+#     causal; each scores <q_idx, coarse key>;
+#   * the C best of them (score descending, chunk ascending) are kept, or all
+#     of them when there are at most C;
+#   * the fine candidates are the blocks of the kept chunks plus the blocks
+#     of the current chunk below J (the nearby blocks are always scored);
+#     each gets the exact max-pooled block score;
+#   * the k-1 best fine candidates (score descending, block ascending) and J
+#     are kept, as in select_blocks; rows with J <= k-1 keep 0..J.
+# With C at least the number of chunks every candidate block is scored and
+# the result is select_blocks' exactly.
+# ------------------------------------------------------------------------
+
+def chunk_keys(k_idx, block_size: int, chunk_blocks: int) -> np.ndarray:
+    """Coarse keys of one sequence: [n_full_chunks, G, d_idx] fp64, the mean
+    of the index keys of every full chunk of chunk_blocks blocks."""
+    k = _f64(k_idx)
+    L, G, di = k.shape
+    span = block_size * chunk_blocks
+    nfull = L // span
+    return k[:nfull * span].reshape(nfull, span, G, di).mean(axis=1)
+
+
+def hierarchical_select(q_idx, k_idx, pos, block_size: int, top_k: int, chunk_blocks: int,
+                        keep_chunks: int):
+    """Kept blocks of the hierarchical reading above, for rows q_idx [n, G, d_idx]
+    at positions pos of one sequence (k_idx [len_kv, G, d_idx]).
+
+    Returns dict(coarse [G, n, n_full_chunks] (-inf where not a candidate),
+    kept_chunks [G, n, keep_chunks] ascending, -1 padded, fine [G, n, NB]
+    (-inf where not a fine candidate), block_idx [G, n, top_k] ascending,
+    -1 padded)."""
+    q = _f64(q_idx)
+    pos = np.asarray(pos, dtype=np.int64)
+    n, G, _ = q.shape
+    B, S, C, k = block_size, chunk_blocks, keep_chunks, top_k
+    kbar = chunk_keys(k_idx, B, S)
+    nch = kbar.shape[0]
+    nb = num_blocks(k_idx.shape[0], B)
+    exact = block_scores(q_idx, k_idx, pos, B)          # fine scores are exact block scores
+    coarse = np.full((G, n, nch), NEG_INF)
+    kept = np.full((G, n, C), -1, dtype=np.int32)
+    fine = np.full((G, n, nb), NEG_INF)
+    out = np.full((G, n, k), -1, dtype=np.int32)
+    for g in range(G):
+        for t in range(n):
+            J = int(pos[t] // B)
+            cJ = J // S
+            cand_chunks = np.arange(cJ)
+            coarse[g, t, :cJ] = kbar[:cJ, g, :] @ q[t, g]
+            if cJ <= C:
+                keep = cand_chunks
+            else:
+                order = np.lexsort((cand_chunks, -coarse[g, t, :cJ]))
+                keep = np.sort(cand_chunks[order[:C]])
+            kept[g, t, :len(keep)] = keep
+            blocks = [c * S + s for c in keep for s in range(S)] + list(range(cJ * S, J))
+            blocks = np.array(sorted(blocks), dtype=np.int64)
+            fine[g, t, blocks] = exact[g, t, blocks]
+            if J <= k - 1:
+                sel = list(range(J + 1))
+            else:
+                order = np.lexsort((blocks, -fine[g, t, blocks]))
+                sel = sorted(int(j) for j in blocks[order[:k - 1]]) + [J]
+            out[g, t, :len(sel)] = sel
+    return {"coarse": coarse, "kept_chunks": kept, "fine": fine, "block_idx": out}
+
+
+def selection_recall(sel, ref, pos, block_size: int, top_k: int) -> float:
+    """Share of the reference's freely chosen blocks (all but the forced
+    current block, on rows with more than k-1 candidates) that sel keeps."""
+    pos = np.asarray(pos, dtype=np.int64)
+    hit = tot = 0
+    G, n, _ = ref.shape
+    for g in range(G):
+        for t in range(n):
+            J = int(pos[t] // block_size)
+            if J <= top_k - 1:
+                continue
+            r = set(int(x) for x in ref[g, t] if 0 <= x < J)
+            s = set(int(x) for x in sel[g, t] if 0 <= x < J)
+            hit += len(r & s)
+            tot += len(r)
+    return hit / tot if tot else 1.0

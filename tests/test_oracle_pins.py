@@ -798,3 +798,113 @@ def test_attention_backward_finite_differences():
             args_p[which], args_m[which] = ap, am
             fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
             assert abs(fd - grad[ix]) < 1e-7
+
+
+# ------------------------------------------------ hierarchical indexing ---
+
+GOLDEN_HIER = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_hier.json")
+
+
+def test_golden_hierarchical_selection():
+    """A hand-worked coarse-to-fine example: mean-pooled chunk keys (a chunk
+    whose max-pooled score would win loses on its mean), a coarse tie going
+    to the lower chunk, and the fine pick among the kept chunk's blocks."""
+    with open(GOLDEN_HIER) as f:
+        gd = json.load(f)
+    k_idx = np.array(gd["k_idx"], float)[:, None, :]
+    q_idx = np.array(gd["q_idx"], float)[:, None, :]
+    pos = np.array([gd["position"]])
+    r = O.hierarchical_select(q_idx, k_idx, pos, gd["block_size"], gd["top_k"],
+                              gd["chunk_blocks"], gd["keep_chunks"])
+    assert np.array_equal(r["coarse"][0, 0], np.array(gd["coarse"], float))
+    assert r["kept_chunks"][0, 0].tolist() == gd["kept_chunks"]
+    assert r["block_idx"][0, 0].tolist() == gd["block_idx"]
+    ex = O.select_blocks(O.block_scores(q_idx, k_idx, pos, gd["block_size"]), pos,
+                         gd["block_size"], gd["top_k"])
+    assert ex[0, 0].tolist() == gd["exact_block_idx"]
+    assert O.selection_recall(r["block_idx"], ex, pos, gd["block_size"], gd["top_k"]) == 0.5
+
+
+def _hier_by_loops(q_idx, k_idx, pos, B, k, S, C):
+    """Brute force of the hierarchical reading with Python loops, math.fsum and
+    sorted() (no numpy reductions or lexsort)."""
+    n, G, di = q_idx.shape
+    L = k_idx.shape[0]
+    span = B * S
+    out = np.full((G, n, k), -1, np.int32)
+    for g in range(G):
+        kbar = []
+        for c in range(L // span):
+            kbar.append([math.fsum(k_idx[c * span + s, g, x] for s in range(span)) / span
+                         for x in range(di)])
+        for t in range(n):
+            p = int(pos[t])
+            J = p // B
+            if J <= k - 1:
+                sel = list(range(J + 1))
+            else:
+                cJ = J // S
+                cs = [(-math.fsum(q_idx[t, g, x] * kbar[c][x] for x in range(di)), c)
+                      for c in range(cJ)]
+                keep = [c for _, c in sorted(cs)[:C]]
+                blocks = [c * S + s for c in keep for s in range(S)] + list(range(cJ * S, J))
+                fs = []
+                for j in blocks:
+                    best = max(math.fsum(q_idx[t, g, x] * k_idx[s, g, x] for x in range(di))
+                               for s in range(j * B, min(j * B + B, p + 1)))
+                    fs.append((-best, j))
+                sel = sorted(j for _, j in sorted(fs)[:k - 1]) + [J]
+            out[g, t, :len(sel)] = sel
+    return out
+
+
+@pytest.mark.parametrize("L,lq,B,S,C,k", [(96, 40, 4, 2, 3, 4), (130, 130, 2, 2, 2, 5),
+                                          (200, 17, 8, 2, 1, 3), (64, 64, 1, 4, 2, 6)])
+def test_hierarchical_matches_loop_bruteforce(L, lq, B, S, C, k):
+    """Small integers and chunk spans B*S that are powers of two keep every
+    mean and dot product exact on both sides, so exact ties are decided by
+    the same rule (lower chunk, lower block) rather than by rounding."""
+    rng = np.random.default_rng(L + 7 * S + C)
+    G, di = 2, 3
+    q = rng.integers(-2, 3, (lq, G, di)).astype(float)   # small integers: many exact ties
+    kk = rng.integers(-2, 3, (L, G, di)).astype(float)
+    pos = O.query_positions(lq, L)
+    r = O.hierarchical_select(q, kk, pos, B, k, S, C)
+    assert np.array_equal(r["block_idx"], _hier_by_loops(q, kk, pos, B, k, S, C))
+
+
+def test_hierarchical_keeping_every_chunk_is_exact():
+    """C at least the number of chunks: every candidate block is scored, so
+    the hierarchical selection is select_blocks' exactly, and recall is 1."""
+    rng = np.random.default_rng(9)
+    L, lq, G, di, B, S, k = 700, 300, 2, 4, 8, 4, 7
+    q, kk = _rand(rng, lq, G, di), _rand(rng, L, G, di)
+    pos = O.query_positions(lq, L)
+    ex = O.select_blocks(O.block_scores(q, kk, pos, B), pos, B, k)
+    r = O.hierarchical_select(q, kk, pos, B, k, S, L // (B * S))
+    assert np.array_equal(r["block_idx"], ex)
+    assert O.selection_recall(r["block_idx"], ex, pos, B, k) == 1.0
+
+
+def test_hierarchical_structure():
+    """Every row keeps J last, only blocks below J besides it, blocks of kept
+    chunks or of the current chunk, and k - 1 free picks once J > k - 1; the
+    coarse candidates are exactly the chunks below the current chunk."""
+    rng = np.random.default_rng(10)
+    L, lq, G, di, B, S, C, k = 900, 400, 2, 4, 4, 5, 3, 6
+    q, kk = _rand(rng, lq, G, di), _rand(rng, L, G, di)
+    pos = O.query_positions(lq, L)
+    r = O.hierarchical_select(q, kk, pos, B, k, S, C)
+    for g in range(G):
+        for t in range(lq):
+            J = pos[t] // B
+            cJ = J // S
+            assert np.all(np.isfinite(r["coarse"][g, t, :cJ]))
+            assert np.all(np.isneginf(r["coarse"][g, t, cJ:]))
+            row = [int(x) for x in r["block_idx"][g, t] if x >= 0]
+            assert row[-1] == J and row == sorted(row)
+            assert len(row) == min(J + 1, k)
+            kept = set(int(c) for c in r["kept_chunks"][g, t] if c >= 0)
+            assert len(kept) == min(cJ, C)
+            for j in row[:-1]:
+                assert j < J and (j // S in kept or j // S == cJ)
