@@ -225,6 +225,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     wbytes = msa.workspace_size(prob)
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     fused = args.fused_topk and not decode_shape(prob)
+    hier = args.hier_index and not fused
+    if hier:
+        hier_keep = args.hier_keep or max(1, -(-2 * (prob.top_k - 1) // args.hier_chunk))
+        hier_ws = torch.empty(max(msa.index_topk_hier_workspace_size(prob, args.hier_chunk,
+                                                                     hier_keep), 1),
+                              dtype=torch.uint8, device=dev)
     if fused:
         itk_ws = torch.empty(max(msa.index_topk_workspace_size(prob), 1), dtype=torch.uint8,
                              device=dev)
@@ -261,6 +267,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
             with fev if fev is not None else _nullctx():
                 msa.index_topk(prob, inp["q_idx"], inp["k_idx"], block_idx, workspace=itk_ws,
                                stream=sid)
+            if ev is not None:
+                ev[1].record(stream)
+        elif hier:
+            with fev if fev is not None else _nullctx():
+                msa.index_topk_hier(prob, inp["q_idx"], inp["k_idx"], args.hier_chunk, hier_keep,
+                                    block_idx, workspace=hier_ws, stream=sid)
             if ev is not None:
                 ev[1].record(stream)
         else:
@@ -307,7 +319,9 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(steps)]
     bevents = [msa.ProfileEvents(len(ab_kernels), dev) if use_bwd else None
                for _ in range(steps)]
-    fevents = [msa.ProfileEvents(2, dev) if fused else None for _ in range(steps)]
+    hier_kernels = ["hi_mean", "hi_coarse", "hi_buckets", "hi_fine", "hi_final"]
+    fevents = [msa.ProfileEvents(2, dev) if fused else
+               (msa.ProfileEvents(len(hier_kernels), dev) if hier else None) for _ in range(steps)]
     log(f"[bench] {name}: {steps} timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -328,6 +342,11 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     if fused:
         kern_all = {"index_topk": [e[0].elapsed_time(fe.events[0]) for e, fe in zip(events, fevents)],
                     "index_topk_merge": [fe.events[0].elapsed_time(fe.events[1]) for fe in fevents]}
+    elif hier:
+        kern_all = {}
+        for i, kn in enumerate(hier_kernels):
+            kern_all[kn] = [(e[0] if i == 0 else fe.events[i - 1]).elapsed_time(fe.events[i])
+                            for e, fe in zip(events, fevents)]
     else:
         kern_all = {index_kernel: [e[0].elapsed_time(e[1]) for e in events],
                     "topk": [e[1].elapsed_time(e[2]) for e in events]}
@@ -402,13 +421,31 @@ def run_workload(name, steps, warmup, args, keep_state=False):
               **({"layers_per_index": args.layers} if args.layers > 1 else {}),
               **({"indexer_kl": True} if use_kl else {}),
               **({"fused_topk": True} if fused else {}),
+              **({"hier_index": {"chunk_blocks": args.hier_chunk, "keep_chunks": hier_keep}}
+                 if hier else {}),
               **({"attn_bwd": True} if use_bwd else {})}
     res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": w.dtype,
            "config": config, "roofline": roof, "stages": stages, "extra": extra,
            "wall_s_timed": wall, "steps": steps, "warmup": warmup}
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step, {value:.4g} {unit}")
     state = None
-    if keep_state and fused:
+    if hier:
+        # recall of the approximation's free picks against the exact selection
+        exact = msa.topk_select(prob, msa.index_score(prob, inp["q_idx"], inp["k_idx"]))
+        hit = tot = 0
+        q0 = 0
+        for lq_, lkv_ in zip(lq, lkv):
+            pos = torch.arange(lkv_ - lq_, lkv_, device=dev)
+            Jr = (pos // prob.B).view(1, -1, 1)
+            e_, h_ = exact[:, q0:q0 + lq_], block_idx[:, q0:q0 + lq_]
+            fe = (e_ >= 0) & (e_ < Jr)
+            fh = (h_ >= 0) & (h_ < Jr)
+            hit += int((fe.unsqueeze(3) & fh.unsqueeze(2) & (e_.unsqueeze(3) == h_.unsqueeze(2))).sum())
+            tot += int(fe.sum())
+            q0 += lq_
+        extra["hier_recall"] = hit / max(tot, 1)
+        del exact
+    if keep_state and (fused or hier):
         # the fused call leaves no score tensor: the parity leg scores the rows itself
         scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
     if keep_state:
@@ -536,6 +573,13 @@ def main():
     ap.add_argument("--fused-topk", action="store_true",
                     help="index scoring and Top-k in one call (msa_index_topk, no score tensor) "
                          "instead of msa_index_score + msa_topk_select")
+    ap.add_argument("--hier-index", action="store_true",
+                    help="hierarchical coarse-to-fine selection (msa_index_topk_hier, an "
+                         "approximation) in place of msa_index_score + msa_topk_select; the "
+                         "recall of its free picks against the exact selection is reported")
+    ap.add_argument("--hier-chunk", type=int, default=16, help="blocks per coarse chunk")
+    ap.add_argument("--hier-keep", type=int, default=0,
+                    help="coarse chunks kept per query (0: enough for twice the free picks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (counter calibration)")
     args = ap.parse_args()

@@ -35,7 +35,8 @@ STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHA
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size",
-            "msa_index_topk", "msa_sparse_attn_workspace_size",
+            "msa_index_topk", "msa_index_topk_hier_workspace_size", "msa_index_topk_hier",
+            "msa_sparse_attn_workspace_size",
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_noalloc", "msa_sparse_attn_fwd_mass",
             "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
@@ -93,6 +94,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_topk_workspace_size.restype = st
     lib.msa_index_topk.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_index_topk.restype = st
+    lib.msa_index_topk_hier_workspace_size.argtypes = [P, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_index_topk_hier_workspace_size.restype = st
+    lib.msa_index_topk_hier.argtypes = [P, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+    lib.msa_index_topk_hier.restype = st
     lib.msa_sparse_attn_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.msa_sparse_attn_workspace_size.restype = st
     lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -241,6 +248,44 @@ def index_topk(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
     s = _stream(q_idx.device) if stream is None else stream
     _check(load_library().msa_index_topk(prob.ref(), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
                                          _ptr(workspace), wbytes, s))
+    return block_idx
+
+
+def index_topk_hier_workspace_size(prob: Problem, chunk_blocks: int, keep_chunks: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_index_topk_hier_workspace_size(prob.ref(), chunk_blocks,
+                                                             keep_chunks, ctypes.byref(n)))
+    return n.value
+
+
+def index_topk_hier(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor, chunk_blocks: int,
+                    keep_chunks: int, block_idx: Optional[torch.Tensor] = None,
+                    kept_chunks: Optional[torch.Tensor] = None, return_kept: bool = False,
+                    workspace: Optional[torch.Tensor] = None, stream: Optional[int] = None):
+    """msa_index_topk_hier: the hierarchical (coarse-to-fine) selection.
+    Returns block_idx [G, total_q, k] int32, and with return_kept (or a given
+    kept_chunks buffer) also the kept chunks [G, total_q, keep_chunks]."""
+    _need(q_idx, "q_idx", (prob.total_q, prob.G, prob.d_idx), prob.torch_dtype)
+    _need(k_idx, "k_idx", (prob.total_kv, prob.G, prob.d_idx), prob.torch_dtype)
+    if block_idx is None:
+        block_idx = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.int32,
+                                device=q_idx.device)
+    _need(block_idx, "block_idx", (prob.G, prob.total_q, prob.top_k), torch.int32)
+    if kept_chunks is None and return_kept:
+        kept_chunks = torch.empty((prob.G, prob.total_q, keep_chunks), dtype=torch.int32,
+                                  device=q_idx.device)
+    if kept_chunks is not None:
+        _need(kept_chunks, "kept_chunks", (prob.G, prob.total_q, keep_chunks), torch.int32)
+    need = index_topk_hier_workspace_size(prob, chunk_blocks, keep_chunks)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _stream(q_idx.device) if stream is None else stream
+    _check(load_library().msa_index_topk_hier(prob.ref(), _ptr(q_idx), _ptr(k_idx), chunk_blocks,
+                                              keep_chunks, _ptr(block_idx), _ptr(kept_chunks),
+                                              _ptr(workspace), wbytes, s))
+    if kept_chunks is not None:
+        return block_idx, kept_chunks
     return block_idx
 
 
@@ -451,6 +496,7 @@ def msa_forward(prob: Problem, q, k, v, q_idx, k_idx, return_lse: bool = False):
 msa_index_score = index_score
 msa_topk_select = topk_select
 msa_index_topk = index_topk
+msa_index_topk_hier = index_topk_hier
 msa_sparse_attn_fwd = sparse_attn_fwd
 msa_sparse_attn_fwd_noalloc = sparse_attn_fwd_noalloc
 msa_sparse_attn_fwd_mass = sparse_attn_fwd_mass

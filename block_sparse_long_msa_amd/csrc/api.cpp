@@ -288,6 +288,55 @@ msa_status_t msa_index_topk(const msa_problem_t *prob, const void *q_idx, const 
                   "index_topk");
 }
 
+msa_status_t msa_index_topk_hier_workspace_size(const msa_problem_t *prob, int chunk_blocks,
+                                               int keep_chunks, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  if (!msa::hier_params_ok(d, chunk_blocks, keep_chunks))
+    return fail(MSA_ERR_BAD_SHAPE,
+                "chunk_blocks must be a power of two in [1, 64] and keep_chunks >= 1 with "
+                "keep_chunks * chunk_blocks >= top_k - 1, (keep_chunks + 1) * chunk_blocks <= "
+                "1024, ceil(NBmax / chunk_blocks) <= 1024 and num_seqs * that <= 16384");
+  *bytes = msa::hier_workspace_bytes(d, chunk_blocks, keep_chunks);
+  return ok();
+}
+
+msa_status_t msa_index_topk_hier(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                                 int chunk_blocks, int keep_chunks, int32_t *block_idx,
+                                 int32_t *kept_chunks, void *workspace,
+                                 size_t workspace_bytes_given, void *stream) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (prob->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED_DTYPE, "the hierarchical selection takes bf16 inputs");
+  size_t need = 0;
+  if ((st = msa_index_topk_hier_workspace_size(prob, chunk_blocks, keep_chunks, &need)) !=
+      MSA_SUCCESS)
+    return st;
+  const bool any_q = d.total_q > 0, any_kv = d.total_kv > 0;
+  if ((st = check_tensor(q_idx, "q_idx", any_q)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(k_idx, "k_idx", any_kv)) != MSA_SUCCESS) return st;
+  if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
+  if (kept_chunks != nullptr && !aligned(kept_chunks, 4))
+    return fail(MSA_ERR_MISALIGNED, "kept_chunks must be 4-byte aligned");
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  if (need > 0 && workspace == nullptr) return fail(MSA_ERR_NULL_POINTER, "workspace is NULL");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MSA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!any_q) return ok();
+  return launched(msa::launch_index_topk_hier(d, chunk_blocks, keep_chunks,
+                                              static_cast<const uint16_t *>(q_idx),
+                                              static_cast<const uint16_t *>(k_idx), block_idx,
+                                              kept_chunks, workspace,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                  "index_topk_hier");
+}
+
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes) {
   msa::Dims d;
   msa_status_t st = check_problem(prob, &d);

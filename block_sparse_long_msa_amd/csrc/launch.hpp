@@ -41,6 +41,14 @@ bool index_topk_supported(const Dims &p);
 hipError_t launch_index_topk(const Dims &p, const uint16_t *q_idx, const uint16_t *k_idx,
                              int32_t *block_idx, void *workspace, hipStream_t s);
 
+// Hierarchical (coarse-to-fine) selection (index_hier.hip).
+bool hier_params_ok(const Dims &p, int chunk_blocks, int keep_chunks);
+size_t hier_workspace_bytes(const Dims &p, int chunk_blocks, int keep_chunks);
+hipError_t launch_index_topk_hier(const Dims &p, int chunk_blocks, int keep_chunks,
+                                  const uint16_t *q_idx, const uint16_t *k_idx,
+                                  int32_t *block_idx, int32_t *kept_chunks, void *workspace,
+                                  hipStream_t s);
+
 // Top-k with the current block forced.
 hipError_t launch_topk(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s);
 

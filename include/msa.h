@@ -150,6 +150,38 @@ msa_status_t msa_index_topk(const msa_problem_t *prob, const void *q_idx, const 
                             int32_t *block_idx, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* Hierarchical (coarse-to-fine) selection: an APPROXIMATION of steps 1 and 2
+ * that scores only a narrowed candidate set (the "LongCat Sparse Attention"
+ * page, Abstract, strategy (3): a coarse-to-fine scoring scheme narrows each
+ * query's candidates to cut the indexing computation; the page gives no
+ * formula, and this is the reading taken).  Chunks of chunk_blocks (S)
+ * consecutive blocks carry a coarse key, the mean of their B * S index keys
+ * (full chunks only).  For a query at position p with current block J and
+ * current chunk cJ = J / S:
+ *   - every chunk c < cJ scores <q_idx, coarse key of c> (fp32);
+ *   - the keep_chunks (C) best are kept (score descending, chunk ascending;
+ *     all of them when cJ <= C);
+ *   - the blocks of the kept chunks and the blocks cJ * S .. J-1 get the
+ *     exact max-pooled block score of msa_index_score;
+ *   - the k-1 best of those (score descending, block ascending) and J are
+ *     kept; rows with J <= k-1 keep 0..J.
+ * With C >= the number of chunks this equals msa_topk_select on
+ * msa_index_score's scores.  block_idx [G, total_q, top_k] as msa_topk_select
+ * (ascending, -1 padded); kept_chunks (optional, may be NULL) [G, total_q, C]
+ * int32 the kept chunks ascending, -1 padded (rows at negative positions get
+ * -1).  Requirements: bf16 (else MSA_ERR_UNSUPPORTED_DTYPE); S a power of two
+ * in [1, 64]; C >= 1 with C * S >= top_k - 1; (C + 1) * S <= 1024;
+ * ceil(NBmax / S) <= 1024 and num_seqs * ceil(NBmax / S) <= 16384 (else
+ * MSA_ERR_BAD_SHAPE).  `workspace` must hold
+ * msa_index_topk_hier_workspace_size() bytes, 256-byte aligned; its contents
+ * need no initialisation. */
+msa_status_t msa_index_topk_hier_workspace_size(const msa_problem_t *prob, int chunk_blocks,
+                                               int keep_chunks, size_t *bytes);
+msa_status_t msa_index_topk_hier(const msa_problem_t *prob, const void *q_idx, const void *k_idx,
+                                 int chunk_blocks, int keep_chunks, int32_t *block_idx,
+                                 int32_t *kept_chunks, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Bytes of device workspace msa_sparse_attn_fwd needs for this problem and
  * schedule (0 is possible).  Writes the size to *bytes (host). */
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes);
