@@ -27,11 +27,15 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# Debug build: every index-driven gather is bounds-checked and failures are
+# counted on the device (read them with debug_bounds_violations()).
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmsa_debug.so")
 
 MSA_SUCCESS = 0
 STATUS_NAMES = {0: "MSA_SUCCESS", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHAPE",
                 3: "MSA_ERR_UNSUPPORTED_DTYPE", 4: "MSA_ERR_MISALIGNED",
-                5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_DEVICE"}
+                5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_DEVICE",
+                7: "MSA_ERR_NOT_AVAILABLE"}
 DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size",
@@ -41,8 +45,8 @@ EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size
             "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
             "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
-            "msa_set_profile_events", "msa_status_string", "msa_last_error_message",
-            "msa_abi_version")
+            "msa_set_profile_events", "msa_debug_bounds_violations", "msa_status_string",
+            "msa_last_error_message", "msa_abi_version")
 
 
 class MsaError(RuntimeError):
@@ -74,13 +78,44 @@ class CProblem(ctypes.Structure):
 
 
 _lib_handle = None
+_lib_path = None
+_loaded = {}
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmsa.so (once).  Raises if it has not been built."""
-    global _lib_handle
-    if _lib_handle is not None:
+def _default_path() -> str:
+    """libmsa.so, or libmsa_debug.so when MSA_LIBRARY=debug is set."""
+    v = os.environ.get("MSA_LIBRARY", "release")
+    if v not in ("release", "debug"):
+        raise RuntimeError(f"MSA_LIBRARY must be 'release' or 'debug', not {v!r}")
+    return DEBUG_LIB_PATH if v == "debug" else LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """The library every call of this module goes through, loaded on first
+    use (libmsa.so unless select_library() or MSA_LIBRARY chose another).
+    Raises if it has not been built."""
+    if _lib_handle is not None and path is None:
         return _lib_handle
+    return select_library(path or _default_path())
+
+
+def select_library(path: str) -> ctypes.CDLL:
+    """Route every later call of this module through the library at `path`
+    (LIB_PATH or DEBUG_LIB_PATH); both may be loaded in one process."""
+    global _lib_handle, _lib_path
+    lib = _loaded.get(path)
+    if lib is None:
+        lib = _open(path)
+        _loaded[path] = lib
+    _lib_handle, _lib_path = lib, path
+    return lib
+
+
+def current_library_path() -> Optional[str]:
+    return _lib_path
+
+
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_long_msa_amd.build`")
     lib = ctypes.CDLL(path)
@@ -127,7 +162,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_abi_version.restype = ctypes.c_int
     lib.msa_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.msa_set_profile_events.restype = None
-    _lib_handle = lib
+    lib.msa_debug_bounds_violations.argtypes = [ctypes.POINTER(ctypes.c_uint64),
+                                                ctypes.POINTER(ctypes.c_uint64), st]
+    lib.msa_debug_bounds_violations.restype = st
     return lib
 
 
@@ -460,6 +497,17 @@ def sparse_attn_bwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                               wbytes, s))
     return dq, dk, dv
+
+
+def debug_bounds_violations(reset: bool = True) -> Tuple[int, int]:
+    """msa_debug_bounds_violations: (failed, run) gather bounds checks counted
+    on the current device since the last reset (the debug library only; the
+    release one raises MSA_ERR_NOT_AVAILABLE).  Synchronises the device first."""
+    torch.cuda.synchronize()
+    v, c = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(load_library().msa_debug_bounds_violations(ctypes.byref(v), ctypes.byref(c),
+                                                      int(bool(reset))))
+    return int(v.value), int(c.value)
 
 
 class ProfileEvents:

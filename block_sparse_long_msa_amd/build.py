@@ -1,8 +1,10 @@
-"""Build libmsa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libmsa.so and libmsa_debug.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m block_sparse_long_msa_amd.build [-v]
-Every call recompiles; objects go to _build/ at the repository root and the
-shared library next to this file.
+Usage: python -m block_sparse_long_msa_amd.build [-v] [--release-only]
+Every call recompiles; objects go to _build/ (release) and _build/debug/ at
+the repository root and the shared libraries next to this file.  The debug
+library is the same code built with -DMSA_DEBUG: its kernels count failed
+gather bounds checks on the device (msa_debug_bounds_violations).
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
+DEBUG_LIB = os.path.join(PKG, "libmsa_debug.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
@@ -30,9 +33,9 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = ["hipcc", "-c", *COMMON, src, "-o", obj]
+def _compile(src: str, verbose: bool, debug: bool) -> str:
+    obj = os.path.join(BUILD, "debug" if debug else "", os.path.basename(src) + ".o")
+    cmd = ["hipcc", "-c", *COMMON, *(["-DMSA_DEBUG"] if debug else []), src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,21 +48,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = ["hipcc", "-shared", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile and link libmsa.so (and, with `debug`, libmsa_debug.so);
+    returns the release library's path."""
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    srcs = sources()
+    jobs = [(s, False) for s in srcs] + ([(s, True) for s in srcs] if debug else [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    if debug:
+        _link(objs[len(srcs):], DEBUG_LIB, verbose)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--release-only" not in sys.argv))

@@ -510,6 +510,29 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
                   "attn_bwd");
 }
 
+msa_status_t msa_debug_bounds_violations(uint64_t *violations, uint64_t *checks, int reset) {
+  if (violations == nullptr) return fail(MSA_ERR_NULL_POINTER, "violations is NULL");
+  *violations = 0;
+  if (checks != nullptr) *checks = 0;
+#ifdef MSA_DEBUG
+  uint64_t c = 0, v = 0;
+  const bool r = reset != 0;
+  const bool read = msa::debug_counters_attn_kvmajor(&c, &v, r) &&
+                    msa::debug_counters_attn_qmajor(&c, &v, r) &&
+                    msa::debug_counters_attn_bwd(&c, &v, r) &&
+                    msa::debug_counters_index_bwd(&c, &v, r) &&
+                    msa::debug_counters_index_topk(&c, &v, r) &&
+                    msa::debug_counters_index_hier(&c, &v, r);
+  if (!read) return fail(MSA_ERR_DEVICE, "reading the debug counters failed");
+  *violations = v;
+  if (checks != nullptr) *checks = c;
+  return ok();
+#else
+  (void)reset;
+  return fail(MSA_ERR_NOT_AVAILABLE, "bounds counters exist only in the debug build (-DMSA_DEBUG)");
+#endif
+}
+
 const char *msa_status_string(msa_status_t status) {
   switch (status) {
     case MSA_SUCCESS: return "success";
@@ -519,6 +542,7 @@ const char *msa_status_string(msa_status_t status) {
     case MSA_ERR_MISALIGNED: return "misaligned pointer";
     case MSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MSA_ERR_DEVICE: return "device error";
+    case MSA_ERR_NOT_AVAILABLE: return "not available in this build";
   }
   return "unknown status";
 }

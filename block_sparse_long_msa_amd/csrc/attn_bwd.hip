@@ -265,6 +265,8 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   int32_t f_e = 0;
   auto fetch = [&](int32_t e) {
     const int64_t t = e / K;
+    // the entry's row is a query of this bucket's sequence for which block j is causal
+    MSA_DCHECK(e >= 0 && t >= q0 && t < cu_q[b + 1] && base_pos + (t - q0) >= s0);
     const int h = g * hpg + r_ld % hpg;
     const int64_t roff = (t * H + h) * (int64_t)kD;
 #pragma unroll
@@ -536,6 +538,8 @@ void zero_fill(float *x, int64_t n, hipStream_t s) {
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(attn_bwd)
 
 bool attn_bwd_supported(const Dims &p) {
   const int hpg = p.G > 0 ? p.H / p.G : 0;

@@ -173,6 +173,7 @@ __device__ __forceinline__ EntryRef entry_ref(const int32_t *__restrict__ block_
   }
   const int64_t p = sq.base + (ep.row - sq.q0);
   if (p < 0 || (int64_t)j >= (p >> cg.lg_bs)) return r;
+  MSA_DCHECK(j < cg.nb_max && b >= 0 && b < cg.num_seqs);
   r.bkt = ((int64_t)b * cg.G + g) * cg.nb_max + j;
   r.bin = b == t.b0 ? j : -1;
   return r;
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
         rank[i] = atomicAdd(&hist[r.bin], 1);
       } else if (r.bkt >= 0) {
         const int pos = atomicAdd(&cursor[r.bkt], 1);
+        MSA_DCHECK(pos < (item_off[r.bkt + 1] - item_off[r.bkt]) * qch);
         entries[(int64_t)item_off[r.bkt] * qch + pos] = (int32_t)((ep.row << 6) | ep.slot);
       }
     }
@@ -253,6 +255,8 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) {
     const int c = hist[i];
     hist[i] = c != 0 ? item_off[ts.bbase + i] * qch + atomicAdd(&cursor[ts.bbase + i], c) : 0;
+    // the tile's run of the bucket ends inside the bucket's items
+    MSA_DCHECK(c == 0 || hist[i] + c <= item_off[ts.bbase + i + 1] * qch);
   }
   __syncthreads();
 #pragma unroll
@@ -707,7 +711,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
     float2 *__restrict__ trash_ml, int H, int G, int K, int nseg, int nb_max, int qch,
-    float scale_log2) {
+    float scale_log2, int64_t total_q, int64_t total_kv) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
   // two separate objects, so the compiler can tell the tile being loaded
   // from the tile being read
@@ -777,6 +781,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     return d;
   };
   auto q_of = [&](bf16x8 (&qb)[D / 16], const ItemDesc &d, int32_t e) {
+    MSA_DCHECK(e >= 0 && (e >> 6) < total_q && (e & 63) < K && d.g >= 0 && d.g < G);
+    MSA_DCHECK(d.kvrow >= 0 && d.kvrow + BS <= total_kv);
     const int half = lane >> 5;
     const uint16_t *qrow = q + ((int64_t)(e >> 6) * H + d.g * hpg + hh) * (int64_t)D + 8 * half;
 #pragma unroll
@@ -1113,7 +1119,7 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
                      dim3(kThreads), 0, s, q, k, v, w.item_off, w.entries, w.item_desc, w.part_o,
                      w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, p.num_seqs * p.G,
-                     p.nb_max, qch, sl2);
+                     p.nb_max, qch, sl2, p.total_q, p.total_kv);
   profile_mark(s);
   // the blocks holding a sequence's queries: at most ceil(max_q_len / B) + 1
   const int ndiag = (int)std::min<int64_t>((p.max_q_len + p.B - 1) / p.B + 1, p.nb_max);
@@ -1130,6 +1136,8 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(attn_kvmajor)
 
 bool kvmajor_fits(const Dims &p) {
   if (p.total_q >= (int64_t)1 << 25) return false;  // entries pack the query row above 6 slot bits

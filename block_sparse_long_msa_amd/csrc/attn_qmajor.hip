@@ -75,6 +75,7 @@ __global__ __launch_bounds__(64) void attn_qmajor_bf16_kernel(
     if (j < 0) continue;
     const int64_t s0 = (int64_t)j * BS;
     if (p < s0) continue;  // not a causal block of this row (ignored)
+    MSA_DCHECK(s0 < sq.lkv);
     const uint16_t *kblk = k + ((sq.kv0 + s0) * G + g) * (int64_t)D;
     const uint16_t *vblk = v + ((sq.kv0 + s0) * G + g) * (int64_t)D;
 
@@ -223,6 +224,7 @@ __global__ __launch_bounds__(64) void attn_qmajor_f32_kernel(
     if (j < 0) continue;
     const int64_t s0 = (int64_t)j * BS;
     if (p < s0) continue;
+    MSA_DCHECK(s0 < sq.lkv);
     const float *kb = k + ((sq.kv0 + s0) * G + g) * (int64_t)D;
     const float *vb = v + ((sq.kv0 + s0) * G + g) * (int64_t)D;
     const int nk = (int)min<int64_t>(BS, p + 1 - s0);  // causal keys of this block
@@ -309,6 +311,8 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(attn_qmajor)
 
 hipError_t launch_attn_qmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                    const uint16_t *v, const int32_t *block_idx, uint16_t *out,

@@ -162,6 +162,7 @@ __global__ __launch_bounds__(64) void bk_scatter_kernel(
       const uint64_t m = ballot64(active && bk == bl);
       const int32_t start = __builtin_amdgcn_readfirstlane(run[bl]);
       if (active && bk == bl) {
+        MSA_DCHECK(start + (int32_t)mbcnt64(m) < gbase[bl + 1]);
         lists[start + mbcnt64(m)] = (int32_t)e;
         active = false;
       }

@@ -153,6 +153,8 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
   for (int x = tid; x < n; x += 256) {
     const int32_t e = lists[first + x];
     const int64_t row = e / K;
+    // the entry's row is a query of this bucket's sequence for which block j is causal
+    MSA_DCHECK(e >= 0 && row >= q0 && row < cu_q[b + 1] && base_pos + (row - q0) >= s0);
     ent_row[x] = (int32_t)row;
     ent_c[x] = grad[(int64_t)g * nent + e];
   }
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void ib_dq_kernel(const T *__restrict__ k_idx,
                                                     const float *__restrict__ grad,
                                                     const int32_t *__restrict__ amax,
                                                     float *__restrict__ dq_idx, int G, int K,
-                                                    int64_t total_q) {
+                                                    int64_t total_q, int64_t total_kv) {
   constexpr int CPL = (DI + 63) / 64;  // channels per lane
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_q) return;
@@ -367,6 +369,7 @@ __global__ __launch_bounds__(256) void ib_dq_kernel(const T *__restrict__ k_idx,
   // order, four key rows requested before any is used (a slot without an
   // arg-max reads key row 0 with weight 0)
   const int32_t am = lane < K ? amax[rk + lane] : -1;
+  MSA_DCHECK(am < total_kv);
   const float gc = lane < K ? grad[rk + lane] : 0.f;
   float acc[CPL];
 #pragma unroll
@@ -431,12 +434,14 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
                      w.pbase, w.part, dk_idx, p.cu_kv, p.G, p.num_seqs, p.nb_max, w.nbk_g);
   profile_mark(s);
   hipLaunchKernelGGL((ib_dq_kernel<T, DI>), dim3((unsigned)((p.total_q + 3) / 4), p.G), dim3(256),
-                     0, s, k_idx, grad, w.amax, dq_idx, p.G, p.top_k, p.total_q);
+                     0, s, k_idx, grad, w.amax, dq_idx, p.G, p.top_k, p.total_q, p.total_kv);
   profile_mark(s);
   return hipGetLastError();
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(index_bwd)
 
 size_t index_bwd_workspace_bytes(const Dims &p) {
   return p.total_q > 0 ? ib_carve(p, nullptr).total_bytes : 0;

@@ -180,6 +180,7 @@ __global__ __launch_bounds__(256) void hi_coarse_kernel(
   }
   const int ncand = cJ;  // coarse candidates: chunks 0 .. cJ - 1
   const int live = (ncand + 63) >> 6;
+  MSA_DCHECK(ncand <= 64 * MAXS && cJ <= nch);
   bool take[MAXS];
   if (ncand <= C) {
 #pragma unroll
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(256) void hi_coarse_kernel(
   for (int u = 0; u < MAXS; ++u) {
     if (u >= live) break;
     const uint64_t m = ballot64(take[u]);
+    MSA_DCHECK(!take[u] || at + (int)mbcnt64(m) < C);
     if (take[u]) {
       const int c = lane + 64 * u;
       srow[at + mbcnt64(m)] = c;
@@ -293,6 +295,8 @@ __global__ __launch_bounds__(256) void hi_fine_kernel(
   const int64_t row = e / K1;
   const int slot = (int)(e - row * K1);
   const int J = (int)((base_pos + (row - q0)) / BS);   // >= c * S + 1 for every listed entry
+  // the entry's row is a query of this bucket's sequence that lies past chunk c
+  MSA_DCHECK(e >= 0 && row >= q0 && row < cu_q[b + 1] && slot < K1 && J >= c * S + 1);
   // blocks of the chunk below the largest J of the item
   int jm = x < n ? J : 0;
 #pragma unroll
@@ -301,6 +305,7 @@ __global__ __launch_bounds__(256) void hi_fine_kernel(
   __syncthreads();
   const int jmax = max(max(jmax_w[0], jmax_w[1]), max(jmax_w[2], jmax_w[3]));
   const int nblk = min(S, jmax - c * S);
+  MSA_DCHECK((int64_t)(c * S + nblk) * BS <= lkv);
 
   // gathered index queries of the wave's two 32-column halves
   bf16x8 qb[2][NK];
@@ -498,6 +503,8 @@ hipError_t launch_hier(const Dims &p, const HiGeom &h, const uint16_t *q_idx,
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(index_hier)
 
 bool hier_params_ok(const Dims &p, int chunk_blocks, int keep_chunks) {
   if (chunk_blocks < 1 || chunk_blocks > 64 || (chunk_blocks & (chunk_blocks - 1)) != 0)

@@ -268,6 +268,7 @@ __global__ __launch_bounds__(256) void index_topk_merge_kernel(
   const int ns = (J + seg - 1) / seg;  // segments holding candidates of this row
   const int n = ns * lst;
   const int live = (n + 63) >> 6;      // slots in use (wave-uniform)
+  MSA_DCHECK(ns <= nseg && n <= 64 * MAXS);
   const uint64_t *src = cand + ((int64_t)g * total_q + row) * nseg * lst;
   uint32_t hi[MAXS], lo[MAXS];
 #pragma unroll
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(256) void index_topk_merge_kernel(
     if (u >= live) break;
     const bool take = hi[u] > tau || (hi[u] == tau && lo[u] >= lo_min);
     const uint64_t m = ballot64(take);
+    MSA_DCHECK(!take || base + (int)mbcnt64(m) < cap);
     if (take) sel[wv][base + mbcnt64(m)] = (int32_t)(0xFFFFFFFFu - lo[u]);
     base += __popcll(m);
   }
@@ -314,6 +316,7 @@ __global__ __launch_bounds__(256) void index_topk_merge_kernel(
     const int32_t mine = sel[wv][lane];
     int rank = 0;
     for (int i = 0; i < cap; ++i) rank += sel[wv][i] < mine;
+    MSA_DCHECK(mine >= 0 && mine < J);
     out[rank] = mine;
   }
   if (lane == 0) out[cap] = J;
@@ -334,6 +337,8 @@ hipError_t launch_fused(const Dims &p, const uint16_t *q_idx, const uint16_t *k_
 }
 
 }  // namespace
+
+MSA_DEBUG_COUNTER(index_topk)
 
 // Candidates kept per (query, segment): k - 1 rounded up to a power of two
 // (at least 4), so the list's compare-and-select network is unrolled for a

@@ -14,6 +14,19 @@ namespace msa {
 void profile_begin_call();
 void profile_mark(hipStream_t s);
 
+// Debug builds: per-source-file device counters of the gather bounds checks
+// (MSA_DCHECK) on the current device: lanes that checked and lanes that
+// failed are added to *checks and *violations; `reset` clears them after
+// reading.  false if the device could not be read.
+#ifdef MSA_DEBUG
+bool debug_counters_attn_kvmajor(uint64_t *checks, uint64_t *violations, bool reset);
+bool debug_counters_attn_qmajor(uint64_t *checks, uint64_t *violations, bool reset);
+bool debug_counters_attn_bwd(uint64_t *checks, uint64_t *violations, bool reset);
+bool debug_counters_index_bwd(uint64_t *checks, uint64_t *violations, bool reset);
+bool debug_counters_index_topk(uint64_t *checks, uint64_t *violations, bool reset);
+bool debug_counters_index_hier(uint64_t *checks, uint64_t *violations, bool reset);
+#endif
+
 struct Dims {
   int num_seqs, H, G, d, d_idx, B, top_k;
   int max_q_len;

@@ -163,4 +163,47 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Debug builds (-DMSA_DEBUG, libmsa_debug.so): MSA_DCHECK(cond) evaluates a
+// bounds condition of a gather in every active lane, and the wave's first
+// active lane adds the number of lanes that checked and the number that
+// failed to two device counters of the source file (internal linkage, one
+// pair per file), so a broken index is reported by
+// msa_debug_bounds_violations() rather than trapping.  The access itself is
+// left as it is.  Release builds compile the checks away.
+#ifdef MSA_DEBUG
+namespace {
+__device__ unsigned long long g_debug_checks;
+__device__ unsigned long long g_debug_violations;
+__device__ __forceinline__ void debug_check(bool ok) {
+  const uint64_t act = __builtin_amdgcn_read_exec();
+  const uint64_t bad = ballot64(!ok);
+  if (mbcnt64(act) == 0) {  // first active lane
+    atomicAdd(&g_debug_checks, (unsigned long long)__popcll(act));
+    if (bad != 0) atomicAdd(&g_debug_violations, (unsigned long long)__popcll(bad));
+  }
+}
+}  // namespace
+#define MSA_DCHECK(cond) ::msa::debug_check(static_cast<bool>(cond))
+// Host accessor of a file's counters (read, then optionally clear); false if
+// the device could not be read.
+#define MSA_DEBUG_COUNTER(name)                                                           \
+  bool debug_counters_##name(uint64_t *checks, uint64_t *violations, bool reset) {        \
+    unsigned long long c = 0, v = 0, z = 0;                                               \
+    if (hipMemcpyFromSymbol(&c, HIP_SYMBOL(g_debug_checks), sizeof(c)) != hipSuccess ||   \
+        hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_violations), sizeof(v)) != hipSuccess) \
+      return false;                                                                       \
+    if (reset && (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_checks), &z, sizeof(z)) != hipSuccess || \
+                  hipMemcpyToSymbol(HIP_SYMBOL(g_debug_violations), &z, sizeof(z)) != hipSuccess)) \
+      return false;                                                                       \
+    *checks += c;                                                                         \
+    *violations += v;                                                                     \
+    return true;                                                                          \
+  }
+#else
+#define MSA_DCHECK(cond) \
+  do {                   \
+  } while (0)
+#define MSA_DEBUG_COUNTER(name)
+#endif
+
 }  // namespace msa

@@ -73,7 +73,8 @@ typedef enum {
   MSA_ERR_UNSUPPORTED_DTYPE = 3,
   MSA_ERR_MISALIGNED = 4,
   MSA_ERR_WORKSPACE_TOO_SMALL = 5,
-  MSA_ERR_DEVICE = 6
+  MSA_ERR_DEVICE = 6,
+  MSA_ERR_NOT_AVAILABLE = 7 /* the entry point is not part of this build */
 } msa_status_t;
 
 typedef enum { MSA_BF16 = 0, MSA_F32 = 1 } msa_dtype_t;
@@ -319,6 +320,27 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
  * off.  The caller keeps ownership of the events and of the array, which
  * must stay valid while the hook is set. */
 void msa_set_profile_events(void *const *events, int num_events);
+
+/* Gather bounds counters (diagnostics; debug builds only).  The debug build
+ * of the library (libmsa_debug.so, compiled with -DMSA_DEBUG) checks every
+ * index that a kernel reads from memory and then follows: the block lists
+ * of the query-major attention, the bucket entries and work-item
+ * descriptors of the KV-major attention and of both backward passes, the
+ * candidate lists of the fused selection and the chunk lists of the
+ * hierarchical one.  Each index is checked against the buffer it addresses
+ * and against what the method fixes for it (the entry's query belongs to
+ * the bucket's sequence, the block is causal for it, a list holds no more
+ * than its capacity).  Every check adds one per lane to a device count of
+ * checks, and a failed one also to a count of violations; the access
+ * itself is not changed, so the debug build reports bookkeeping errors
+ * that read valid memory with the wrong meaning, and cannot prevent a
+ * fault from one that leaves the allocation.  This call writes the
+ * violations on the current device to *violations (host) and, when
+ * `checks` (host) is not NULL, the checks to *checks; nonzero `reset`
+ * clears both counts.  It copies from the device: synchronise the streams
+ * of earlier calls first.  The release library returns
+ * MSA_ERR_NOT_AVAILABLE and writes 0. */
+msa_status_t msa_debug_bounds_violations(uint64_t *violations, uint64_t *checks, int reset);
 
 /* Static text for a status code. */
 const char *msa_status_string(msa_status_t status);

@@ -38,13 +38,36 @@ def test_library_exports_every_declared_symbol():
     assert lib.msa_abi_version() == 1
 
 
-def test_every_kernel_launch_stub_is_defined():
+def test_debug_library_exports_the_same_symbols():
+    """libmsa_debug.so is the same ABI built with -DMSA_DEBUG."""
+    if not os.path.exists(msa.DEBUG_LIB_PATH):
+        pytest.skip("libmsa_debug.so not built")
+    lib = ctypes.CDLL(msa.DEBUG_LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.msa_abi_version() == 1
+
+
+def test_release_library_has_no_bounds_counters():
+    lib = msa.load_library()
+    n, c = ctypes.c_uint64(5), ctypes.c_uint64(5)
+    assert lib.msa_debug_bounds_violations(None, None, 1) == 1
+    assert lib.msa_debug_bounds_violations(ctypes.byref(n), ctypes.byref(c), 0) == 7
+    assert n.value == 0 and c.value == 0
+    assert lib.msa_debug_bounds_violations(ctypes.byref(n), None, 0) == 7
+    assert lib.msa_status_string(7).decode() == "not available in this build"
+
+
+@pytest.mark.parametrize("path", ["release", "debug"])
+def test_every_kernel_launch_stub_is_defined(path):
     """Each kernel's host launch stub is compiled into the library.  If the
     host pass rejects a kernel body (a gfx950-only builtin written directly
     in a __global__ function does this without an error), the stub stays an
     undefined symbol and the library only fails when it is loaded."""
-    nm = subprocess.run(["nm", "-D", "--undefined-only", msa.LIB_PATH],
-                        capture_output=True, text=True)
+    lib = msa.LIB_PATH if path == "release" else msa.DEBUG_LIB_PATH
+    if not os.path.exists(lib):
+        pytest.skip(f"{lib} not built")
+    nm = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
     if nm.returncode != 0:
         pytest.skip("nm not available")
     missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
@@ -170,7 +193,7 @@ def test_empty_batch_is_a_no_op():
 
 def test_status_strings():
     lib = msa.load_library()
-    for code in range(7):
+    for code in range(8):
         assert lib.msa_status_string(code).decode()
     assert lib.msa_status_string(99).decode() == "unknown status"
 

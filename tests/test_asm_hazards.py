@@ -56,12 +56,13 @@ def test_scanner_flags_a_clobbered_address():
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
-def test_kv_major_asm_blocks_keep_their_address():
+@pytest.mark.parametrize("variant", ["release", "debug"])
+def test_kv_major_asm_blocks_keep_their_address(variant):
     src = os.path.join(B.CSRC, "attn_kvmajor.hip")
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "attn_kvmajor.s")
-        cmd = ["hipcc", "--cuda-device-only", "-S", *[a for a in B.COMMON if a != "-fPIC"], src,
-               "-o", out]
+        cmd = ["hipcc", "--cuda-device-only", "-S", *[a for a in B.COMMON if a != "-fPIC"],
+               *(["-DMSA_DEBUG"] if variant == "debug" else []), src, "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         text = open(out).read()
