@@ -223,6 +223,9 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         msa._check(msa.load_library().msa_indexer_bwd_workspace_size(prob.ref(), ctypes.byref(nbw)))
         bwd_ws = torch.empty(max(nbw.value, 1), dtype=torch.uint8, device=dev)
     wbytes = msa.workspace_size(prob)
+    if args.attn_workspace_gib > 0:  # bounded workspace: the KV-major rows run in passes
+        wbytes = max(msa.workspace_size_min(prob), min(wbytes, int(args.attn_workspace_gib * 2**30)))
+    passes = -(-prob.total_q // max(1, msa.rows_per_pass(prob, wbytes))) if prob.total_q else 1
     workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     fused = args.fused_topk and not decode_shape(prob)
     hier = args.hier_index and not fused
@@ -316,7 +319,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
-    pevents = [msa.ProfileEvents(len(attn_kernels), dev) for _ in range(steps)]
+    pevents = [msa.ProfileEvents(len(attn_kernels) * passes, dev) for _ in range(steps)]
     bevents = [msa.ProfileEvents(len(ab_kernels), dev) if use_bwd else None
                for _ in range(steps)]
     hier_kernels = ["hi_mean", "hi_coarse", "hi_buckets", "hi_fine", "hi_final"]
@@ -350,8 +353,10 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     else:
         kern_all = {index_kernel: [e[0].elapsed_time(e[1]) for e in events],
                     "topk": [e[1].elapsed_time(e[2]) for e in events]}
-    for i, kn in enumerate(attn_kernels):
-        kern_all[kn] = [(e[2] if i == 0 else pe.events[i - 1]).elapsed_time(pe.events[i])
+    na = len(attn_kernels)
+    for i, kn in enumerate(attn_kernels):  # summed over the passes of a step
+        kern_all[kn] = [sum((e[2] if j == 0 else pe.events[j - 1]).elapsed_time(pe.events[j])
+                            for j in range(i, na * passes, na))
                         for e, pe in zip(events, pevents)]
     if use_kl:
         kern_all["indexer_kl"] = [e[3].elapsed_time(e[4]) for e in events]
@@ -397,7 +402,8 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         roof = hbm_roof(dom, sum(x * w.num_kv_groups * w.idx_dim * 2 for x in lkv), kern_ms[dom])
     else:
         roof = mfma_roof(dom, f_attn, kern_ms[dom])
-    roof["traffic"] = measured_traffic(dom, w.name)
+    # counter records are per single-pass launch
+    roof["traffic"] = measured_traffic(dom, w.name) if passes == 1 else None
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -423,7 +429,9 @@ def run_workload(name, steps, warmup, args, keep_state=False):
               **({"fused_topk": True} if fused else {}),
               **({"hier_index": {"chunk_blocks": args.hier_chunk, "keep_chunks": hier_keep}}
                  if hier else {}),
-              **({"attn_bwd": True} if use_bwd else {})}
+              **({"attn_bwd": True} if use_bwd else {}),
+              **({"attn_workspace_bytes": wbytes, "attn_passes": passes}
+                 if args.attn_workspace_gib > 0 else {})}
     res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": w.dtype,
            "config": config, "roofline": roof, "stages": stages, "extra": extra,
            "wall_s_timed": wall, "steps": steps, "warmup": warmup}
@@ -558,6 +566,9 @@ def main():
                          f"under extra.workloads (default with the main workload: {ALSO_WORKLOADS}; "
                          "'none' for none)")
     ap.add_argument("--schedule", default="auto", choices=["auto", "query_major", "kv_major"])
+    ap.add_argument("--attn-workspace-gib", type=float, default=0.0,
+                    help="bound the attention workspace (GiB): the KV-major schedule then runs "
+                         "its query rows in passes (0: one pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--layers", type=int, default=1,

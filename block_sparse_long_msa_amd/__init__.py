@@ -40,7 +40,8 @@ DTYPES = {"bf16": 0, "f32": 1}
 SCHEDULES = {"auto": 0, "query_major": 1, "kv_major": 2}
 EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size",
             "msa_index_topk", "msa_index_topk_hier_workspace_size", "msa_index_topk_hier",
-            "msa_sparse_attn_workspace_size",
+            "msa_sparse_attn_workspace_size", "msa_sparse_attn_workspace_size_min",
+            "msa_sparse_attn_rows_per_pass",
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_noalloc", "msa_sparse_attn_fwd_mass",
             "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
@@ -137,6 +138,10 @@ def _open(path: str) -> ctypes.CDLL:
     lib.msa_index_topk_hier.restype = st
     lib.msa_sparse_attn_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.msa_sparse_attn_workspace_size.restype = st
+    lib.msa_sparse_attn_workspace_size_min.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_sparse_attn_workspace_size_min.restype = st
+    lib.msa_sparse_attn_rows_per_pass.argtypes = [P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64)]
+    lib.msa_sparse_attn_rows_per_pass.restype = st
     lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msa_sparse_attn_fwd.restype = st
     lib.msa_sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -327,8 +332,27 @@ def index_topk_hier(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor, chu
 
 
 def workspace_size(prob: Problem) -> int:
+    """msa_sparse_attn_workspace_size: bytes for a single pass."""
     n = ctypes.c_size_t(0)
     _check(load_library().msa_sparse_attn_workspace_size(prob.ref(), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_size_min(prob: Problem) -> int:
+    """msa_sparse_attn_workspace_size_min: the least workspace the forward
+    calls accept (the KV-major schedule runs in passes below the single-pass
+    size)."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_sparse_attn_workspace_size_min(prob.ref(), ctypes.byref(n)))
+    return n.value
+
+
+def rows_per_pass(prob: Problem, workspace_bytes: int) -> int:
+    """msa_sparse_attn_rows_per_pass: query rows per pass of the forward with
+    a workspace of that many bytes."""
+    n = ctypes.c_int64(0)
+    _check(load_library().msa_sparse_attn_rows_per_pass(prob.ref(), workspace_bytes,
+                                                        ctypes.byref(n)))
     return n.value
 
 

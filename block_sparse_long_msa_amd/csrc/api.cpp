@@ -133,16 +133,27 @@ size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
       if (n_split <= 1) return 0;
       return (size_t)n_split * (size_t)d.total_q * (size_t)d.H * (size_t)(d.d + 1) * sizeof(float);
     case AttnPath::kKvMajor:
-      return msa::kvmajor_workspace_bytes(d);
+      return msa::kvmajor_workspace_bytes(d, d.total_q);
     case AttnPath::kQueryMajor:
       return 0;
   }
   return 0;
 }
 
+// The least workspace the call accepts: the KV-major path can run its rows in
+// passes over one smaller workspace; every other path needs its full size.
+size_t workspace_min_bytes(const msa_problem_t *p, const msa::Dims &d) {
+  int n_split = 1;
+  if (d.total_q > 0 && attn_path(p, d, &n_split) == AttnPath::kKvMajor)
+    return msa::kvmajor_workspace_min_bytes(d);
+  return workspace_bytes(p, d);
+}
+
 // With fixed_scratch, `workspace` is ignored: once every argument has been
 // validated, the library's fixed device scratch (noalloc.hip) serves as the
-// workspace, and a problem that needs more than it holds is rejected.
+// workspace, and a problem whose single-pass workspace exceeds it is rejected.
+// Otherwise a workspace below the single-pass size (but at least the minimum)
+// runs the KV-major path in passes over the query rows.
 msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, const void *v,
                       const int32_t *block_idx, void *out, float *lse, float *block_mass,
                       void *workspace, size_t workspace_bytes_given, void *stream,
@@ -157,7 +168,8 @@ msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, c
   if ((st = check_tensor(block_idx, "block_idx", any_q)) != MSA_SUCCESS) return st;
   if ((st = check_tensor(out, "out", any_q)) != MSA_SUCCESS) return st;
   if (lse != nullptr && !aligned(lse, 4)) return fail(MSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
-  const size_t need = workspace_bytes(prob, d);
+  const size_t full = workspace_bytes(prob, d);
+  size_t need = fixed_scratch ? full : workspace_min_bytes(prob, d);
   if (fixed_scratch) {
     const size_t have = msa::noalloc_scratch_bytes();
     if (need > have)
@@ -183,13 +195,17 @@ msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int n_split = 1;
   const AttnPath path = attn_path(prob, d, &n_split);
-  if (path == AttnPath::kKvMajor)
+  if (path == AttnPath::kKvMajor) {
+    const int64_t rows = msa::kvmajor_rows_per_pass(d, workspace_bytes_given);
+    if (rows <= 0)  // cannot happen once the minimum is checked
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace holds no pass of query rows");
     return launched(msa::launch_attn_kvmajor_bf16(d, static_cast<const uint16_t *>(q),
                                                   static_cast<const uint16_t *>(k),
                                                   static_cast<const uint16_t *>(v), block_idx,
                                                   static_cast<uint16_t *>(out), lse, block_mass,
-                                                  workspace, s),
+                                                  workspace, rows, s),
                     "attn_kvmajor");
+  }
   float *part_o = nullptr, *part_lse = nullptr;
   if (n_split > 1) {
     part_o = static_cast<float *>(workspace);
@@ -343,6 +359,33 @@ msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *b
   if (st != MSA_SUCCESS) return st;
   if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
   *bytes = workspace_bytes(prob, d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_workspace_size_min(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = workspace_min_bytes(prob, d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_rows_per_pass(const msa_problem_t *prob, size_t workspace_bytes_given,
+                                           int64_t *rows) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (rows == nullptr) return fail(MSA_ERR_NULL_POINTER, "rows is NULL");
+  *rows = 0;
+  const size_t need = workspace_min_bytes(prob, d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  int n_split = 1;
+  *rows = d.total_q > 0 && attn_path(prob, d, &n_split) == AttnPath::kKvMajor
+              ? msa::kvmajor_rows_per_pass(d, workspace_bytes_given)
+              : d.total_q;
   return ok();
 }
 

@@ -36,6 +36,8 @@ namespace msa {
 namespace {
 
 constexpr int kRowsPerItem = 256;  // gathered (query, head) rows per work item
+// Fewest query rows per pass when the workspace is too small for one pass.
+constexpr int64_t kMinPassRows = 256;
 constexpr int kWaves = 8;          // one 32-row tile per wave
 constexpr int kThreads = 64 * kWaves;
 
@@ -49,8 +51,8 @@ constexpr int kScanTile = 4096;  // buckets per block of the item-count scan
 struct KvWs {
   int32_t *counts, *cursor, *item_off, *entries, *scan_blk;
   int32_t *item_desc;  // per work item: g << 16 | j, 0, entry count, first KV row
-  float2 *part_ml;     // [total_q][K][H]      (m, l) of each slot
-  uint16_t *part_o;    // [total_q][K][H][d]   unnormalised O of each slot, bf16
+  float2 *part_ml;     // [rows][K][H]      (m, l) of each slot of the pass's rows
+  uint16_t *part_o;    // [rows][K][H][d]   unnormalised O of each slot, bf16
   uint16_t *trash_o;   // [64][d]  write target of lanes without a row (never read)
   float2 *trash_ml;    // [64]
   int64_t nbk, nscan, max_entries, max_items;
@@ -59,11 +61,13 @@ struct KvWs {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-KvWs carve(const Dims &p, void *base) {
+// Workspace of one pass over at most `rows` consecutive query rows (the
+// bucket arrays do not depend on it; entries, items and partials do).
+KvWs carve(const Dims &p, void *base, int64_t rows) {
   KvWs w;
   w.nbk = (int64_t)p.num_seqs * p.G * p.nb_max;
   w.nscan = (w.nbk + kScanTile - 1) / kScanTile;
-  w.max_entries = (int64_t)p.G * p.total_q * p.top_k;
+  w.max_entries = (int64_t)p.G * rows * p.top_k;
   const int qch = kRowsPerItem / (p.H / p.G);
   // every bucket adds at most one partly filled item
   w.max_items = w.max_entries / qch + std::min(w.nbk, w.max_entries) + 1;
@@ -81,8 +85,8 @@ KvWs carve(const Dims &p, void *base) {
   // item-major with qch slots per item (a bucket's last item is padded)
   w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_items * qch));
   w.item_desc = reinterpret_cast<int32_t *>(take(4 * sizeof(int32_t) * w.max_items));
-  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * p.total_q * p.top_k * p.H));
-  w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * p.total_q * p.top_k * p.H * p.d));
+  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * rows * p.top_k * p.H));
+  w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * rows * p.top_k * p.H * p.d));
   w.trash_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * 64 * p.d));
   w.trash_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * 64));
   w.total_bytes = off;
@@ -135,11 +139,13 @@ struct EntryRef {
 struct EntGeom {
   int G, K, lg_bs, nb_max, num_seqs;
   uint32_t kmagic_lo, kmagic_hi;  // ceil(2^32 / K) as two words (it is 2^32 for K = 1)
-  int64_t total_q;
+  int64_t total_q;                // row stride of block_idx's groups
+  int64_t row_lo, nrows;          // the pass's query rows [row_lo, row_lo + nrows)
 };
 
-// Entries of one tile: group-local entry index el = row * K + slot runs over
-// [el0, el0 + kEntTile); thread entry i of the tile is el0 + tid + 256 i.
+// Entries of one tile: the pass-local entry index el = (row - row_lo) * K +
+// slot runs over [el0, el0 + kEntTile); thread entry i of the tile is
+// el0 + tid + 256 i.
 struct TileStart {
   int64_t el0, row0;  // the tile's first entry and its row
   int off0;           // its slot
@@ -183,8 +189,9 @@ __device__ __forceinline__ TileStart tile_start(int g, const EntGeom &cg, const 
                                                 const int64_t *cu_kv) {
   TileStart t;
   t.el0 = (int64_t)blockIdx.x * kEntTile;
-  t.row0 = t.el0 / cg.K;  // once per work-group
-  t.off0 = (int)(t.el0 - t.row0 * cg.K);
+  const int64_t lrow = t.el0 / cg.K;  // once per work-group
+  t.off0 = (int)(t.el0 - lrow * cg.K);
+  t.row0 = cg.row_lo + lrow;
   t.b0 = find_seq(cu_q, cg.num_seqs, t.row0);
   t.s0 = seq_geom(cu_q, cu_kv, t.b0);
   t.bbase = ((int64_t)t.b0 * cg.G + g) * cg.nb_max;
@@ -198,11 +205,11 @@ __global__ __launch_bounds__(256) void kv_count_kernel(const int32_t *__restrict
                                                        EntGeom cg) {
   extern __shared__ int32_t hist[];  // nb_max bins
   const int g = blockIdx.y;
-  const int64_t per_g = cg.total_q * cg.K;
+  const int64_t per_g = cg.nrows * cg.K;
   const TileStart ts = tile_start(g, cg, cu_q, cu_kv);
   const int n = (int)min<int64_t>(kEntTile, per_g - ts.el0);
   if (n <= 0) return;
-  const int32_t *bi = block_idx + (int64_t)g * per_g + ts.el0;
+  const int32_t *bi = block_idx + ((int64_t)g * cg.total_q + cg.row_lo) * cg.K + ts.el0;
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   for (int local = threadIdx.x; local < n; local += 256) {
@@ -227,11 +234,11 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
                                                          EntGeom cg, int qch) {
   extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
   const int g = blockIdx.y;
-  const int64_t per_g = cg.total_q * cg.K;
+  const int64_t per_g = cg.nrows * cg.K;
   const TileStart ts = tile_start(g, cg, cu_q, cu_kv);
   const int n = (int)min<int64_t>(kEntTile, per_g - ts.el0);
   if (n <= 0) return;
-  const int32_t *bi = block_idx + (int64_t)g * per_g + ts.el0;
+  const int32_t *bi = block_idx + ((int64_t)g * cg.total_q + cg.row_lo) * cg.K + ts.el0;
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   int rank[kEntPerThread];
@@ -342,15 +349,15 @@ __global__ __launch_bounds__(256) void kv_scan_add_kernel(int32_t *__restrict__ 
 // descriptors of the bucket's work items (g << 16 | block, 0, entry count,
 // packed row of the block's first key), so a work item starts after one
 // 16-byte load and no divisions, and fill the unused entry slots of the
-// bucket's last item with row 0 / slot 0 (a valid row to load; the partial
-// kernel never stores for those lanes).
+// bucket's last item with the pass's first row / slot 0 (a valid row to
+// load; the partial kernel never stores for those lanes).
 __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict__ counts,
                                                        const int32_t *__restrict__ item_off,
                                                        int32_t *__restrict__ entries,
                                                        int32_t *__restrict__ item_desc,
                                                        const int64_t *__restrict__ cu_kv,
                                                        int64_t nbk, int G, int nb_max, int BS,
-                                                       int qch) {
+                                                       int qch, int32_t pad_entry) {
   const int lane = threadIdx.x & 63;
   const int64_t bkt = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (bkt >= nbk) return;
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
     u32x4 d = {g << 16 | j, 0u, (uint32_t)min(qch, cnt - i * qch), kvrow};
     st16(item_desc + 4 * (int64_t)(first + i), d);
   }
-  for (int i = cnt + lane; i < nitems * qch; i += 64) entries[(int64_t)first * qch + i] = 0;
+  for (int i = cnt + lane; i < nitems * qch; i += 64) entries[(int64_t)first * qch + i] = pad_entry;
 }
 
 // LDS tile of one K/V block, both row-major [key][d] without padding.  The
@@ -711,7 +718,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
     float2 *__restrict__ trash_ml, int H, int G, int K, int nseg, int nb_max, int qch,
-    float scale_log2, int64_t total_q, int64_t total_kv) {
+    float scale_log2, int64_t row_lo, int64_t row_hi, int64_t total_kv) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
   // two separate objects, so the compiler can tell the tile being loaded
   // from the tile being read
@@ -781,7 +788,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     return d;
   };
   auto q_of = [&](bf16x8 (&qb)[D / 16], const ItemDesc &d, int32_t e) {
-    MSA_DCHECK(e >= 0 && (e >> 6) < total_q && (e & 63) < K && d.g >= 0 && d.g < G);
+    MSA_DCHECK(e >= 0 && (e >> 6) >= row_lo && (e >> 6) < row_hi && (e & 63) < K && d.g >= 0 &&
+               d.g < G);
     MSA_DCHECK(d.kvrow >= 0 && d.kvrow + BS <= total_kv);
     const int half = lane >> 5;
     const uint16_t *qrow = q + ((int64_t)(e >> 6) * H + d.g * hpg + hh) * (int64_t)D + 8 * half;
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     pin(en);
     const ItemDesc dc = decode(wc);
     const bool own = qi < dc.n;
-    const int64_t ps = ((int64_t)(ec >> 6) * K + (ec & 63)) * H + dc.g * hpg + hh;
+    const int64_t ps = (((int64_t)(ec >> 6) - row_lo) * K + (ec & 63)) * H + dc.g * hpg + hh;
     uint16_t *od = own ? part_o + ps * D : trash_o + lane * D;
     float2 *md = own ? part_ml + ps : trash_ml + lane;
     const ItemDesc dn = decode(wn);
@@ -866,18 +874,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
     float2 *__restrict__ trash_ml, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
-    int64_t total_q, float scale_log2) {
+    int64_t total_q, float scale_log2, int64_t row_lo, int64_t row_hi) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const SeqGeom sq = seq_geom(cu_q, cu_kv, b);
-  // blockIdx.x counts the blocks that hold this sequence's queries, from the
-  // block of its first query at a non-negative position
-  const int J = (int)(max<int64_t>(sq.base, 0) / BS) + blockIdx.x;
+  // the sequence's local queries in this pass
+  const int64_t ilo = max<int64_t>(0, row_lo - sq.q0), ihi = min<int64_t>(sq.lq, row_hi - sq.q0);
+  if (ihi <= ilo) return;
+  // blockIdx.x counts the blocks that hold those queries, from the block of
+  // the first one at a non-negative position
+  const int J = (int)(max<int64_t>(sq.base + ilo, 0) / BS) + blockIdx.x;
   if (J >= nb_max) return;
-  // local queries whose position lies in block J
-  const int64_t i0 = max<int64_t>(0, (int64_t)J * BS - sq.base);
-  const int64_t i1 = min<int64_t>(sq.lq, (int64_t)(J + 1) * BS - sq.base);
+  // local queries of the pass whose position lies in block J
+  const int64_t i0 = max<int64_t>(ilo, (int64_t)J * BS - sq.base);
+  const int64_t i1 = min<int64_t>(ihi, (int64_t)(J + 1) * BS - sq.base);
   if (i1 <= i0) return;
   const int64_t s0 = (int64_t)J * BS;
   const int hpg = H / G;
@@ -910,7 +921,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int slot = cur.valid ? last_slot_of(block_idx + ((int64_t)g * total_q + cur.row) * K, K, J)
                                : -1;
     const bool write = cur.valid && slot >= 0;
-    const int64_t ps = (cur.row * K + (slot < 0 ? 0 : slot)) * H + cur.h;
+    const int64_t ps = ((cur.row - row_lo) * K + (slot < 0 ? 0 : slot)) * H + cur.h;
     const int lane = threadIdx.x & 63;
     attend_rows<D, BS, true, false>(tile, qa, s0, cur.pos, scale_log2,
                              write ? part_o + ps * D : trash_o + lane * D,
@@ -936,13 +947,14 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     const float2 *__restrict__ part_ml, uint16_t *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ block_mass,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int K, int BS, int64_t total_q) {
+    int G, int K, int BS, int64_t total_q, int64_t row_lo) {
   extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum
   float *lsh = wsh + K * H;
   float *winv = lsh + K * H;
-  const int64_t row = blockIdx.x;
+  const int64_t lrow = blockIdx.x;    // row of the pass (its partials)
+  const int64_t row = row_lo + lrow;  // query row
   constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
-  const uint16_t *base = part_o + row * (int64_t)K * H * D;
+  const uint16_t *base = part_o + lrow * (int64_t)K * H * D;
   // The first four slots of this thread's first octet are requested before
   // the weights are formed, so the partial stream is under way during that
   // work.  Addresses are clamped into the row (a thread without an octet, or
@@ -971,7 +983,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
       sl[u] = t / H;
       h[u] = t - sl[u] * H;
       j[u] = block_idx[((int64_t)(h[u] / hpg) * total_q + row) * K + sl[u]];
-      mlr[u] = part_ml[(row * K + sl[u]) * H + h[u]];
+      mlr[u] = part_ml[(lrow * K + sl[u]) * H + h[u]];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1083,11 +1095,16 @@ int persistent_grid(int64_t max_items) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(n, max_items));
 }
 
+// One pass of the KV-major path over query rows [row_lo, row_hi): bucket
+// the pass's kept-slot entries, run the partial, diagonal and merge kernels.
+// Each row's result depends on its own entries only, so splitting the rows
+// into passes changes no output bit.
 template <int D, int BS>
-hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                      const int32_t *block_idx, uint16_t *out, float *lse, float *block_mass,
-                      void *workspace, hipStream_t s) {
-  KvWs w = carve(p, workspace);
+void launch_pass(const Dims &p, const KvWs &w, int64_t row_lo, int64_t row_hi,
+                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                 const int32_t *block_idx, uint16_t *out, float *lse, float *block_mass,
+                 hipStream_t s) {
+  const int64_t nrows = row_hi - row_lo;
   const int hpg = p.H / p.G;
   const int qch = kRowsPerItem / hpg;
   const float sl2 = p.scale * kLog2e;
@@ -1096,8 +1113,8 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   profile_mark(s);
   const uint64_t kmagic = ((1ull << 32) + (uint64_t)p.top_k - 1) / (uint64_t)p.top_k;
   const EntGeom cg{p.G, p.top_k, 31 - __builtin_clz(p.B), p.nb_max, p.num_seqs,
-                   (uint32_t)kmagic, (uint32_t)(kmagic >> 32), p.total_q};
-  const int64_t per_g = p.total_q * p.top_k;
+                   (uint32_t)kmagic, (uint32_t)(kmagic >> 32), p.total_q, row_lo, nrows};
+  const int64_t per_g = nrows * p.top_k;
   const dim3 tiles((unsigned)((per_g + kEntTile - 1) / kEntTile), p.G);
   const size_t hist_bytes = sizeof(int32_t) * p.nb_max;
   hipLaunchKernelGGL(kv_count_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.counts,
@@ -1114,25 +1131,41 @@ hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const
   profile_mark(s);
   hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 3) / 4)), dim3(256), 0, s,
                      w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.G,
-                     p.nb_max, p.B, qch);
+                     p.nb_max, p.B, qch, (int32_t)(row_lo << 6));
   profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
                      dim3(kThreads), 0, s, q, k, v, w.item_off, w.entries, w.item_desc, w.part_o,
                      w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, p.num_seqs * p.G,
-                     p.nb_max, qch, sl2, p.total_q, p.total_kv);
+                     p.nb_max, qch, sl2, row_lo, row_hi, p.total_kv);
   profile_mark(s);
-  // the blocks holding a sequence's queries: at most ceil(max_q_len / B) + 1
-  const int ndiag = (int)std::min<int64_t>((p.max_q_len + p.B - 1) / p.B + 1, p.nb_max);
+  // the blocks holding a sequence's queries of the pass: at most
+  // ceil(min(max_q_len, nrows) / B) + 1
+  const int64_t span = std::min<int64_t>(p.max_q_len, nrows);
+  const int ndiag = (int)std::min<int64_t>((span + p.B - 1) / p.B + 1, p.nb_max);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(ndiag, p.G, p.num_seqs), dim3(kThreads), 0, s,
-                     q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv, p.num_seqs, p.H,
-                     p.G, p.top_k, p.nb_max, p.total_q, sl2);
+                     q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q,
+                     p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, p.total_q, sl2, row_lo,
+                     row_hi);
   profile_mark(s);
   const size_t merge_lds = sizeof(float) * (2 * (size_t)p.top_k * p.H + p.H);
-  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)p.total_q), dim3(256), merge_lds, s, block_idx,
-                     w.part_o, w.part_ml, out, lse, block_mass, p.cu_q, p.cu_kv, p.num_seqs,
-                     p.H, p.G, p.top_k, p.B, p.total_q);
+  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)nrows), dim3(256), merge_lds, s,
+                     block_idx, w.part_o, w.part_ml, out, lse, block_mass, p.cu_q, p.cu_kv,
+                     p.num_seqs, p.H, p.G, p.top_k, p.B, p.total_q, row_lo);
   profile_mark(s);
-  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_all(const Dims &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const int32_t *block_idx, uint16_t *out, float *lse, float *block_mass,
+                      void *workspace, int64_t rows_per_pass, hipStream_t s) {
+  const KvWs w = carve(p, workspace, rows_per_pass);
+  for (int64_t r0 = 0; r0 < p.total_q; r0 += rows_per_pass) {
+    launch_pass<D, BS>(p, w, r0, std::min(p.total_q, r0 + rows_per_pass), q, k, v, block_idx,
+                       out, lse, block_mass, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1143,20 +1176,37 @@ bool kvmajor_fits(const Dims &p) {
   if (p.total_q >= (int64_t)1 << 25) return false;  // entries pack the query row above 6 slot bits
   // the merge keeps (m, l) of every (slot, head) of a row in LDS
   if ((2 * (int64_t)p.top_k * p.H + p.H) * (int64_t)sizeof(float) > 64 * 1024) return false;
-  const KvWs w = carve(p, nullptr);
+  const KvWs w = carve(p, nullptr, p.total_q);
   return w.max_items * (kRowsPerItem / (p.H / p.G)) < (int64_t)INT32_MAX;
 }
 
-size_t kvmajor_workspace_bytes(const Dims &p) { return carve(p, nullptr).total_bytes; }
+size_t kvmajor_workspace_bytes(const Dims &p, int64_t rows_per_pass) {
+  return carve(p, nullptr, std::max<int64_t>(1, std::min(rows_per_pass, p.total_q))).total_bytes;
+}
+
+size_t kvmajor_workspace_min_bytes(const Dims &p) { return kvmajor_workspace_bytes(p, kMinPassRows); }
+
+int64_t kvmajor_rows_per_pass(const Dims &p, size_t workspace_bytes) {
+  if (kvmajor_workspace_bytes(p, p.total_q) <= workspace_bytes) return p.total_q;
+  if (kvmajor_workspace_bytes(p, kMinPassRows) > workspace_bytes) return 0;
+  int64_t lo = std::min<int64_t>(kMinPassRows, p.total_q), hi = p.total_q;  // fits, does not
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (kvmajor_workspace_bytes(p, mid) <= workspace_bytes) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
                                     float *lse, float *block_mass, void *workspace,
-                                    hipStream_t s) {
+                                    int64_t rows_per_pass, hipStream_t s) {
   if (p.total_q <= 0) return hipSuccess;
+  if (rows_per_pass <= 0) return hipErrorInvalidValue;
 #define MSA_KV_CASE(D_, BS_) \
   if (p.d == D_ && p.B == BS_)  \
-    return launch_all<D_, BS_>(p, q, k, v, block_idx, out, lse, block_mass, workspace, s);
+    return launch_all<D_, BS_>(p, q, k, v, block_idx, out, lse, block_mass, workspace, \
+                               rows_per_pass, s);
   MSA_KV_CASE(64, 64) MSA_KV_CASE(64, 128) MSA_KV_CASE(128, 64) MSA_KV_CASE(128, 128)
 #undef MSA_KV_CASE
   return hipErrorInvalidValue;

@@ -80,14 +80,21 @@ hipError_t launch_combine_splits(const Dims &p, int n_split, const float *part_o
                                  const float *part_lse, void *out, bool out_bf16, float *lse,
                                  hipStream_t s);
 
-// Attention, KV-major prefill (bf16): see attn_kvmajor.hip.
-// True if the KV-major schedule's 32-bit entry and item indices hold this problem.
+// Attention, KV-major prefill (bf16): see attn_kvmajor.hip.  The query rows
+// run in passes of rows_per_pass rows that share one workspace of
+// kvmajor_workspace_bytes(p, rows_per_pass) bytes; kvmajor_rows_per_pass
+// gives the most rows a workspace holds (0 if not even the fewest,
+// kvmajor_workspace_min_bytes).  kvmajor_fits: the schedule's 32-bit entry
+// and item indices hold this problem.  block_mass (may be NULL):
+// [G, total_q, top_k] Main Branch mass per kept slot.
 bool kvmajor_fits(const Dims &p);
-size_t kvmajor_workspace_bytes(const Dims &p);
-// block_mass (may be NULL): [G, total_q, top_k] Main Branch mass per kept slot.
+size_t kvmajor_workspace_bytes(const Dims &p, int64_t rows_per_pass);
+size_t kvmajor_workspace_min_bytes(const Dims &p);
+int64_t kvmajor_rows_per_pass(const Dims &p, size_t workspace_bytes);
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
-                                    float *lse, float *block_mass, void *workspace, hipStream_t s);
+                                    float *lse, float *block_mass, void *workspace,
+                                    int64_t rows_per_pass, hipStream_t s);
 
 // Backward of the Index Branch max-pooling (index_bwd.hip).
 size_t index_bwd_workspace_bytes(const Dims &p);

@@ -184,8 +184,27 @@ msa_status_t msa_index_topk_hier(const msa_problem_t *prob, const void *q_idx, c
                                  void *stream);
 
 /* Bytes of device workspace msa_sparse_attn_fwd needs for this problem and
- * schedule (0 is possible).  Writes the size to *bytes (host). */
+ * schedule to run in one pass (0 is possible).  Writes the size to *bytes
+ * (host). */
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes);
+
+/* The least workspace msa_sparse_attn_fwd and msa_sparse_attn_fwd_mass
+ * accept for this problem and schedule (host *bytes).  It equals
+ * msa_sparse_attn_workspace_size() except on the KV-major schedule, whose
+ * workspace grows with total_q * top_k * num_q_heads * head_dim (the
+ * per-slot partial results): given less than the single-pass size, that
+ * schedule runs the query rows in consecutive passes of as many rows as the
+ * workspace holds (at least 256 rows, or all of them), reusing it for every
+ * pass.  Each pass re-reads the K/V blocks its rows keep; the outputs are
+ * identical bit for bit to a single pass. */
+msa_status_t msa_sparse_attn_workspace_size_min(const msa_problem_t *prob, size_t *bytes);
+
+/* Query rows per pass that msa_sparse_attn_fwd (or _mass) runs with a
+ * workspace of `workspace_bytes` (host *rows): total_q when one pass fits or
+ * the schedule is not KV-major.  MSA_ERR_WORKSPACE_TOO_SMALL (and *rows = 0)
+ * below msa_sparse_attn_workspace_size_min(). */
+msa_status_t msa_sparse_attn_rows_per_pass(const msa_problem_t *prob, size_t workspace_bytes,
+                                           int64_t *rows);
 
 /* Step 3 - exact softmax attention over the kept blocks.
  * For query row r, head h of group g: keys = every s <= p(r) inside a block
@@ -195,8 +214,10 @@ msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *b
  * If lse is not NULL, lse[r,h] = m + ln(sum_s exp(z_s - m)).
  * Rows with max_q_len == 1 use the split-KV decode kernels.  out has the
  * input dtype (bf16 rounding to nearest even).  `workspace` must hold at
- * least msa_sparse_attn_workspace_size() bytes (it may be NULL if that is
- * 0); its contents need no initialisation and are clobbered. */
+ * least msa_sparse_attn_workspace_size_min() bytes (it may be NULL if that
+ * is 0; workspace_bytes is its size, and a workspace below
+ * msa_sparse_attn_workspace_size() runs the KV-major schedule in passes);
+ * its contents need no initialisation and are clobbered. */
 msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const void *k,
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *stream);
@@ -206,9 +227,9 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
  * allocation).  Same arguments, same kernels and same results as
  * msa_sparse_attn_fwd, without a workspace: the call uses a fixed scratch
  * array of 64 MiB that the library holds on every GPU it runs on until the
- * process ends.  It allocates and frees nothing.  A problem whose
- * msa_sparse_attn_workspace_size() exceeds 64 MiB is rejected with
- * MSA_ERR_WORKSPACE_TOO_SMALL before anything is launched (use
+ * process ends.  It allocates and frees nothing, and runs in one pass.  A
+ * problem whose msa_sparse_attn_workspace_size() exceeds 64 MiB is rejected
+ * with MSA_ERR_WORKSPACE_TOO_SMALL before anything is launched (use
  * msa_sparse_attn_fwd for those).  All calls on one GPU share the scratch:
  * calls that overlap in time on one GPU (on different streams) race and
  * must be serialised by the caller; consecutive calls need no clearing. */

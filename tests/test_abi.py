@@ -180,6 +180,44 @@ def test_workspace_size_and_too_small():
     assert _attn(pd, ws=FAKE, wsb=n.value - 1) == 5
     assert _attn(pd, ws=None, wsb=n.value) == 1
     assert _attn(pd, ws=FAKE + 16, wsb=n.value) == 4
+    m = ctypes.c_size_t(0)
+    assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(pd), ctypes.byref(m)) == 0
+    assert m.value == n.value  # only the KV-major schedule runs in passes
+    assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(pd), None) == 1
+
+
+def test_kv_major_workspace_passes():
+    """The KV-major schedule's workspace: a single pass needs the per-slot
+    partials of every row; the least accepted workspace holds a pass of 256
+    rows; anything between is accepted (the rows then run in passes)."""
+    lib = msa.load_library()
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p = _prob(max_q_len=4096, total_q=4096, max_kv_len=4096, total_kv=4096, top_k=8)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(full)) == 0
+    assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(p), ctypes.byref(least)) == 0
+    per_row = 8 * 8 * (128 * 2 + 8)  # top_k * H * (bf16 partial row + (m, l))
+    assert full.value - least.value >= (4096 - 256) * per_row
+    assert full.value - least.value < (4096 - 256) * per_row + (4096 - 256) * 8 * 8 * 4 + 4096 * 64
+    # below the least size: rejected before any launch (FAKE pointers are never read)
+    assert _attn(p, ws=FAKE, wsb=least.value - 1) == 5
+    assert b"workspace needs" in lib.msa_last_error_message()
+    rows = ctypes.c_int64(-1)
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p), least.value - 1, ctypes.byref(rows)) == 5
+    assert rows.value == 0
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p), least.value, ctypes.byref(rows)) == 0
+    assert rows.value == 256
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p), full.value, ctypes.byref(rows)) == 0
+    assert rows.value == 4096
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p), full.value - 1, ctypes.byref(rows)) == 0
+    assert 256 <= rows.value < 4096
+    mid = least.value + (full.value - least.value) // 2
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p), mid, ctypes.byref(rows)) == 0
+    assert abs(rows.value - 2176) <= 40  # halfway between 256 and 4096 rows
+    # a small problem needs its single pass either way
+    small = _prob()
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(small), ctypes.byref(full)) == 0
+    assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(small), ctypes.byref(least)) == 0
+    assert full.value == least.value
 
 
 def test_empty_batch_is_a_no_op():

@@ -129,3 +129,30 @@ def test_debug_build_prefill_32k(debug_then_release):
                         w.block_size, w.top_k, w.dtype, hier=(16, 2))
     assert n == 0, f"{n} failed bounds checks"
     _compare(rel, dbg)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[4]],
+                         ids=[CASES[0][0], CASES[1][0], CASES[4][0]])
+def test_debug_build_kv_major_passes(case, debug_then_release):
+    """The KV-major forward in passes of 256 rows (the least workspace)."""
+    name, lq, lkv, H, G, d, di, B, k, dtype, _ = case
+    _log(f"debug bounds, passes: {name}")
+    inp = W.random_case(CASES.index(case), lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
+
+    def run():
+        prob = msa.Problem(inp["cu_q"], inp["cu_kv"], lq, lkv, H, G, d, di, B, k, dtype)
+        bi = msa.topk_select(prob, msa.index_score(prob, inp["q_idx"], inp["k_idx"]))
+        ws = torch.empty(msa.workspace_size_min(prob), dtype=torch.uint8, device=DEV)
+        outs = list(msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], bi, workspace=ws))
+        torch.cuda.synchronize()
+        return outs
+
+    msa.select_library(msa.LIB_PATH)
+    rel = run()
+    msa.select_library(msa.DEBUG_LIB_PATH)
+    msa.debug_bounds_violations(reset=True)
+    dbg = run()
+    bad, ran = msa.debug_bounds_violations(reset=True)
+    _log(f"  {ran} lane checks, {bad} failed")
+    assert ran > 0 and bad == 0
+    _compare(rel, dbg)

@@ -333,3 +333,58 @@ def test_cross_layer_reuse():
             err = C.check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l,
                                     "bf16")
             _log(f"cross-layer reuse, {sched}, layer {layer}: max |O - O_ref| = {err:.3g}")
+
+
+def _passes_equal_single_pass(inp, H, G, d, di, B, k, sizes):
+    """The KV-major forward with a workspace below its single-pass size runs
+    the query rows in passes; every output equals the single pass's bit for
+    bit (out, LSE and the block mass)."""
+    prob = msa.Problem(inp["cu_q"], inp["cu_kv"], inp["len_q"], inp["len_kv"], H, G, d, di, B, k,
+                       "bf16")
+    bi = msa.topk_select(prob, msa.index_score(prob, inp["q_idx"], inp["k_idx"]))
+    ref = msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], bi)
+    full, least = msa.workspace_size(prob), msa.workspace_size_min(prob)
+    assert 0 < least < full
+    with pytest.raises(msa.MsaError) as e:
+        ws = torch.empty(least - 1, dtype=torch.uint8, device=DEV)
+        msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], bi, workspace=ws)
+    assert e.value.status == 5
+    for nbytes in sizes(least, full):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        got = msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], bi, workspace=ws)
+        o2, l2 = msa.sparse_attn_fwd(prob, inp["q"], inp["k"], inp["v"], bi, return_lse=True,
+                                     workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+        assert torch.equal(o2.view(torch.int16), ref[0].view(torch.int16))
+        assert torch.equal(l2.view(torch.int32), ref[1].view(torch.int32))
+        _log(f"  workspace {nbytes} of {full} bytes: equal to the single pass")
+        del ws
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[5]],
+                         ids=[SMALL[0][0], SMALL[1][0], SMALL[5][0]])
+def test_kv_major_passes_small(case):
+    name, lq, lkv, H, G, d, di, B, k = case
+    _log(f"passes {name}")
+    inp = W.random_case(60 + SMALL.index(case), lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    _passes_equal_single_pass(inp, H, G, d, di, B, k,
+                              lambda least, full: [least, (least + full) // 2, full - 1])
+
+
+@pytest.mark.parametrize("name", ["chunked-prefill-1m", "prefill-128k"])
+def test_kv_major_passes_full_size(name):
+    """The long workloads with a bounded workspace: the 1M chunk in passes of
+    the fewest rows (256) and of a quarter of its rows; prefill-128k within
+    8 GiB instead of its ~69 GB single-pass workspace."""
+    w = W.WORKLOADS[name]
+    _log(f"passes {name}: generating")
+    inp = W.make_inputs(w, device=DEV, seed=0)
+    if name == "prefill-128k":
+        sizes = lambda least, full: [8 << 30]  # noqa: E731
+    else:
+        sizes = lambda least, full: [least, full // 4 + 1]  # noqa: E731
+    _passes_equal_single_pass(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
+                              w.block_size, w.top_k, sizes)
