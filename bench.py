@@ -213,7 +213,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         nab = ctypes.c_size_t(0)
         msa._check(msa.load_library().msa_sparse_attn_bwd_workspace_size(prob.ref(),
                                                                          ctypes.byref(nab)))
-        ab_ws = torch.empty(max(nab.value, 1), dtype=torch.uint8, device=dev)
+        ab_bytes = nab.value
+        if args.attn_workspace_gib > 0:  # bounded: the backward's rows run in passes too
+            ab_bytes = max(msa.sparse_attn_bwd_workspace_size(prob, minimum=True),
+                           min(ab_bytes, int(args.attn_workspace_gib * 2**30)))
+        ab_passes = -(-prob.total_q // max(1, msa.sparse_attn_bwd_rows_per_pass(prob, ab_bytes)))
+        ab_ws = torch.empty(max(ab_bytes, 1), dtype=torch.uint8, device=dev)
         ab_kernels = ["ab_dsum", "ab_buckets", "ab_zero_unkept", "ab_item", "ab_reduce", "ab_dq"]
     if train and args.indexer_kl:
         mass = torch.empty((prob.G, prob.total_q, prob.top_k), dtype=torch.float32, device=dev)
@@ -320,7 +325,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     pevents = [msa.ProfileEvents(len(attn_kernels) * passes, dev) for _ in range(steps)]
-    bevents = [msa.ProfileEvents(len(ab_kernels), dev) if use_bwd else None
+    bevents = [msa.ProfileEvents(1 + (len(ab_kernels) - 1) * ab_passes, dev) if use_bwd else None
                for _ in range(steps)]
     hier_kernels = ["hi_mean", "hi_coarse", "hi_buckets", "hi_fine", "hi_final"]
     fevents = [msa.ProfileEvents(2, dev) if fused else
@@ -361,9 +366,12 @@ def run_workload(name, steps, warmup, args, keep_state=False):
     if use_kl:
         kern_all["indexer_kl"] = [e[3].elapsed_time(e[4]) for e in events]
         kern_all["indexer_bwd"] = [e[4].elapsed_time(e[5]) for e in events]
-    if use_bwd:
-        for i, kn in enumerate(ab_kernels):
-            kern_all[kn] = [(e[5] if i == 0 else be.events[i - 1]).elapsed_time(be.events[i])
+    if use_bwd:  # the D kernel, then per pass the other kernels (summed over the passes)
+        nb_ = len(ab_kernels) - 1
+        kern_all[ab_kernels[0]] = [e[5].elapsed_time(be.events[0]) for e, be in zip(events, bevents)]
+        for i, kn in enumerate(ab_kernels[1:], start=1):
+            kern_all[kn] = [sum(be.events[j - 1].elapsed_time(be.events[j])
+                                for j in range(i, 1 + nb_ * ab_passes, nb_))
                             for e, be in zip(events, bevents)]
     kern_ms = {kn: float(np.mean(v)) for kn, v in kern_all.items()}        # average launch
     kern_med = {kn: med(v) for kn, v in kern_all.items()}
@@ -431,7 +439,9 @@ def run_workload(name, steps, warmup, args, keep_state=False):
                  if hier else {}),
               **({"attn_bwd": True} if use_bwd else {}),
               **({"attn_workspace_bytes": wbytes, "attn_passes": passes}
-                 if args.attn_workspace_gib > 0 else {})}
+                 if args.attn_workspace_gib > 0 else {}),
+              **({"attn_bwd_workspace_bytes": ab_bytes, "attn_bwd_passes": ab_passes}
+                 if args.attn_workspace_gib > 0 and use_bwd else {})}
     res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": w.dtype,
            "config": config, "roofline": roof, "stages": stages, "extra": extra,
            "wall_s_timed": wall, "steps": steps, "warmup": warmup}

@@ -45,7 +45,8 @@ EXPORTED = ("msa_index_score", "msa_topk_select", "msa_index_topk_workspace_size
             "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_noalloc", "msa_sparse_attn_fwd_mass",
             "msa_indexer_kl",
             "msa_indexer_bwd_workspace_size", "msa_indexer_bwd",
-            "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
+            "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd_workspace_size_min",
+            "msa_sparse_attn_bwd_rows_per_pass", "msa_sparse_attn_bwd",
             "msa_set_profile_events", "msa_debug_bounds_violations", "msa_status_string",
             "msa_last_error_message", "msa_abi_version")
 
@@ -156,6 +157,11 @@ def _open(path: str) -> ctypes.CDLL:
     lib.msa_indexer_bwd.restype = st
     lib.msa_sparse_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.msa_sparse_attn_bwd_workspace_size.restype = st
+    lib.msa_sparse_attn_bwd_workspace_size_min.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msa_sparse_attn_bwd_workspace_size_min.restype = st
+    lib.msa_sparse_attn_bwd_rows_per_pass.argtypes = [P, ctypes.c_size_t,
+                                                      ctypes.POINTER(ctypes.c_int64)]
+    lib.msa_sparse_attn_bwd_rows_per_pass.restype = st
     lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
     lib.msa_sparse_attn_bwd.restype = st
@@ -489,6 +495,25 @@ def indexer_bwd(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor,
                                           _ptr(grad), _ptr(dq), _ptr(dk), _ptr(workspace), wbytes,
                                           s))
     return dq, dk
+
+
+def sparse_attn_bwd_workspace_size(prob: Problem, minimum: bool = False) -> int:
+    """msa_sparse_attn_bwd_workspace_size (single pass), or with `minimum`
+    msa_sparse_attn_bwd_workspace_size_min (the least accepted)."""
+    n = ctypes.c_size_t(0)
+    lib = load_library()
+    fn = lib.msa_sparse_attn_bwd_workspace_size_min if minimum else lib.msa_sparse_attn_bwd_workspace_size
+    _check(fn(prob.ref(), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_bwd_rows_per_pass(prob: Problem, workspace_bytes: int) -> int:
+    """msa_sparse_attn_bwd_rows_per_pass: query rows per pass of the backward
+    with a workspace of that many bytes."""
+    n = ctypes.c_int64(0)
+    _check(load_library().msa_sparse_attn_bwd_rows_per_pass(prob.ref(), workspace_bytes,
+                                                            ctypes.byref(n)))
+    return n.value
 
 
 def sparse_attn_bwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -492,7 +492,13 @@ bool attn_bwd_mfma(const msa_problem_t *prob, const msa::Dims &d) {
   return prob->dtype == MSA_BF16 && msa::attn_bwd_supported(d);
 }
 size_t attn_bwd_bytes(const msa_problem_t *prob, const msa::Dims &d) {
-  return attn_bwd_mfma(prob, d) ? msa::attn_bwd_workspace_bytes(d)
+  return attn_bwd_mfma(prob, d) ? msa::attn_bwd_workspace_bytes(d, d.total_q)
+                                : msa::attn_bwd_fma_workspace_bytes(d);
+}
+// The MFMA backward runs its rows in passes below its single-pass size; the
+// FMA one needs its full workspace.
+size_t attn_bwd_min_bytes(const msa_problem_t *prob, const msa::Dims &d) {
+  return attn_bwd_mfma(prob, d) ? msa::attn_bwd_workspace_min_bytes(d)
                                 : msa::attn_bwd_fma_workspace_bytes(d);
 }
 }  // namespace
@@ -503,6 +509,32 @@ msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_
   if (st != MSA_SUCCESS) return st;
   if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
   *bytes = attn_bwd_bytes(prob, d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_bwd_workspace_size_min(const msa_problem_t *prob, size_t *bytes) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (bytes == nullptr) return fail(MSA_ERR_NULL_POINTER, "bytes is NULL");
+  *bytes = attn_bwd_min_bytes(prob, d);
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_bwd_rows_per_pass(const msa_problem_t *prob,
+                                               size_t workspace_bytes_given, int64_t *rows) {
+  msa::Dims d;
+  msa_status_t st = check_problem(prob, &d);
+  if (st != MSA_SUCCESS) return st;
+  if (rows == nullptr) return fail(MSA_ERR_NULL_POINTER, "rows is NULL");
+  *rows = 0;
+  const size_t need = attn_bwd_min_bytes(prob, d);
+  if (workspace_bytes_given < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes_given);
+  *rows = attn_bwd_mfma(prob, d) && d.total_q > 0
+              ? msa::attn_bwd_rows_per_pass(d, workspace_bytes_given)
+              : d.total_q;
   return ok();
 }
 
@@ -531,7 +563,7 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
     return fail(MSA_ERR_BAD_SHAPE,
                 "num_seqs * ceil(max_kv_len / block_size) must be at most 16384 for the "
                 "attention backward (one LDS histogram bin per (sequence, block))");
-  const size_t need = attn_bwd_bytes(prob, d);
+  const size_t need = attn_bwd_min_bytes(prob, d);
   if (workspace_bytes_given < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace_bytes_given);
@@ -549,6 +581,7 @@ msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const
                       static_cast<const uint16_t *>(v), block_idx,
                       static_cast<const uint16_t *>(out), lse,
                       static_cast<const uint16_t *>(dout), dq, dk, dv, workspace,
+                      msa::attn_bwd_rows_per_pass(d, workspace_bytes_given),
                       reinterpret_cast<hipStream_t>(stream)),
                   "attn_bwd");
 }

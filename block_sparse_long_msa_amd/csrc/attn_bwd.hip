@@ -45,7 +45,7 @@ constexpr int kItemThreads = 512;  // 8 waves: 4 key groups x 2 halves
 struct AbWs {
   int32_t *cnt, *base, *lists, *ibase, *pbase;
   float *dsum;        // [total_q][H] rowsum(dO * O)
-  uint16_t *dq_part;  // [total_q * K * H][d] bf16: the dQ of each kept slot, unscaled
+  uint16_t *dq_part;  // [rows * K * H][d] bf16: the dQ of each kept slot of a pass's rows, unscaled
   float *part;        // [max_parts][2][BS][d]: dV, dK (unscaled) of the items of shared buckets
   int64_t ntiles, nbk_g, nent_g, max_items, max_parts, tile;
   int32_t per_item;
@@ -54,9 +54,11 @@ struct AbWs {
 
 size_t ab_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
-AbWs ab_carve(const Dims &p, void *base) {
+// Workspace of passes over at most `rows` query rows (the buckets, lists,
+// slot dQ and item partials of one pass; D of every row).
+AbWs ab_carve(const Dims &p, void *base, int64_t rows) {
   AbWs w;
-  w.nent_g = p.total_q * (int64_t)p.top_k;
+  w.nent_g = rows * (int64_t)p.top_k;
   w.nbk_g = (int64_t)p.num_seqs * p.nb_max;
   w.tile = bucket_tile(w.nent_g, w.nbk_g);
   w.ntiles = (w.nent_g + w.tile - 1) / w.tile;
@@ -200,7 +202,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                uint16_t *__restrict__ dq_part, float *__restrict__ dk, float *__restrict__ dv,
                float *__restrict__ part, const int64_t *__restrict__ cu_q,
                const int64_t *__restrict__ cu_kv, int G, int H, int K, int nb_max,
-               int64_t nbuckets, int per_item, float scale) {
+               int64_t nbuckets, int per_item, float scale, int64_t e_lo, int accumulate) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kBS * kD];     // K [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t vs[kBS * kD];     // V [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t qs[kRows * kD];   // Q [row][d]
@@ -292,7 +294,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       m_lse[r_ld] = ok ? f_lse * kLog2e : __builtin_inff();
       m_d[r_ld] = ok ? f_d : 0.f;
       m_pos[r_ld] = ok ? (int)(base_pos + (t - q0)) : -1;
-      m_off[r_ld] = ok ? f_e * H + g * hpg + r_ld % hpg : -1;
+      m_off[r_ld] = ok ? (f_e - (int32_t)e_lo) * H + g * hpg + r_ld % hpg : -1;
     }
   };
 
@@ -433,15 +435,21 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     kscale = 1.f;
   }
   // lane holds key 32 kg + li, channels 64 hf + 32 y + 8 (r / 4) + 4 hh + r % 4
+  // a pass after the first adds to the dk / dv of the earlier passes
+  const bool add = accumulate != 0 && nit == 1;
 #pragma unroll
   for (int y = 0; y < 2; ++y)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int dc = 64 * hf + 32 * y + 8 * q4 + 4 * hh;
-      const f32x4 vv = {acc_v[y][4 * q4], acc_v[y][4 * q4 + 1], acc_v[y][4 * q4 + 2],
-                        acc_v[y][4 * q4 + 3]};
-      const f32x4 kk = {acc_k[y][4 * q4] * kscale, acc_k[y][4 * q4 + 1] * kscale,
-                        acc_k[y][4 * q4 + 2] * kscale, acc_k[y][4 * q4 + 3] * kscale};
+      f32x4 vv = {acc_v[y][4 * q4], acc_v[y][4 * q4 + 1], acc_v[y][4 * q4 + 2],
+                  acc_v[y][4 * q4 + 3]};
+      f32x4 kk = {acc_k[y][4 * q4] * kscale, acc_k[y][4 * q4 + 1] * kscale,
+                  acc_k[y][4 * q4 + 2] * kscale, acc_k[y][4 * q4 + 3] * kscale};
+      if (add) {
+        vv += *reinterpret_cast<const f32x4 *>(dvp + dc);
+        kk += *reinterpret_cast<const f32x4 *>(dkp + dc);
+      }
       *reinterpret_cast<f32x4 *>(dvp + dc) = vv;
       *reinterpret_cast<f32x4 *>(dkp + dc) = kk;
     }
@@ -457,7 +465,8 @@ __global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restric
                                                         float *__restrict__ dk,
                                                         float *__restrict__ dv,
                                                         const int64_t *__restrict__ cu_kv, int G,
-                                                        int nb_max, int64_t nbk_g, float scale) {
+                                                        int nb_max, int64_t nbk_g, float scale,
+                                                        int accumulate) {
   const int64_t gb = blockIdx.x;
   const int32_t nit = ibase[gb + 1] - ibase[gb];
   if (nit <= 1) return;
@@ -478,8 +487,13 @@ __global__ __launch_bounds__(256) void ab_reduce_kernel(const int32_t *__restric
     }
     const int s = x / kD, c = x - s * kD;
     const int64_t o = ((kv0 + s0 + s) * G + g) * (int64_t)kD + c;
+    ak *= scale;
+    if (accumulate) {  // a pass after the first adds to the earlier passes' sums
+      av += *reinterpret_cast<const f32x4 *>(dv + o);
+      ak += *reinterpret_cast<const f32x4 *>(dk + o);
+    }
     *reinterpret_cast<f32x4 *>(dv + o) = av;
-    *reinterpret_cast<f32x4 *>(dk + o) = ak * scale;
+    *reinterpret_cast<f32x4 *>(dk + o) = ak;
   }
 }
 
@@ -499,9 +513,10 @@ __global__ __launch_bounds__(256) void ab_dq_kernel(const uint16_t *__restrict__
                                                     const int64_t *__restrict__ cu_q,
                                                     const int64_t *__restrict__ cu_kv,
                                                     int num_seqs, int H, int G, int K,
-                                                    int64_t total_q, int nb_max, float scale) {
-  const int64_t rh = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (rh >= total_q * H) return;
+                                                    int64_t total_q, int nb_max, float scale,
+                                                    int64_t row_lo, int64_t row_hi) {
+  const int64_t rh = row_lo * H + (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (rh >= row_hi * H) return;
   const int part = threadIdx.x & 15;
   const int64_t row = rh / H;
   const int h = (int)(rh - row * H);
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(256) void ab_dq_kernel(const uint16_t *__restrict__
   for (int i = 0; i < K; ++i) {
     const int jb = bi[i];
     if (jb < 0 || jb >= nb_max || pos < 0 || (int64_t)jb * kBS > pos) continue;
-    const u32x4 x = ld16(dq_part + (((row * K + i) * H) + h) * (int64_t)kD + part * 8);
+    const u32x4 x = ld16(dq_part + ((((row - row_lo) * K + i) * H) + h) * (int64_t)kD + part * 8);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       acc[2 * m] += bf16_lo(x[m]);
@@ -547,48 +562,63 @@ bool attn_bwd_supported(const Dims &p) {
          (hpg == 1 || hpg == 2 || hpg == 4 || hpg == 8 || hpg == 16);
 }
 
+// Fewest query rows per pass when the workspace is too small for one pass.
+constexpr int64_t kMinPassRows = 256;
+
 // With no query row the call only clears dk and dv, and needs no workspace.
-size_t attn_bwd_workspace_bytes(const Dims &p) {
-  return p.total_q > 0 ? ab_carve(p, nullptr).total_bytes : 0;
+size_t attn_bwd_workspace_bytes(const Dims &p, int64_t rows_per_pass) {
+  return p.total_q > 0
+             ? ab_carve(p, nullptr, std::max<int64_t>(1, std::min(rows_per_pass, p.total_q))).total_bytes
+             : 0;
 }
 
-hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
-                                const uint16_t *v, const int32_t *block_idx, const uint16_t *out,
-                                const float *lse, const uint16_t *dout, float *dq, float *dk,
-                                float *dv, void *workspace, hipStream_t s) {
-  AbWs w = ab_carve(p, workspace);
-  if (p.total_q == 0 || p.total_kv == 0) {  // nothing kept: all gradients are 0
-    zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
-    zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
-    zero_fill(dq, p.total_q * p.H * (int64_t)kD, s);
-    profile_mark(s);
-    return hipGetLastError();
+size_t attn_bwd_workspace_min_bytes(const Dims &p) { return attn_bwd_workspace_bytes(p, kMinPassRows); }
+
+int64_t attn_bwd_rows_per_pass(const Dims &p, size_t workspace_bytes) {
+  if (attn_bwd_workspace_bytes(p, p.total_q) <= workspace_bytes) return p.total_q;
+  if (attn_bwd_workspace_bytes(p, kMinPassRows) > workspace_bytes) return 0;
+  int64_t lo = std::min<int64_t>(kMinPassRows, p.total_q), hi = p.total_q;  // fits, does not
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (attn_bwd_workspace_bytes(p, mid) <= workspace_bytes) lo = mid; else hi = mid;
   }
-  const int64_t nrows = p.total_q * p.H;
-  hipLaunchKernelGGL(ab_dsum_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, out,
-                     dout, w.dsum, nrows);
-  profile_mark(s);
+  return lo;
+}
+
+// Rows [row_lo, row_hi) of the backward: bucket their kept slots, then the
+// item, reduce and dQ kernels.  With `accumulate`, dk and dv (cleared before
+// the first pass) get this pass's sums added; otherwise they are written.
+namespace {
+void bwd_pass(const Dims &p, const AbWs &w, int64_t row_lo, int64_t row_hi, bool accumulate,
+              const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *block_idx,
+              const float *lse, const uint16_t *dout, float *dq, float *dk, float *dv,
+              hipStream_t s) {
+  const int64_t e_lo = row_lo * p.top_k, e_hi = row_hi * p.top_k;
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
-  hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
+  const int64_t ntiles = std::max<int64_t>(1, (e_hi - e_lo + w.tile - 1) / w.tile);
+  hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, p.top_k, p.total_q,
-                     p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     e_lo, e_hi, p.nb_max, p.B, ntiles, w.nbk_g, w.tile);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
-                     w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, w.per_item);
+                     w.cnt, w.base, w.ibase, w.pbase, p.G, ntiles, w.nbk_g, w.per_item);
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.pbase, ncol);
-  hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
+  hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
-                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     p.total_q, e_lo, e_hi, p.nb_max, p.B, ntiles, w.nbk_g, w.tile);
   profile_mark(s);
-  hipLaunchKernelGGL(ab_zero_unkept_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.base, dk, dv,
-                     p.cu_kv, p.G, p.nb_max, w.nbk_g);
+  if (!accumulate)
+    hipLaunchKernelGGL(ab_zero_unkept_kernel, dim3((unsigned)ncol), dim3(256), 0, s, w.base, dk,
+                       dv, p.cu_kv, p.G, p.nb_max, w.nbk_g);
   profile_mark(s);
+  const int acc = accumulate ? 1 : 0;
   auto item = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)w.max_items), dim3(kItemThreads), 0, s, q, k, v, dout,
                        lse, w.dsum, w.base, w.ibase, w.pbase, w.lists, w.dq_part, dk, dv, w.part,
-                       p.cu_q, p.cu_kv, p.G, p.H, p.top_k, p.nb_max, ncol, w.per_item, p.scale);
+                       p.cu_q, p.cu_kv, p.G, p.H, p.top_k, p.nb_max, ncol, w.per_item, p.scale,
+                       e_lo, acc);
   };
   switch (p.H / p.G) {
     case 1: item(ab_item_kernel<1>); break;
@@ -599,14 +629,46 @@ hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t
   }
   profile_mark(s);
   hipLaunchKernelGGL(ab_reduce_kernel, dim3((unsigned)ncol, kReduceSplit), dim3(256), 0, s,
-                     w.ibase, w.pbase,
-                     w.part, dk, dv, p.cu_kv, p.G, p.nb_max, w.nbk_g, p.scale);
+                     w.ibase, w.pbase, w.part, dk, dv, p.cu_kv, p.G, p.nb_max, w.nbk_g, p.scale,
+                     acc);
   profile_mark(s);
-  hipLaunchKernelGGL(ab_dq_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s,
+  const int64_t nrh = (row_hi - row_lo) * p.H;
+  hipLaunchKernelGGL(ab_dq_kernel, dim3((unsigned)((nrh + 15) / 16)), dim3(256), 0, s,
                      w.dq_part, block_idx, dq, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k,
-                     p.total_q, p.nb_max, p.scale);
+                     p.total_q, p.nb_max, p.scale, row_lo, row_hi);
   profile_mark(s);
-  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
+                                const uint16_t *v, const int32_t *block_idx, const uint16_t *out,
+                                const float *lse, const uint16_t *dout, float *dq, float *dk,
+                                float *dv, void *workspace, int64_t rows_per_pass, hipStream_t s) {
+  if (p.total_q == 0 || p.total_kv == 0) {  // nothing kept: all gradients are 0
+    zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
+    zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
+    zero_fill(dq, p.total_q * p.H * (int64_t)kD, s);
+    profile_mark(s);
+    return hipGetLastError();
+  }
+  if (rows_per_pass <= 0) return hipErrorInvalidValue;
+  const AbWs w = ab_carve(p, workspace, rows_per_pass);
+  const int64_t nrows = p.total_q * p.H;
+  hipLaunchKernelGGL(ab_dsum_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, out,
+                     dout, w.dsum, nrows);
+  profile_mark(s);
+  const bool passes = rows_per_pass < p.total_q;
+  if (passes) {  // every pass adds its sums
+    zero_fill(dk, p.total_kv * p.G * (int64_t)kD, s);
+    zero_fill(dv, p.total_kv * p.G * (int64_t)kD, s);
+  }
+  for (int64_t r0 = 0; r0 < p.total_q; r0 += rows_per_pass) {
+    bwd_pass(p, w, r0, std::min(p.total_q, r0 + rows_per_pass), passes, q, k, v, block_idx, lse,
+             dout, dq, dk, dv, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace msa

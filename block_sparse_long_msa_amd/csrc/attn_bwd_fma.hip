@@ -218,14 +218,14 @@ hipError_t launch_fb(const Dims &p, const T *q, const T *k, const T *v, const in
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
   hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, p.top_k, p.total_q,
-                     p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     (int64_t)0, w.nent_g, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
                      w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, 1 << 16);
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.base, ncol);
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
-                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     p.total_q, (int64_t)0, w.nent_g, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   hipLaunchKernelGGL((fb_dq_kernel<T>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, q, k,
                      v, block_idx, lse, dout, w.dsum, dq, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G,

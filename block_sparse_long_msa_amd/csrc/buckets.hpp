@@ -1,7 +1,9 @@
 // Stable bucketing of kept-slot entries, shared by the backward passes.
 //
 // An entry e = row * K + slot of group g names kept slot `slot` of query row
-// `row`.  Its bucket is the (sequence, block) pair the slot keeps, numbered
+// `row`.  A call buckets the entries [e_lo, e_hi) of every group (a range of
+// whole rows: all of them, or one pass of a caller that runs its rows in
+// passes); tiles and lists cover that range only.  Its bucket is the (sequence, block) pair the slot keeps, numbered
 // b * nb_max + j within the group; padding slots and slots whose block holds
 // no causal key of the row belong to no bucket.  Every bucket's list ends up
 // in (row, slot) order, so sums taken in list order are deterministic:
@@ -61,16 +63,16 @@ __device__ __forceinline__ EntryInfo entry_info(const int32_t *__restrict__ bloc
 __global__ __launch_bounds__(256) void bk_count_kernel(
     const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, int32_t *__restrict__ cnt, int32_t *__restrict__ amax,  // may be null
-    int num_seqs, int K, int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g,
-    int64_t tile_len) {
+    int num_seqs, int K, int64_t total_q, int64_t e_lo, int64_t e_hi, int nb_max, int BS,
+    int64_t ntiles, int64_t nbk_g, int64_t tile_len) {
   extern __shared__ int32_t hist[];  // [nbk_g]
   const int g = blockIdx.y;
   const int64_t tile = blockIdx.x;
   for (int64_t x = threadIdx.x; x < nbk_g; x += 256) hist[x] = 0;
   __syncthreads();
-  const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * tile_len);
-  for (int64_t e = tile * tile_len + threadIdx.x; e < e1; e += 256) {
+  const int64_t nent = total_q * K;  // entries of a group
+  const int64_t e1 = min(e_hi, e_lo + (tile + 1) * tile_len);
+  for (int64_t e = e_lo + tile * tile_len + threadIdx.x; e < e1; e += 256) {
     const EntryInfo ei = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS);
     if (ei.bucket >= 0) atomicAdd(&hist[ei.bucket], 1);
     else if (amax != nullptr) amax[(int64_t)g * nent + e] = -1;
@@ -138,7 +140,8 @@ __global__ __launch_bounds__(64) void bk_scatter_kernel(
     const int32_t *__restrict__ block_idx, const int64_t *__restrict__ cu_q,
     const int64_t *__restrict__ cu_kv, const int32_t *__restrict__ cnt,
     const int32_t *__restrict__ base, int32_t *__restrict__ lists, int num_seqs, int K,
-    int64_t total_q, int nb_max, int BS, int64_t ntiles, int64_t nbk_g, int64_t tile_len) {
+    int64_t total_q, int64_t e_lo, int64_t e_hi, int nb_max, int BS, int64_t ntiles,
+    int64_t nbk_g, int64_t tile_len) {
   extern __shared__ int32_t run[];  // [nbk_g] next list position of each bucket
   const int g = blockIdx.y;
   const int64_t tile = blockIdx.x;
@@ -148,9 +151,8 @@ __global__ __launch_bounds__(64) void bk_scatter_kernel(
   const int32_t *gbase = base + (int64_t)g * nbk_g;
   for (int64_t x = lane; x < nbk_g; x += 64) run[x] = gbase[x] + toff[x];
   __syncthreads();
-  const int64_t nent = total_q * K;
-  const int64_t e1 = min(nent, (tile + 1) * tile_len);
-  for (int64_t c0 = tile * tile_len; c0 < e1; c0 += 64) {
+  const int64_t e1 = min(e_hi, e_lo + (tile + 1) * tile_len);
+  for (int64_t c0 = e_lo + tile * tile_len; c0 < e1; c0 += 64) {
     const int64_t e = c0 + lane;
     int bk = -1;
     if (e < e1) bk = entry_info(block_idx, cu_q, cu_kv, num_seqs, g, e, K, total_q, nb_max, BS).bucket;

@@ -413,7 +413,7 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
   hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.amax, p.num_seqs, p.top_k, p.total_q,
-                     p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     (int64_t)0, w.nent_g, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
@@ -424,7 +424,7 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   profile_mark(s);
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      block_idx, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, p.top_k,
-                     p.total_q, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
+                     p.total_q, (int64_t)0, w.nent_g, p.nb_max, p.B, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   hipLaunchKernelGGL((ib_item_kernel<T, DI, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s,
                      q_idx, k_idx, grad, w.base, w.ibase, w.pbase, w.lists, w.amax, dk_idx, w.part,

@@ -472,8 +472,8 @@ hipError_t launch_hier(const Dims &p, const HiGeom &h, const uint16_t *q_idx,
   profile_mark(s);
   const size_t hist_bytes = sizeof(int32_t) * (size_t)w.nbk_g;
   hipLaunchKernelGGL(bk_count_kernel, dim3((unsigned)w.ntiles, p.G), dim3(256), hist_bytes, s,
-                     w.sel, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, h.K1, p.total_q, h.nch,
-                     h.span, w.ntiles, w.nbk_g, w.tile);
+                     w.sel, p.cu_q, p.cu_kv, w.cnt, nullptr, p.num_seqs, h.K1, p.total_q,
+                     (int64_t)0, w.nent_g, h.nch, h.span, w.ntiles, w.nbk_g, w.tile);
   const int64_t ncol = (int64_t)p.G * w.nbk_g;
   hipLaunchKernelGGL(bk_colscan_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
                      w.cnt, w.base, w.ibase, w.pbase, p.G, w.ntiles, w.nbk_g, kHE);
@@ -481,7 +481,7 @@ hipError_t launch_hier(const Dims &p, const HiGeom &h, const uint16_t *q_idx,
   hipLaunchKernelGGL(bk_basescan_kernel, dim3(1), dim3(1024), 0, s, w.ibase, ncol);
   hipLaunchKernelGGL(bk_scatter_kernel, dim3((unsigned)w.ntiles, p.G), dim3(64), hist_bytes, s,
                      w.sel, p.cu_q, p.cu_kv, w.cnt, w.base, w.lists, p.num_seqs, h.K1,
-                     p.total_q, h.nch, h.span, w.ntiles, w.nbk_g, w.tile);
+                     p.total_q, (int64_t)0, w.nent_g, h.nch, h.span, w.ntiles, w.nbk_g, w.tile);
   profile_mark(s);
   hipLaunchKernelGGL((hi_fine_kernel<DI, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s,
                      q_idx, k_idx, w.base, w.ibase, w.lists, w.fine, p.cu_q, p.cu_kv, p.G, h.K1,

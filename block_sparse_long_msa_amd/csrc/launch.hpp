@@ -105,11 +105,18 @@ hipError_t launch_index_bwd(const Dims &p, bool bf16, const void *q_idx, const v
 
 // Backward of the Main Branch attention, bf16 (attn_bwd.hip).
 bool attn_bwd_supported(const Dims &p);  // head dim 128, block size 128, 64 % (H/G) == 0
-size_t attn_bwd_workspace_bytes(const Dims &p);
+// The query rows run in passes of rows_per_pass rows over one workspace of
+// attn_bwd_workspace_bytes(p, rows_per_pass) bytes (the per-slot dQ shares
+// and item partials of one pass); attn_bwd_rows_per_pass gives the most rows
+// a workspace holds (0 below attn_bwd_workspace_min_bytes).
+size_t attn_bwd_workspace_bytes(const Dims &p, int64_t rows_per_pass);
+size_t attn_bwd_workspace_min_bytes(const Dims &p);
+int64_t attn_bwd_rows_per_pass(const Dims &p, size_t workspace_bytes);
 hipError_t launch_attn_bwd_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                 const uint16_t *v, const int32_t *block_idx, const uint16_t *out,
                                 const float *lse, const uint16_t *dout, float *dq, float *dk,
-                                float *dv, void *workspace, hipStream_t s);
+                                float *dv, void *workspace, int64_t rows_per_pass,
+                                hipStream_t s);
 
 // The same backward with plain fp32 FMA for every other shape and dtype
 // (attn_bwd_fma.hip).

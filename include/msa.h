@@ -326,8 +326,21 @@ msa_status_t msa_indexer_bwd(const msa_problem_t *prob, const void *q_idx, const
  * plain fp32 multiply-adds.  Requirements beyond the common ones:
  * total_q * top_k * H < 2^31 and num_seqs * NBmax <= 16384 (else
  * MSA_ERR_BAD_SHAPE).  All tensors 16-byte aligned; `workspace` must hold
- * msa_sparse_attn_bwd_workspace_size() bytes, 256-byte aligned. */
+ * at least msa_sparse_attn_bwd_workspace_size_min() bytes, 256-byte
+ * aligned.  msa_sparse_attn_bwd_workspace_size() is the single-pass size;
+ * the matrix-core backward's workspace grows with total_q * top_k *
+ * num_q_heads * head_dim (each kept slot's share of dq), and given less it
+ * runs the query rows in consecutive passes of as many rows as fit (at
+ * least 256, or all of them).  dq is then identical bit for bit; dk and dv
+ * add the passes' sums in pass order (deterministic, rounded differently
+ * from a single pass). */
 msa_status_t msa_sparse_attn_bwd_workspace_size(const msa_problem_t *prob, size_t *bytes);
+msa_status_t msa_sparse_attn_bwd_workspace_size_min(const msa_problem_t *prob, size_t *bytes);
+/* Query rows per pass of msa_sparse_attn_bwd with a workspace of
+ * `workspace_bytes` (host *rows; total_q for one pass or the FMA backward);
+ * MSA_ERR_WORKSPACE_TOO_SMALL (and *rows = 0) below the minimum. */
+msa_status_t msa_sparse_attn_bwd_rows_per_pass(const msa_problem_t *prob, size_t workspace_bytes,
+                                               int64_t *rows);
 msa_status_t msa_sparse_attn_bwd(const msa_problem_t *prob, const void *q, const void *k,
                                  const void *v, const int32_t *block_idx, const void *out,
                                  const float *lse, const void *dout, float *dq, float *dk,

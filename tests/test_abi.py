@@ -186,6 +186,33 @@ def test_workspace_size_and_too_small():
     assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(pd), None) == 1
 
 
+def test_attn_bwd_workspace_passes():
+    """The matrix-core backward's workspace: the least holds a pass of 256
+    rows; the FMA backward (fp32 here) needs its full size."""
+    lib = msa.load_library()
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p = _prob(max_q_len=4096, total_q=4096, max_kv_len=4096, total_kv=4096, top_k=8)
+    assert lib.msa_sparse_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(full)) == 0
+    assert lib.msa_sparse_attn_bwd_workspace_size_min(ctypes.byref(p), ctypes.byref(least)) == 0
+    per_row = 8 * 8 * 128 * 2  # top_k * H * d bf16 dQ shares
+    assert full.value - least.value >= (4096 - 256) * per_row
+    rows = ctypes.c_int64(-1)
+    assert lib.msa_sparse_attn_bwd_rows_per_pass(ctypes.byref(p), least.value - 1,
+                                                 ctypes.byref(rows)) == 5
+    assert rows.value == 0
+    assert lib.msa_sparse_attn_bwd_rows_per_pass(ctypes.byref(p), least.value, ctypes.byref(rows)) == 0
+    assert rows.value == 256
+    assert lib.msa_sparse_attn_bwd_rows_per_pass(ctypes.byref(p), full.value, ctypes.byref(rows)) == 0
+    assert rows.value == 4096
+    assert _abwd(p, ws=FAKE, wsb=least.value - 1) == 5
+    f32 = _prob(max_q_len=4096, total_q=4096, max_kv_len=4096, total_kv=4096, top_k=8, dtype=1)
+    assert lib.msa_sparse_attn_bwd_workspace_size(ctypes.byref(f32), ctypes.byref(full)) == 0
+    assert lib.msa_sparse_attn_bwd_workspace_size_min(ctypes.byref(f32), ctypes.byref(least)) == 0
+    assert full.value == least.value
+    assert lib.msa_sparse_attn_bwd_rows_per_pass(ctypes.byref(f32), full.value, ctypes.byref(rows)) == 0
+    assert rows.value == 4096
+
+
 def test_kv_major_workspace_passes():
     """The KV-major schedule's workspace: a single pass needs the per-slot
     partials of every row; the least accepted workspace holds a pass of 256

@@ -110,6 +110,63 @@ def test_attn_backward_small(case):
     _log(f"{name}: errors dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
 
 
+def _bwd_with_workspace(prob, inp, bi, out, lse, dout, nbytes):
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    got = msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], bi, out, lse, dout, workspace=ws)
+    torch.cuda.synchronize()
+    return got
+
+
+def _check_passes(prob, inp, bi, out, lse, dout, ref, nbytes, tag):
+    """The backward over a workspace of nbytes (passes over the query rows):
+    dq equal to the single pass bit for bit, dk and dv within fp32 rounding
+    of it (the passes' sums are added in pass order), two runs identical."""
+    dq, dk, dv = _bwd_with_workspace(prob, inp, bi, out, lse, dout, nbytes)
+    dq2, dk2, dv2 = _bwd_with_workspace(prob, inp, bi, out, lse, dout, nbytes)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dq, ref[0]), f"{tag}: dq differs from the single pass"
+    for got, r, nm in ((dk, ref[1], "dk"), (dv, ref[2], "dv")):
+        scale = float(r.abs().max())
+        err = float((got - r).abs().max()) / max(scale, 1e-30)
+        assert err <= 1e-5, f"{tag}: {nm} differs from the single pass by {err:.2e} x max"
+    _log(f"  {tag}: workspace {nbytes} bytes: dq equal, dk / dv within rounding")
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("case", [BWD_CASES[0], BWD_CASES[1], BWD_CASES[3]],
+                         ids=[BWD_CASES[0][0], BWD_CASES[1][0], BWD_CASES[3][0]])
+def test_attn_backward_passes_small(case):
+    """A workspace below the single-pass size runs the rows in passes (256
+    rows at the least): results as above, and against the oracle."""
+    name, lq, lkv, H, G, k = case
+    d, di, B = 128, 64, 128
+    inp = W.random_case(71, lq, lkv, H, G, d, di, B, k, "bf16", device=DEV)
+    prob, bi, out, lse, dout, dq, dk, dv = _forward_and_backward(inp, H, G, d, di, B, k)
+    full = msa.sparse_attn_bwd_workspace_size(prob)
+    least = msa.sparse_attn_bwd_workspace_size(prob, minimum=True)
+    assert 0 < least < full
+    with pytest.raises(msa.MsaError) as e:
+        _bwd_with_workspace(prob, inp, bi, out, lse, dout, least - 1)
+    assert e.value.status == 5
+    got = _check_passes(prob, inp, bi, out, lse, dout, (dq, dk, dv), least, name)
+    rq, rk, rv = _oracle_all(inp, bi, dout, B, d)
+    for g_, r_, nm in zip(got, (rq, rk, rv), ("dq", "dk", "dv")):
+        _close(g_.cpu().numpy(), r_, nm)
+
+
+def test_attn_backward_passes_prefill_32k():
+    """prefill-32k with the least workspace (128 passes) and a quarter of the
+    single-pass one."""
+    w = W.WORKLOADS["prefill-32k"]
+    inp = W.make_inputs(w, device=DEV, seed=0)
+    H, G, d, di, B, k = w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim, w.block_size, w.top_k
+    prob, bi, out, lse, dout, dq, dk, dv = _forward_and_backward(inp, H, G, d, di, B, k)
+    full = msa.sparse_attn_bwd_workspace_size(prob)
+    least = msa.sparse_attn_bwd_workspace_size(prob, minimum=True)
+    for nbytes in (least, full // 4):
+        _check_passes(prob, inp, bi, out, lse, dout, (dq, dk, dv), nbytes, "prefill-32k")
+
+
 @pytest.mark.parametrize("seed", [3, 4])
 def test_attn_backward_arbitrary_lists(seed):
     """Kept-block lists that no selection produced: distinct blocks up to J,

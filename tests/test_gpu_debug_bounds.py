@@ -134,7 +134,8 @@ def test_debug_build_prefill_32k(debug_then_release):
 @pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[4]],
                          ids=[CASES[0][0], CASES[1][0], CASES[4][0]])
 def test_debug_build_kv_major_passes(case, debug_then_release):
-    """The KV-major forward in passes of 256 rows (the least workspace)."""
+    """The KV-major forward and the backward in passes of 256 rows (the
+    least workspaces)."""
     name, lq, lkv, H, G, d, di, B, k, dtype, _ = case
     _log(f"debug bounds, passes: {name}")
     inp = W.random_case(CASES.index(case), lq, lkv, H, G, d, di, B, k, dtype, device=DEV)
@@ -144,6 +145,11 @@ def test_debug_build_kv_major_passes(case, debug_then_release):
         bi = msa.topk_select(prob, msa.index_score(prob, inp["q_idx"], inp["k_idx"]))
         ws = torch.empty(msa.workspace_size_min(prob), dtype=torch.uint8, device=DEV)
         outs = list(msa.sparse_attn_fwd_mass(prob, inp["q"], inp["k"], inp["v"], bi, workspace=ws))
+        dout = W.random_out_grad(4, prob.total_q, H, d, dtype, device=DEV)
+        bws = torch.empty(msa.sparse_attn_bwd_workspace_size(prob, minimum=True),
+                          dtype=torch.uint8, device=DEV)
+        outs += list(msa.sparse_attn_bwd(prob, inp["q"], inp["k"], inp["v"], bi, outs[0], outs[1],
+                                         dout, workspace=bws))
         torch.cuda.synchronize()
         return outs
 
