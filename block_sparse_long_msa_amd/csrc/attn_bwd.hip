@@ -142,20 +142,20 @@ __global__ __launch_bounds__(256) void ab_dsum_kernel(const uint16_t *__restrict
 }
 
 
-// LDS rows are unpadded with their 16-byte chunks XOR-swizzled by the row, so
-// that both access patterns are free of bank conflicts: 16 consecutive rows
-// reading one chunk (MFMA operands of row-major data), and 4 consecutive rows
-// reading 4 consecutive chunks (the transposing reads below).
-// Element offset of element e of row r in rows of 128 bf16 (Q, dO, K, V):
-__device__ __forceinline__ int off256(int r, int e) {
-  const int f = ((r & 3) << 2) | ((r >> 2) & 3);
-  return r * 128 + ((((e >> 3) ^ f) << 3) | (e & 7));
-}
-// ... and in rows of 64 bf16 (P^T, dS^T), two rows per 256 bytes:
-__device__ __forceinline__ int off128(int r, int e) {
-  const int m = r >> 1, f = ((m & 1) << 2) | ((m >> 1) & 3);
-  return r * 64 + ((((e >> 3) ^ f) << 3) | (e & 7));
-}
+// LDS rows are padded so that every access pattern below is free of bank
+// conflicts while each address is a per-lane base plus a compile-time
+// offset (the loops' steps then cost no address arithmetic):
+//  - rows of 128 bf16 (Q, dO, K, V) take 288 bytes, 8 banks apart: 8
+//    consecutive rows reading 16 bytes of one column (MFMA operands, 8 lanes
+//    per LDS cycle) cover 32 banks, and 4 consecutive rows reading 32 bytes
+//    each (the transposing reads, 16 lanes per cycle) cover 32 banks;
+//  - rows of 64 bf16 (P^T, dS^T) take 144 bytes, 36 banks apart: 16
+//    consecutive rows writing 8 bytes, 8 rows reading 16 bytes and 4 rows
+//    reading 32 bytes each fall on distinct banks.
+constexpr int kRS = 144;  // elements per row of 128
+constexpr int kPS = 72;   // elements per row of 64
+__device__ __forceinline__ int off256(int r, int e) { return r * kRS + e; }
+__device__ __forceinline__ int off128(int r, int e) { return r * kPS + e; }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  In each 16-lane group, lane i
 // names a 4-element chunk; lane 4a + b receives element b of the chunks of
@@ -169,8 +169,8 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
   return __builtin_bit_cast(u32x2, r);
 }
 // MFMA 32x32x16 operand holding X[k0 + 8 hh .. k0 + 8 hh + 7][n0 + lane % 32]
-// (hh = lane / 32) of a row-major, swizzled X (OFF = off256 or off128): two
-// transposing reads of 4 rows each.
+// (hh = lane / 32) of a row-major X with padded rows (OFF = off256 or
+// off128): two transposing reads of 4 rows each.
 template <int (*OFF)(int, int)>
 __device__ __forceinline__ u32x4 ld_op_tr(const uint16_t *x, int k0, int n0, int lane) {
   const int i = lane & 15, grp = lane >> 4;
@@ -203,12 +203,12 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                float *__restrict__ part, const int64_t *__restrict__ cu_q,
                const int64_t *__restrict__ cu_kv, int G, int H, int K, int nb_max,
                int64_t nbuckets, int per_item, float scale, int64_t e_lo, int accumulate) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBS * kD];     // K [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kBS * kD];     // V [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t qs[kRows * kD];   // Q [row][d]
-  __shared__ __attribute__((aligned(16))) uint16_t os[kRows * kD];   // dO [row][d]
-  __shared__ __attribute__((aligned(16))) uint16_t pt[kBS * kRows];  // P^T [key][row]
-  __shared__ __attribute__((aligned(16))) uint16_t st_[kBS * kRows]; // dS^T [key][row]
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kBS * kRS];    // K [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kBS * kRS];    // V [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kRows * kRS];  // Q [row][d]
+  __shared__ __attribute__((aligned(16))) uint16_t os[kRows * kRS];  // dO [row][d]
+  __shared__ __attribute__((aligned(16))) uint16_t pt[kBS * kPS];    // P^T [key][row]
+  __shared__ __attribute__((aligned(16))) uint16_t st_[kBS * kPS];   // dS^T [key][row]
   __shared__ __attribute__((aligned(16))) float m_lse[kRows];  // log2-domain LSE (+inf: no row)
   __shared__ __attribute__((aligned(16))) float m_d[kRows];    // D
   __shared__ __attribute__((aligned(16))) int32_t m_pos[kRows];  // position (-1: no row)
@@ -318,21 +318,16 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   }
   for (int st = 0; st < nsteps; ++st) {
     __syncthreads();
-    // The swizzled LDS addresses are recomputed in every step from these
-    // copies of the lane index (the empty asm keeps the compiler from
-    // hoisting them all out of the loop, which spilled registers).
-    int li_s = li, lane_s = lane;
-    asm volatile("" : "+v"(li_s), "+v"(lane_s));
     // phase 1: S and dP for rows 32 hf .., keys 32 kg ..
     f32x16 sacc, pacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const u32x4 aq = ld16(&qs[off256(32 * hf + li_s, 16 * x + 8 * hh)]);
-      const u32x4 bk = ld16(&ks[off256(32 * kg + li_s, 16 * x + 8 * hh)]);
-      const u32x4 ao = ld16(&os[off256(32 * hf + li_s, 16 * x + 8 * hh)]);
-      const u32x4 bv = ld16(&vs[off256(32 * kg + li_s, 16 * x + 8 * hh)]);
+      const u32x4 aq = ld16(&qs[off256(32 * hf + li, 16 * x + 8 * hh)]);
+      const u32x4 bk = ld16(&ks[off256(32 * kg + li, 16 * x + 8 * hh)]);
+      const u32x4 ao = ld16(&os[off256(32 * hf + li, 16 * x + 8 * hh)]);
+      const u32x4 bv = ld16(&vs[off256(32 * kg + li, 16 * x + 8 * hh)]);
       sacc = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
       pacc = mfma32x32x16(as_bf16x8(ao), as_bf16x8(bv), pacc);
     }
@@ -363,8 +358,8 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                         pack_bf16x2(sacc[4 * q4 + 2], sacc[4 * q4 + 3])};
       const u32x2 dsv = {pack_bf16x2(pacc[4 * q4], pacc[4 * q4 + 1]),
                          pack_bf16x2(pacc[4 * q4 + 2], pacc[4 * q4 + 3])};
-      *reinterpret_cast<u32x2 *>(&pt[off128(32 * kg + li_s, row)]) = pv;
-      *reinterpret_cast<u32x2 *>(&st_[off128(32 * kg + li_s, row)]) = dsv;
+      *reinterpret_cast<u32x2 *>(&pt[off128(32 * kg + li, row)]) = pv;
+      *reinterpret_cast<u32x2 *>(&st_[off128(32 * kg + li, row)]) = dsv;
     }
     __syncthreads();
     if (st + 1 < nsteps) {
@@ -374,12 +369,12 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     // phase 2: dV^T += dO^T P, dK^T += Q^T dS (channels 64 hf .., keys 32 kg .., 64 rows)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const u32x4 bp = ld16(&pt[off128(32 * kg + li_s, 16 * x + 8 * hh)]);
-      const u32x4 bs = ld16(&st_[off128(32 * kg + li_s, 16 * x + 8 * hh)]);
+      const u32x4 bp = ld16(&pt[off128(32 * kg + li, 16 * x + 8 * hh)]);
+      const u32x4 bs = ld16(&st_[off128(32 * kg + li, 16 * x + 8 * hh)]);
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
-        const u32x4 ao = ld_op_tr<off256>(os, 16 * x, 64 * hf + 32 * y, lane_s);
-        const u32x4 aq = ld_op_tr<off256>(qs, 16 * x, 64 * hf + 32 * y, lane_s);
+        const u32x4 ao = ld_op_tr<off256>(os, 16 * x, 64 * hf + 32 * y, lane);
+        const u32x4 aq = ld_op_tr<off256>(qs, 16 * x, 64 * hf + 32 * y, lane);
         acc_v[y] = mfma32x32x16(as_bf16x8(ao), as_bf16x8(bp), acc_v[y]);
         acc_k[y] = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bs), acc_k[y]);
       }
@@ -390,10 +385,10 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     for (int r = 0; r < 16; ++r) qa0[r] = qa1[r] = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; x += 2) {
-      const u32x4 a0 = ld_op_tr<off256>(ks, 16 * x, 32 * kg, lane_s);
-      const u32x4 b0 = ld_op_tr<off128>(st_, 16 * x, 32 * hf, lane_s);
-      const u32x4 a1 = ld_op_tr<off256>(ks, 16 * x + 16, 32 * kg, lane_s);
-      const u32x4 b1 = ld_op_tr<off128>(st_, 16 * x + 16, 32 * hf, lane_s);
+      const u32x4 a0 = ld_op_tr<off256>(ks, 16 * x, 32 * kg, lane);
+      const u32x4 b0 = ld_op_tr<off128>(st_, 16 * x, 32 * hf, lane);
+      const u32x4 a1 = ld_op_tr<off256>(ks, 16 * x + 16, 32 * kg, lane);
+      const u32x4 b1 = ld_op_tr<off128>(st_, 16 * x + 16, 32 * hf, lane);
       qa0 = mfma32x32x16(as_bf16x8(a0), as_bf16x8(b0), qa0);
       qa1 = mfma32x32x16(as_bf16x8(a1), as_bf16x8(b1), qa1);
     }
