@@ -7,8 +7,11 @@
 //   dq_idx[r, g] = sum over slots i (in slot order) of c[g,r,i] * k_idx[a, g]
 //   dk_idx[s, g] = sum over (r, i) with a = s (in (r, i) order) of c[g,r,i] * q_idx[r, g]
 // The arg-max is an integer decided by floating point: each key's dot
-// product is summed in fp32 in channel order, every product rounded to fp32
-// before it is added (no fused multiply-add), and ties go to the lower key.
+// product is summed in fp32 (bf16 inputs on the matrix cores, whose bf16
+// products are exact in fp32; fp32 inputs in channel order, every product
+// rounded to fp32 before it is added), and ties go to the lower key.  Any
+// fp32 summation order is within the same rounding bound of the exact dot
+// product, so keys whose products differ by less than that bound may swap.
 //
 // Deterministic, without floating-point atomics:
 //   ib_zero      dk_idx <- 0 (keys no slot takes keep 0)
@@ -17,8 +20,10 @@
 //                into items of kIE entries; invalid slots get arg-max -1
 //   ib_item      per work item (at most kIE consecutive entries of one
 //                bucket's list, so popular blocks are shared out): for each
-//                entry in list order the arg-max over the causal keys (key
-//                operands in scalar registers), then each key row sums
+//                entry in list order the arg-max over the causal keys (bf16:
+//                S^T = K Q^T tiles on the matrix cores from the block's keys
+//                staged once in LDS; fp32: key operands in scalar
+//                registers), then each key row sums
 //                c * q_idx over the entries that chose it, in list order.  A
 //                bucket of one item writes dk_idx; the items of a larger
 //                bucket write partial sums.  The arg-max is stored for ib_dq.
@@ -26,6 +31,7 @@
 //                sums added in item order
 //   ib_dq        per (group, row): dq_idx from the stored arg-max keys
 #include <algorithm>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "buckets.hpp"
@@ -101,12 +107,13 @@ __global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ x, int
 
 // One work-group per work item: entries [it * kIE, min(n, (it + 1) * kIE))
 // of one bucket's list.  The item's rows and score gradients are staged in
-// LDS first; the index queries of each 64-entry
-// chunk are loaded into registers while the chunk before it is processed
-// (two LDS buffers); the keys are read with scalar loads.  Lane x handles entry x of a
-// chunk for the arg-max in every wave, the waves splitting the keys; for the
-// key-side sum, the TPR threads of key row s each own DI / TPR of its
-// channels.
+// LDS first; the index queries of each 64-entry chunk are loaded into
+// registers while the chunk before it is processed (two LDS buffers, bf16
+// kept as bf16).  For bf16 the block's index keys are staged in LDS once and
+// the arg-max runs on the matrix cores; for fp32 the keys are read with
+// scalar loads, lane x handling entry x of a chunk in every wave and the
+// waves splitting the keys.  For the key-side sum, the TPR threads of key row
+// s each own DI / TPR of its channels.
 template <typename T, int DI, int BS>
 __global__ __launch_bounds__(256) void ib_item_kernel(
     const T *__restrict__ q_idx, const T *__restrict__ k_idx, const float *__restrict__ grad,
@@ -115,14 +122,18 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
     int32_t *__restrict__ amax, float *__restrict__ dk_idx, float *__restrict__ part,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G, int K,
     int64_t total_q, int nb_max, int64_t nbuckets) {
+  constexpr bool BF = sizeof(T) == 2;    // bf16: arg-max on the matrix cores
+  using QE = std::conditional_t<BF, uint16_t, float>;  // element of the staged queries
   constexpr int TPR = 256 / BS;          // threads per key row (2 or 4)
   constexpr int CPT = DI / TPR;          // channels per thread in the key-side sum
-  constexpr int KS = DI + 4;             // padded LDS row of the chunk's queries (16-byte rows)
+  constexpr int KS = BF ? DI + 8 : DI + 4;  // padded LDS row of the chunk's queries (16-byte rows)
   constexpr int EPP = 16 / (int)sizeof(T);         // elements per 16-byte piece
   constexpr int PPR = DI / EPP;                    // pieces per query row
   constexpr int PPT = (64 * PPR + 255) / 256;      // pieces per thread and chunk
+  constexpr int KR = DI + 8;             // padded LDS row of the block's index keys (bf16)
   typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) float qs[2][64 * KS];  // index queries of a chunk's entries
+  __shared__ __attribute__((aligned(16))) QE qs[2][64 * KS];  // index queries of a chunk's entries
+  __shared__ __attribute__((aligned(16))) uint16_t kst[BF ? BS * KR : 8];  // the block's index keys
   __shared__ int32_t ent_row[kIE];       // the item's rows
   __shared__ float ent_c[kIE];           // and score gradients
   __shared__ int32_t as_[64];            // arg-max of the chunk's entries (-1 none)
@@ -171,18 +182,14 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
           q_idx + ((int64_t)ent_row[xe] * G + g) * DI + EPP * (pc % PPR));
     }
   };
-  auto stash = [&](float *dst) {
+  auto stash = [&](QE *dst) {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int pc = tid + 256 * u;
       if (PPT * 256 != 64 * PPR && pc >= 64 * PPR) break;
       const int xe = pc / PPR, c = EPP * (pc % PPR);
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[xe * KS + c + 2 * i] = bf16_lo(pf[u][i]);
-          dst[xe * KS + c + 2 * i + 1] = bf16_hi(pf[u][i]);
-        }
+      if constexpr (BF) {
+        *reinterpret_cast<piece_t *>(&dst[xe * KS + c]) = pf[u];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[xe * KS + c + i] = __uint_as_float(pf[u][i]);
@@ -193,85 +200,141 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
   float acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+  if constexpr (BF) {
+    // the block's index keys, rows past the sequence's keys read its last key
+    // (an entry's causal limit never reaches them)
+    constexpr int KP = BS * DI / 8;  // 16-byte pieces of the block
+    for (int pc = tid; pc < KP; pc += 256) {
+      const int r = pc / (DI / 8), c = 8 * (pc % (DI / 8));
+      const T *src = k_idx + ((kv0 + s0 + min(r, nkeys - 1)) * G + g) * (int64_t)DI + c;
+      *reinterpret_cast<piece_t *>(&kst[r * KR + c]) = *reinterpret_cast<const piece_t *>(src);
+    }
+  }
   prefetch(0);
   stash(qs[0]);
   for (int32_t c0 = 0, buf = 0; c0 < n; c0 += 64, buf ^= 1) {
     const int cn = min(64, n - c0);
     __syncthreads();  // qs[buf] is filled; the previous chunk's as_ / bv are consumed
     if (c0 + 64 < n) prefetch(c0 + 64);
-    // arg-max: lane x of every wave holds entry x's index query in registers;
-    // wave wv takes keys wv, wv + 4, ..., so all lanes of a wave need the same
-    // key element, which comes from global memory at a wave-uniform address
-    // into scalar registers.  Four keys' sums run at a time as independent
-    // chains; each sum still runs in channel order.  Keys past an entry's
-    // causal limit are computed and ignored.
-    {
-      const int x = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-      // causal keys of the block for entry x's row
-      const int lim = x < cn ? (int)min<int64_t>(nkeys, base_pos + (ent_row[c0 + x] - q0) - s0 + 1) : 0;
-      float best = neg_inf();
-      int bsel = -1;
-      float qr[DI];
+    if constexpr (BF) {
+      // arg-max on the matrix cores: S^T = K Q^T tiles of 32 keys x 32
+      // entries (bf16 products are exact in fp32, sums in fp32).  The
+      // (key tile, entry tile) pairs are dealt to the waves; a lane ends with
+      // the best of its 16 keys for entry 32 et + lane % 32 (keys in
+      // increasing order, the lower key on a tie), then the two halves of the
+      // wave combine.  Keys past an entry's causal limit are ignored.
+      constexpr int NKT = BS / 32, NU = NKT * 2, UPW = NU / 4;  // units per wave
+      const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int li = lane & 31, hh = lane >> 5;
 #pragma unroll
-      for (int c = 0; c < DI; c += 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c]);
-        qr[c] = v.x;
-        qr[c + 1] = v.y;
-        qr[c + 2] = v.z;
-        qr[c + 3] = v.w;
+      for (int uu = 0; uu < UPW; ++uu) {
+        const int unit = wv * UPW + uu, kt = unit % NKT, et = unit / NKT;
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int x = 0; x < DI / 16; ++x) {
+          const u32x4 ak = *reinterpret_cast<const u32x4 *>(&kst[(32 * kt + li) * KR + 16 * x + 8 * hh]);
+          const u32x4 bq = *reinterpret_cast<const u32x4 *>(&qs[buf][(32 * et + li) * KS + 16 * x + 8 * hh]);
+          sc = mfma32x32x16(as_bf16x8(ak), as_bf16x8(bq), sc);
+        }
+        const int xe = 32 * et + li;  // the lane's entry
+        const int lim = xe < cn ? (int)min<int64_t>(nkeys, base_pos + (ent_row[c0 + xe] - q0) - s0 + 1) : 0;
+        float best = neg_inf();
+        int bsel = -1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {  // key 32 kt + 8 (r / 4) + 4 hh + r % 4, increasing in r
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key < lim && (bsel < 0 || sc[r] > best)) {
+            best = sc[r];
+            bsel = key;
+          }
+        }
+        const float ob = shfl_xor_f(best, 32);
+        const int os = __shfl_xor(bsel, 32, 64);
+        if (os >= 0 && (bsel < 0 || ob > best || (ob == best && os < bsel))) {
+          best = ob;
+          bsel = os;
+        }
+        if (hh == 0) {
+          bv[64 * kt + xe] = best;
+          bs[64 * kt + xe] = bsel;
+        }
       }
-      for (int s = wv; s < nkeys; s += 16) {
-        float d[4] = {0.f, 0.f, 0.f, 0.f};
-        // the four key rows, read from global memory at wave-uniform
-        // addresses (scalar loads; rows past the block's end read its last row)
-        const T *kr[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          kr[u] = k_idx + ((kv0 + s0 + min(s + 4 * u, nkeys - 1)) * G + g) * (int64_t)DI;
-        // 16 channels of the four rows at a time (a scheduling barrier keeps
-        // the compiler from hoisting further scalar loads): a modest number
-        // of scalar registers in flight
+    } else {
+      // fp32 inputs: lane x of every wave holds entry x's index query in registers;
+      // wave wv takes keys wv, wv + 4, ..., so all lanes of a wave need the same
+      // key element, which comes from global memory at a wave-uniform address
+      // into scalar registers.  Four keys' sums run at a time as independent
+      // chains; each sum still runs in channel order.  Keys past an entry's
+      // causal limit are computed and ignored.
+      {
+        const int x = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        // causal keys of the block for entry x's row
+        const int lim = x < cn ? (int)min<int64_t>(nkeys, base_pos + (ent_row[c0 + x] - q0) - s0 + 1) : 0;
+        float best = neg_inf();
+        int bsel = -1;
+        float qr[DI];
 #pragma unroll
         for (int c = 0; c < DI; c += 4) {
-          if (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+          const float4 v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c]);
+          qr[c] = v.x;
+          qr[c + 1] = v.y;
+          qr[c + 2] = v.z;
+          qr[c + 3] = v.w;
+        }
+        for (int s = wv; s < nkeys; s += 16) {
+          float d[4] = {0.f, 0.f, 0.f, 0.f};
+          // the four key rows, read from global memory at wave-uniform
+          // addresses (scalar loads; rows past the block's end read its last row)
+          const T *kr[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float kv[4];
-            if constexpr (sizeof(T) == 2) {
-              const u32x2 w2 = *reinterpret_cast<const u32x2 *>(kr[u] + c);
-              kv[0] = bf16_lo(w2.x);
-              kv[1] = bf16_hi(w2.x);
-              kv[2] = bf16_lo(w2.y);
-              kv[3] = bf16_hi(w2.y);
-            } else {
-              const float4 w4 = *reinterpret_cast<const float4 *>(kr[u] + c);
-              kv[0] = w4.x;
-              kv[1] = w4.y;
-              kv[2] = w4.z;
-              kv[3] = w4.w;
+          for (int u = 0; u < 4; ++u)
+            kr[u] = k_idx + ((kv0 + s0 + min(s + 4 * u, nkeys - 1)) * G + g) * (int64_t)DI;
+          // 16 channels of the four rows at a time (a scheduling barrier keeps
+          // the compiler from hoisting further scalar loads): a modest number
+          // of scalar registers in flight
+#pragma unroll
+          for (int c = 0; c < DI; c += 4) {
+            if (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              float kv[4];
+              if constexpr (sizeof(T) == 2) {
+                const u32x2 w2 = *reinterpret_cast<const u32x2 *>(kr[u] + c);
+                kv[0] = bf16_lo(w2.x);
+                kv[1] = bf16_hi(w2.x);
+                kv[2] = bf16_lo(w2.y);
+                kv[3] = bf16_hi(w2.y);
+              } else {
+                const float4 w4 = *reinterpret_cast<const float4 *>(kr[u] + c);
+                kv[0] = w4.x;
+                kv[1] = w4.y;
+                kv[2] = w4.z;
+                kv[3] = w4.w;
+              }
+              d[u] = dot_step(d[u], qr[c], kv[0], T());
+              d[u] = dot_step(d[u], qr[c + 1], kv[1], T());
+              d[u] = dot_step(d[u], qr[c + 2], kv[2], T());
+              d[u] = dot_step(d[u], qr[c + 3], kv[3], T());
             }
-            d[u] = dot_step(d[u], qr[c], kv[0], T());
-            d[u] = dot_step(d[u], qr[c + 1], kv[1], T());
-            d[u] = dot_step(d[u], qr[c + 2], kv[2], T());
-            d[u] = dot_step(d[u], qr[c + 3], kv[3], T());
           }
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {  // keys in increasing order; past the limit ignored
-          if (s + 4 * u < lim && (d[u] > best || bsel < 0)) {
-            best = d[u];
-            bsel = s + 4 * u;
+          for (int u = 0; u < 4; ++u) {  // keys in increasing order; past the limit ignored
+            if (s + 4 * u < lim && (d[u] > best || bsel < 0)) {
+              best = d[u];
+              bsel = s + 4 * u;
+            }
           }
         }
+        bv[tid] = best;
+        bs[tid] = bsel;
       }
-      bv[tid] = best;
-      bs[tid] = bsel;
     }
     __syncthreads();
     if (tid < cn) {
       float best = bv[tid];
       int bsel = bs[tid];
-      for (int u = 1; u < 4; ++u) {  // the larger value; the lower key on a tie
+      constexpr int NCAND = BF ? BS / 32 : 4;  // candidates per entry: key tiles, or waves
+      for (int u = 1; u < NCAND; ++u) {  // the larger value; the lower key on a tie
         const float v = bv[64 * u + tid];
         const int s = bs[64 * u + tid];
         if (s >= 0 && (bsel < 0 || v > best || (v == best && s < bsel))) {
@@ -300,7 +363,13 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
           const float cx = ent_c[c0 + x];
 #pragma unroll
           for (int c = 0; c < CPT; c += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c_lo + c]);
+            float4 v;
+            if constexpr (BF) {
+              const u32x2 w2 = *reinterpret_cast<const u32x2 *>(&qs[buf][x * KS + c_lo + c]);
+              v = float4{bf16_lo(w2.x), bf16_hi(w2.x), bf16_lo(w2.y), bf16_hi(w2.y)};
+            } else {
+              v = *reinterpret_cast<const float4 *>(&qs[buf][x * KS + c_lo + c]);
+            }
             acc[c] = fmaf(cx, v.x, acc[c]);
             acc[c + 1] = fmaf(cx, v.y, acc[c + 1]);
             acc[c + 2] = fmaf(cx, v.z, acc[c + 2]);
