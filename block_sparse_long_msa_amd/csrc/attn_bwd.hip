@@ -298,6 +298,12 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   };
 
+  // The wave's K operands of phase 1 stay in registers for the whole item
+  // (one LDS read of them per item instead of one per step).
+  __syncthreads();
+  u32x4 kreg[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) kreg[x] = ld16(&ks[off256(32 * kg + li, 16 * x + 8 * hh)]);
   f32x16 acc_v[2], acc_k[2];  // dV^T, dK^T tiles [channel][key] of channels 64 hf ..
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -325,7 +331,7 @@ ab_item_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const u32x4 aq = ld16(&qs[off256(32 * hf + li, 16 * x + 8 * hh)]);
-      const u32x4 bk = ld16(&ks[off256(32 * kg + li, 16 * x + 8 * hh)]);
+      const u32x4 bk = kreg[x];
       const u32x4 ao = ld16(&os[off256(32 * hf + li, 16 * x + 8 * hh)]);
       const u32x4 bv = ld16(&vs[off256(32 * kg + li, 16 * x + 8 * hh)]);
       sacc = mfma32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
