@@ -608,8 +608,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        msg = ("bench.py measures one GPU only: the path shards by KV group with no exchange, "
-               "and no multi-GPU run is part of this build; use --gpus 1")
+        msg = ("bench.py measures one GPU only (the path would shard by KV group with no "
+               "exchange between GPUs); run it with --gpus 1")
         print(msg, file=sys.stderr, flush=True)
         sys.exit(2)
 
