@@ -618,7 +618,7 @@ const char *msa_status_string(msa_status_t status) {
     case MSA_ERR_MISALIGNED: return "misaligned pointer";
     case MSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MSA_ERR_DEVICE: return "device error";
-    case MSA_ERR_NOT_AVAILABLE: return "not available in this build";
+    case MSA_ERR_NOT_AVAILABLE: return "not available in this library variant";
   }
   return "unknown status";
 }

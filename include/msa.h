@@ -74,7 +74,7 @@ typedef enum {
   MSA_ERR_MISALIGNED = 4,
   MSA_ERR_WORKSPACE_TOO_SMALL = 5,
   MSA_ERR_DEVICE = 6,
-  MSA_ERR_NOT_AVAILABLE = 7 /* the entry point is not part of this build */
+  MSA_ERR_NOT_AVAILABLE = 7 /* the entry point is not part of this library variant */
 } msa_status_t;
 
 typedef enum { MSA_BF16 = 0, MSA_F32 = 1 } msa_dtype_t;

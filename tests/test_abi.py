@@ -55,7 +55,7 @@ def test_release_library_has_no_bounds_counters():
     assert lib.msa_debug_bounds_violations(ctypes.byref(n), ctypes.byref(c), 0) == 7
     assert n.value == 0 and c.value == 0
     assert lib.msa_debug_bounds_violations(ctypes.byref(n), None, 0) == 7
-    assert lib.msa_status_string(7).decode() == "not available in this build"
+    assert lib.msa_status_string(7).decode() == "not available in this library variant"
 
 
 @pytest.mark.parametrize("path", ["release", "debug"])
