@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/msa.h: argument validation
 // (pure host code, before any HIP call), launch-geometry selection and
-// dispatch to the kernels.  The library keeps no state between calls apart
-// from the per-thread error text.
+// dispatch to the kernels.  Between calls the library keeps per-thread state
+// only (the error text, the opt-in profiling events) and per-device lookups
+// (the compute-unit count, the no-allocation scratch address).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
