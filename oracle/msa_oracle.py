@@ -36,6 +36,10 @@ Readings where the page is silent (each also listed in the design notes):
 
 Everything runs in float64 on exact upcasts of the inputs.  Loops are over
 rows; the inner steps are numpy matrix products and reductions.
+
+Every function here is pinned to something other than itself by
+tests/test_oracle_pins.py (hand-worked fixtures, brute force, closed forms,
+library routines on special cases); none is parity-unpinned.
 """
 from __future__ import annotations
 
