@@ -873,6 +873,37 @@ def test_hierarchical_matches_loop_bruteforce(L, lq, B, S, C, k):
     assert np.array_equal(r["block_idx"], _hier_by_loops(q, kk, pos, B, k, S, C))
 
 
+def test_chunk_keys_and_coarse_scores_by_loops():
+    """The coarse key of a full chunk is the MEAN of its B*S index keys (a sum
+    would rank the same, so the values are pinned, not only the selection);
+    the trailing partial chunk has none; a row's coarse scores are its dot
+    products with the coarse keys of the chunks below its current chunk and
+    -inf elsewhere."""
+    rng = np.random.default_rng(12)
+    L, lq, G, di, B, S, C, k = 150, 60, 2, 3, 4, 4, 2, 4
+    q, kk = _rand(rng, lq, G, di), _rand(rng, L, G, di)
+    span = B * S
+    kbar = O.chunk_keys(kk, B, S)
+    assert kbar.shape == (L // span, G, di)  # 9 full chunks; keys 144..149 form none
+    for c in range(L // span):
+        for g in range(G):
+            for x in range(di):
+                want = math.fsum(float(kk[c * span + s, g, x]) for s in range(span)) / span
+                assert abs(kbar[c, g, x] - want) <= 1e-15 * max(1.0, abs(want))
+    pos = O.query_positions(lq, L)
+    r = O.hierarchical_select(q, kk, pos, B, k, S, C)
+    for g in range(G):
+        for t in range(lq):
+            cJ = (int(pos[t]) // B) // S
+            for c in range(L // span):
+                got = r["coarse"][g, t, c]
+                if c < cJ and int(pos[t]) // B > k - 1:
+                    want = math.fsum(float(q[t, g, x]) * kbar[c, g, x] for x in range(di))
+                    assert abs(got - want) <= 1e-12 * max(1.0, abs(want))
+                else:
+                    assert got == -np.inf
+
+
 def test_hierarchical_keeping_every_chunk_is_exact():
     """C at least the number of chunks: every candidate block is scored, so
     the hierarchical selection is select_blocks' exactly, and recall is 1."""
