@@ -208,6 +208,32 @@ def test_long_prefill(name):
     _log(f"  {st}")
 
 
+def test_large_varlen_batch():
+    """A packed batch of four planted sequences of the prefill-32k shape with
+    mixed lengths (a full prefill, a single-query row at 70K keys, a 9K-query
+    chunk at the end of 40K keys, and the longest prefill last): the KV-major
+    schedule's segments and entries span sequences.  Sampled rows of every
+    sequence against the oracle, and the Top-k of every row against the
+    selection rule on the library's own scores."""
+    w = W.Workload("varlen-batch", 32, 8, 128, 64, 128, 16, "bf16", True,
+                   len_q=(20000, 1, 9000, 30000), len_kv=(20000, 70000, 40000, 30000),
+                   num_seqs=4)
+    _log("varlen batch: generating")
+    inp = W.make_inputs(w, device=DEV, seed=11)
+    rng = np.random.default_rng(11)
+    rows = []
+    for lq in w.len_q:
+        r = set(range(min(64, lq))) | set(range(max(0, lq - 64), lq))
+        r |= set(rng.integers(0, lq, 64).tolist())
+        rows.append(np.array(sorted(r)))
+    _log(f"varlen batch: oracle on {sum(len(r) for r in rows)} rows, Top-k on every row")
+    st = C.run_and_check(inp, w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim,
+                         w.block_size, w.top_k, w.dtype, rows_per_seq=rows,
+                         topk_every_row=True, cheap_bound=True, progress=True)
+    assert st["rows"] == sum(len(r) for r in rows)
+    _log(f"  {st}")
+
+
 def test_decode_workload_every_sequence():
     w = W.WORKLOADS["decode-64x256k"]
     _log("decode workload: generating")
