@@ -9,15 +9,19 @@
 // (query, slot) entries that kept it, and a work item stages ONE block in LDS
 // and runs it against up to 256 gathered (query, head) rows with MFMA.  Each
 // item writes an unnormalised partial result (sum of exp2(z - m) v in bf16,
-// with the row's log2-domain max m and its sum l) into the slot of the
-// query's kept-block list; a merge kernel then combines the slots of every
-// (query, head) in slot order (deterministic, no atomics).
+// with the row's log2-domain max m and its sum l) for each of its entries,
+// at the entry's own position: an item's results are one contiguous run, so
+// the partial kernel's stores stream.  The scatter records that position per
+// (query, slot of its kept-block list), and a merge kernel gathers and
+// combines the slots of every (query, head) in slot order (deterministic, no
+// atomics).
 //
 // Kernels, in launch order:
 //   kv_clear        counts and cursors <- 0
 //   kv_count        entries per bucket (integer atomics: only counting)
 //   kv_scan_*       exclusive scan of the per-bucket work-item counts
-//   kv_scatter      entry lists (t << 6 | slot) per bucket, item-major
+//   kv_scatter      entry lists (t << 6 | slot) per bucket, item-major, and the
+//                   position of each (query, slot) entry
 //   kv_items        work-item descriptors (group, block, first entry, count, sequence)
 //   kv_partial      persistent: one work-group per CU walks a contiguous range
 //                   of work items (one bucket chunk of <= 256/hpg queries each),
@@ -50,9 +54,16 @@ constexpr int kScanTile = 4096;  // buckets per block of the item-count scan
 
 struct KvWs {
   int32_t *counts, *cursor, *item_off, *entries, *scan_blk;
+  int32_t *cbase;      // [nbk + 1] first entry of each bucket in entry order (scan of counts)
   int32_t *item_desc;  // per work item: g << 16 | j, 0, entry count, first KV row
-  float2 *part_ml;     // [rows][K][H]      (m, l) of each slot of the pass's rows
-  uint16_t *part_o;    // [rows][K][H][d]   unnormalised O of each slot, bf16
+  // Partials of the bucket entries in entry order (bucket after bucket, no
+  // padding): entry c holds the H/G heads of its (row, kept block) pair.
+  float2 *part_ml;     // [max_entries][H/G]     (m, l)
+  uint16_t *part_o;    // [max_entries][H/G][d]  unnormalised O, bf16
+  // Partials of the current block of every row of the pass (kv_diag).
+  float2 *diag_ml;     // [rows][H]
+  uint16_t *diag_o;    // [rows][H][d]
+  int32_t *pmap;       // [G][rows][K]  entry index of each (row, kept block below J)
   uint16_t *trash_o;   // [64][d]  write target of lanes without a row (never read)
   float2 *trash_ml;    // [64]
   int64_t nbk, nscan, max_entries, max_items;
@@ -81,12 +92,17 @@ KvWs carve(const Dims &p, void *base, int64_t rows) {
   w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
   w.cursor = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.nbk));
   w.item_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
-  w.scan_blk = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nscan + 1)));
+  w.cbase = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (w.nbk + 1)));
+  w.scan_blk = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * 2 * (w.nscan + 1)));
   // item-major with qch slots per item (a bucket's last item is padded)
   w.entries = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * w.max_items * qch));
   w.item_desc = reinterpret_cast<int32_t *>(take(4 * sizeof(int32_t) * w.max_items));
-  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * rows * p.top_k * p.H));
-  w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * rows * p.top_k * p.H * p.d));
+  const int64_t hpg = p.H / p.G;
+  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * w.max_entries * hpg));
+  w.part_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * w.max_entries * hpg * p.d));
+  w.diag_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * rows * p.H));
+  w.diag_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * rows * p.H * p.d));
+  w.pmap = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * p.G * rows * p.top_k));
   w.trash_o = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * 64 * p.d));
   w.trash_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * 64));
   w.total_bytes = off;
@@ -224,15 +240,22 @@ __global__ __launch_bounds__(256) void kv_count_kernel(const int32_t *__restrict
 
 // Entries are laid out item-major: the bucket's entry of rank `pos` goes to
 // item_off[bucket] * qch + pos, so work item t owns entries [t*qch, t*qch + qch).
-// An entry is stored as row << 6 | slot.
+// An entry is stored as row << 6 | slot.  Its partial result goes to entry
+// index cbase[bucket] + pos (the same order without the padding of the last
+// items), which pmap[g][row][slot] records for the merge.
 __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restrict__ block_idx,
                                                          int32_t *__restrict__ cursor,
                                                          const int32_t *__restrict__ item_off,
+                                                         const int32_t *__restrict__ cbase,
                                                          int32_t *__restrict__ entries,
+                                                         int32_t *__restrict__ pmap,
                                                          const int64_t *__restrict__ cu_q,
                                                          const int64_t *__restrict__ cu_kv,
                                                          EntGeom cg, int qch) {
-  extern __shared__ int32_t hist[];  // nb_max bins: local counts, then the tile's base per bin
+  // nb_max bins: local counts, then the tile's base per bin; then the
+  // tile's base per bin in entry-index order
+  extern __shared__ int32_t hist[];
+  int32_t *hist2 = hist + cg.nb_max;
   const int g = blockIdx.y;
   const int64_t per_g = cg.nrows * cg.K;
   const TileStart ts = tile_start(g, cg, cu_q, cu_kv);
@@ -254,14 +277,17 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
       } else if (r.bkt >= 0) {
         const int pos = atomicAdd(&cursor[r.bkt], 1);
         MSA_DCHECK(pos < (item_off[r.bkt + 1] - item_off[r.bkt]) * qch);
-        entries[(int64_t)item_off[r.bkt] * qch + pos] = (int32_t)((ep.row << 6) | ep.slot);
+        entries[item_off[r.bkt] * qch + pos] = (int32_t)((ep.row << 6) | ep.slot);
+        pmap[((int64_t)g * cg.nrows + (ep.row - cg.row_lo)) * cg.K + ep.slot] = cbase[r.bkt] + pos;
       }
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < cg.nb_max; i += 256) {
     const int c = hist[i];
-    hist[i] = c != 0 ? item_off[ts.bbase + i] * qch + atomicAdd(&cursor[ts.bbase + i], c) : 0;
+    const int pb = c != 0 ? atomicAdd(&cursor[ts.bbase + i], c) : 0;
+    hist[i] = c != 0 ? item_off[ts.bbase + i] * qch + pb : 0;
+    hist2[i] = c != 0 ? cbase[ts.bbase + i] + pb : 0;
     // the tile's run of the bucket ends inside the bucket's items
     MSA_DCHECK(c == 0 || hist[i] + c <= item_off[ts.bbase + i + 1] * qch);
   }
@@ -271,14 +297,18 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const int32_t *__restri
     if (rank[i] < 0) continue;
     const int local = threadIdx.x + 256 * i;
     const EntPos ep = entry_pos(ts, cg, local);
-    entries[hist[bi[local]] + rank[i]] = (int32_t)((ep.row << 6) | ep.slot);
+    const int j = bi[local];
+    entries[hist[j] + rank[i]] = (int32_t)((ep.row << 6) | ep.slot);
+    pmap[((int64_t)g * cg.nrows + (ep.row - cg.row_lo)) * cg.K + ep.slot] = hist2[j] + rank[i];
   }
 }
 
-// Exclusive scan of the per-bucket work-item counts ceil(count / qch) into
-// item_off (item_off[nbk] = total), in three passes: per block of kScanTile
-// buckets a local scan and the block's total; a single work-group scan of the
-// block totals; then each block adds its offset.
+// Exclusive scans of the per-bucket work-item counts ceil(count / qch) into
+// item_off and of the entry counts into cbase (item_off[nbk], cbase[nbk] =
+// totals), in three passes: per block of kScanTile buckets a local scan and
+// the block's totals; a single work-group scan of the block totals; then
+// each block adds its offsets.  scan_blk holds the item totals, then (at
+// nscan + 1) the entry totals.
 __device__ __forceinline__ int32_t block_excl_scan256(int32_t v, int32_t *sh, int32_t *total) {
   const int tid = threadIdx.x;
   sh[tid] = v;
@@ -297,62 +327,84 @@ __device__ __forceinline__ int32_t block_excl_scan256(int32_t v, int32_t *sh, in
 
 __global__ __launch_bounds__(256) void kv_scan_local_kernel(const int32_t *__restrict__ counts,
                                                             int32_t *__restrict__ item_off,
+                                                            int32_t *__restrict__ cbase,
                                                             int32_t *__restrict__ scan_blk,
-                                                            int64_t nbk, int qch) {
+                                                            int64_t nbk, int64_t nscan, int qch) {
   __shared__ int32_t sh[256];
   constexpr int PER = kScanTile / 256;
   const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * PER;
-  int32_t v[PER];
-  int32_t sum = 0;
+  int32_t v[PER], c[PER];
+  int32_t sum_v = 0, sum_c = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t bk = base + i;
-    const int32_t c = bk < nbk ? counts[bk] : 0;
-    v[i] = (c + qch - 1) / qch;
-    sum += v[i];
+    c[i] = bk < nbk ? counts[bk] : 0;
+    v[i] = (c[i] + qch - 1) / qch;
+    sum_v += v[i];
+    sum_c += c[i];
   }
-  int32_t total;
-  int32_t run = block_excl_scan256(sum, sh, &total);
+  int32_t tot_v, tot_c;
+  int32_t run_v = block_excl_scan256(sum_v, sh, &tot_v);
+  int32_t run_c = block_excl_scan256(sum_c, sh, &tot_c);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t bk = base + i;
-    if (bk < nbk) item_off[bk] = run;
-    run += v[i];
+    if (bk < nbk) {
+      item_off[bk] = run_v;
+      cbase[bk] = run_c;
+    }
+    run_v += v[i];
+    run_c += c[i];
   }
-  if (threadIdx.x == 0) scan_blk[blockIdx.x] = total;
+  if (threadIdx.x == 0) {
+    scan_blk[blockIdx.x] = tot_v;
+    scan_blk[nscan + 1 + blockIdx.x] = tot_c;
+  }
 }
 
 __global__ __launch_bounds__(256) void kv_scan_top_kernel(int32_t *__restrict__ scan_blk,
                                                           int64_t nscan) {
   __shared__ int32_t sh[256];
-  int32_t carry = 0;
-  for (int64_t b0 = 0; b0 < nscan; b0 += 256) {
-    const int64_t i = b0 + threadIdx.x;
-    const int32_t v = i < nscan ? scan_blk[i] : 0;
-    int32_t total;
-    const int32_t ex = block_excl_scan256(v, sh, &total);
-    if (i < nscan) scan_blk[i] = carry + ex;
-    carry += total;
+  for (int part = 0; part < 2; ++part) {  // item totals, then entry totals
+    int32_t *a = scan_blk + part * (nscan + 1);
+    int32_t carry = 0;
+    for (int64_t b0 = 0; b0 < nscan; b0 += 256) {
+      const int64_t i = b0 + threadIdx.x;
+      const int32_t v = i < nscan ? a[i] : 0;
+      int32_t total;
+      const int32_t ex = block_excl_scan256(v, sh, &total);
+      if (i < nscan) a[i] = carry + ex;
+      carry += total;
+    }
+    if (threadIdx.x == 0) a[nscan] = carry;
   }
-  if (threadIdx.x == 0) scan_blk[nscan] = carry;
 }
 
 __global__ __launch_bounds__(256) void kv_scan_add_kernel(int32_t *__restrict__ item_off,
+                                                          int32_t *__restrict__ cbase,
                                                           const int32_t *__restrict__ scan_blk,
                                                           int64_t nbk, int64_t nscan) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < nbk) item_off[i] += scan_blk[i / kScanTile];
-  if (i == 0) item_off[nbk] = scan_blk[nscan];
+  if (i < nbk) {
+    item_off[i] += scan_blk[i / kScanTile];
+    cbase[i] += scan_blk[nscan + 1 + i / kScanTile];
+  }
+  if (i == 0) {
+    item_off[nbk] = scan_blk[nscan];
+    cbase[nbk] = scan_blk[2 * nscan + 1];
+  }
 }
 
 // One wave per bucket (four buckets per work-group): the lanes write the
-// descriptors of the bucket's work items (g << 16 | block, 0, entry count,
-// packed row of the block's first key), so a work item starts after one
-// 16-byte load and no divisions, and fill the unused entry slots of the
-// bucket's last item with the pass's first row / slot 0 (a valid row to
-// load; the partial kernel never stores for those lanes).
+// descriptors of the bucket's work items (g << 16 | block, entry index of the
+// item's first entry, entry count, packed row of the block's first key), so a
+// work item starts after one 16-byte load and no divisions, and fill the
+// unused entry slots of the bucket's last item with the pass's first row /
+// slot 0 (a valid row to load; the partial kernel never stores for those
+// lanes).
 __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict__ counts,
                                                        const int32_t *__restrict__ item_off,
+                                                       const int32_t *__restrict__ cbase,
                                                        int32_t *__restrict__ entries,
                                                        int32_t *__restrict__ item_desc,
                                                        const int64_t *__restrict__ cu_kv,
@@ -364,6 +416,7 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
   const int cnt = counts[bkt];
   if (cnt == 0) return;
   const int first = item_off[bkt];
+  const uint32_t c0 = (uint32_t)cbase[bkt];
   const int64_t t = bkt / nb_max;  // scalar, once per bucket
   const uint32_t j = (uint32_t)(bkt - t * nb_max);
   const int64_t b = t / G;
@@ -371,7 +424,7 @@ __global__ __launch_bounds__(256) void kv_items_kernel(const int32_t *__restrict
   const uint32_t kvrow = (uint32_t)(cu_kv[b] + (int64_t)j * BS);
   const int nitems = (cnt + qch - 1) / qch;
   for (int i = lane; i < nitems; i += 64) {
-    u32x4 d = {g << 16 | j, 0u, (uint32_t)min(qch, cnt - i * qch), kvrow};
+    u32x4 d = {g << 16 | j, c0 + (uint32_t)(i * qch), (uint32_t)min(qch, cnt - i * qch), kvrow};
     st16(item_desc + 4 * (int64_t)(first + i), d);
   }
   for (int i = cnt + lane; i < nitems * qch; i += 64) entries[(int64_t)first * qch + i] = pad_entry;
@@ -680,6 +733,7 @@ __device__ __forceinline__ void tile_handover() {
 struct ItemDesc {
   int g, n;
   int64_t kvrow;  // packed K/V row of the block's first key
+  int64_t c0;     // entry index of the item's first entry (its partials start there)
 };
 
 // A zero the compiler cannot see through: addresses built from it are
@@ -718,7 +772,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
     float2 *__restrict__ trash_ml, int H, int G, int K, int nseg, int nb_max, int qch,
-    float scale_log2, int64_t row_lo, int64_t row_hi, int64_t total_kv) {
+    float scale_log2, int64_t row_lo, int64_t row_hi, int64_t total_kv, int64_t max_entries) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
   // two separate objects, so the compiler can tell the tile being loaded
   // from the tile being read
@@ -785,6 +839,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     d.g = (int)(__builtin_amdgcn_readfirstlane(w[0]) >> 16);
     d.n = (int)__builtin_amdgcn_readfirstlane(w[2]);
     d.kvrow = (int64_t)__builtin_amdgcn_readfirstlane(w[3]);
+    d.c0 = (int64_t)__builtin_amdgcn_readfirstlane(w[1]);
     return d;
   };
   auto q_of = [&](bf16x8 (&qb)[D / 16], const ItemDesc &d, int32_t e) {
@@ -809,7 +864,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     pin(en);
     const ItemDesc dc = decode(wc);
     const bool own = qi < dc.n;
-    const int64_t ps = (((int64_t)(ec >> 6) - row_lo) * K + (ec & 63)) * H + dc.g * hpg + hh;
+    // the partial goes to the entry's index in entry order, so an item's
+    // stores fill one contiguous range
+    MSA_DCHECK(!own || dc.c0 + qi < max_entries);
+    const int64_t ps = (dc.c0 + qi) * hpg + hh;
     uint16_t *od = own ? part_o + ps * D : trash_o + lane * D;
     float2 *md = own ? part_ml + ps : trash_ml + lane;
     const ItemDesc dn = decode(wn);
@@ -842,39 +900,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-// Last slot of a kept-block list (K <= 64 entries) that holds block J, or
-// -1.  When the list is 16-byte aligned (K a multiple of 4) all of its loads
-// are issued, 16 bytes at a time, before any is compared.
-__device__ __forceinline__ int last_slot_of(const int32_t *__restrict__ br, int K, int J) {
-  int slot = -1;
-  if ((K & 3) == 0) {
-    u32x4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (4 * i < K) v[i] = ld16(br + 4 * i);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * i < K && (int)v[i][e] == J) slot = 4 * i + e;
-  } else {
-#pragma unroll 8
-    for (int i = 0; i < K; ++i)
-      if (br[i] == J) slot = i;
-  }
-  return slot;
-}
-
 // The current block of each 128-query block of positions, with the causal
-// mask; its partial goes to the slot holding that block (if listed).
+// mask; every row's partial goes to its row of the diagonal buffer (the merge
+// uses it when the row's list holds that block).
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kv_diag_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const int32_t *__restrict__ block_idx,
-    uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
-    float2 *__restrict__ trash_ml, const int64_t *__restrict__ cu_q,
-    const int64_t *__restrict__ cu_kv, int num_seqs, int H, int G, int K, int nb_max,
-    int64_t total_q, float scale_log2, int64_t row_lo, int64_t row_hi) {
+    const uint16_t *__restrict__ v, uint16_t *__restrict__ diag_o, float2 *__restrict__ diag_ml,
+    uint16_t *__restrict__ trash_o, float2 *__restrict__ trash_ml,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
+    int G, int nb_max, float scale_log2, int64_t row_lo, int64_t row_hi) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
@@ -918,25 +953,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const RowT cur = row_of(rt);
     bf16x8 qa[D / 16];
     load_q<D>(qa, q + (cur.row * H + cur.h) * (int64_t)D, cur.valid);
-    const int slot = cur.valid ? last_slot_of(block_idx + ((int64_t)g * total_q + cur.row) * K, K, J)
-                               : -1;
-    const bool write = cur.valid && slot >= 0;
-    const int64_t ps = ((cur.row - row_lo) * K + (slot < 0 ? 0 : slot)) * H + cur.h;
+    const int64_t ps = (cur.row - row_lo) * H + cur.h;
     const int lane = threadIdx.x & 63;
     attend_rows<D, BS, true, false>(tile, qa, s0, cur.pos, scale_log2,
-                             write ? part_o + ps * D : trash_o + lane * D,
-                             write ? part_ml + ps : trash_ml + lane);
+                             cur.valid ? diag_o + ps * D : trash_o + lane * D,
+                             cur.valid ? diag_ml + ps : trash_ml + lane);
   }
 }
 
 // Per query row: merge the slots whose block is causal (0 <= j <= J).
-// Phase 1 spreads the (slot, head) pairs over the work-group: each loads its
-// slot's (m, l) (m = -inf for unused slots) into LDS; then one thread per
-// head forms M = max m, the weights w = exp2(m - M) (0 for unused slots) and
-// 1 / sum(w l).  Phase 2 streams the bf16 partials, each thread owning 8
-// consecutive output values of one head, with the slot loop unrolled so
-// several 16-byte loads are in flight.  Unused slots are never multiplied
-// (their memory may hold anything): the select below drops them.
+// Phase 0 finds, per (group, slot), where that slot's partial lies: the
+// entry position pmap recorded for a block below J, the row of the diagonal
+// buffer for the last slot listing J, or nothing (-1).  Phase 1 spreads the
+// (slot, head) pairs over the work-group: each loads its slot's (m, l) (m =
+// -inf for unused slots) into LDS; then one thread per head forms M = max m,
+// the weights w = exp2(m - M) (0 for unused slots) and 1 / sum(w l).  Phase 2
+// gathers the bf16 partials (the H/G heads of an entry are one contiguous
+// run), each thread owning 8 consecutive output values of one head, with the
+// slot loop unrolled so several 16-byte loads are in flight.  Unused slots
+// read the row's diagonal partial (valid memory) and are never multiplied:
+// the select below drops them.
 // With block_mass set, the kernel also writes the Main Branch distribution
 // over each group's kept blocks (the target of the indexer's KL objective,
 // "MiniMax Sparse Attention" page, Summary, paragraph 2): head h puts
@@ -944,59 +980,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 template <int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(
     const int32_t *__restrict__ block_idx, const uint16_t *__restrict__ part_o,
-    const float2 *__restrict__ part_ml, uint16_t *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ block_mass,
+    const float2 *__restrict__ part_ml, const uint16_t *__restrict__ diag_o,
+    const float2 *__restrict__ diag_ml, const int32_t *__restrict__ pmap,
+    uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ block_mass,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int K, int BS, int64_t total_q, int64_t row_lo) {
-  extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum
+    int G, int K, int BS, int64_t total_q, int64_t row_lo, int64_t nslots) {
+  extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum; [K][G] sources
   float *lsh = wsh + K * H;
   float *winv = lsh + K * H;
+  int32_t *src_sh = reinterpret_cast<int32_t *>(winv + H);
+  constexpr int kDiag = -2, kNone = -1;
+  const int64_t nrows = gridDim.x;    // rows of the pass
   const int64_t lrow = blockIdx.x;    // row of the pass (its partials)
   const int64_t row = row_lo + lrow;  // query row
   constexpr int OPH = D / 8;  // octets per head (of stored, d-permuted partial positions)
-  const uint16_t *base = part_o + lrow * (int64_t)K * H * D;
-  // The first four slots of this thread's first octet are requested before
-  // the weights are formed, so the partial stream is under way during that
-  // work.  Addresses are clamped into the row (a thread without an octet, or
-  // a row of fewer than four slots, reads data it then ignores).
-  const bool pre_use = (int)threadIdx.x < H * OPH && K >= 4;
-  u32x4 pre[4];
-  {
-    const uint16_t *src = base + (int64_t)min((int)threadIdx.x, H * OPH - 1) * 8;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      pre[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4 *>(src + (int64_t)min(u, K - 1) * H * D));
-  }
   const RowInfo ri = row_info(cu_q, cu_kv, num_seqs, row);
   const int64_t J = ri.p < 0 ? -1 : ri.p / BS;
   const int hpg = H / G;
-  // (slot, head) pairs in batches of four per thread: the block indices and
-  // the (m, l) of a batch are all requested before any is used; (m, l) of an
-  // unused slot is read too (it may hold anything) and then dropped.
+  for (int t = threadIdx.x; t < G * K; t += 256) {
+    const int g = t / K, sl = t - g * K;
+    const int32_t *br = block_idx + ((int64_t)g * total_q + row) * K;
+    const int j = br[sl];
+    int src = kNone;
+    if (j >= 0 && j < J) {
+      src = pmap[((int64_t)g * nrows + lrow) * K + sl];
+      MSA_DCHECK(src >= 0 && src < nslots);
+    } else if (J >= 0 && j == J) {  // the last slot listing J takes the diagonal partial
+      src = kDiag;
+      for (int s2 = sl + 1; s2 < K; ++s2)
+        if (br[s2] == J) src = kNone;
+    }
+    src_sh[sl * G + g] = src;
+  }
+  __syncthreads();
+  // (slot, head) pairs in batches of four per thread: the (m, l) of a batch
+  // are all requested before any is used
   for (int t0 = threadIdx.x; t0 < K * H; t0 += 4 * 256) {
-    int j[4], sl[4], h[4];
+    int src[4];
     float2 mlr[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = min(t0 + 256 * u, K * H - 1);
-      sl[u] = t / H;
-      h[u] = t - sl[u] * H;
-      j[u] = block_idx[((int64_t)(h[u] / hpg) * total_q + row) * K + sl[u]];
-      mlr[u] = part_ml[(lrow * K + sl[u]) * H + h[u]];
+      const int sl = t / H, h = t - sl * H;
+      src[u] = src_sh[sl * G + h / hpg];
+      const float2 *p = src[u] >= 0 ? part_ml + (int64_t)src[u] * hpg + (h - (h / hpg) * hpg)
+                                    : diag_ml + lrow * H + h;
+      mlr[u] = *p;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + 256 * u;
       if (t >= K * H) break;
-      bool use = j[u] >= 0 && j[u] < J;
-      if (J >= 0 && j[u] == J) {  // the last slot listing J is the one the diagonal kernel wrote
-        const int32_t *br = block_idx + ((int64_t)(h[u] / hpg) * total_q + row) * K;
-        use = true;
-        for (int s2 = sl[u] + 1; s2 < K; ++s2)
-          if (br[s2] == J) use = false;
-      }
-      const float2 ml = use ? mlr[u] : float2{neg_inf(), 0.f};
+      const float2 ml = src[u] != kNone ? mlr[u] : float2{neg_inf(), 0.f};
       wsh[t] = ml.y > 0.f ? ml.x : neg_inf();
       lsh[t] = ml.y;
     }
@@ -1026,29 +1061,24 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     }
   }
   for (int oc = threadIdx.x; oc < H * OPH; oc += 256) {
-    const int h = oc / OPH;
+    const int h = oc / OPH, g = h / hpg;
+    const int o8 = oc - h * OPH;
+    // element offset of the head's octet inside an entry, and the diagonal row's
+    const int64_t in_entry = (int64_t)(h - g * hpg) * D + 8 * o8;
+    const uint16_t *dsrc = diag_o + (lrow * H + h) * (int64_t)D + 8 * o8;
+    auto slot_src = [&](int sl) {
+      const int e = src_sh[sl * G + g];
+      return e >= 0 ? part_o + (int64_t)e * hpg * D + in_entry : dsrc;
+    };
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const uint16_t *src = base + (int64_t)oc * 8;
     int s = 0;
-    if (pre_use && oc == (int)threadIdx.x) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = wsh[u * H + h];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += w > 0.f ? w * bf16_lo(pre[u][i]) : 0.f;
-          acc[2 * i + 1] += w > 0.f ? w * bf16_hi(pre[u][i]) : 0.f;
-        }
-      }
-      s = 4;
-    }
     for (; s + 4 <= K; s += 4) {
       u32x4 x[4];
       float w[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         w[u] = wsh[(s + u) * H + h];
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (int64_t)(s + u) * H * D));
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(slot_src(s + u)));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1061,7 +1091,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     }
     for (; s < K; ++s) {
       const float w = wsh[s * H + h];
-      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (int64_t)s * H * D));
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(slot_src(s)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += w > 0.f ? w * bf16_lo(x[i]) : 0.f;
@@ -1070,7 +1100,6 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     }
     const float inv = winv[h];
     // the 8 stored positions 8*o8 .. +7 are two runs of 4 consecutive dv
-    const int o8 = oc - h * OPH;
     const int dv0 = partial_dv(8 * o8), dv1 = partial_dv(8 * o8 + 4);
     uint16_t *orow = out + row * (int64_t)H * D + (int64_t)h * D;
     u32x2 r0 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
@@ -1093,6 +1122,13 @@ int persistent_grid(int64_t max_items) {
     cus[dev].store(n, std::memory_order_relaxed);
   }
   return (int)std::max<int64_t>(1, std::min<int64_t>(n, max_items));
+}
+
+// LDS of the merge: (m, l) of every (slot, head), 1 / sum per head, and the
+// source of every (slot, group).
+size_t merge_lds_bytes(const Dims &p) {
+  return sizeof(float) * (2 * (size_t)p.top_k * p.H + p.H) +
+         sizeof(int32_t) * (size_t)p.top_k * p.G;
 }
 
 // One pass of the KV-major path over query rows [row_lo, row_hi): bucket
@@ -1121,36 +1157,35 @@ void launch_pass(const Dims &p, const KvWs &w, int64_t row_lo, int64_t row_hi,
                      p.cu_q, p.cu_kv, cg);
   profile_mark(s);
   hipLaunchKernelGGL(kv_scan_local_kernel, dim3((unsigned)w.nscan), dim3(256), 0, s, w.counts,
-                     w.item_off, w.scan_blk, w.nbk, qch);
+                     w.item_off, w.cbase, w.scan_blk, w.nbk, w.nscan, qch);
   hipLaunchKernelGGL(kv_scan_top_kernel, dim3(1), dim3(256), 0, s, w.scan_blk, w.nscan);
   hipLaunchKernelGGL(kv_scan_add_kernel, dim3((unsigned)((w.nbk + 255) / 256)), dim3(256), 0, s,
-                     w.item_off, w.scan_blk, w.nbk, w.nscan);
+                     w.item_off, w.cbase, w.scan_blk, w.nbk, w.nscan);
   profile_mark(s);
-  hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), hist_bytes, s, block_idx, w.cursor,
-                     w.item_off, w.entries, p.cu_q, p.cu_kv, cg, qch);
+  hipLaunchKernelGGL(kv_scatter_kernel, tiles, dim3(256), 2 * hist_bytes, s, block_idx, w.cursor,
+                     w.item_off, w.cbase, w.entries, w.pmap, p.cu_q, p.cu_kv, cg, qch);
   profile_mark(s);
   hipLaunchKernelGGL(kv_items_kernel, dim3((unsigned)((w.nbk + 3) / 4)), dim3(256), 0, s,
-                     w.counts, w.item_off, w.entries, w.item_desc, p.cu_kv, w.nbk, p.G,
+                     w.counts, w.item_off, w.cbase, w.entries, w.item_desc, p.cu_kv, w.nbk, p.G,
                      p.nb_max, p.B, qch, (int32_t)(row_lo << 6));
   profile_mark(s);
   hipLaunchKernelGGL((kv_partial_kernel<D, BS>), dim3((unsigned)persistent_grid(w.max_items)),
                      dim3(kThreads), 0, s, q, k, v, w.item_off, w.entries, w.item_desc, w.part_o,
                      w.part_ml, w.trash_o, w.trash_ml, p.H, p.G, p.top_k, p.num_seqs * p.G,
-                     p.nb_max, qch, sl2, row_lo, row_hi, p.total_kv);
+                     p.nb_max, qch, sl2, row_lo, row_hi, p.total_kv, w.max_entries);
   profile_mark(s);
   // the blocks holding a sequence's queries of the pass: at most
   // ceil(min(max_q_len, nrows) / B) + 1
   const int64_t span = std::min<int64_t>(p.max_q_len, nrows);
   const int ndiag = (int)std::min<int64_t>((span + p.B - 1) / p.B + 1, p.nb_max);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(ndiag, p.G, p.num_seqs), dim3(kThreads), 0, s,
-                     q, k, v, block_idx, w.part_o, w.part_ml, w.trash_o, w.trash_ml, p.cu_q,
-                     p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.nb_max, p.total_q, sl2, row_lo,
-                     row_hi);
+                     q, k, v, w.diag_o, w.diag_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv,
+                     p.num_seqs, p.H, p.G, p.nb_max, sl2, row_lo, row_hi);
   profile_mark(s);
-  const size_t merge_lds = sizeof(float) * (2 * (size_t)p.top_k * p.H + p.H);
-  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)nrows), dim3(256), merge_lds, s,
-                     block_idx, w.part_o, w.part_ml, out, lse, block_mass, p.cu_q, p.cu_kv,
-                     p.num_seqs, p.H, p.G, p.top_k, p.B, p.total_q, row_lo);
+  hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)nrows), dim3(256), merge_lds_bytes(p), s,
+                     block_idx, w.part_o, w.part_ml, w.diag_o, w.diag_ml, w.pmap, out, lse,
+                     block_mass, p.cu_q, p.cu_kv, p.num_seqs, p.H, p.G, p.top_k, p.B, p.total_q,
+                     row_lo, w.max_entries);
   profile_mark(s);
 }
 
@@ -1175,7 +1210,7 @@ MSA_DEBUG_COUNTER(attn_kvmajor)
 bool kvmajor_fits(const Dims &p) {
   if (p.total_q >= (int64_t)1 << 25) return false;  // entries pack the query row above 6 slot bits
   // the merge keeps (m, l) of every (slot, head) of a row in LDS
-  if ((2 * (int64_t)p.top_k * p.H + p.H) * (int64_t)sizeof(float) > 64 * 1024) return false;
+  if (merge_lds_bytes(p) > 64 * 1024) return false;
   const KvWs w = carve(p, nullptr, p.total_q);
   return w.max_items * (kRowsPerItem / (p.H / p.G)) < (int64_t)INT32_MAX;
 }

@@ -215,15 +215,19 @@ def test_attn_bwd_workspace_passes():
 
 def test_kv_major_workspace_passes():
     """The KV-major schedule's workspace: a single pass needs the per-slot
-    partials of every row; the least accepted workspace holds a pass of 256
-    rows; anything between is accepted (the rows then run in passes)."""
+    partials of every row (entry-ordered), its diagonal partials and the
+    position of every (row, slot) entry; the least accepted workspace holds a
+    pass of 256 rows; anything between is accepted (the rows then run in
+    passes)."""
     lib = msa.load_library()
     full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
     p = _prob(max_q_len=4096, total_q=4096, max_kv_len=4096, total_kv=4096, top_k=8)
     assert lib.msa_sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(full)) == 0
     assert lib.msa_sparse_attn_workspace_size_min(ctypes.byref(p), ctypes.byref(least)) == 0
-    per_row = 8 * 8 * (128 * 2 + 8)  # top_k * H * (bf16 partial row + (m, l))
-    assert full.value - least.value >= (4096 - 256) * per_row
+    # per row: top_k * H partial rows (bf16 O + (m, l)), H diagonal rows, and
+    # one int32 entry position per (group, slot)
+    per_row = 8 * 8 * (128 * 2 + 8) + 8 * (128 * 2 + 8) + 2 * 8 * 4
+    assert full.value - least.value >= (4096 - 256) * per_row - 16 * 8 * 264
     assert full.value - least.value < (4096 - 256) * per_row + (4096 - 256) * 8 * 8 * 4 + 4096 * 64
     # below the least size: rejected before any launch (FAKE pointers are never read)
     assert _attn(p, ws=FAKE, wsb=least.value - 1) == 5
