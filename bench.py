@@ -134,10 +134,11 @@ def copy_bandwidth(mib: int = 1024, reps: int = 10) -> float:
     return 2.0 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, launches: int = 1):
     """HBM bytes per launch from the committed counter summary for this kernel
-    and workload, or None if there is none or the kernel source has changed
-    since the counters were taken."""
+    and workload, or None if there is none, it was taken with another number
+    of launches per step (passes), or the kernel source has changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm-traffic.json")
     src = {"kv_partial": "attn_kvmajor.hip", "kv_merge": "attn_kvmajor.hip",
@@ -149,7 +150,7 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(f)
     with open(os.path.join(ROOT, "block_sparse_long_msa_amd", "csrc", src), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or rec.get("launches_per_step", 1) != launches:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -206,6 +207,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
         layers.append((lin["q"], lin["k"], lin["v"]))
         del lin
     train = keep_state and (args.indexer_kl or args.attn_bwd)
+    ab_passes, ab_kernels = 1, []
     if train:
         lse_buf = torch.empty((prob.total_q, prob.H), dtype=torch.float32, device=dev)
     if train and args.attn_bwd:
@@ -400,18 +402,21 @@ def run_workload(name, steps, warmup, args, keep_state=False):
                                "design_bytes": part_bytes,
                                "design_gbps": part_bytes / (kern_ms["kv_partial"] * 1e-3) / 1e9}
     dom = max(kern_ms, key=lambda kk: kern_ms[kk])
+    # the KV-major kernels launch once per pass: the roofline is per launch
+    # (the step's work and time divided by the launches), like the counters
+    nl = passes if dom in attn_kernels else (ab_passes if dom in ab_kernels[1:] else 1)
     if dom in ("index_score_mfma", "index_topk"):
         roof = mfma_roof(dom, f_idx, kern_ms[dom])
     elif dom == "ab_item":
-        roof = mfma_roof(dom, f_bwd, kern_ms[dom])
+        roof = mfma_roof(dom, f_bwd / nl, kern_ms[dom] / nl)
     elif dom == "kv_partial":
-        roof = mfma_roof(dom, part_flops, kern_ms[dom])
+        roof = mfma_roof(dom, part_flops / nl, kern_ms[dom] / nl)
     elif dom == "index_score_decode":
         roof = hbm_roof(dom, sum(x * w.num_kv_groups * w.idx_dim * 2 for x in lkv), kern_ms[dom])
     else:
-        roof = mfma_roof(dom, f_attn, kern_ms[dom])
-    # counter records are per single-pass launch
-    roof["traffic"] = measured_traffic(dom, w.name) if passes == 1 else None
+        roof = mfma_roof(dom, f_attn / nl, kern_ms[dom] / nl)
+    roof["launches_per_step"] = nl
+    roof["traffic"] = measured_traffic(dom, w.name, nl)
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -439,7 +444,7 @@ def run_workload(name, steps, warmup, args, keep_state=False):
                  if hier else {}),
               **({"attn_bwd": True} if use_bwd else {}),
               **({"attn_workspace_bytes": wbytes, "attn_passes": passes}
-                 if args.attn_workspace_gib > 0 else {}),
+                 if args.attn_workspace_gib > 0 or passes > 1 else {}),
               **({"attn_bwd_workspace_bytes": ab_bytes, "attn_bwd_passes": ab_passes}
                  if args.attn_workspace_gib > 0 and use_bwd else {})}
     res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": w.dtype,

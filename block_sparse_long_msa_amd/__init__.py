@@ -338,7 +338,9 @@ def index_topk_hier(prob: Problem, q_idx: torch.Tensor, k_idx: torch.Tensor, chu
 
 
 def workspace_size(prob: Problem) -> int:
-    """msa_sparse_attn_workspace_size: bytes for a single pass."""
+    """msa_sparse_attn_workspace_size: bytes with which the forward runs at
+    full speed (long KV-major prefills then run in passes of the library's
+    preferred size; more workspace is not used)."""
     n = ctypes.c_size_t(0)
     _check(load_library().msa_sparse_attn_workspace_size(prob.ref(), ctypes.byref(n)))
     return n.value
@@ -346,8 +348,8 @@ def workspace_size(prob: Problem) -> int:
 
 def workspace_size_min(prob: Problem) -> int:
     """msa_sparse_attn_workspace_size_min: the least workspace the forward
-    calls accept (the KV-major schedule runs in passes below the single-pass
-    size)."""
+    calls accept (the KV-major schedule runs in smaller passes below
+    workspace_size)."""
     n = ctypes.c_size_t(0)
     _check(load_library().msa_sparse_attn_workspace_size_min(prob.ref(), ctypes.byref(n)))
     return n.value

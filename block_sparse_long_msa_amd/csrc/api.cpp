@@ -5,6 +5,7 @@
 // (the compute-unit count, the no-allocation scratch address).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
@@ -133,8 +134,8 @@ size_t workspace_bytes(const msa_problem_t *p, const msa::Dims &d) {
     case AttnPath::kDecodeSplit:
       if (n_split <= 1) return 0;
       return (size_t)n_split * (size_t)d.total_q * (size_t)d.H * (size_t)(d.d + 1) * sizeof(float);
-    case AttnPath::kKvMajor:
-      return msa::kvmajor_workspace_bytes(d, d.total_q);
+    case AttnPath::kKvMajor:  // one pass of the preferred size
+      return msa::kvmajor_workspace_bytes(d, std::min(d.total_q, msa::kvmajor_preferred_rows(d)));
     case AttnPath::kQueryMajor:
       return 0;
   }
@@ -152,9 +153,11 @@ size_t workspace_min_bytes(const msa_problem_t *p, const msa::Dims &d) {
 
 // With fixed_scratch, `workspace` is ignored: once every argument has been
 // validated, the library's fixed device scratch (noalloc.hip) serves as the
-// workspace, and a problem whose single-pass workspace exceeds it is rejected.
-// Otherwise a workspace below the single-pass size (but at least the minimum)
-// runs the KV-major path in passes over the query rows.
+// workspace, and a problem whose full-speed workspace (workspace_bytes)
+// exceeds it is rejected.  Otherwise a workspace below that size (but at
+// least the minimum) runs the KV-major path in passes of as many query rows
+// as it holds; at or above it, in passes of the preferred size (one pass for
+// all but long prefills).
 msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, const void *v,
                       const int32_t *block_idx, void *out, float *lse, float *block_mass,
                       void *workspace, size_t workspace_bytes_given, void *stream,
@@ -197,7 +200,8 @@ msa_status_t attn_fwd(const msa_problem_t *prob, const void *q, const void *k, c
   int n_split = 1;
   const AttnPath path = attn_path(prob, d, &n_split);
   if (path == AttnPath::kKvMajor) {
-    const int64_t rows = msa::kvmajor_rows_per_pass(d, workspace_bytes_given);
+    const int64_t rows = std::min(msa::kvmajor_rows_per_pass(d, workspace_bytes_given),
+                                  msa::kvmajor_preferred_rows(d));
     if (rows <= 0)  // cannot happen once the minimum is checked
       return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace holds no pass of query rows");
     return launched(msa::launch_attn_kvmajor_bf16(d, static_cast<const uint16_t *>(q),
@@ -385,7 +389,8 @@ msa_status_t msa_sparse_attn_rows_per_pass(const msa_problem_t *prob, size_t wor
                 workspace_bytes_given);
   int n_split = 1;
   *rows = d.total_q > 0 && attn_path(prob, d, &n_split) == AttnPath::kKvMajor
-              ? msa::kvmajor_rows_per_pass(d, workspace_bytes_given)
+              ? std::min(msa::kvmajor_rows_per_pass(d, workspace_bytes_given),
+                         msa::kvmajor_preferred_rows(d))
               : d.total_q;
   return ok();
 }

@@ -42,6 +42,11 @@ namespace {
 constexpr int kRowsPerItem = 256;  // gathered (query, head) rows per work item
 // Fewest query rows per pass when the workspace is too small for one pass.
 constexpr int64_t kMinPassRows = 256;
+// Long prefills run in passes whose gathered Q rows of one group take about
+// this many bytes: such a pass's rows stay in the memory-side cache between
+// the many reads of each row (one per kept block), which outweighs the
+// passes' extra launches (measured at 128K; shorter problems run in one).
+constexpr int64_t kPassQBytes = 32ll << 20;
 constexpr int kWaves = 8;          // one 32-row tile per wave
 constexpr int kThreads = 64 * kWaves;
 
@@ -1220,6 +1225,11 @@ size_t kvmajor_workspace_bytes(const Dims &p, int64_t rows_per_pass) {
 }
 
 size_t kvmajor_workspace_min_bytes(const Dims &p) { return kvmajor_workspace_bytes(p, kMinPassRows); }
+
+int64_t kvmajor_preferred_rows(const Dims &p) {
+  const int64_t row_bytes = (int64_t)(p.H / p.G) * p.d * 2;
+  return std::max<int64_t>(kMinPassRows, kPassQBytes / row_bytes);
+}
 
 int64_t kvmajor_rows_per_pass(const Dims &p, size_t workspace_bytes) {
   if (kvmajor_workspace_bytes(p, p.total_q) <= workspace_bytes) return p.total_q;

@@ -91,6 +91,9 @@ bool kvmajor_fits(const Dims &p);
 size_t kvmajor_workspace_bytes(const Dims &p, int64_t rows_per_pass);
 size_t kvmajor_workspace_min_bytes(const Dims &p);
 int64_t kvmajor_rows_per_pass(const Dims &p, size_t workspace_bytes);
+// The most rows per pass the path uses (a pass of them stays cached); a
+// larger workspace changes nothing.
+int64_t kvmajor_preferred_rows(const Dims &p);
 hipError_t launch_attn_kvmajor_bf16(const Dims &p, const uint16_t *q, const uint16_t *k,
                                     const uint16_t *v, const int32_t *block_idx, uint16_t *out,
                                     float *lse, float *block_mass, void *workspace,

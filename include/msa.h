@@ -183,25 +183,32 @@ msa_status_t msa_index_topk_hier(const msa_problem_t *prob, const void *q_idx, c
                                  int32_t *kept_chunks, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
-/* Bytes of device workspace msa_sparse_attn_fwd needs for this problem and
- * schedule to run in one pass (0 is possible).  Writes the size to *bytes
- * (host). */
+/* Bytes of device workspace with which msa_sparse_attn_fwd runs this
+ * problem and schedule at full speed (0 is possible); a larger workspace is
+ * not used.  Writes the size to *bytes (host).  On the KV-major schedule
+ * (multi-query bf16 rows) long prefills run in consecutive passes over the
+ * query rows: at most as many rows per pass as make the gathered query rows
+ * of one group about 32 MiB (16,384 rows at H/G = 8 and d = 128), so that a
+ * pass's rows stay cached between their many reads; this size holds one such
+ * pass (all rows of shorter problems: one pass).  The outputs are identical
+ * bit for bit whatever the passes. */
 msa_status_t msa_sparse_attn_workspace_size(const msa_problem_t *prob, size_t *bytes);
 
 /* The least workspace msa_sparse_attn_fwd and msa_sparse_attn_fwd_mass
  * accept for this problem and schedule (host *bytes).  It equals
  * msa_sparse_attn_workspace_size() except on the KV-major schedule, whose
- * workspace grows with total_q * top_k * num_q_heads * head_dim (the
- * per-slot partial results): given less than the single-pass size, that
- * schedule runs the query rows in consecutive passes of as many rows as the
- * workspace holds (at least 256 rows, or all of them), reusing it for every
- * pass.  Each pass re-reads the K/V blocks its rows keep; the outputs are
- * identical bit for bit to a single pass. */
+ * workspace grows with the rows of a pass times top_k * num_q_heads *
+ * head_dim (the per-slot partial results): given less than
+ * msa_sparse_attn_workspace_size(), that schedule runs the query rows in
+ * consecutive passes of as many rows as the workspace holds (at least 256
+ * rows, or all of them), reusing it for every pass.  Each pass re-reads the
+ * K/V blocks its rows keep; the outputs are identical bit for bit. */
 msa_status_t msa_sparse_attn_workspace_size_min(const msa_problem_t *prob, size_t *bytes);
 
 /* Query rows per pass that msa_sparse_attn_fwd (or _mass) runs with a
- * workspace of `workspace_bytes` (host *rows): total_q when one pass fits or
- * the schedule is not KV-major.  MSA_ERR_WORKSPACE_TOO_SMALL (and *rows = 0)
+ * workspace of `workspace_bytes` (host *rows): the rows it holds, at most the
+ * preferred pass size of msa_sparse_attn_workspace_size(); total_q when the
+ * schedule is not KV-major.  MSA_ERR_WORKSPACE_TOO_SMALL (and *rows = 0)
  * below msa_sparse_attn_workspace_size_min(). */
 msa_status_t msa_sparse_attn_rows_per_pass(const msa_problem_t *prob, size_t workspace_bytes,
                                            int64_t *rows);
@@ -216,7 +223,8 @@ msa_status_t msa_sparse_attn_rows_per_pass(const msa_problem_t *prob, size_t wor
  * input dtype (bf16 rounding to nearest even).  `workspace` must hold at
  * least msa_sparse_attn_workspace_size_min() bytes (it may be NULL if that
  * is 0; workspace_bytes is its size, and a workspace below
- * msa_sparse_attn_workspace_size() runs the KV-major schedule in passes);
+ * msa_sparse_attn_workspace_size() runs the KV-major schedule in smaller
+ * passes);
  * its contents need no initialisation and are clobbered. */
 msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const void *k,
                                  const void *v, const int32_t *block_idx, void *out, float *lse,
@@ -227,7 +235,8 @@ msa_status_t msa_sparse_attn_fwd(const msa_problem_t *prob, const void *q, const
  * allocation).  Same arguments, same kernels and same results as
  * msa_sparse_attn_fwd, without a workspace: the call uses a fixed scratch
  * array of 64 MiB that the library holds on every GPU it runs on until the
- * process ends.  It allocates and frees nothing, and runs in one pass.  A
+ * process ends.  It allocates and frees nothing, and runs as
+ * msa_sparse_attn_fwd does with msa_sparse_attn_workspace_size() bytes.  A
  * problem whose msa_sparse_attn_workspace_size() exceeds 64 MiB is rejected
  * with MSA_ERR_WORKSPACE_TOO_SMALL before anything is launched (use
  * msa_sparse_attn_fwd for those).  All calls on one GPU share the scratch:

@@ -251,6 +251,36 @@ def test_kv_major_workspace_passes():
     assert full.value == least.value
 
 
+def test_kv_major_preferred_pass_size():
+    """Long prefills run in passes whose gathered query rows of one group take
+    32 MiB: 16,384 rows at H/G = 8 and d = 128, 32,768 at H/G = 4.  The
+    full-speed workspace holds one such pass, and no workspace makes a pass
+    longer; shorter problems run in one pass."""
+    lib = msa.load_library()
+    n, rows = ctypes.c_size_t(0), ctypes.c_int64(0)
+    long_ = _prob(num_q_heads=64, num_kv_groups=8, max_q_len=131072, total_q=131072,
+                  max_kv_len=131072, total_kv=131072, top_k=32)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(long_), ctypes.byref(n)) == 0
+    for ws in (n.value, 1 << 62):
+        assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(long_), ws, ctypes.byref(rows)) == 0
+        assert rows.value == 16384
+    # per row: 32 slots x 64 heads and 64 diagonal heads of (bf16 O + (m, l)), 8 x 32 entry indices
+    per_row = 32 * 64 * (128 * 2 + 8) + 64 * (128 * 2 + 8) + 8 * 32 * 4
+    assert 16384 * per_row <= n.value < 16384 * per_row + (64 << 20)
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(long_), n.value - 1, ctypes.byref(rows)) == 0
+    assert rows.value < 16384
+    p32 = _prob(num_q_heads=32, num_kv_groups=8, max_q_len=32768, total_q=32768,
+                max_kv_len=32768, total_kv=32768, top_k=16)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(p32), ctypes.byref(n)) == 0
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(p32), 1 << 62, ctypes.byref(rows)) == 0
+    assert rows.value == 32768
+    chunk = _prob(num_q_heads=64, num_kv_groups=8, max_q_len=8192, total_q=8192,
+                  max_kv_len=1 << 20, total_kv=1 << 20, top_k=64)
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(chunk), ctypes.byref(n)) == 0
+    assert lib.msa_sparse_attn_rows_per_pass(ctypes.byref(chunk), n.value, ctypes.byref(rows)) == 0
+    assert rows.value == 8192
+
+
 def test_empty_batch_is_a_no_op():
     """total_q = 0 returns success without touching the device."""
     p = _prob(max_q_len=0, total_q=0)

@@ -362,9 +362,10 @@ def test_cross_layer_reuse():
 
 
 def _passes_equal_single_pass(inp, H, G, d, di, B, k, sizes):
-    """The KV-major forward with a workspace below its single-pass size runs
-    the query rows in passes; every output equals the single pass's bit for
-    bit (out, LSE and the block mass)."""
+    """The KV-major forward with a workspace below its default size runs the
+    query rows in (more) passes; every output equals that of the default
+    workspace bit for bit (out, LSE and the block mass).  The default is one
+    pass except on long prefills (prefill-128k: passes of 16,384 rows)."""
     prob = msa.Problem(inp["cu_q"], inp["cu_kv"], inp["len_q"], inp["len_kv"], H, G, d, di, B, k,
                        "bf16")
     bi = msa.topk_select(prob, msa.index_score(prob, inp["q_idx"], inp["k_idx"]))
@@ -386,7 +387,7 @@ def _passes_equal_single_pass(inp, H, G, d, di, B, k, sizes):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
         assert torch.equal(o2.view(torch.int16), ref[0].view(torch.int16))
         assert torch.equal(l2.view(torch.int32), ref[1].view(torch.int32))
-        _log(f"  workspace {nbytes} of {full} bytes: equal to the single pass")
+        _log(f"  workspace {nbytes} of {full} bytes: equal to the default workspace's outputs")
         del ws
 
 
@@ -403,8 +404,8 @@ def test_kv_major_passes_small(case):
 @pytest.mark.parametrize("name", ["chunked-prefill-1m", "prefill-128k"])
 def test_kv_major_passes_full_size(name):
     """The long workloads with a bounded workspace: the 1M chunk in passes of
-    the fewest rows (256) and of a quarter of its rows; prefill-128k within
-    8 GiB instead of its ~69 GB single-pass workspace."""
+    the fewest rows (256) and of a quarter of its rows (its default is one
+    pass); prefill-128k within 8 GiB (9 passes against the default 8)."""
     w = W.WORKLOADS[name]
     _log(f"passes {name}: generating")
     inp = W.make_inputs(w, device=DEV, seed=0)
