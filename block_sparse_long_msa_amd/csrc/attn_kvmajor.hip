@@ -776,8 +776,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t *__restrict__ v, const int32_t *__restrict__ item_off,
     const int32_t *__restrict__ entries, const int32_t *__restrict__ item_desc,
     uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, uint16_t *__restrict__ trash_o,
-    float2 *__restrict__ trash_ml, int H, int G, int K, int nseg, int nb_max, int qch,
-    float scale_log2, int64_t row_lo, int64_t row_hi, int64_t total_kv, int64_t max_entries) {
+    float2 *__restrict__ trash_ml, int H, int G, [[maybe_unused]] int K, int nseg, int nb_max,
+    int qch, float scale_log2, [[maybe_unused]] int64_t row_lo, [[maybe_unused]] int64_t row_hi,
+    [[maybe_unused]] int64_t total_kv, [[maybe_unused]] int64_t max_entries) {
   static_assert(kRowsPerItem == 32 * kWaves, "one 32-row tile per wave");
   // two separate objects, so the compiler can tell the tile being loaded
   // from the tile being read
@@ -913,8 +914,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ diag_o, float2 *__restrict__ diag_ml,
     uint16_t *__restrict__ trash_o, float2 *__restrict__ trash_ml,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int nb_max, float scale_log2, int64_t row_lo, int64_t row_hi) {
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int H, int G,
+    int nb_max, float scale_log2, int64_t row_lo, int64_t row_hi) {
   __shared__ __attribute__((aligned(16))) KvTile<D, BS> tile;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
@@ -989,7 +990,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(
     const float2 *__restrict__ diag_ml, const int32_t *__restrict__ pmap,
     uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ block_mass,
     const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int H,
-    int G, int K, int BS, int64_t total_q, int64_t row_lo, int64_t nslots) {
+    int G, int K, int BS, int64_t total_q, int64_t row_lo, [[maybe_unused]] int64_t nslots) {
   extern __shared__ float wsh[];  // [K][H] m, then weights; [K][H] l; [H] 1/sum; [K][G] sources
   float *lsh = wsh + K * H;
   float *winv = lsh + K * H;
@@ -1185,7 +1186,7 @@ void launch_pass(const Dims &p, const KvWs &w, int64_t row_lo, int64_t row_hi,
   const int ndiag = (int)std::min<int64_t>((span + p.B - 1) / p.B + 1, p.nb_max);
   hipLaunchKernelGGL((kv_diag_kernel<D, BS>), dim3(ndiag, p.G, p.num_seqs), dim3(kThreads), 0, s,
                      q, k, v, w.diag_o, w.diag_ml, w.trash_o, w.trash_ml, p.cu_q, p.cu_kv,
-                     p.num_seqs, p.H, p.G, p.nb_max, sl2, row_lo, row_hi);
+                     p.H, p.G, p.nb_max, sl2, row_lo, row_hi);
   profile_mark(s);
   hipLaunchKernelGGL((kv_merge_kernel<D>), dim3((unsigned)nrows), dim3(256), merge_lds_bytes(p), s,
                      block_idx, w.part_o, w.part_ml, w.diag_o, w.diag_ml, w.pmap, out, lse,
