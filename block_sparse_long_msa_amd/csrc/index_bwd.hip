@@ -88,14 +88,9 @@ IbWs ib_carve(const Dims &p, void *base) {
 __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 
-// One step of an arg-max dot product: acc + q * k with the product rounded
-// to fp32 before the add.  For bf16 inputs the product is exact in fp32, so
-// a fused multiply-add gives the same value; fp32 inputs need the two
-// roundings, so contraction is switched off there.
-__device__ __forceinline__ float dot_step(float acc, float q, float k, uint16_t) {
-  return fmaf(q, k, acc);
-}
-__device__ __forceinline__ float dot_step(float acc, float q, float k, float) {
+// One step of the fp32 arg-max dot product: acc + q * k with the product
+// rounded to fp32 before the add (contraction switched off).
+__device__ __forceinline__ float dot_step(float acc, float q, float k) {
 #pragma clang fp contract(off)
   return acc + q * k;
 }
@@ -120,7 +115,7 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
     const int32_t *__restrict__ base, const int32_t *__restrict__ ibase,
     const int32_t *__restrict__ pbase, const int32_t *__restrict__ lists,
     int32_t *__restrict__ amax, float *__restrict__ dk_idx, float *__restrict__ part,
-    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int num_seqs, int G, int K,
+    const int64_t *__restrict__ cu_q, const int64_t *__restrict__ cu_kv, int G, int K,
     int64_t total_q, int nb_max, int64_t nbuckets) {
   constexpr bool BF = sizeof(T) == 2;    // bf16: arg-max on the matrix cores
   using QE = std::conditional_t<BF, uint16_t, float>;  // element of the staged queries
@@ -297,24 +292,11 @@ __global__ __launch_bounds__(256) void ib_item_kernel(
             if (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              float kv[4];
-              if constexpr (sizeof(T) == 2) {
-                const u32x2 w2 = *reinterpret_cast<const u32x2 *>(kr[u] + c);
-                kv[0] = bf16_lo(w2.x);
-                kv[1] = bf16_hi(w2.x);
-                kv[2] = bf16_lo(w2.y);
-                kv[3] = bf16_hi(w2.y);
-              } else {
-                const float4 w4 = *reinterpret_cast<const float4 *>(kr[u] + c);
-                kv[0] = w4.x;
-                kv[1] = w4.y;
-                kv[2] = w4.z;
-                kv[3] = w4.w;
-              }
-              d[u] = dot_step(d[u], qr[c], kv[0], T());
-              d[u] = dot_step(d[u], qr[c + 1], kv[1], T());
-              d[u] = dot_step(d[u], qr[c + 2], kv[2], T());
-              d[u] = dot_step(d[u], qr[c + 3], kv[3], T());
+              const float4 kv = *reinterpret_cast<const float4 *>(kr[u] + c);
+              d[u] = dot_step(d[u], qr[c], kv.x);
+              d[u] = dot_step(d[u], qr[c + 1], kv.y);
+              d[u] = dot_step(d[u], qr[c + 2], kv.z);
+              d[u] = dot_step(d[u], qr[c + 3], kv.w);
             }
           }
 #pragma unroll
@@ -401,7 +383,7 @@ __global__ __launch_bounds__(256) void ib_reduce_kernel(const int32_t *__restric
                                                         const float *__restrict__ part,
                                                         float *__restrict__ dk_idx,
                                                         const int64_t *__restrict__ cu_kv, int G,
-                                                        int num_seqs, int nb_max, int64_t nbk_g) {
+                                                        int nb_max, int64_t nbk_g) {
   const int64_t gb = blockIdx.x;
   const int32_t nit = ibase[gb + 1] - ibase[gb];
   if (nit <= 1) return;
@@ -427,7 +409,8 @@ __global__ __launch_bounds__(256) void ib_dq_kernel(const T *__restrict__ k_idx,
                                                     const float *__restrict__ grad,
                                                     const int32_t *__restrict__ amax,
                                                     float *__restrict__ dq_idx, int G, int K,
-                                                    int64_t total_q, int64_t total_kv) {
+                                                    int64_t total_q,
+                                                    [[maybe_unused]] int64_t total_kv) {
   constexpr int CPL = (DI + 63) / 64;  // channels per lane
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_q) return;
@@ -497,10 +480,10 @@ hipError_t launch_ib(const Dims &p, const T *q_idx, const T *k_idx, const int32_
   profile_mark(s);
   hipLaunchKernelGGL((ib_item_kernel<T, DI, BS>), dim3((unsigned)w.max_items), dim3(256), 0, s,
                      q_idx, k_idx, grad, w.base, w.ibase, w.pbase, w.lists, w.amax, dk_idx, w.part,
-                     p.cu_q, p.cu_kv, p.num_seqs, p.G, p.top_k, p.total_q, p.nb_max, ncol);
+                     p.cu_q, p.cu_kv, p.G, p.top_k, p.total_q, p.nb_max, ncol);
   profile_mark(s);
   hipLaunchKernelGGL((ib_reduce_kernel<DI, BS>), dim3((unsigned)ncol), dim3(256), 0, s, w.ibase,
-                     w.pbase, w.part, dk_idx, p.cu_kv, p.G, p.num_seqs, p.nb_max, w.nbk_g);
+                     w.pbase, w.part, dk_idx, p.cu_kv, p.G, p.nb_max, w.nbk_g);
   profile_mark(s);
   hipLaunchKernelGGL((ib_dq_kernel<T, DI>), dim3((unsigned)((p.total_q + 3) / 4), p.G), dim3(256),
                      0, s, k_idx, grad, w.amax, dq_idx, p.G, p.top_k, p.total_q, p.total_kv);

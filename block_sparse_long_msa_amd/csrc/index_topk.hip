@@ -46,10 +46,6 @@ __device__ __forceinline__ void dma16_fused(const uint16_t *src, uint8_t *lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
 }
 
-__device__ __forceinline__ uint64_t cand_key(float score, int j) {
-  return ((uint64_t)ordered_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-}
-
 // Inserts candidate (nk, nj) into a lane's list of the CAPP best candidates,
 // held in registers in descending key order (key = ordered score, 0 = empty).
 // Blocks arrive in ascending order, so a new candidate ranks after every

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
                                                    int32_t *__restrict__ block_idx,
                                                    const int64_t *__restrict__ cu_q,
                                                    const int64_t *__restrict__ cu_kv,
-                                                   int num_seqs, int G, int64_t total_q,
+                                                   int num_seqs, int64_t total_q,
                                                    int nb_max, int BS, int K) {
   __shared__ uint32_t cand_key_all[4][kCandCap];
   __shared__ int32_t cand_idx_all[4][kCandCap];
@@ -404,7 +404,7 @@ template <int NCH>
 hipError_t launch_nch(const Dims &p, const float *scores, int32_t *block_idx, hipStream_t s) {
   dim3 grid((unsigned)((p.total_q + 3) / 4), p.G);
   hipLaunchKernelGGL((topk_kernel<NCH>), grid, dim3(256), 0, s, scores, block_idx, p.cu_q,
-                     p.cu_kv, p.num_seqs, p.G, p.total_q, p.nb_max, p.B, p.top_k);
+                     p.cu_kv, p.num_seqs, p.total_q, p.nb_max, p.B, p.top_k);
   profile_mark(s);
   return hipGetLastError();
 }
