@@ -132,25 +132,26 @@ def test_index_backward_exact_ties_small_integers(dtype):
     _log(f"  {dtype}: worst error / tolerance {worst:.3g}; slots with a tied maximum: {ties}")
 
 
-def test_index_backward_prefill_32k():
-    """The 32K prefill workload after the GPU's own index scores and Top-k:
+@pytest.mark.parametrize("name", ["prefill-32k", "prefill-128k", "chunked-prefill-1m"])
+def test_index_backward_full_size(name):
+    """The long-context workloads after the GPU's own index scores and Top-k:
     the identity above on every group, and dq_idx on sampled rows against
     the oracle (their kept lists are the oracle's own selection)."""
-    w = W.WORKLOADS["prefill-32k"]
-    _log("prefill-32k: generating")
+    w = W.WORKLOADS[name]
+    _log(f"{name}: generating")
     inp = W.make_inputs(w, device=DEV, seed=0, with_attention=False)
     G, di, B, k = w.num_kv_groups, w.idx_dim, w.block_size, w.top_k
     prob = C.problem_for(inp, w.num_q_heads, G, w.head_dim, di, B, k, w.dtype)
     lq, lkv = inp["len_q"][0], inp["len_kv"][0]
     rng = np.random.default_rng(5)
     rows = np.array(sorted(set([0, 1, 127, 128, lq - 1] + rng.integers(0, lq, 16).tolist())))
-    _log(f"prefill-32k: oracle selection on {len(rows)} rows")
+    _log(f"{name}: oracle selection on {len(rows)} rows")
     pos = O.query_positions(lq, lkv)[rows]
     q_idx_h, k_idx_h = inp["q_idx"].cpu(), inp["k_idx"].cpu()
     S_ref = O.block_scores(q_idx_h[torch.from_numpy(rows)], k_idx_h, pos, B)
     idx_ref = O.select_blocks(S_ref, pos, B, k)
     grad = W.random_slot_grads(7, G, lq, k)
-    _log("prefill-32k: GPU")
+    _log(f"{name}: GPU")
     scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
     idx = msa.topk_select(prob, scores)
     gr = torch.from_numpy(rows).to(DEV)
@@ -165,9 +166,9 @@ def test_index_backward_prefill_32k():
     gsum = (grad.to(DEV).double() * sc * (idx >= 0)).sum(dim=(1, 2))
     for g in range(G):
         scale = float((grad.to(DEV).double().abs() * sc.abs() * (idx >= 0))[g].sum())
-        for name, v in (("<dq, q>", lhs_all[g]), ("<dk, k>", rhs_all[g])):
+        for what, v in (("<dq, q>", lhs_all[g]), ("<dk, k>", rhs_all[g])):
             rel = abs(float(v) - float(gsum[g])) / scale
-            assert rel < 1e-5, f"group {g}: {name} off by {rel:.3g} of sum |grad * score|"
+            assert rel < 1e-5, f"{name}, group {g}: {what} off by {rel:.3g} of sum |grad * score|"
     # sampled rows against the oracle, outside the rounding tie band
     dq_r, _ = O.index_backward(q_idx_h[torch.from_numpy(rows)], k_idx_h, idx_ref, pos, B,
                                grad[:, torch.from_numpy(rows), :].numpy())

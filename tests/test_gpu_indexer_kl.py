@@ -95,25 +95,26 @@ def _sample(lq, planted, seed):
     return np.array(sorted(r for r in rows if 0 <= r < lq))
 
 
-def test_mass_and_kl_prefill_32k():
-    """The 32K prefill workload in the benchmark's launch configuration:
+@pytest.mark.parametrize("name", ["prefill-32k", "prefill-128k", "chunked-prefill-1m"])
+def test_mass_and_kl_full_size(name):
+    """The long-context workloads in the benchmark's launch configuration:
     properties on every row, the oracle on sampled rows (whose kept lists
     are the oracle's own selection, fed to the GPU)."""
-    w = W.WORKLOADS["prefill-32k"]
-    _log("prefill-32k: generating")
+    w = W.WORKLOADS[name]
+    _log(f"{name}: generating")
     inp = W.make_inputs(w, device=DEV, seed=0)
     H, G, d, di, B, k = w.num_q_heads, w.num_kv_groups, w.head_dim, w.idx_dim, w.block_size, w.top_k
     prob = C.problem_for(inp, H, G, d, di, B, k, w.dtype)
     lq, lkv = inp["len_q"][0], inp["len_kv"][0]
     rows = _sample(lq, inp["planted_q"][0], 3)
-    _log(f"prefill-32k: oracle on {len(rows)} rows")
+    _log(f"{name}: oracle on {len(rows)} rows")
     scale = 1.0 / math.sqrt(d)
     q_h, k_h, v_h = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu()
     r = O.msa_forward(q_h, k_h, v_h, inp["q_idx"].cpu(), inp["k_idx"].cpu(), lq, lkv, B, k, scale,
                       rows=rows)
     m_ref = O.block_mass(q_h[torch.from_numpy(rows)], k_h, r["block_idx"], r["pos"], B, scale)
     kl_ref, g_ref = O.indexer_kl(r["scores"], r["block_idx"], m_ref)
-    _log("prefill-32k: GPU")
+    _log(f"{name}: GPU")
     scores = msa.index_score(prob, inp["q_idx"], inp["k_idx"])
     idx = msa.topk_select(prob, scores)
     gr = torch.from_numpy(rows).to(DEV)
