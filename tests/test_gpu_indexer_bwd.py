@@ -177,6 +177,29 @@ def test_index_backward_full_size(name):
     worst = _close(dq[gr].cpu().numpy()[row_ok], dq_r[row_ok], "dq_idx")
     _log(f"  sampled dq_idx worst error / tolerance {worst:.3g}; "
          f"{int((~row_ok).sum())} of {row_ok.size} (row, group) pairs in the tie band")
+    # dk_idx on every key of two blocks (a late one, and the one of group G-1
+    # the most rows keep): the oracle over every (row, slot) that names the
+    # block, which are the only slots whose gradient reaches its keys
+    idx_h, grad_h = idx.cpu().numpy(), grad.numpy()
+    pos_all = O.query_positions(lq, lkv)
+    nb = (lkv + B - 1) // B
+    last = idx_h[G - 1]
+    popular = int(np.argmax(np.bincount(last[last >= 0], minlength=nb)))
+    for g, jb in ((0, nb - 2), (G - 1, popular)):
+        hit = idx_h[g] == jb                       # [lq, k]
+        keep = np.nonzero(hit.any(axis=1))[0]
+        _log(f"{name}: oracle dk_idx of block {jb}, group {g} ({keep.size} rows keep it)")
+        sub = np.full((G, keep.size, k), -1, dtype=np.int32)
+        sub[g] = np.where(hit[keep], jb, -1)
+        gsub = np.zeros((G, keep.size, k))
+        gsub[g] = np.where(hit[keep], grad_h[g][keep], 0.0)
+        tk = torch.from_numpy(keep)
+        _, dk_r = O.index_backward(q_idx_h[tk], k_idx_h, sub, pos_all[keep], B, gsub)
+        _, band = C.argmax_tie_band(q_idx_h[tk], k_idx_h, sub, pos_all[keep], B, di)
+        ks = np.array([s for s in range(jb * B, min((jb + 1) * B, lkv)) if s not in band[g]])
+        e = _close(dk[torch.from_numpy(ks).to(DEV), g].cpu().numpy(), dk_r[ks, g],
+                   f"dk_idx block {jb} group {g}")
+        _log(f"  dk_idx worst error / tolerance {e:.3g}; {B - ks.size} keys in the tie band")
 
 
 def test_training_calls_with_more_queries_than_keys():
