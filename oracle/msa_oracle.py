@@ -427,6 +427,9 @@ def sparse_attention_backward(q, k, v, block_idx, pos, block_size: int, scale: f
                 continue
             kg = _gather_f64(k, keys, g)
             vg = _gather_f64(v, keys, g)
+            # the keys are distinct and ascending (so are the kept blocks):
+            # runs of consecutive positions, each added to dk and dv as a slice
+            cut = np.concatenate(([0], np.flatnonzero(np.diff(keys) != 1) + 1, [keys.size]))
             for h in range(g * hpg, (g + 1) * hpg):
                 z = scale * (kg @ qf[t, h])
                 a = np.exp(z - z.max())
@@ -435,8 +438,12 @@ def sparse_attention_backward(q, k, v, block_idx, pos, block_size: int, scale: f
                 dp = vg @ do[t, h]
                 dz = a * (dp - do[t, h] @ out)
                 dq[t, h] += scale * (dz @ kg)
-                np.add.at(dk[:, g, :], keys, scale * np.outer(dz, qf[t, h]))
-                np.add.at(dv[:, g, :], keys, np.outer(a, do[t, h]))
+                gk = scale * np.outer(dz, qf[t, h])
+                gv = np.outer(a, do[t, h])
+                for r0, r1 in zip(cut[:-1], cut[1:]):
+                    s0 = int(keys[r0])
+                    dk[s0:s0 + r1 - r0, g, :] += gk[r0:r1]
+                    dv[s0:s0 + r1 - r0, g, :] += gv[r0:r1]
     return dq, dk, dv
 
 

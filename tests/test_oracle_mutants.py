@@ -74,8 +74,8 @@ MUTANTS = [
      "dz = a * (dp - do[t, h] @ out)",
      "dz = a * dp"),
     ("dk without the softmax scale",
-     "np.add.at(dk[:, g, :], keys, scale * np.outer(dz, qf[t, h]))",
-     "np.add.at(dk[:, g, :], keys, np.outer(dz, qf[t, h]))"),
+     "gk = scale * np.outer(dz, qf[t, h])",
+     "gk = np.outer(dz, qf[t, h])"),
     ("coarse keys summed instead of averaged",
      "return k[:nfull * span].reshape(nfull, span, G, di).mean(axis=1)",
      "return k[:nfull * span].reshape(nfull, span, G, di).sum(axis=1)"),
