@@ -220,8 +220,9 @@ def test_attn_backward_more_queries_than_keys():
 @pytest.mark.parametrize("name", ["prefill-32k", "prefill-128k", "chunked-prefill-1m"])
 def test_attn_backward_full_size(name):
     """The long-context workloads with the default (single-pass) workspace:
-    sampled dq rows, every key of block NB-2 of group 0 and of block NB-1 of
-    group G-1 (all rows that keep them), and the two identities over every
+    sampled dq rows, every key of block NB-2 of group 0, of block NB-1 of
+    group G-1 and of a block of group 1 kept by more rows than one work item
+    holds (all rows that keep them), and the two identities over every
     key."""
     w = W.WORKLOADS[name]
     _log(f"{name}: generating")
@@ -241,21 +242,30 @@ def test_attn_backward_full_size(name):
     rq, _, _ = O.sparse_attention_backward(q_h[tr], k_h, v_h, bi_h[:, rows, :], pos_all[rows], B,
                                            scale, do_h[tr])
     e_q = _close(dq[torch.from_numpy(rows).to(DEV)].cpu().numpy(), rq, "dq rows")
-    # two late blocks: all rows that keep them
+    # two late blocks, and a block whose list the matrix-core backward splits
+    # into two work items (4096 (query, head) rows each) summed in item
+    # order: all rows that keep them, on their group alone (its heads, keys
+    # and values; the other groups do not reach these keys)
     nb = (L + B - 1) // B
+    hpg = H // G
+    per_item = 4096 // hpg
+    counts = np.bincount(bi_h[1][bi_h[1] >= 0], minlength=nb)
+    two = np.nonzero(counts > per_item)[0]
+    blocks = [(0, nb - 2), (G - 1, nb - 1)]
+    if two.size:
+        blocks.append((1, int(two[np.argmin(counts[two])])))
     e_k = e_v = 0.0
-    for g, jb in ((0, nb - 2), (G - 1, nb - 1)):
+    for g, jb in blocks:
         keep = np.nonzero((bi_h[g] == jb).any(axis=1))[0]
         _log(f"{name}: oracle block {jb} of group {g} ({keep.size} rows keep it)")
         assert keep.size > 0
-        sub = np.full((G, keep.size, k), -1, dtype=bi_h.dtype)
-        sub[g] = bi_h[g, keep]
-        tk = torch.from_numpy(keep)
-        _, rk, rv = O.sparse_attention_backward(q_h[tk], k_h, v_h, sub, pos_all[keep], B, scale,
-                                                do_h[tk])
+        tk, hs = torch.from_numpy(keep), slice(g * hpg, (g + 1) * hpg)
+        _, rk, rv = O.sparse_attention_backward(q_h[tk][:, hs], k_h[:, g:g + 1], v_h[:, g:g + 1],
+                                                bi_h[g:g + 1, keep], pos_all[keep], B, scale,
+                                                do_h[tk][:, hs])
         ks = slice(jb * B, min((jb + 1) * B, L))
-        e_k = max(e_k, _close(dk[ks, g].cpu().numpy(), rk[ks, g], f"dk block {jb} group {g}"))
-        e_v = max(e_v, _close(dv[ks, g].cpu().numpy(), rv[ks, g], f"dv block {jb} group {g}"))
+        e_k = max(e_k, _close(dk[ks, g].cpu().numpy(), rk[ks, 0], f"dk block {jb} group {g}"))
+        e_v = max(e_v, _close(dv[ks, g].cpu().numpy(), rv[ks, 0], f"dv block {jb} group {g}"))
         del rk, rv
     # identities over every key
     dk64, dv64 = dk.double(), dv.double()
