@@ -200,6 +200,14 @@ class Problem:
                  len_kv: Sequence[int], num_q_heads: int, num_kv_groups: int, head_dim: int,
                  idx_dim: int, block_size: int, top_k: int, dtype: str = "bf16",
                  softmax_scale: Optional[float] = None, schedule: str = "auto"):
+        if len(len_q) != len(len_kv):
+            raise ValueError(f"len_q and len_kv need one entry per sequence "
+                             f"(got {len(len_q)} and {len(len_kv)})")
+        for name, cu in (("cu_q", cu_q), ("cu_kv", cu_kv)):
+            if (cu.dtype != torch.int64 or not cu.is_cuda or not cu.is_contiguous()
+                    or cu.numel() != len(len_q) + 1):
+                raise ValueError(f"{name}: expected {len(len_q) + 1} contiguous int64 offsets on "
+                                 f"the GPU, got {cu.dtype} {tuple(cu.shape)} on {cu.device}")
         self.cu_q, self.cu_kv = cu_q, cu_kv            # keep alive
         self.len_q, self.len_kv = list(len_q), list(len_kv)
         self.H, self.G, self.d, self.d_idx = num_q_heads, num_kv_groups, head_dim, idx_dim

@@ -465,3 +465,16 @@ def test_index_topk_validation():
     big = _prob(max_kv_len=128 * 8192, total_kv=128 * 8192, top_k=64)
     assert lib.msa_index_topk_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
     assert n.value == 2 * 256 * 16 * 64 * 8
+
+
+def test_binding_problem_rejects_bad_offset_tensors():
+    """The binding's Problem checks its offset tensors before anything reads
+    them: host tensors, the wrong dtype or count, and lengths that disagree."""
+    import torch
+    cpu = torch.tensor([0, 100], dtype=torch.int64)
+    with pytest.raises(ValueError, match="cu_q"):
+        msa.Problem(cpu, cpu, [100], [100], 4, 1, 64, 32, 64, 4)
+    with pytest.raises(ValueError, match="one entry per sequence"):
+        msa.Problem(cpu, cpu, [100], [100, 5], 4, 1, 64, 32, 64, 4)
+    with pytest.raises(ValueError, match="cu_q"):
+        msa.Problem(cpu.to(torch.int32), cpu, [100], [100], 4, 1, 64, 32, 64, 4)
