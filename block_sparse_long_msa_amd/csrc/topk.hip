@@ -237,7 +237,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         const uint32_t tau = kth_largest_in<CC>(ck, need, lb, wave_max_key<CC>(ck));
         emit_selected<CC>(ck, [&](int c) { return ci[c]; }, tau, need, dst);
       };
-      if (n_cand <= 128) finish(std::integral_constant<int, 2>());
+      if (n_cand <= 64) finish(std::integral_constant<int, 1>());
+      else if (n_cand <= 128) finish(std::integral_constant<int, 2>());
       else if (n_cand <= 256) finish(std::integral_constant<int, 4>());
       else finish(std::integral_constant<int, kCandCap / 64>());
       if (lane == 0) dst[need] = J;
@@ -346,7 +347,8 @@ __global__ __launch_bounds__(256) void topk_long_kernel(const float *__restrict_
       const uint32_t tau = kth_largest_in<CC>(ck, need, lb, wave_max_key<CC>(ck));
       emit_selected<CC>(ck, [&](int c) { return ci[c]; }, tau, need, dst);
     };
-    if (total <= 128) finish(std::integral_constant<int, 2>());
+    if (total <= 64) finish(std::integral_constant<int, 1>());
+    else if (total <= 128) finish(std::integral_constant<int, 2>());
     else if (total <= 256) finish(std::integral_constant<int, 4>());
     else finish(std::integral_constant<int, kCandCap / 64>());
     if (lane == 0) dst[need] = J;
